@@ -1,0 +1,336 @@
+"""CPU oracle for the SchNet continuous-filter-convolution energy/force path.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain reference that the
+GPU library is checked against.  Only the test-suite, the package smoke check
+and the benchmark's CPU-baseline leg may import or call it; the product path
+never does.  It shares no code with the HIP library.
+
+Sources (cited by page title and section):
+  [FS-sum]  "FlashSchNet: Fast and Accurate Coarse-Grained Neural Network
+            Molecular Dynamics" -- paper-curation summary page, sections
+            "Motivation", "Achievement", "How".
+  [FS-abs]  OpenAlex record of the same paper (arXiv 2602.13140), abstract,
+            techniques (1)-(4).
+  [GMX]     "Making Room for AI: Multi-GPU MD with Deep Potentials in GROMACS"
+            slide summary, section 1 (a machine-learned potential needs a full
+            neighbour list).
+
+The pages name the stages (distance, Gaussian radial basis, cosine envelope,
+filter network, neighbour gather times filter, CSR segment reduce, forces
+from the backward pass, batched MD replicas) but print no equations.  Where
+they are silent this oracle takes the plain SchNet reading; every such choice
+is listed in the design notes of the repository:
+  * embedding h0 = Emb[type]; I interaction blocks, each
+        x = h @ W_in                       (no bias)
+        a = rbf(d) @ A1 + b1 ; phi = ssp(a) @ A2 + b2 ; W = fc(d) * phi
+        y_i = sum over directed edges (i, j) of W_ij * x_j
+        h <- h + ssp(y @ Wo1 + bo1) @ Wo2 + bo2
+    readout  eps_i = ssp(h_i @ R1 + c1) . R2 + c2 ;  E_b = sum of eps_i over replica b
+  * ssp(x) = ln(exp(x)/2 + 1/2) (shifted softplus)
+  * Gaussian centres mu_k = lo + k (hi - lo)/(K - 1), width exp(-gamma (d - mu_k)^2)
+  * cosine envelope fc(d) = (cos(pi d / rc) + 1)/2 for d < rc, else 0,
+    applied to the filter output
+  * full directed neighbour list: j in N(i) iff same replica, j != i and the
+    float32 squared distance is strictly below the float32 r_list^2.
+
+Parity status: every function here is pinned by the CPU tests (finite
+differences, invariances, closed forms, a 50-digit scalar evaluation of tiny
+cases, a library k-d tree for the neighbour sets, Verlet special cases); the
+accuracy of the 16-bit filter weights against trained weights is not
+(no trained weights exist here) -- that one claim is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+LN2 = float(np.log(2.0))
+
+
+# ---------------------------------------------------------------------------
+# 1. neighbour list  [FS-sum How: flash message passing (cutoff masking),
+#    flash aggregation (CSR)]; full list [GMX section 1]
+# ---------------------------------------------------------------------------
+
+def neighbors_bruteforce(pos, replica_ptr, r_list, box=None, row_block=2048):
+    """All ordered pairs (i, j), i != j, of one replica with r2_ij < r_list^2.
+
+    The predicate is evaluated in float32, one rounding per operation, in the
+    order dx = x_j - x_i ; (periodic) dx = dx - L * rint(dx * invL) with
+    invL = float32(1/L) ; r2 = (dx*dx + dy*dy) + dz*dz ; r2 < rl2 with
+    rl2 = float32(r_list) * float32(r_list).  Minimum image for a periodic
+    orthorhombic box.
+
+    Returns CSR (row_ptr [N+1], col [E] ascending within each row) and
+    rev [E], the position of the reverse edge (j, i) in row j.
+    Rows are processed in blocks only to bound memory.
+    """
+    p = np.asarray(pos, dtype=np.float32)
+    rp = np.asarray(replica_ptr, dtype=np.int64)
+    n = p.shape[0]
+    rl = np.float32(r_list)
+    rl2 = np.float32(rl * rl)
+    if box is not None:
+        L = np.asarray(box, dtype=np.float32)
+        invL = np.array([np.float32(1.0 / np.float64(v)) for v in L], dtype=np.float32)
+    counts = np.zeros(n, dtype=np.int64)
+    cols = []
+    for b in range(len(rp) - 1):
+        s, e = int(rp[b]), int(rp[b + 1])
+        P = p[s:e]
+        for r0 in range(s, e, row_block):
+            r1 = min(e, r0 + row_block)
+            Q = p[r0:r1]
+            d = []
+            for c in range(3):
+                dc = P[None, :, c] - Q[:, None, c]           # x_j - x_i, float32
+                if box is not None:
+                    dc = dc - L[c] * np.rint(dc * invL[c])
+                d.append(dc)
+            r2 = (d[0] * d[0] + d[1] * d[1]) + d[2] * d[2]
+            assert r2.dtype == np.float32
+            mask = r2 < rl2
+            idx = np.arange(r0, r1)
+            mask[idx - r0, idx - s] = False                  # no self pairs
+            for k in range(r1 - r0):
+                js = np.flatnonzero(mask[k]) + s
+                counts[r0 + k] = len(js)
+                cols.append(js)
+    row_ptr = np.zeros(n + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col = np.concatenate(cols) if cols else np.zeros(0, np.int64)
+    row = np.repeat(np.arange(n), counts)
+    # edges are in (row, col) order, so key = row*n + col is ascending and the
+    # reverse edge (col, row) is found by binary search on the same keys
+    key = row * n + col
+    rkey = col * n + row
+    rev = np.searchsorted(key, rkey)
+    if len(col) and (np.any(rev >= len(col)) or np.any(key[np.minimum(rev, len(col) - 1)] != rkey)):
+        raise AssertionError("neighbour list not symmetric")
+    return row_ptr.astype(np.int32), col.astype(np.int32), rev.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# 2. radial functions  [FS-sum How: flash radial basis; FS-abs (1)]
+# ---------------------------------------------------------------------------
+
+def cosine_envelope(d, rc):
+    """fc(d) = (cos(pi d/rc) + 1)/2 inside the cutoff, 0 outside; and dfc/dd."""
+    d = np.asarray(d, dtype=np.float64)
+    inside = d < rc
+    fc = np.where(inside, 0.5 * (np.cos(np.pi * d / rc) + 1.0), 0.0)
+    dfc = np.where(inside, -0.5 * np.pi / rc * np.sin(np.pi * d / rc), 0.0)
+    return fc, dfc
+
+
+def gaussian_centres(K, lo, hi):
+    return lo + np.arange(K, dtype=np.float64) * ((hi - lo) / (K - 1))
+
+
+def gaussian_rbf(d, K, lo, hi, gamma):
+    """e_k(d) = exp(-gamma (d - mu_k)^2) and de_k/dd, shapes [E, K]."""
+    d = np.asarray(d, dtype=np.float64)[:, None]
+    diff = d - gaussian_centres(K, lo, hi)[None, :]
+    e = np.exp(-gamma * diff * diff)
+    return e, -2.0 * gamma * diff * e
+
+
+def ssp(x):
+    """Shifted softplus ln(exp(x)/2 + 1/2), evaluated without overflow."""
+    return np.logaddexp(x, 0.0) - LN2
+
+
+def sigmoid(x):
+    """Derivative of ssp: 1/(1 + exp(-x))."""
+    return 0.5 * (1.0 + np.tanh(0.5 * x))
+
+
+# ---------------------------------------------------------------------------
+# 3. geometry of the directed edges
+# ---------------------------------------------------------------------------
+
+def edge_geometry(pos, row_ptr, col, box=None):
+    """d_e = |r_j - r_i| and u_e = (r_j - r_i)/d_e for every directed edge, fp64.
+
+    Minimum image for a periodic box.
+    """
+    r = np.asarray(pos, dtype=np.float64)
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    col = np.asarray(col, dtype=np.int64)
+    i = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+    delta = r[col] - r[i]
+    if box is not None:
+        L = np.asarray(box, dtype=np.float64)
+        delta = delta - L * np.rint(delta / L)
+    d = np.sqrt((delta * delta).sum(axis=1))
+    if np.any(d == 0.0):
+        raise ValueError("coincident atoms on an edge")
+    return i, col, d, delta / d[:, None]
+
+
+def _f64(params):
+    out = {k: np.asarray(v, dtype=np.float64) for k, v in params.items() if k != "interactions"}
+    out["interactions"] = [{k: np.asarray(v, dtype=np.float64) for k, v in blk.items()}
+                           for blk in params["interactions"]]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# 4. energy and forces  [FS-sum How: flash message passing, flash aggregation
+#    (forward and backward); FS-abs (2), (3)]
+# ---------------------------------------------------------------------------
+
+def energy_forces(params, hyper, types, pos, replica_ptr, csr, box=None, return_intermediates=False):
+    """Per-replica energies E_b and forces F = -dE/dr, all in fp64.
+
+    params: named weights (float32 arrays are promoted to fp64).
+    hyper:  n_rbf, cutoff, rbf_lo, rbf_hi, rbf_gamma.
+    csr:    (row_ptr, col, rev) -- only row_ptr and col are used; the edge
+            set is taken as given (the full directed list).
+
+    Forward, then the analytic gradient written out by the chain rule.  The
+    CFConv is a plain scatter over the directed edges, y_i += W_e * x_j, and
+    its adjoint is the transposed scatter, g_x_j += W_e * g_y_i.
+    """
+    P = _f64(params)
+    K = int(hyper["n_rbf"])
+    rc = float(hyper["cutoff"])
+    lo, hi, gamma = float(hyper["rbf_lo"]), float(hyper["rbf_hi"]), float(hyper["rbf_gamma"])
+    row_ptr, col = csr[0], csr[1]
+    n = len(row_ptr) - 1
+    ei, ej, d, u = edge_geometry(pos, row_ptr, col, box)
+    fc, dfc = cosine_envelope(d, rc)
+    e, de = gaussian_rbf(d, K, lo, hi, gamma)
+
+    h = P["emb"][np.asarray(types, dtype=np.int64)].copy()
+    saved = []
+    for blk in P["interactions"]:
+        x = h @ blk["W_in"]
+        a = e @ blk["A1"] + blk["b1"]
+        phi = ssp(a) @ blk["A2"] + blk["b2"]
+        W = fc[:, None] * phi
+        y = np.zeros_like(x)
+        np.add.at(y, ei, W * x[ej])
+        o = y @ blk["Wo1"] + blk["bo1"]
+        h = h + ssp(o) @ blk["Wo2"] + blk["bo2"]
+        saved.append((x, a, phi, W, y, o))
+    q = h @ P["R1"] + P["c1"]
+    eps = ssp(q) @ P["R2"] + P["c2"]
+    rp = np.asarray(replica_ptr, dtype=np.int64)
+    energy = np.array([eps[rp[b]:rp[b + 1]].sum() for b in range(len(rp) - 1)])
+
+    # backward: dE_b/dh_i for i in replica b (replicas are independent)
+    g_h = (sigmoid(q) * P["R2"][None, :]) @ P["R1"].T
+    s = np.zeros(len(d))                          # dE/dd_e accumulated over blocks
+    for blk, (x, a, phi, W, y, o) in zip(reversed(P["interactions"]), reversed(saved)):
+        g_o = (g_h @ blk["Wo2"].T) * sigmoid(o)
+        g_y = g_o @ blk["Wo1"].T
+        g_x = np.zeros_like(x)
+        np.add.at(g_x, ej, W * g_y[ei])
+        g_W = g_y[ei] * x[ej]
+        g_fc = (g_W * phi).sum(axis=1)
+        g_phi = fc[:, None] * g_W
+        g_a = (g_phi @ blk["A2"].T) * sigmoid(a)
+        g_e = g_a @ blk["A1"].T
+        s += (g_e * de).sum(axis=1) + g_fc * dfc
+        g_h = g_h + g_x @ blk["W_in"].T
+
+    # d(d_e)/dr_i = -u_e, d(d_e)/dr_j = +u_e
+    grad = np.zeros((n, 3))
+    np.add.at(grad, ei, -s[:, None] * u)
+    np.add.at(grad, ej, s[:, None] * u)
+    forces = -grad
+    if return_intermediates:
+        inter = {"d": d, "u": u, "fc": fc, "s": s, "eps": eps, "q": q,
+                 "blocks": [dict(zip(("x", "a", "phi", "W", "y", "o"), sv)) for sv in saved]}
+        return energy, forces, inter
+    return energy, forces
+
+
+def energy_only(params, hyper, types, pos, replica_ptr, csr, box=None):
+    """Forward pass only (used by the finite-difference pins)."""
+    return energy_forces(params, hyper, types, pos, replica_ptr, csr, box)[0]
+
+
+def cfconv(W, x, row_ptr, col):
+    """y_i = sum_{e in row i} W_e * x_{col(e)} -- the CSR segment reduce."""
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    i = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+    y = np.zeros((len(row_ptr) - 1, x.shape[1]))
+    np.add.at(y, i, np.asarray(W, np.float64) * np.asarray(x, np.float64)[np.asarray(col)])
+    return y
+
+
+# ---------------------------------------------------------------------------
+# 5. channel-wise 16-bit filter weights  [FS-sum How: channel-wise 16-bit
+#    quantization; FS-abs (4)]
+# ---------------------------------------------------------------------------
+
+def quantize_per_out_channel(w):
+    """Symmetric int16 quantisation of w[in, out], one scale per output column.
+
+    s_f = float32(max_k |w_kf| / 32767) (ratio in fp64);
+    q_kf = clip(round-half-even(w_kf / s_f), -32767, 32767) (ratio in fp64);
+    q = 0 where s_f = 0.  Returns (q int16, s float32).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.abs(w).max(axis=0).astype(np.float64)
+    s = (amax / 32767.0).astype(np.float32)
+    s64 = s.astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(s64 > 0, w.astype(np.float64) / np.where(s64 > 0, s64, 1.0), 0.0)
+    q = np.clip(np.rint(r), -32767, 32767).astype(np.int16)
+    return q, s
+
+
+def dequantize(q, s):
+    """float32(q) * s in float32."""
+    return (q.astype(np.float32) * np.asarray(s, np.float32)[None, :]).astype(np.float32)
+
+
+def dequantized_params(params):
+    """Copy of params with every A1, A2 replaced by its int16 round trip."""
+    out = dict(params)
+    out["interactions"] = []
+    for blk in params["interactions"]:
+        b = dict(blk)
+        for key in ("A1", "A2"):
+            b[key] = dequantize(*quantize_per_out_channel(blk[key]))
+        out["interactions"].append(b)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# 6. velocity Verlet over independent replicas  [FS-sum Achievement 1:
+#    aggregate throughput of parallel replicas]
+# ---------------------------------------------------------------------------
+
+def kinetic_energy(vel, inv_mass, replica_ptr, force_to_accel):
+    """Per-replica 0.5 m v^2 in energy units: m v^2 / (2 c)."""
+    v2 = (np.asarray(vel, np.float64) ** 2).sum(axis=1) / np.asarray(inv_mass, np.float64)
+    rp = np.asarray(replica_ptr, dtype=np.int64)
+    return np.array([0.5 * v2[rp[b]:rp[b + 1]].sum() / force_to_accel for b in range(len(rp) - 1)])
+
+
+def verlet(params, hyper, types, pos, vel, inv_mass, replica_ptr, dt, force_to_accel, n_steps,
+           r_list, box=None):
+    """n velocity-Verlet steps, neighbour list rebuilt at every step.
+
+    a = c F / m ; v += dt/2 a ; r += dt v ; rebuild ; F(r) ; v += dt/2 a.
+    Positions and velocities are carried in fp64.  Returns the final
+    (pos, vel, forces) and per-step potential and kinetic energies [n, B].
+    """
+    r = np.asarray(pos, np.float64).copy()
+    v = np.asarray(vel, np.float64).copy()
+    im = np.asarray(inv_mass, np.float64)[:, None]
+    csr = neighbors_bruteforce(r.astype(np.float32), replica_ptr, r_list, box)
+    _, f = energy_forces(params, hyper, types, r, replica_ptr, csr, box)
+    epot, ekin = [], []
+    for _ in range(n_steps):
+        v += 0.5 * dt * force_to_accel * f * im
+        r += dt * v
+        csr = neighbors_bruteforce(r.astype(np.float32), replica_ptr, r_list, box)
+        en, f = energy_forces(params, hyper, types, r, replica_ptr, csr, box)
+        v += 0.5 * dt * force_to_accel * f * im
+        epot.append(en)
+        ekin.append(kinetic_energy(v, inv_mass, replica_ptr, force_to_accel))
+    return r, v, f, np.array(epot), np.array(ekin)
