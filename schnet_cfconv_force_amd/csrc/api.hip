@@ -1,0 +1,420 @@
+// C-ABI entry points of libsn.so: argument checks, workspace carving, the
+// energy/force pipeline, the velocity-Verlet driver and per-kernel timing.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "sn_internal.h"
+
+namespace sn {
+
+// --------------------------------------------------------------- timing
+
+namespace {
+struct ProfRecord {
+    int cls;
+    hipEvent_t start, stop;
+};
+bool g_prof_on = false;
+std::mutex g_prof_mu;
+std::vector<ProfRecord> g_prof_open;   // started, not yet stopped (stack per class)
+std::vector<ProfRecord> g_prof_done;
+const char *kClassNames[K_NUM_CLASSES] = {
+    "nb_grid", "nb_bin", "nb_scan", "nb_count", "nb_fill", "nb_rev", "pairs", "embed", "dense",
+    "filter_fwd", "cfconv", "readout", "energy", "filter_bwd", "forces", "verlet", "kinetic"};
+}  // namespace
+
+void prof_begin(int cls, hipStream_t s) {
+    if (!g_prof_on) return;
+    ProfRecord r{cls, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
+    hipEventRecord(r.start, s);
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof_open.push_back(r);
+}
+
+void prof_end(int cls, hipStream_t s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    for (size_t k = g_prof_open.size(); k-- > 0;) {
+        if (g_prof_open[k].cls == cls) {
+            ProfRecord r = g_prof_open[k];
+            g_prof_open.erase(g_prof_open.begin() + k);
+            hipEventRecord(r.stop, s);
+            g_prof_done.push_back(r);
+            return;
+        }
+    }
+}
+
+// --------------------------------------------------------------- layout
+
+EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t base) {
+    EfLayout L;
+    const int64_t N = sys.n_atoms, P = E / 2, F = m.n_features, I = m.n_interactions, H = F / 2;
+    const int64_t B = sys.n_replicas;
+    size_t o = base;
+    auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+    L.up_first = take(4 * N);
+    L.up_ptr = take(4 * (N + 1));
+    L.edge_pair = take(4 * E);
+    L.pair_ij = take(8 * P);
+    L.pgeo = take(16 * P);
+    L.pfc = take(4 * P);
+    L.phi = take(4 * I * P * F);
+    L.x = take(4 * I * N * F);
+    L.o = take(4 * I * N * F);
+    L.gy = take(4 * I * N * F);
+    L.h = take(4 * N * F);
+    L.y = take(4 * N * F);
+    L.gh = take(4 * N * F);
+    L.gt = take(4 * N * F);
+    L.q = take(4 * N * H);
+    L.gq = take(4 * N * H);
+    L.eps = take(4 * N + 4 * B);   // eps[N], then an energy scratch [B]
+    L.S = take(4 * P);
+    L.total = o;
+    return L;
+}
+
+namespace {
+
+__global__ void clear_status_kernel(int *status) {
+    if (threadIdx.x < kStatusSlots) status[threadIdx.x] = 0;
+}
+
+sn_status clear_status(void *ws, hipStream_t s) {
+    clear_status_kernel<<<1, 64, 0, s>>>(reinterpret_cast<int *>(ws));
+    return launch_status();
+}
+
+// v += dt/2 c F / m ; if drift: r += dt v
+__global__ void verlet_kernel(int N, float *pos, float *vel, const float *forces, const float *inv_mass, float half_dt_c,
+                              float dt, int drift) {
+    int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= 3 * N) return;
+    int i = idx / 3;
+    float v = vel[idx] + half_dt_c * forces[idx] * inv_mass[i];
+    vel[idx] = v;
+    if (drift) pos[idx] += dt * v;
+}
+
+__global__ __launch_bounds__(256) void kinetic_kernel(const int32_t *rptr, const float *vel, const float *inv_mass,
+                                                      float inv_2c, float *out) {
+    __shared__ double red[256];
+    const int b = blockIdx.x;
+    double s = 0.0;
+    for (int i = rptr[b] + threadIdx.x; i < rptr[b + 1]; i += 256) {
+        double v2 = (double)vel[3 * i] * vel[3 * i] + (double)vel[3 * i + 1] * vel[3 * i + 1] +
+                    (double)vel[3 * i + 2] * vel[3 * i + 2];
+        s += v2 / (double)inv_mass[i];
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[b] = (float)(red[0] * inv_2c);
+}
+
+sn_status check_system(const sn_system *sys) {
+    if (!sys || sys->n_atoms < 0 || sys->n_replicas < 1 || !sys->replica_ptr) return SN_ERR_INVALID;
+    if (sys->n_atoms > 0 && !sys->types) return SN_ERR_INVALID;
+    if (sys->periodic)
+        for (int c = 0; c < 3; ++c)
+            if (!(sys->box[c] > 0.0f) || !std::isfinite(sys->box[c])) return SN_ERR_BOX;
+    return SN_OK;
+}
+
+sn_status check_model(const sn_model *m) {
+    if (!m || !m->params) return SN_ERR_INVALID;
+    const int F = m->n_features;
+    if (F != 32 && F != 64 && F != 128) return SN_ERR_INVALID;
+    if (m->n_rbf < 2 || m->n_rbf > 64 || m->n_interactions < 1 || m->n_interactions > 16 || m->n_types < 1)
+        return SN_ERR_INVALID;
+    if (!(m->cutoff > 0.0f) || !(m->rbf_gamma > 0.0f) || !std::isfinite(m->rbf_lo) || !std::isfinite(m->rbf_hi))
+        return SN_ERR_INVALID;
+    if (m->filter_format != 0 && m->filter_format != 1) return SN_ERR_INVALID;
+    if (m->filter_format == 1 && (!m->qweights || !m->qscales)) return SN_ERR_INVALID;
+    return SN_OK;
+}
+
+sn_status check_ws(void *ws, size_t ws_bytes, size_t need) {
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) != 0 || ws_bytes < need) return SN_ERR_WORKSPACE;
+    return SN_OK;
+}
+
+size_t bytes_needed(const sn_model *m, const sn_system *s, int64_t E) {
+    size_t nb = nb_layout(*s, 256).total;
+    size_t ef = m ? ef_layout(*m, *s, E, 256).total : 256;
+    return std::max(nb, ef);
+}
+
+// The pipeline itself; arguments already checked, status not cleared.
+sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const float *pos, const int32_t *row_ptr,
+                             const int32_t *col, const int32_t *rev, int64_t E, float *energy, float *forces,
+                             char *ws, hipStream_t s) {
+    const int N = sys.n_atoms, B = sys.n_replicas, F = m.n_features, I = m.n_interactions, H = F / 2;
+    const int64_t P = E / 2;
+    int *status = reinterpret_cast<int *>(ws);
+    const EfLayout L = ef_layout(m, sys, E, 256);
+    float *eps = reinterpret_cast<float *>(ws + L.eps);
+    if (N == 0) return replica_sum(B, sys.replica_ptr, eps, energy, s);
+
+    int64_t off[9 * 16 + 6];
+    sn_param_offsets(m.n_types, I, F, m.n_rbf, off, (int32_t)(sizeof(off) / sizeof(off[0])));
+    const float *prm = m.params;
+    auto blk = [&](int t, int k) { return prm + off[1 + 9 * t + k]; };
+    enum { W_IN = 0, A1, B1, A2, B2, WO1, BO1, WO2, BO2 };
+    const float *R1 = prm + off[1 + 9 * I], *c1 = prm + off[2 + 9 * I], *R2 = prm + off[3 + 9 * I],
+                *c2 = prm + off[4 + 9 * I];
+
+    auto F32 = [&](size_t o) { return reinterpret_cast<float *>(ws + o); };
+    const int32_t *edge_pair = reinterpret_cast<const int32_t *>(ws + L.edge_pair);
+    const int2 *pair_ij = reinterpret_cast<const int2 *>(ws + L.pair_ij);
+    const float4 *pgeo = reinterpret_cast<const float4 *>(ws + L.pgeo);
+    const float *pfc = F32(L.pfc);
+    float *h = F32(L.h), *y = F32(L.y), *gh = F32(L.gh), *gt = F32(L.gt), *q = F32(L.q), *gq = F32(L.gq);
+    float *S = F32(L.S);
+    const int64_t NF = (int64_t)N * F, PF = P * F;
+    auto phi_t = [&](int t) { return F32(L.phi) + PF * t; };
+    auto x_t = [&](int t) { return F32(L.x) + NF * t; };
+    auto o_t = [&](int t) { return F32(L.o) + NF * t; };
+    auto gy_t = [&](int t) { return F32(L.gy) + NF * t; };
+
+    SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, E, m.cutoff, ws, L, status, s));
+    SN_TRY(embed(N, F, m.n_types, sys.types, prm + off[0], h, status, s));
+    for (int t = 0; t < I; ++t) {
+        SN_TRY(dense(N, F, F, h, blk(t, W_IN), 0, nullptr, PRO_NONE, EPI_STORE, nullptr, x_t(t), s));
+        SN_TRY(filter_forward(m, t, pgeo, P, phi_t(t), s));
+        SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, s));
+        SN_TRY(dense(N, F, F, y, blk(t, WO1), 0, blk(t, BO1), PRO_NONE, EPI_STORE, nullptr, o_t(t), s));
+        SN_TRY(dense(N, F, F, o_t(t), blk(t, WO2), 0, blk(t, BO2), PRO_SSP, EPI_ACCUM, nullptr, h, s));
+    }
+    SN_TRY(dense(N, F, H, h, R1, 0, c1, PRO_NONE, EPI_STORE, nullptr, q, s));
+    SN_TRY(readout(N, H, q, R2, c2, eps, gq, s));
+    SN_TRY(replica_sum(B, sys.replica_ptr, eps, energy, s));
+    // backward: dE/dh, then through the interactions in reverse
+    SN_TRY(dense(N, H, F, gq, R1, 1, nullptr, PRO_NONE, EPI_STORE, nullptr, gh, s));
+    for (int t = I - 1; t >= 0; --t) {
+        SN_TRY(dense(N, F, F, gh, blk(t, WO2), 1, nullptr, PRO_NONE, EPI_SIGMUL, o_t(t), gt, s));
+        SN_TRY(dense(N, F, F, gt, blk(t, WO1), 1, nullptr, PRO_NONE, EPI_STORE, nullptr, gy_t(t), s));
+        SN_TRY(filter_backward(m, t, pgeo, pair_ij, P, phi_t(t), x_t(t), gy_t(t), S, t != I - 1, s));
+        if (t > 0) {   // dE/dh below the first block is not needed for forces
+            SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, s));
+            SN_TRY(dense(N, F, F, y, blk(t, W_IN), 1, nullptr, PRO_NONE, EPI_ACCUM, nullptr, gh, s));
+        }
+    }
+    return forces_rows(N, row_ptr, col, edge_pair, pgeo, S, forces, status, s);
+}
+
+}  // namespace
+}  // namespace sn
+
+using namespace sn;
+
+extern "C" {
+
+int32_t sn_version(void) { return 1; }
+
+const char *sn_status_string(sn_status st) {
+    switch (st) {
+        case SN_OK: return "ok";
+        case SN_ERR_INVALID: return "invalid argument";
+        case SN_ERR_CAPACITY: return "edge capacity too small";
+        case SN_ERR_BOX: return "periodic box too small for the neighbour cutoff";
+        case SN_ERR_HIP: return "HIP runtime error";
+        case SN_ERR_NONFINITE: return "non-finite value";
+        case SN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case SN_ERR_ROW: return "neighbour row longer than SN_MAX_ROW";
+        default: return "unknown status";
+    }
+}
+
+int32_t sn_param_offsets(int32_t T, int32_t I, int32_t F, int32_t K, int64_t *offsets, int32_t max_offsets) {
+    if (T < 1 || I < 1 || F < 2 || (F % 2) || K < 1) return -1;
+    const int32_t n = 9 * I + 6;
+    const int64_t H = F / 2;
+    std::vector<int64_t> tab;
+    tab.reserve(n);
+    int64_t o = 0;
+    tab.push_back(o); o += (int64_t)T * F;                          // Emb
+    for (int t = 0; t < I; ++t) {
+        const int64_t sizes[9] = {(int64_t)F * F, (int64_t)K * F, F, (int64_t)F * F, F,
+                                  (int64_t)F * F, F, (int64_t)F * F, F};
+        for (int k = 0; k < 9; ++k) { tab.push_back(o); o += sizes[k]; }
+    }
+    tab.push_back(o); o += F * H;     // R1
+    tab.push_back(o); o += H;         // c1
+    tab.push_back(o); o += H;         // R2
+    tab.push_back(o); o += 1;         // c2
+    tab.push_back(o);                 // total
+    if (offsets)
+        for (int32_t k = 0; k < std::min(n, max_offsets); ++k) offsets[k] = tab[k];
+    return n;
+}
+
+int64_t sn_param_count(int32_t T, int32_t I, int32_t F, int32_t K) {
+    int64_t off[9 * 16 + 6];
+    if (I > 16) {
+        std::vector<int64_t> v(9 * I + 6);
+        if (sn_param_offsets(T, I, F, K, v.data(), (int32_t)v.size()) < 0) return -1;
+        return v.back();
+    }
+    int32_t n = sn_param_offsets(T, I, F, K, off, 9 * 16 + 6);
+    return n < 0 ? -1 : off[n - 1];
+}
+
+sn_status sn_quantize_filter_weights(int32_t T, int32_t I, int32_t F, int32_t K, const float *params_host,
+                                     int16_t *q_host, float *s_host) {
+    if (!params_host || !q_host || !s_host) return SN_ERR_INVALID;
+    std::vector<int64_t> off(9 * (size_t)std::max(I, 1) + 6);
+    if (sn_param_offsets(T, I, F, K, off.data(), (int32_t)off.size()) < 0) return SN_ERR_INVALID;
+    for (int t = 0; t < I; ++t) {
+        for (int which = 0; which < 2; ++which) {
+            const int rows = which == 0 ? K : F;
+            const float *w = params_host + off[1 + 9 * t + (which == 0 ? 1 : 3)];
+            int16_t *q = q_host + ((int64_t)K * F + (int64_t)F * F) * t + (which == 0 ? 0 : (int64_t)K * F);
+            float *sc = s_host + (int64_t)2 * F * t + (which == 0 ? 0 : F);
+            for (int f = 0; f < F; ++f) {
+                float amax = 0.0f;
+                for (int k = 0; k < rows; ++k) amax = std::max(amax, std::fabs(w[(int64_t)k * F + f]));
+                const float s = (float)((double)amax / 32767.0);
+                sc[f] = s;
+                for (int k = 0; k < rows; ++k) {
+                    double r = s > 0.0f ? (double)w[(int64_t)k * F + f] / (double)s : 0.0;
+                    r = std::nearbyint(r);   // default rounding mode: to nearest, ties to even
+                    r = std::min(32767.0, std::max(-32767.0, r));
+                    q[(int64_t)k * F + f] = (int16_t)r;
+                }
+            }
+        }
+    }
+    return SN_OK;
+}
+
+size_t sn_workspace_bytes(const sn_model *model, const sn_system *sys, int64_t max_edges) {
+    if (!sys || max_edges < 0) return 0;
+    return bytes_needed(model, sys, max_edges);
+}
+
+sn_status sn_build_csr_neighbors(const sn_system *sys, const float *pos, float r_list, int32_t *row_ptr,
+                                 int32_t *col_idx, int32_t *rev_idx, int64_t capacity, int64_t *n_edges, void *ws,
+                                 size_t ws_bytes, void *stream) {
+    SN_TRY(check_system(sys));
+    if (!n_edges || !row_ptr || capacity < 0 || !(r_list > 0.0f) || !std::isfinite(r_list)) return SN_ERR_INVALID;
+    if (sys->n_atoms > 0 && (!pos || (capacity > 0 && (!col_idx || !rev_idx)))) return SN_ERR_INVALID;
+    SN_TRY(check_ws(ws, ws_bytes, nb_layout(*sys, 256).total));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    SN_TRY(clear_status(ws, s));
+    return nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, n_edges, reinterpret_cast<char *>(ws), s);
+}
+
+sn_status sn_energy_forces(const sn_model *model, const sn_system *sys, const float *pos, const int32_t *row_ptr,
+                           const int32_t *col_idx, const int32_t *rev_idx, int64_t n_edges, float *energy,
+                           float *forces, void *ws, size_t ws_bytes, void *stream) {
+    SN_TRY(check_system(sys));
+    SN_TRY(check_model(model));
+    if (n_edges < 0 || (n_edges & 1) || n_edges > INT32_MAX || !energy) return SN_ERR_INVALID;
+    if (sys->n_atoms > 0 && (!pos || !row_ptr || !forces)) return SN_ERR_INVALID;
+    if (n_edges > 0 && (!col_idx || !rev_idx)) return SN_ERR_INVALID;
+    SN_TRY(check_ws(ws, ws_bytes, bytes_needed(model, sys, n_edges)));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    SN_TRY(clear_status(ws, s));
+    return energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, n_edges, energy, forces,
+                              reinterpret_cast<char *>(ws), s);
+}
+
+sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos, float *vel, float *forces,
+                         const float *inv_mass, float dt, float force_to_accel, int32_t n_steps, float r_list,
+                         int32_t *row_ptr, int32_t *col_idx, int32_t *rev_idx, int64_t capacity, int64_t *n_edges,
+                         float *epot_log, float *ekin_log, int32_t *n_steps_done, void *ws, size_t ws_bytes,
+                         void *stream) {
+    if (n_steps_done) *n_steps_done = 0;
+    SN_TRY(check_system(sys));
+    SN_TRY(check_model(model));
+    if (n_steps < 0 || !n_edges || !row_ptr || !(r_list > 0.0f) || !std::isfinite(dt) ||
+        !std::isfinite(force_to_accel))
+        return SN_ERR_INVALID;
+    const int N = sys->n_atoms, B = sys->n_replicas;
+    if (N > 0 && (!pos || !vel || !forces || !inv_mass || !col_idx || !rev_idx)) return SN_ERR_INVALID;
+    SN_TRY(check_ws(ws, ws_bytes, bytes_needed(model, sys, capacity)));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char *w = reinterpret_cast<char *>(ws);
+    SN_TRY(clear_status(ws, s));
+    const float half = 0.5f * dt * force_to_accel;
+    for (int32_t step = 0; step < n_steps; ++step) {
+        if (N > 0) {
+            ProfScope ps(K_VERLET, s);
+            verlet_kernel<<<(3 * N + 255) / 256, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, 1);
+            SN_TRY(launch_status());
+        }
+        int64_t E = 0;
+        sn_status st = nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, &E, w, s);
+        *n_edges = E;
+        if (st != SN_OK) return st;   // includes a non-finite force flagged in the previous step
+        float *eout = epot_log ? epot_log + (int64_t)step * B
+                               : reinterpret_cast<float *>(w + ef_layout(*model, *sys, E, 256).eps) + N;
+        SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, E, eout, forces, w, s));
+        if (N > 0) {
+            ProfScope ps(K_VERLET, s);
+            verlet_kernel<<<(3 * N + 255) / 256, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, 0);
+            SN_TRY(launch_status());
+        }
+        if (ekin_log) {
+            ProfScope ps(K_KINETIC, s);
+            kinetic_kernel<<<B, 256, 0, s>>>(sys->replica_ptr, vel, inv_mass, 0.5f / force_to_accel,
+                                             ekin_log + (int64_t)step * B);
+            SN_TRY(launch_status());
+        }
+        if (n_steps_done) *n_steps_done = step + 1;
+    }
+    sn_status st = sn_read_status(ws, stream);
+    if (st != SN_OK && n_steps_done && *n_steps_done > 0) *n_steps_done -= 1;
+    return st;
+}
+
+sn_status sn_filter_forward(const sn_model *model, int32_t interaction, const float *d, int64_t n, float *phi,
+                            void *stream) {
+    SN_TRY(check_model(model));
+    if (interaction < 0 || interaction >= model->n_interactions || n < 0 || (n > 0 && (!d || !phi)))
+        return SN_ERR_INVALID;
+    return filter_forward_plain(*model, interaction, d, n, phi, reinterpret_cast<hipStream_t>(stream));
+}
+
+sn_status sn_read_status(void *ws, void *stream) {
+    if (!ws) return SN_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int v = 0;
+    SN_HIP(hipMemcpyAsync(&v, ws, sizeof(int), hipMemcpyDeviceToHost, s));
+    SN_HIP(hipStreamSynchronize(s));
+    SN_TRY(clear_status(ws, s));
+    return v;
+}
+
+void sn_profile_enable(int32_t on) { g_prof_on = on != 0; }
+
+int32_t sn_profile_classes(void) { return K_NUM_CLASSES; }
+
+const char *sn_profile_name(int32_t id) { return (id >= 0 && id < K_NUM_CLASSES) ? kClassNames[id] : ""; }
+
+sn_status sn_profile_collect(double *ms_total, int64_t *launches) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    sn_status st = SN_OK;
+    for (auto &r : g_prof_done) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+            st = SN_ERR_HIP;
+        if (ms_total) ms_total[r.cls] += ms;
+        if (launches) launches[r.cls] += 1;
+        hipEventDestroy(r.start);
+        hipEventDestroy(r.stop);
+    }
+    g_prof_done.clear();
+    return st;
+}
+
+}  // extern "C"

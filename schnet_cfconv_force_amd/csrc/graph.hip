@@ -1,0 +1,240 @@
+// Edge-side kernels: pair setup, the CFConv CSR segment reduce, and force
+// assembly.
+//
+// Pair indexing.  The filter W(d) depends only on the distance, so the two
+// directed edges (i, j) and (j, i) share one filter row.  Each unordered
+// pair {i < j} gets an index p, numbered in CSR order of the "upper" edges
+// (j > i); edge_pair[e] maps every directed edge to its pair, so the filter
+// network runs once per pair (half the directed edges) and the CFConv reads
+// the shared row from both ends.
+//
+// CFConv ("How", flash message passing and flash aggregation -- FlashSchNet
+// summary page): y_i = sum_{e in row i} fc(d_e) phi_{p(e)} (.) x_{col(e)}.
+// One group of F/4 lanes owns a row and accumulates it in registers, so no
+// atomics are needed and the summation order is fixed.  Because W is the
+// same for (i, j) and (j, i), the same kernel applied to g_y gives the
+// input gradient of the backward pass.
+//
+// Forces: F_i = sum_{e in row i} S_{p(e)} u_e, with u_e = (r_j - r_i)/d and
+// S_p = dE/dd_p -- again one lane group per row, no atomics.
+#include "sn_internal.h"
+
+namespace sn {
+
+namespace {
+
+constexpr float kPi = 3.14159265358979323846f;
+
+// thread per row: first upper edge and number of upper edges
+__global__ void pair_count_kernel(int N, const int32_t *row_ptr, const int32_t *col, int32_t *up_first,
+                                  int32_t *up_cnt) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N) return;
+    int lo = row_ptr[i], hi = row_ptr[i + 1];
+    const int end = hi;
+    while (lo < hi) {                     // first e with col[e] > i
+        int mid = (lo + hi) >> 1;
+        if (col[mid] > i) hi = mid; else lo = mid + 1;
+    }
+    up_first[i] = lo;
+    up_cnt[i] = end - lo;
+}
+
+struct PairArgs {
+    int N;
+    const int32_t *row_ptr, *col, *rev, *up_first, *up_ptr;
+    const float *pos;
+    int32_t *edge_pair;
+    int2 *pair_ij;
+    float4 *pgeo;
+    float *pfc;
+    int periodic;
+    float L[3], invL[3];
+    float cutoff;
+    int64_t E, P;
+    int *status;
+};
+
+// one wavefront per row: pair index of every edge; geometry of upper edges
+__global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
+    const int lane = threadIdx.x % 64;
+    const int i = blockIdx.x * 4 + threadIdx.x / 64;
+    if (i >= a.N) return;
+    const int e0 = a.row_ptr[i], e1 = a.row_ptr[i + 1];
+    const int uf = a.up_first[i], up = a.up_ptr[i];
+    const float xi = a.pos[3 * i], yi = a.pos[3 * i + 1], zi = a.pos[3 * i + 2];
+    for (int e = e0 + lane; e < e1; e += 64) {
+        const int j = a.col[e];
+        if (j < 0 || j >= a.N || j == i) {
+            flag_status(a.status, SN_ERR_INVALID);
+            a.edge_pair[e] = 0;
+            continue;
+        }
+        if (j > i) {
+            const int p = up + (e - uf);
+            if (p >= a.P) {                       // more upper edges than E/2: not symmetric
+                flag_status(a.status, SN_ERR_INVALID);
+                a.edge_pair[e] = 0;
+                continue;
+            }
+            a.edge_pair[e] = p;
+            a.pair_ij[p] = make_int2(i, j);
+            float dx = a.pos[3 * j] - xi, dy = a.pos[3 * j + 1] - yi, dz = a.pos[3 * j + 2] - zi;
+            if (a.periodic) {
+                dx -= a.L[0] * rintf(dx * a.invL[0]);
+                dy -= a.L[1] * rintf(dy * a.invL[1]);
+                dz -= a.L[2] * rintf(dz * a.invL[2]);
+            }
+            const float d = sqrtf(dx * dx + dy * dy + dz * dz);
+            const float inv = 1.0f / d;
+            a.pgeo[p] = make_float4(dx * inv, dy * inv, dz * inv, d);
+            float fc = 0.0f;
+            if (d < a.cutoff) {
+                // (cos(pi d/rc) + 1)/2 written as cos^2(pi d/(2 rc)): no cancellation near rc
+                float c = cosf(0.5f * kPi * d / a.cutoff);
+                fc = c * c;
+            }
+            a.pfc[p] = fc;
+        } else {
+            // the reverse edge (j, i) is an upper edge of row j
+            const int r = a.rev[e];
+            const int p = (r >= a.up_first[j] && r < a.row_ptr[j + 1] && a.col[r] == i)
+                              ? a.up_ptr[j] + (r - a.up_first[j]) : -1;
+            if (p < 0 || p >= a.P) {
+                flag_status(a.status, SN_ERR_INVALID);
+                a.edge_pair[e] = 0;
+                continue;
+            }
+            a.edge_pair[e] = p;
+        }
+    }
+}
+
+__global__ void pair_check_kernel(const int32_t *up_ptr, int N, int64_t P, int *status) {
+    if (up_ptr[N] != P) flag_status(status, SN_ERR_INVALID);
+}
+
+// y_i = sum_{e in row i} pfc[p] * phi[p] (.) in[col(e)], LPR = F/4 lanes per row
+template <int F>
+__global__ __launch_bounds__(256) void cfconv_kernel(int N, const int32_t *row_ptr, const int32_t *col,
+                                                     const int32_t *edge_pair, const float *pfc,
+                                                     const float *phi, const float *in, float *out) {
+    constexpr int LPR = F / 4;
+    const int sub = threadIdx.x % LPR;
+    const int row = (blockIdx.x * 256 + threadIdx.x) / LPR;
+    if (row >= N) return;                      // whole lane group leaves together
+    const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int eb = e0; eb < e1; eb += LPR) {
+        const int k = eb + sub;
+        int cj = 0, cp = 0;
+        float cw = 0.0f;
+        if (k < e1) {
+            cj = col[k];
+            cp = edge_pair[k];
+            cw = pfc[cp];
+        }
+        const int n = min(LPR, e1 - eb);
+#pragma unroll 4
+        for (int t = 0; t < n; ++t) {
+            const int j = __shfl(cj, t, LPR);
+            const int p = __shfl(cp, t, LPR);
+            const float w = __shfl(cw, t, LPR);
+            const float4 f = *reinterpret_cast<const float4 *>(phi + (int64_t)p * F + 4 * sub);
+            const float4 x = *reinterpret_cast<const float4 *>(in + (int64_t)j * F + 4 * sub);
+            acc.x += w * f.x * x.x;
+            acc.y += w * f.y * x.y;
+            acc.z += w * f.z * x.z;
+            acc.w += w * f.w * x.w;
+        }
+    }
+    *reinterpret_cast<float4 *>(out + (int64_t)row * F + 4 * sub) = acc;
+}
+
+// F_i = sum_{e in row i} S[p(e)] * u_e, 16 lanes per row
+__global__ __launch_bounds__(256) void forces_kernel(int N, const int32_t *row_ptr, const int32_t *col,
+                                                     const int32_t *edge_pair, const float4 *pgeo, const float *S,
+                                                     float *forces, int *status) {
+    const int sub = threadIdx.x % 16;
+    const int i = (blockIdx.x * 256 + threadIdx.x) / 16;
+    if (i >= N) return;
+    const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
+    float fx = 0.f, fy = 0.f, fz = 0.f;
+    for (int e = e0 + sub; e < e1; e += 16) {
+        const int p = edge_pair[e];
+        const float4 g = pgeo[p];
+        const float s = (col[e] > i) ? S[p] : -S[p];
+        fx += s * g.x;
+        fy += s * g.y;
+        fz += s * g.z;
+    }
+    for (int o = 8; o > 0; o >>= 1) {
+        fx += __shfl_xor(fx, o, 16);
+        fy += __shfl_xor(fy, o, 16);
+        fz += __shfl_xor(fz, o, 16);
+    }
+    if (sub == 0) {
+        forces[3 * i] = fx;
+        forces[3 * i + 1] = fy;
+        forces[3 * i + 2] = fz;
+        if (!(isfinite(fx) && isfinite(fy) && isfinite(fz))) flag_status(status, SN_ERR_NONFINITE);
+    }
+}
+
+}  // namespace
+
+sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
+                      const int32_t *rev, int64_t E, float cutoff, char *ws, const EfLayout &L, int *status,
+                      hipStream_t s) {
+    const int N = sys.n_atoms;
+    ProfScope ps(K_PAIRS, s);
+    int32_t *up_first = reinterpret_cast<int32_t *>(ws + L.up_first);
+    int32_t *up_ptr = reinterpret_cast<int32_t *>(ws + L.up_ptr);
+    pair_count_kernel<<<(N + 255) / 256, 256, 0, s>>>(N, row_ptr, col, up_first, up_ptr);
+    SN_TRY(launch_status());
+    SN_TRY(scan_exclusive(up_ptr, up_ptr, N, nullptr, s));
+    pair_check_kernel<<<1, 1, 0, s>>>(up_ptr, N, E / 2, status);
+    SN_TRY(launch_status());
+    PairArgs a;
+    a.N = N;
+    a.row_ptr = row_ptr; a.col = col; a.rev = rev; a.up_first = up_first; a.up_ptr = up_ptr;
+    a.pos = pos;
+    a.edge_pair = reinterpret_cast<int32_t *>(ws + L.edge_pair);
+    a.pair_ij = reinterpret_cast<int2 *>(ws + L.pair_ij);
+    a.pgeo = reinterpret_cast<float4 *>(ws + L.pgeo);
+    a.pfc = reinterpret_cast<float *>(ws + L.pfc);
+    a.periodic = sys.periodic ? 1 : 0;
+    for (int c = 0; c < 3; ++c) {
+        a.L[c] = sys.periodic ? sys.box[c] : 1.0f;
+        a.invL[c] = (float)(1.0 / (double)a.L[c]);
+    }
+    a.cutoff = cutoff;
+    a.E = E;
+    a.P = E / 2;
+    a.status = status;
+    pair_fill_kernel<<<(N + 3) / 4, 256, 0, s>>>(a);
+    return launch_status();
+}
+
+sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
+                 const float *pfc, const float *phi, const float *in, float *out, hipStream_t s) {
+    ProfScope ps(K_CFCONV, s);
+    const int rows_per_block = 256 / (F / 4);
+    const int grid = (N + rows_per_block - 1) / rows_per_block;
+    switch (F) {
+        case 32: cfconv_kernel<32><<<grid, 256, 0, s>>>(N, row_ptr, col, edge_pair, pfc, phi, in, out); break;
+        case 64: cfconv_kernel<64><<<grid, 256, 0, s>>>(N, row_ptr, col, edge_pair, pfc, phi, in, out); break;
+        case 128: cfconv_kernel<128><<<grid, 256, 0, s>>>(N, row_ptr, col, edge_pair, pfc, phi, in, out); break;
+        default: return SN_ERR_INVALID;
+    }
+    return launch_status();
+}
+
+sn_status forces_rows(int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
+                      const float4 *pgeo, const float *S, float *forces, int *status, hipStream_t s) {
+    ProfScope ps(K_FORCES, s);
+    forces_kernel<<<(N + 15) / 16, 256, 0, s>>>(N, row_ptr, col, edge_pair, pgeo, S, forces, status);
+    return launch_status();
+}
+
+}  // namespace sn

@@ -1,0 +1,436 @@
+// Cell-list CSR neighbour builder.
+//
+// Produces the full, directed neighbour list ("How", flash message passing:
+// cutoff masking; flash aggregation: CSR -- FlashSchNet summary page) of
+// every replica: row i lists, in ascending order, every atom j != i of the
+// same replica with fp32 squared distance strictly below r_list^2.  The
+// predicate is evaluated with one rounding per operation and no fused
+// multiply-add, so the list is bit-for-bit reproducible from the positions.
+//
+// Pipeline (all on the caller's stream):
+//   grid    one block per replica: bounding box -> per-replica cell grid
+//   bin     one thread per atom: cell index, atomic cell histogram
+//   scan    cell histogram -> cell start offsets
+//   place   one thread per atom: atom copied into its cell's slot range
+//   count   one wavefront per atom: candidates of the 27 surrounding cells,
+//           exact predicate, row length
+//   scan    row lengths -> row_ptr, total read back by the host
+//   fill    one wavefront per atom: same candidates, survivors compacted
+//           into LDS by ballot, then rank-sorted into col_idx
+//   rev     one wavefront per row: binary search of i in row j
+// The order of atoms inside a cell depends on atomic arrival order; the
+// sorted rows do not, so the output is deterministic.
+#pragma clang fp contract(off)
+
+#include "sn_internal.h"
+
+namespace sn {
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kNbWaves = 4;   // wavefronts per block in the per-atom kernels
+
+struct PredParams {
+    float rl2;
+    float L[3];
+    float invL[3];
+    int periodic;
+};
+
+__global__ void fill_int_kernel(int *p, int v, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// One block per replica: atom -> replica map, bounding box, cell grid.
+__global__ __launch_bounds__(256) void grid_kernel(const float *pos, const int32_t *rptr, int periodic,
+                                                   PredParams pp, float cell_edge, CellGrid *grid,
+                                                   int *rep_of, int *status) {
+    __shared__ float red[6][256];
+    const int b = blockIdx.x;
+    const int s = rptr[b], e = rptr[b + 1];
+    float lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
+    bool bad = false;
+    for (int i = s + threadIdx.x; i < e; i += blockDim.x) {
+        rep_of[i] = b;
+        for (int c = 0; c < 3; ++c) {
+            float v = pos[3 * i + c];
+            if (!isfinite(v)) bad = true;
+            lo[c] = fminf(lo[c], v);
+            hi[c] = fmaxf(hi[c], v);
+        }
+    }
+    if (bad) flag_status(status, SN_ERR_NONFINITE);
+    for (int c = 0; c < 3; ++c) { red[c][threadIdx.x] = lo[c]; red[3 + c][threadIdx.x] = hi[c]; }
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w)
+            for (int c = 0; c < 3; ++c) {
+                red[c][threadIdx.x] = fminf(red[c][threadIdx.x], red[c][threadIdx.x + w]);
+                red[3 + c][threadIdx.x] = fmaxf(red[3 + c][threadIdx.x], red[3 + c][threadIdx.x + w]);
+            }
+        __syncthreads();
+    }
+    if (threadIdx.x != 0) return;
+    const long cap = 8L * (e - s) + 64;
+    CellGrid g;
+    if (periodic) {
+        int n[3];
+        for (int c = 0; c < 3; ++c) n[c] = (int)floorf(pp.L[c] / cell_edge);
+        while ((long)n[0] * n[1] * n[2] > cap) {           // coarser cells for sparse replicas
+            int c = (n[0] >= n[1] && n[0] >= n[2]) ? 0 : (n[1] >= n[2] ? 1 : 2);
+            if (n[c] <= 3) break;
+            n[c] = max(3, (n[c] * 4) / 5);
+        }
+        for (int c = 0; c < 3; ++c) {
+            g.lo[c] = 0.0f;
+            g.n[c] = n[c];
+            g.inv[c] = (float)n[c] / pp.L[c];
+        }
+    } else {
+        float ce = cell_edge;
+        int n[3];
+        for (;;) {
+            for (int c = 0; c < 3; ++c) {
+                float ext = (e > s && !bad) ? red[3 + c][0] - red[c][0] : 0.0f;
+                n[c] = (int)fminf(floorf(ext / ce) + 1.0f, 1048576.0f);
+            }
+            if ((double)n[0] * n[1] * n[2] <= (double)cap) break;
+            ce *= 1.25f;
+        }
+        for (int c = 0; c < 3; ++c) {
+            g.lo[c] = (e > s && !bad) ? red[c][0] : 0.0f;
+            g.n[c] = n[c];
+            g.inv[c] = 1.0f / ce;
+        }
+    }
+    g.offset = 8 * s + 64 * b;
+    grid[b] = g;
+}
+
+__device__ inline int cell_coord(float x, int c, const CellGrid &g, const PredParams &pp) {
+    float t;
+    if (pp.periodic) {
+        float xw = x - pp.L[c] * floorf(x * pp.invL[c]);
+        t = floorf(xw * g.inv[c]);
+    } else {
+        t = floorf((x - g.lo[c]) * g.inv[c]);
+    }
+    int k = (t != t) ? 0 : (int)fminf(fmaxf(t, 0.0f), (float)(g.n[c] - 1));
+    return k;
+}
+
+__global__ void bin_kernel(const float *pos, int n_atoms, const CellGrid *grid, const int *rep_of, PredParams pp,
+                           int *cell_of, int *cell_cnt) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_atoms) return;
+    const CellGrid g = grid[rep_of[i]];
+    int c0 = cell_coord(pos[3 * i + 0], 0, g, pp);
+    int c1 = cell_coord(pos[3 * i + 1], 1, g, pp);
+    int c2 = cell_coord(pos[3 * i + 2], 2, g, pp);
+    int cell = g.offset + (c2 * g.n[1] + c1) * g.n[0] + c0;
+    cell_of[i] = cell;
+    atomicAdd(&cell_cnt[cell], 1);
+}
+
+__global__ void place_kernel(const float *pos, int n_atoms, const int *cell_of, const int *cell_start,
+                             int *cell_fill, float4 *spos) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_atoms) return;
+    int cell = cell_of[i];
+    int slot = atomicAdd(&cell_fill[cell], 1);
+    spos[cell_start[cell] + slot] = make_float4(pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], __int_as_float(i));
+}
+
+// Order this wavefront's LDS writes before its later LDS reads (LDS requests
+// of one wavefront complete in issue order; this also stops the compiler
+// from moving the reads up).
+__device__ inline void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The exact fp32 neighbour predicate (contraction is off in this file).
+__device__ inline bool within(float xi, float yi, float zi, float4 q, const PredParams &pp) {
+    float dx = q.x - xi, dy = q.y - yi, dz = q.z - zi;
+    if (pp.periodic) {
+        dx = dx - pp.L[0] * rintf(dx * pp.invL[0]);
+        dy = dy - pp.L[1] * rintf(dy * pp.invL[1]);
+        dz = dz - pp.L[2] * rintf(dz * pp.invL[2]);
+    }
+    float r2 = (dx * dx + dy * dy) + dz * dz;
+    return r2 < pp.rl2;
+}
+
+// One wavefront per atom.  FILL = false: write the row length into cnt[i].
+// FILL = true: write the sorted row into col[row_ptr[i] ...].
+template <bool FILL>
+__global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos, int n_atoms, const CellGrid *grid,
+                                                               const int *rep_of, const int *cell_start,
+                                                               const float4 *spos, PredParams pp, int *cnt,
+                                                               const int32_t *row_ptr, int32_t *col, int *status) {
+    __shared__ int s_start[kNbWaves][28];
+    __shared__ int s_pre[kNbWaves][28];
+    __shared__ int s_buf[FILL ? kNbWaves : 1][FILL ? SN_MAX_ROW : 1];
+    const int wv = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int i = blockIdx.x * kNbWaves + wv;
+    if (i >= n_atoms) return;                       // whole wavefront exits together
+    const CellGrid g = grid[rep_of[i]];
+    const float xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+    const int ci[3] = {cell_coord(xi, 0, g, pp), cell_coord(yi, 1, g, pp), cell_coord(zi, 2, g, pp)};
+
+    int len = 0, start = 0;
+    if (lane < 27) {
+        int d[3] = {lane % 3 - 1, (lane / 3) % 3 - 1, lane / 9 - 1};
+        int cc[3];
+        bool ok = true;
+        for (int c = 0; c < 3; ++c) {
+            int v = ci[c] + d[c];
+            if (pp.periodic) {
+                v = (v + g.n[c]) % g.n[c];
+            } else if (v < 0 || v >= g.n[c]) {
+                ok = false;
+            }
+            cc[c] = v;
+        }
+        if (ok) {
+            int cell = g.offset + (cc[2] * g.n[1] + cc[1]) * g.n[0] + cc[0];
+            start = cell_start[cell];
+            len = cell_start[cell + 1] - start;
+        }
+    }
+    // inclusive prefix of the 27 lengths across the wavefront
+    int incl = len;
+    for (int o = 1; o < 32; o <<= 1) {
+        int t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    const int total = __shfl(incl, 26, kWave);
+    if (lane < 27) {
+        s_start[wv][lane] = start;
+        s_pre[wv][lane] = incl - len;
+    }
+    if (lane == 27) s_pre[wv][27] = total;
+    wave_sync();                    // only this wavefront touches its LDS slice
+
+    int base = 0;
+    for (int k0 = 0; k0 < total; k0 += kWave) {
+        const int k = k0 + lane;
+        bool pass = false;
+        int j = -1;
+        if (k < total) {
+            int lo = 0, hi = 26;                    // largest r with pre[r] <= k
+            while (lo < hi) {
+                int mid = (lo + hi + 1) >> 1;
+                if (s_pre[wv][mid] <= k) lo = mid; else hi = mid - 1;
+            }
+            float4 q = spos[s_start[wv][lo] + (k - s_pre[wv][lo])];
+            j = __float_as_int(q.w);
+            pass = (j != i) && within(xi, yi, zi, q, pp);
+        }
+        uint64_t mask = __ballot(pass);
+        if (FILL) {
+            int off = base + __popcll(mask & ((1ull << lane) - 1ull));
+            if (pass && off < SN_MAX_ROW) s_buf[FILL ? wv : 0][FILL ? off : 0] = j;
+        }
+        base += __popcll(mask);
+    }
+    if (!FILL) {
+        if (lane == 0) {
+            cnt[i] = base;
+            atomicMax(&status[kMaxRow], base);
+        }
+        return;
+    }
+    const int r0 = row_ptr[i];
+    const int n = row_ptr[i + 1] - r0;
+    if (n != base || n > SN_MAX_ROW) {
+        if (lane == 0) flag_status(status, SN_ERR_INVALID);
+        return;
+    }
+    wave_sync();
+    for (int k = lane; k < n; k += kWave) {
+        int v = s_buf[FILL ? wv : 0][FILL ? k : 0];
+        int rank = 0;
+        for (int m = 0; m < n; ++m) rank += (s_buf[FILL ? wv : 0][FILL ? m : 0] < v);
+        col[r0 + rank] = v;
+    }
+}
+
+// One wavefront per row: rev[e] = index of (j, i) in row j.
+__global__ __launch_bounds__(256) void rev_kernel(int n_atoms, const int32_t *row_ptr, const int32_t *col,
+                                                  int32_t *rev, int *status) {
+    const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int i = blockIdx.x * 4 + wv;
+    if (i >= n_atoms) return;
+    const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
+    for (int e = e0 + lane; e < e1; e += kWave) {
+        const int j = col[e];
+        int lo = row_ptr[j], hi = row_ptr[j + 1] - 1, found = -1;
+        while (lo <= hi) {
+            int mid = (lo + hi) >> 1;
+            int v = col[mid];
+            if (v == i) { found = mid; break; }
+            if (v < i) lo = mid + 1; else hi = mid - 1;
+        }
+        if (found < 0) flag_status(status, SN_ERR_INVALID);
+        rev[e] = found;
+    }
+}
+
+// Single-workgroup exclusive scan: out[k] = sum in[0..k), out[n] = total.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t *in, int32_t *out, int n, int32_t *total_slot) {
+    __shared__ int part[1024];
+    const int t = threadIdx.x;
+    const int chunk = (n + 1023) / 1024;
+    const int b = min(n, t * chunk), e = min(n, b + chunk);
+    int s = 0;
+    for (int k = b; k < e; ++k) s += in[k];
+    part[t] = s;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {           // Hillis-Steele inclusive scan of the partials
+        int v = (t >= o) ? part[t - o] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    int run = part[t] - s;
+    for (int k = b; k < e; ++k) {
+        int v = in[k];
+        out[k] = run;
+        run += v;
+    }
+    if (t == 1023) {
+        out[n] = part[1023];
+        if (total_slot) *total_slot = part[1023];
+    }
+}
+
+}  // namespace
+
+sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, hipStream_t s) {
+    ProfScope ps(K_NB_SCAN, s);
+    scan_kernel<<<1, 1024, 0, s>>>(in, out, n, total_slot);
+    return launch_status();
+}
+
+static sn_status fill_int(int *p, int v, int64_t n, hipStream_t s) {
+    if (n <= 0) return SN_OK;
+    fill_int_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, v, n);
+    return launch_status();
+}
+
+NbLayout nb_layout(const sn_system &sys, size_t base) {
+    NbLayout L;
+    const int64_t N = sys.n_atoms, B = sys.n_replicas;
+    L.n_cells = 8 * N + 64 * B;
+    size_t o = base;
+    L.grid = o;       o = align256(o + sizeof(CellGrid) * B);
+    L.rep_of = o;     o = align256(o + 4 * N);
+    L.cell_of = o;    o = align256(o + 4 * N);
+    L.cell_cnt = o;   o = align256(o + 4 * (L.n_cells + 1));
+    L.cell_start = o; o = align256(o + 4 * (L.n_cells + 1));
+    L.cell_fill = o;  o = align256(o + 4 * (L.n_cells + 1));
+    L.spos = o;       o = align256(o + 16 * N);
+    L.total = o;
+    return L;
+}
+
+// Host-pinned landing slot for the counters read back once per build.
+static int *pinned_counters() {
+    static int *p = nullptr;
+    if (!p) {
+        if (hipHostMalloc((void **)&p, 256, hipHostMallocDefault) != hipSuccess) p = nullptr;
+    }
+    return p;
+}
+
+sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
+                   int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s) {
+    const int N = sys.n_atoms, B = sys.n_replicas;
+    int *status = reinterpret_cast<int *>(ws);
+    PredParams pp;
+    pp.rl2 = r_list * r_list;
+    pp.periodic = sys.periodic ? 1 : 0;
+    for (int c = 0; c < 3; ++c) {
+        pp.L[c] = sys.periodic ? sys.box[c] : 1.0f;
+        pp.invL[c] = (float)(1.0 / (double)pp.L[c]);
+    }
+    // cell edge with a margin above r_list: rounding in the cell index can never
+    // hide a pair that passes the fp32 predicate
+    const float cell_edge = r_list * 1.001f + 0.01f;
+    if (sys.periodic)
+        for (int c = 0; c < 3; ++c)
+            if (!(sys.box[c] > 0.0f) || (int)floorf(sys.box[c] / cell_edge) < 3) return SN_ERR_BOX;
+
+    NbLayout L = nb_layout(sys, 256);
+    CellGrid *grid = reinterpret_cast<CellGrid *>(ws + L.grid);
+    int *rep_of = reinterpret_cast<int *>(ws + L.rep_of);
+    int *cell_of = reinterpret_cast<int *>(ws + L.cell_of);
+    int *cell_cnt = reinterpret_cast<int *>(ws + L.cell_cnt);
+    int *cell_start = reinterpret_cast<int *>(ws + L.cell_start);
+    int *cell_fill = reinterpret_cast<int *>(ws + L.cell_fill);
+    float4 *spos = reinterpret_cast<float4 *>(ws + L.spos);
+
+    // reset the counters but keep the status word: an error flagged by earlier
+    // work on this workspace (e.g. a non-finite force) is reported below
+    SN_TRY(fill_int(status + 1, 0, kStatusSlots - 1, s));
+    if (N == 0) {
+        SN_TRY(fill_int(row_ptr, 0, 1, s));
+        *n_edges = 0;
+        return SN_OK;
+    }
+    SN_TRY(fill_int(cell_cnt, 0, L.n_cells + 1, s));
+    SN_TRY(fill_int(cell_fill, 0, L.n_cells + 1, s));
+    {
+        ProfScope ps(K_NB_GRID, s);
+        grid_kernel<<<B, 256, 0, s>>>(pos, sys.replica_ptr, pp.periodic, pp, cell_edge, grid, rep_of, status);
+        SN_TRY(launch_status());
+    }
+    {
+        ProfScope ps(K_NB_BIN, s);
+        bin_kernel<<<(N + 255) / 256, 256, 0, s>>>(pos, N, grid, rep_of, pp, cell_of, cell_cnt);
+        SN_TRY(launch_status());
+    }
+    SN_TRY(scan_exclusive(cell_cnt, cell_start, (int)L.n_cells, nullptr, s));
+    {
+        ProfScope ps(K_NB_BIN, s);
+        place_kernel<<<(N + 255) / 256, 256, 0, s>>>(pos, N, cell_of, cell_start, cell_fill, spos);
+        SN_TRY(launch_status());
+    }
+    const int blocks = (N + kNbWaves - 1) / kNbWaves;
+    {
+        ProfScope ps(K_NB_COUNT, s);
+        rows_kernel<false><<<blocks, kWave * kNbWaves, 0, s>>>(pos, N, grid, rep_of, cell_start, spos, pp,
+                                                               row_ptr, nullptr, nullptr, status);
+        SN_TRY(launch_status());
+    }
+    SN_TRY(scan_exclusive(row_ptr, row_ptr, N, status + kEdgeTotal, s));
+    int *host = pinned_counters();
+    if (!host) return SN_ERR_HIP;
+    SN_HIP(hipMemcpyAsync(host, status, 4 * 4, hipMemcpyDeviceToHost, s));
+    SN_HIP(hipStreamSynchronize(s));
+    const int st = host[kStatusWord], max_row = host[kMaxRow];
+    const int64_t E = host[kEdgeTotal];
+    *n_edges = E;
+    if (st != 0) return st;
+    if (max_row > SN_MAX_ROW) return SN_ERR_ROW;
+    if (E > capacity) return SN_ERR_CAPACITY;
+    {
+        ProfScope ps(K_NB_FILL, s);
+        rows_kernel<true><<<blocks, kWave * kNbWaves, 0, s>>>(pos, N, grid, rep_of, cell_start, spos, pp, nullptr,
+                                                              row_ptr, col, status);
+        SN_TRY(launch_status());
+    }
+    {
+        ProfScope ps(K_NB_REV, s);
+        rev_kernel<<<(N + 3) / 4, 256, 0, s>>>(N, row_ptr, col, rev, status);
+        SN_TRY(launch_status());
+    }
+    return SN_OK;
+}
+
+}  // namespace sn

@@ -1,0 +1,124 @@
+// Internal declarations shared by the translation units of libsn.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/sn.h"
+
+namespace sn {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// --------------------------------------------------------------- status
+
+// Device status word slots (int32, in the first 256 bytes of the workspace).
+enum StatusSlot { kStatusWord = 0, kMaxRow = 1, kEdgeTotal = 2, kStatusSlots = 64 };
+
+#define SN_TRY(expr)                               \
+    do {                                           \
+        sn_status _st = (expr);                    \
+        if (_st != SN_OK) return _st;              \
+    } while (0)
+
+#define SN_HIP(expr)                               \
+    do {                                           \
+        if ((expr) != hipSuccess) return SN_ERR_HIP; \
+    } while (0)
+
+inline sn_status launch_status() {
+    return hipGetLastError() == hipSuccess ? SN_OK : SN_ERR_HIP;
+}
+
+// Record the first error code in the device status word.
+__device__ inline void flag_status(int *status, int code) { atomicCAS(status, 0, code); }
+
+// --------------------------------------------------------------- math
+
+// Shifted softplus ln(e^x/2 + 1/2) = max(x,0) + log1p(exp(-|x|)) - ln 2.
+__device__ inline float ssp(float x) {
+    return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))) - 0.69314718055994531f;
+}
+// Its derivative, the logistic sigmoid.
+__device__ inline float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// --------------------------------------------------------------- timing
+
+enum KernelClass {
+    K_NB_GRID = 0, K_NB_BIN, K_NB_SCAN, K_NB_COUNT, K_NB_FILL, K_NB_REV,
+    K_PAIRS, K_EMBED, K_DENSE, K_FILTER_FWD, K_CFCONV, K_READOUT, K_ENERGY,
+    K_FILTER_BWD, K_FORCES, K_VERLET, K_KINETIC, K_NUM_CLASSES
+};
+
+void prof_begin(int cls, hipStream_t s);
+void prof_end(int cls, hipStream_t s);
+
+struct ProfScope {
+    int cls; hipStream_t s;
+    ProfScope(int c, hipStream_t st) : cls(c), s(st) { prof_begin(c, st); }
+    ~ProfScope() { prof_end(cls, s); }
+};
+
+// --------------------------------------------------------------- workspace
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
+    size_t grid, rep_of, cell_of, cell_cnt, cell_start, cell_fill, spos, total;
+    int64_t n_cells;         // capacity of the cell table
+};
+
+struct EfLayout {            // energy/force scratch (offsets from ws base)
+    size_t up_first, up_ptr, edge_pair, pair_ij, pgeo, pfc, phi, x, o, gy, h, y, gh, gt, q, gq, eps, S, total;
+};
+
+NbLayout nb_layout(const sn_system &sys, size_t base);
+EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t n_edges, size_t base);
+
+// Per-replica cell grid (device struct).
+struct CellGrid {
+    float lo[3];
+    float inv[3];      // 1 / cell edge per dimension
+    int n[3];
+    int offset;        // first cell of this replica in the global cell table
+};
+
+// --------------------------------------------------------------- launchers
+
+// neighbors.hip
+sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
+                   int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s);
+sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, hipStream_t s);
+
+// filter.hip
+sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, hipStream_t s);
+sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
+sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const int2 *pair_ij, int64_t P,
+                          const float *phi, const float *x, const float *gy, float *S, int accumulate,
+                          hipStream_t s);
+
+// graph.hip
+sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
+                      const int32_t *rev, int64_t E, float cutoff, char *ws, const EfLayout &L, int *status,
+                      hipStream_t s);
+sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
+                 const float *pfc, const float *phi, const float *in, float *out, hipStream_t s);
+sn_status forces_rows(int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
+                      const float4 *pgeo, const float *S, float *forces, int *status, hipStream_t s);
+
+// atomwise.hip
+enum Prologue { PRO_NONE = 0, PRO_SSP = 1 };
+enum Epilogue { EPI_STORE = 0, EPI_SIGMUL = 1, EPI_ACCUM = 2 };
+sn_status dense(int N, int Fi, int Fo, const float *X, const float *W, int transW, const float *bias,
+                int pro, int epi, const float *aux, float *Y, hipStream_t s);
+sn_status embed(int N, int F, int T, const int32_t *types, const float *emb, float *h, int *status,
+                hipStream_t s);
+sn_status readout(int N, int H, const float *q, const float *R2, const float *c2, float *eps, float *gq,
+                  hipStream_t s);
+sn_status replica_sum(int B, const int32_t *replica_ptr, const float *eps, float *energy, hipStream_t s);
+
+// verlet (api.hip)
+
+}  // namespace sn
