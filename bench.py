@@ -1,0 +1,227 @@
+"""Benchmark of the SchNet CFConv energy/force MD step on one MI355X.
+
+A step is one velocity-Verlet step of all replicas: half kick + drift,
+neighbour-list rebuild (cell list, exact fp32 predicate), one energy+force
+evaluation (radial basis, filter network, CFConv, readout, analytic
+backward, forces) and the second half kick.  Inputs are seeded synthetic CG
+chains resident in HBM before timing starts.
+
+Prints one JSON line.  Usage:
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched_replicas]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# peaks of one MI355X (AMD datasheet)
+PEAK_HBM_GBS = 8000.0
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+WORKLOAD_TEXT = {
+    "batched_replicas": "64 replicas x 269-bead CG chain (block-diagonal CSR), rc 12 A, 3 interactions, "
+                        "F=128, 50 Gaussians; velocity Verlet 2 fs, neighbour list rebuilt every step",
+    "larger_cg": "16 replicas x 1000-bead compact CG chain, rc 12 A, 5 interactions, F=128, 50 Gaussians; "
+                 "velocity Verlet 2 fs, rebuild every step",
+    "dense_box": "15,668 particles, periodic box at 0.1/A^3, rc 6 A, 3 interactions, F=128, 32 Gaussians; "
+                 "velocity Verlet 2 fs, rebuild every step",
+    "single_protein": "1 x 269-bead CG chain, rc 12 A, 3 interactions, F=128, 50 Gaussians",
+    "tiny_chain": "1 x 32-bead CG chain, rc 10 A, 2 interactions, F=32, 16 Gaussians",
+}
+
+
+def filter_flops_per_pair(F: int, K: int):
+    """Algorithmic FLOPs of one pair (both directed edges) in one interaction.
+
+    forward : rbf @ A1 (2KF) + ssp(a) @ A2 (2F^2)
+    backward: recomputed rbf @ A1 (2KF) + g_phi @ A2^T (2F^2) + g_a @ A1^T (2FK)
+    """
+    return 2 * K * F + 2 * F * F, 4 * K * F + 2 * F * F
+
+
+def cfconv_bytes(E: int, N: int, F: int):
+    """Algorithmic HBM bytes of one CFConv launch: per directed edge the filter
+    row (4F), col, pair index and envelope (12 B); per atom one input row read
+    and one output row written."""
+    return E * (4 * F + 12) + 2 * N * F * 4
+
+
+def cpu_baseline(cfg, seconds: float):
+    """Time the CPU oracle (as it is) on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    rp = cfg["replica_ptr"]
+    B = len(rp) - 1
+    n_sample = min(B, 4)
+    idx = [int(b) for b in np.linspace(0, B - 1, n_sample).round()]
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        for b in idx:
+            s, e = rp[b], rp[b + 1]
+            sub = np.array([0, e - s], np.int32)
+            csr = O.neighbors_bruteforce(cfg["pos"][s:e], sub, cfg["hyper"]["cutoff"], cfg["box"])
+            O.energy_forces(cfg["params"], cfg["hyper"], cfg["types"][s:e], cfg["pos"][s:e], sub, csr, cfg["box"])
+            done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    per_replica = dt / done
+    evals_per_s = 1.0 / (per_replica * B)
+    return {"value": evals_per_s, "unit": "evals/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} single-replica oracle evaluations (brute-force neighbour list + fp64 energy "
+                      f"and forces) of replicas {idx}, {dt:.1f} s, scaled to all {B} replicas",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="batched_replicas", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--filter-format", type=int, default=0, choices=[0, 1])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not part of "
+              f"this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import schnet_cfconv_force_amd as sn
+    import synth
+
+    cfg = synth.make_config(args.workload)
+    h = cfg["hyper"]
+    N, B = len(cfg["pos"]), len(cfg["replica_ptr"]) - 1
+    F, K, I = h["n_features"], h["n_rbf"], h["n_interactions"]
+    dt_fs = cfg.get("dt_fs", 2.0)
+    if "vel" not in cfg:
+        cfg["vel"] = synth.maxwell_boltzmann(N, cfg["replica_ptr"], 110.0, 300.0, 2)
+        cfg["inv_mass"] = np.full(N, 1.0 / 110.0, np.float32)
+
+    model = sn.Model(cfg["params"], h, filter_format=args.filter_format)
+    system = sn.System(cfg["replica_ptr"], cfg["types"], cfg["box"])
+    pos = torch.from_numpy(cfg["pos"]).cuda()
+    vel = torch.from_numpy(cfg["vel"]).cuda()
+    inv_mass = torch.from_numpy(cfg["inv_mass"]).cuda()
+    capacity = N * 160
+    ws = sn.workspace(model, system, capacity)
+    row_ptr = torch.empty(N + 1, dtype=torch.int32, device="cuda")
+    col = torch.empty(capacity, dtype=torch.int32, device="cuda")
+    rev = torch.empty(capacity, dtype=torch.int32, device="cuda")
+    rp_, col_, rev_, E0 = sn.build_csr_neighbors(system, pos, h["cutoff"], capacity, ws)
+    _, forces = sn.energy_forces(model, system, pos, rp_, col_, rev_, E0, ws)
+    csr = (row_ptr, col, rev)
+
+    def md(n):
+        edges = []
+        for _ in range(n):
+            _, _, _, E = sn.verlet_step(model, system, pos, vel, forces, inv_mass, dt_fs, synth.FORCE_TO_ACCEL, 1,
+                                        h["cutoff"], capacity, ws, csr=csr)
+            edges.append(E)
+        return edges
+
+    md(args.warmup)
+    torch.cuda.synchronize()
+    sn.profile_enable(True)
+    sn.profile_collect()
+    t0 = time.perf_counter()
+    edges = md(args.steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = sn.profile_collect()
+    sn.profile_enable(False)
+    assert sn.read_status(ws) == sn.SN_OK
+
+    sec = (t1 - t0) / args.steps
+    evals_per_s = 1.0 / sec
+    E_mean = float(np.mean(edges))
+    P_total = sum(e // 2 for e in edges)
+    ns_per_day = B * evals_per_s * dt_fs * 1e-6 * 86400.0
+
+    # fixed-CSR energy+force evaluations (the same kernels without rebuild / integration)
+    E_last = edges[-1]
+    for _ in range(3):
+        sn.energy_forces(model, system, pos, row_ptr, col, rev, E_last, ws, forces=forces)
+    torch.cuda.synchronize()
+    n_fixed = max(10, args.steps)
+    t2 = time.perf_counter()
+    for _ in range(n_fixed):
+        sn.energy_forces(model, system, pos, row_ptr, col, rev, E_last, ws, forces=forces)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    fixed_evals_per_s = n_fixed / (t3 - t2)
+
+    fwd_pp, bwd_pp = filter_flops_per_pair(F, K)
+    kernels = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps,
+                   "avg_us": 1e3 * v[0] / max(v[1], 1)} for k, v in prof.items()}
+    dominant = max(prof.items(), key=lambda kv: kv[1][0])[0]
+    rl = {}
+    for name, per_pair in (("filter_bwd", bwd_pp), ("filter_fwd", fwd_pp)):
+        if name in prof:
+            ms, n = prof[name]
+            flops = per_pair * P_total * I          # summed over every launch of the timed region
+            achieved = flops / (ms * 1e-3) / 1e12
+            rl[name] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None,
+                        "avg_launch_us": round(1e3 * ms / n, 2),
+                        "flops_per_launch": int(per_pair * P_total * I / n)}
+    if "cfconv" in prof:
+        ms, n = prof["cfconv"]
+        byts = cfconv_bytes(int(E_mean), N, F) * n
+        achieved = byts / (ms * 1e-3) / 1e9
+        rl["cfconv"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                        "avg_launch_us": round(1e3 * ms / n, 2), "bytes_per_launch": int(byts / n)}
+    main_rl = rl.get(dominant) or rl.get("filter_bwd")
+
+    out = {
+        "metric": "energy+force evals/sec and edges/sec at 1 GPU; aggregate ns/day (2 fs step)",
+        "value": round(evals_per_s, 2),
+        "unit": "evals/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if args.filter_format == 0 else "f32 (int16 filter weights)",
+        "data": "synthetic (seeded CG chains / particle box, random-init weights)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload, "n_atoms": N,
+                   "n_replicas": B, "n_edges_mean": round(E_mean, 1), "n_interactions": I, "n_features": F,
+                   "n_rbf": K, "dt_fs": dt_fs, "parallelism": "single GPU"},
+        "edges_per_s": round(E_mean * evals_per_s, 1),
+        "ns_per_day": round(ns_per_day, 1),
+        "evals_per_s_fixed_csr": round(fixed_evals_per_s, 2),
+        "edges_per_s_fixed_csr": round(E_last * fixed_evals_per_s, 1),
+        "roofline": main_rl,
+        "roofline_kernels": rl,
+        "dominant_kernel": dominant,
+        "kernels": kernels,
+        "context": {"pages_ns_per_day": 1000, "pages_hardware": "1x NVIDIA RTX PRO 6000, 64 x 269-bead 1ENH"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -26,12 +26,25 @@ const char *kClassNames[K_NUM_CLASSES] = {
     "filter_fwd", "cfconv", "readout", "energy", "filter_bwd", "forces", "verlet", "kinetic"};
 }  // namespace
 
+std::vector<hipEvent_t> g_event_pool;     // reused events (creating events is slow)
+
+static hipEvent_t pooled_event() {
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
 void prof_begin(int cls, hipStream_t s) {
     if (!g_prof_on) return;
-    ProfRecord r{cls, nullptr, nullptr};
-    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
-    hipEventRecord(r.start, s);
     std::lock_guard<std::mutex> g(g_prof_mu);
+    ProfRecord r{cls, pooled_event(), pooled_event()};
+    if (!r.start || !r.stop) return;
+    hipEventRecord(r.start, s);
     g_prof_open.push_back(r);
 }
 
@@ -148,8 +161,8 @@ sn_status check_ws(void *ws, size_t ws_bytes, size_t need) {
 }
 
 size_t bytes_needed(const sn_model *m, const sn_system *s, int64_t E) {
-    size_t nb = nb_layout(*s, 256).total;
-    size_t ef = m ? ef_layout(*m, *s, E, 256).total : 256;
+    size_t nb = nb_layout(*s, kWsBase).total;
+    size_t ef = m ? ef_layout(*m, *s, E, kWsBase).total : kWsBase;
     return std::max(nb, ef);
 }
 
@@ -160,7 +173,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     const int N = sys.n_atoms, B = sys.n_replicas, F = m.n_features, I = m.n_interactions, H = F / 2;
     const int64_t P = E / 2;
     int *status = reinterpret_cast<int *>(ws);
-    const EfLayout L = ef_layout(m, sys, E, 256);
+    const EfLayout L = ef_layout(m, sys, E, kWsBase);
     float *eps = reinterpret_cast<float *>(ws + L.eps);
     if (N == 0) return replica_sum(B, sys.replica_ptr, eps, energy, s);
 
@@ -307,7 +320,7 @@ sn_status sn_build_csr_neighbors(const sn_system *sys, const float *pos, float r
     SN_TRY(check_system(sys));
     if (!n_edges || !row_ptr || capacity < 0 || !(r_list > 0.0f) || !std::isfinite(r_list)) return SN_ERR_INVALID;
     if (sys->n_atoms > 0 && (!pos || (capacity > 0 && (!col_idx || !rev_idx)))) return SN_ERR_INVALID;
-    SN_TRY(check_ws(ws, ws_bytes, nb_layout(*sys, 256).total));
+    SN_TRY(check_ws(ws, ws_bytes, nb_layout(*sys, kWsBase).total));
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     SN_TRY(clear_status(ws, s));
     return nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, n_edges, reinterpret_cast<char *>(ws), s);
@@ -357,7 +370,7 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
         *n_edges = E;
         if (st != SN_OK) return st;   // includes a non-finite force flagged in the previous step
         float *eout = epot_log ? epot_log + (int64_t)step * B
-                               : reinterpret_cast<float *>(w + ef_layout(*model, *sys, E, 256).eps) + N;
+                               : reinterpret_cast<float *>(w + ef_layout(*model, *sys, E, kWsBase).eps) + N;
         SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, E, eout, forces, w, s));
         if (N > 0) {
             ProfScope ps(K_VERLET, s);
@@ -410,8 +423,8 @@ sn_status sn_profile_collect(double *ms_total, int64_t *launches) {
             st = SN_ERR_HIP;
         if (ms_total) ms_total[r.cls] += ms;
         if (launches) launches[r.cls] += 1;
-        hipEventDestroy(r.start);
-        hipEventDestroy(r.stop);
+        g_event_pool.push_back(r.start);
+        g_event_pool.push_back(r.stop);
     }
     g_prof_done.clear();
     return st;

@@ -30,7 +30,8 @@ namespace sn {
 
 namespace {
 
-constexpr int kFilterThreads = 512;
+constexpr int kFwdThreads = 1024;   // 4 wavefronts per SIMD (<= 128 VGPRs)
+constexpr int kBwdThreads = 512;    // 2 wavefronts per SIMD (<= 256 VGPRs)
 constexpr float kPi = 3.14159265358979323846f;
 
 struct FilterArgs {
@@ -67,29 +68,41 @@ __device__ inline float w2(const FilterArgs &a, int g, int f) {   // A2[g][f]
 __device__ inline float rbf(const FilterArgs &a, float d, int k) {
     if (k >= a.K) return 0.0f;
     const float t = d - (a.lo + (float)k * a.dmu);
-    return expf(-a.gamma * t * t);
+    return fast_exp(-a.gamma * t * t);
 }
 
 // GEMM 1 shared by both passes: acc[m] = (rbf(d) A1)^T for the lane's pair.
 // s_f1 layout: [m][kq][lane] float4, component r = step 4kq + r, holding
-// A1[4 step + lane/16][16 m + lane%16].
+// A1[4 step + lane/16][16 m + lane%16].  KS = ceil(K/4) steps are issued;
+// the zero padding of the last group of four is skipped.
 template <int F>
-__device__ inline void gemm_rbf(const FilterArgs &a, const float4 *s_f1, int KQ, float d, int lane,
+__device__ inline void gemm_rbf(const FilterArgs &a, const float4 *s_f1, int KQ, int KS, float d, int lane,
                                 floatx4 (&acc)[F / 16]) {
     constexpr int MT = F / 16;
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
     for (int kq = 0; kq < KQ; ++kq) {
+        const int nstep = min(4, KS - 4 * kq);
         float bv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) bv[r] = rbf(a, d, 4 * (4 * kq + r) + lane / 16);
+        if (nstep == 4) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const float4 w = s_f1[(m * KQ + kq) * 64 + lane];
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.x, bv[0], acc[m], 0, 0, 0);
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.y, bv[1], acc[m], 0, 0, 0);
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.z, bv[2], acc[m], 0, 0, 0);
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.w, bv[3], acc[m], 0, 0, 0);
+            for (int m = 0; m < MT; ++m) {
+                const float4 w = s_f1[(m * KQ + kq) * 64 + lane];
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.x, bv[0], acc[m], 0, 0, 0);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.y, bv[1], acc[m], 0, 0, 0);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.z, bv[2], acc[m], 0, 0, 0);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.w, bv[3], acc[m], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float4 w = s_f1[(m * KQ + kq) * 64 + lane];
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.x, bv[0], acc[m], 0, 0, 0);
+                if (nstep > 1) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.y, bv[1], acc[m], 0, 0, 0);
+                if (nstep > 2) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.z, bv[2], acc[m], 0, 0, 0);
+            }
         }
     }
 }
@@ -107,12 +120,13 @@ __device__ inline void stage_f1(const FilterArgs &a, float4 *s_f1, int KQ) {
 }
 
 template <int F>
-__global__ __launch_bounds__(kFilterThreads) void filter_fwd_kernel(FilterArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
     __shared__ float4 s_f1[MT * 4 * 64];          // K <= 64: at most 4 groups of 4 steps
     __shared__ float4 s_f2[MT * MT * 64];         // [m][m2][lane]: A2[16 m2 + 4(l/16) + r][16 m + l%16]
     __shared__ float s_b1[F], s_b2[F];
-    const int KQ = ((a.K + 3) / 4 + 3) / 4;
+    const int KS = (a.K + 3) / 4;
+    const int KQ = (KS + 3) / 4;
     stage_f1<F>(a, s_f1, KQ);
     for (int idx = threadIdx.x; idx < MT * MT * 64; idx += blockDim.x) {
         const int m = idx / (MT * 64), m2 = (idx / 64) % MT, l = idx % 64;
@@ -129,10 +143,13 @@ __global__ __launch_bounds__(kFilterThreads) void filter_fwd_kernel(FilterArgs a
     const int64_t ntiles = (a.P + 15) / 16;
     for (int64_t tile = (int64_t)blockIdx.x * waves + threadIdx.x / 64; tile < ntiles;
          tile += (int64_t)gridDim.x * waves) {
+        // keep the weight-fragment LDS reads inside the loop: hoisted out of
+        // it they would need hundreds of registers
+        asm volatile("" ::: "memory");
         const int64_t p = tile * 16 + lane % 16;
         const float d = (p < a.P) ? a.dsrc[p * a.dstride + a.doff] : 0.0f;
         floatx4 acc1[MT];
-        gemm_rbf<F>(a, s_f1, KQ, d, lane, acc1);
+        gemm_rbf<F>(a, s_f1, KQ, KS, d, lane, acc1);
         float z[MT][4];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
@@ -165,7 +182,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_fwd_kernel(FilterArgs a
 }
 
 template <int F>
-__global__ __launch_bounds__(kFilterThreads) void filter_bwd_kernel(FilterArgs a) {
+__global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
     constexpr int FS = F / 4;        // features per k-slot in the g_phi GEMM
     constexpr int SQ = FS / 4;
@@ -173,7 +190,8 @@ __global__ __launch_bounds__(kFilterThreads) void filter_bwd_kernel(FilterArgs a
     __shared__ float4 s_f2b[MT * SQ * 64];   // [m][sq][lane]: A2[16 m + l%16][FS (l/16) + 4 sq + r]
     __shared__ float4 s_f1b[4 * MT * 64];    // [kt][m2][lane]: A1[16 kt + l%16][16 m2 + 4(l/16) + r]
     __shared__ float s_b1[F];
-    const int KQ = ((a.K + 3) / 4 + 3) / 4;
+    const int KS = (a.K + 3) / 4;
+    const int KQ = (KS + 3) / 4;
     const int KT = (a.K + 15) / 16;
     stage_f1<F>(a, s_f1, KQ);
     for (int idx = threadIdx.x; idx < MT * SQ * 64; idx += blockDim.x) {
@@ -199,6 +217,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_bwd_kernel(FilterArgs a
     const int64_t ntiles = (a.P + 15) / 16;
     for (int64_t tile = (int64_t)blockIdx.x * waves + threadIdx.x / 64; tile < ntiles;
          tile += (int64_t)gridDim.x * waves) {
+        asm volatile("" ::: "memory");
         const int64_t p = tile * 16 + lane % 16;
         const bool live = p < a.P;
         const float d = live ? a.dsrc[p * a.dstride + a.doff] : 0.0f;
@@ -210,34 +229,32 @@ __global__ __launch_bounds__(kFilterThreads) void filter_bwd_kernel(FilterArgs a
             fc = c * c;
             dfc = -(kPi / a.cutoff) * sn * c;
         }
-        // G = g_y_i x_j + g_y_j x_i over this lane's quarter of the features
+        // G = g_y_i x_j + g_y_j x_i over this lane's quarter of the features,
+        // gathered in two halves to bound the loads in flight
         float gphi[FS];
         float gfc = 0.0f;
         {
             const int64_t bi = (int64_t)ij.x * F + FS * slot, bj = (int64_t)ij.y * F + FS * slot;
             const int64_t bp = (live ? p : 0) * F + FS * slot;
 #pragma unroll
-            for (int q = 0; q < SQ; ++q) {
-                const float4 gyi = *reinterpret_cast<const float4 *>(a.gy + bi + 4 * q);
-                const float4 gyj = *reinterpret_cast<const float4 *>(a.gy + bj + 4 * q);
-                const float4 xi = *reinterpret_cast<const float4 *>(a.x + bi + 4 * q);
-                const float4 xj = *reinterpret_cast<const float4 *>(a.x + bj + 4 * q);
-                const float4 ph = *reinterpret_cast<const float4 *>(a.phi_in + bp + 4 * q);
-                const float g0 = gyi.x * xj.x + gyj.x * xi.x, g1 = gyi.y * xj.y + gyj.y * xi.y;
-                const float g2 = gyi.z * xj.z + gyj.z * xi.z, g3 = gyi.w * xj.w + gyj.w * xi.w;
-                gfc += g0 * ph.x + g1 * ph.y + g2 * ph.z + g3 * ph.w;
-                gphi[4 * q + 0] = fc * g0; gphi[4 * q + 1] = fc * g1;
-                gphi[4 * q + 2] = fc * g2; gphi[4 * q + 3] = fc * g3;
+            for (int half = 0; half < 2; ++half) {
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int qq = 0; qq < SQ / 2; ++qq) {
+                    const int q = half * (SQ / 2) + qq;
+                    const float4 gyi = *reinterpret_cast<const float4 *>(a.gy + bi + 4 * q);
+                    const float4 gyj = *reinterpret_cast<const float4 *>(a.gy + bj + 4 * q);
+                    const float4 xi = *reinterpret_cast<const float4 *>(a.x + bi + 4 * q);
+                    const float4 xj = *reinterpret_cast<const float4 *>(a.x + bj + 4 * q);
+                    const float4 ph = *reinterpret_cast<const float4 *>(a.phi_in + bp + 4 * q);
+                    const float g0 = gyi.x * xj.x + gyj.x * xi.x, g1 = gyi.y * xj.y + gyj.y * xi.y;
+                    const float g2 = gyi.z * xj.z + gyj.z * xi.z, g3 = gyi.w * xj.w + gyj.w * xi.w;
+                    gfc += g0 * ph.x + g1 * ph.y + g2 * ph.z + g3 * ph.w;
+                    gphi[4 * q + 0] = fc * g0; gphi[4 * q + 1] = fc * g1;
+                    gphi[4 * q + 2] = fc * g2; gphi[4 * q + 3] = fc * g3;
+                }
             }
         }
-        // recompute a = rbf A1 + b1 -> sigmoid(a)
-        floatx4 acc1[MT];
-        gemm_rbf<F>(a, s_f1, KQ, d, lane, acc1);
-        float sg[MT][4];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sg[m][r] = sigm(acc1[m][r] + s_b1[16 * m + 4 * slot + r]);
         // g_z^T = A2 g_phi^T  (k = feature f = FS slot + step)
         floatx4 gz[MT];
 #pragma unroll
@@ -253,23 +270,27 @@ __global__ __launch_bounds__(kFilterThreads) void filter_bwd_kernel(FilterArgs a
                 gz[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.w, gphi[4 * sq + 3], gz[m], 0, 0, 0);
             }
         }
-        // g_a = g_z (.) sigmoid(a);  g_rbf^T = A1 g_a^T
+        // recompute a = rbf A1 + b1;  g_a = g_z (.) sigmoid(a)
+        floatx4 acc1[MT];
+        gemm_rbf<F>(a, s_f1, KQ, KS, d, lane, acc1);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gz[m][r] *= sigm(acc1[m][r] + s_b1[16 * m + 4 * slot + r]);
+        // g_rbf^T = A1 g_a^T
         floatx4 ge[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) ge[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m2 = 0; m2 < MT; ++m2) {
-            float ga[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ga[r] = gz[m2][r] * sg[m2][r];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
                 if (kt < KT) {
                     const float4 w = s_f1b[(kt * MT + m2) * 64 + lane];
-                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.x, ga[0], ge[kt], 0, 0, 0);
-                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.y, ga[1], ge[kt], 0, 0, 0);
-                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.z, ga[2], ge[kt], 0, 0, 0);
-                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.w, ga[3], ge[kt], 0, 0, 0);
+                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.x, gz[m2][0], ge[kt], 0, 0, 0);
+                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.y, gz[m2][1], ge[kt], 0, 0, 0);
+                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.z, gz[m2][2], ge[kt], 0, 0, 0);
+                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.w, gz[m2][3], ge[kt], 0, 0, 0);
                 }
             }
         }
@@ -283,7 +304,7 @@ __global__ __launch_bounds__(kFilterThreads) void filter_bwd_kernel(FilterArgs a
                     const int k = 16 * kt + 4 * slot + r;
                     if (k < a.K) {
                         const float t = d - (a.lo + (float)k * a.dmu);
-                        sp += ge[kt][r] * (-2.0f * a.gamma * t * expf(-a.gamma * t * t));
+                        sp += ge[kt][r] * (-2.0f * a.gamma * t * fast_exp(-a.gamma * t * t));
                     }
                 }
             }
@@ -335,18 +356,18 @@ FilterArgs make_args(const sn_model &m, int t) {
 template <int F>
 sn_status launch_fwd(const FilterArgs &a, hipStream_t s) {
     const int64_t tiles = (a.P + 15) / 16;
-    const int waves = kFilterThreads / 64;
+    const int waves = kFwdThreads / 64;
     const int grid = (int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves);
-    filter_fwd_kernel<F><<<grid, kFilterThreads, 0, s>>>(a);
+    filter_fwd_kernel<F><<<grid, kFwdThreads, 0, s>>>(a);
     return launch_status();
 }
 
 template <int F>
 sn_status launch_bwd(const FilterArgs &a, hipStream_t s) {
     const int64_t tiles = (a.P + 15) / 16;
-    const int waves = kFilterThreads / 64;
+    const int waves = kBwdThreads / 64;
     const int grid = (int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves);
-    filter_bwd_kernel<F><<<grid, kFilterThreads, 0, s>>>(a);
+    filter_bwd_kernel<F><<<grid, kBwdThreads, 0, s>>>(a);
     return launch_status();
 }
 

@@ -192,7 +192,7 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
     int32_t *up_ptr = reinterpret_cast<int32_t *>(ws + L.up_ptr);
     pair_count_kernel<<<(N + 255) / 256, 256, 0, s>>>(N, row_ptr, col, up_first, up_ptr);
     SN_TRY(launch_status());
-    SN_TRY(scan_exclusive(up_ptr, up_ptr, N, nullptr, s));
+    SN_TRY(scan_exclusive(up_ptr, up_ptr, N, nullptr, nullptr, scan_scratch(ws), s));
     pair_check_kernel<<<1, 1, 0, s>>>(up_ptr, N, E / 2, status);
     SN_TRY(launch_status());
     PairArgs a;

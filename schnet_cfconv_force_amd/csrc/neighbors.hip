@@ -239,10 +239,7 @@ __global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos
         base += __popcll(mask);
     }
     if (!FILL) {
-        if (lane == 0) {
-            cnt[i] = base;
-            atomicMax(&status[kMaxRow], base);
-        }
+        if (lane == 0) cnt[i] = base;
         return;
     }
     const int r0 = row_ptr[i];
@@ -281,39 +278,132 @@ __global__ __launch_bounds__(256) void rev_kernel(int n_atoms, const int32_t *ro
     }
 }
 
-// Single-workgroup exclusive scan: out[k] = sum in[0..k), out[n] = total.
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t *in, int32_t *out, int n, int32_t *total_slot) {
-    __shared__ int part[1024];
-    const int t = threadIdx.x;
-    const int chunk = (n + 1023) / 1024;
-    const int b = min(n, t * chunk), e = min(n, b + chunk);
-    int s = 0;
-    for (int k = b; k < e; ++k) s += in[k];
-    part[t] = s;
+// ------------------------------------------------------------------ scan
+// Exclusive prefix sum in three passes over tiles of 4096 values (1024
+// threads x 4): tile sums (and maxima), a scan of the tile sums in one
+// block, then each tile's own scan plus its offset.  out may alias in.
+
+constexpr int kScanThreads = 1024;
+constexpr int kScanTile = 4 * kScanThreads;
+
+// block-wide exclusive scan of one value per thread; *total receives the sum
+__device__ inline int block_exclusive(int v, int *s_w, int *total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(x, o, 64);
+        if (lane >= o) x += t;
+    }
+    if (lane == 63) s_w[wv] = x;
     __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {           // Hillis-Steele inclusive scan of the partials
-        int v = (t >= o) ? part[t - o] : 0;
-        __syncthreads();
-        part[t] += v;
-        __syncthreads();
+    if (wv == 0) {
+        int w = (lane < kScanThreads / 64) ? s_w[lane] : 0;
+        for (int o = 1; o < 16; o <<= 1) {
+            int t = __shfl_up(w, o, 64);
+            if (lane >= o) w += t;
+        }
+        if (lane < kScanThreads / 64) s_w[lane] = w;
     }
-    int run = part[t] - s;
-    for (int k = b; k < e; ++k) {
-        int v = in[k];
-        out[k] = run;
-        run += v;
+    __syncthreads();
+    const int base = wv > 0 ? s_w[wv - 1] : 0;
+    *total = s_w[kScanThreads / 64 - 1];
+    __syncthreads();
+    return base + x - v;
+}
+
+__device__ inline int block_max(int v, int *s_w) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    if (lane == 0) s_w[wv] = v;
+    __syncthreads();
+    int m = s_w[0];
+    for (int k = 1; k < kScanThreads / 64; ++k) m = max(m, s_w[k]);
+    __syncthreads();
+    return m;
+}
+
+__device__ inline void load4(const int32_t *in, int n, int64_t b, int v[4]) {
+    for (int r = 0; r < 4; ++r) v[r] = (b + r < n) ? in[b + r] : 0;
+}
+
+// pass 1: per-tile sum and max
+__global__ __launch_bounds__(kScanThreads) void scan_tiles_kernel(const int32_t *in, int n, int32_t *tsum,
+                                                                  int32_t *tmax) {
+    __shared__ int s_w[kScanThreads / 64];
+    int v[4];
+    load4(in, n, (int64_t)blockIdx.x * kScanTile + 4 * threadIdx.x, v);
+    int tot;
+    block_exclusive(v[0] + v[1] + v[2] + v[3], s_w, &tot);
+    const int m = block_max(max(max(v[0], v[1]), max(v[2], v[3])), s_w);
+    if (threadIdx.x == 0) {
+        tsum[blockIdx.x] = tot;
+        tmax[blockIdx.x] = m;
     }
-    if (t == 1023) {
-        out[n] = part[1023];
-        if (total_slot) *total_slot = part[1023];
+}
+
+// pass 2 (one block): exclusive scan of the tile sums in place; total and max
+__global__ __launch_bounds__(kScanThreads) void scan_sums_kernel(int32_t *tsum, const int32_t *tmax, int ntiles,
+                                                                 int32_t *out_n, int32_t *total_slot,
+                                                                 int32_t *max_slot) {
+    __shared__ int s_w[kScanThreads / 64];
+    int v[4], mv[4];
+    const int64_t b = 4 * threadIdx.x;
+    load4(tsum, ntiles, b, v);
+    load4(tmax, ntiles, b, mv);
+    int tot;
+    int run = block_exclusive(v[0] + v[1] + v[2] + v[3], s_w, &tot);
+    const int m = block_max(max(max(mv[0], mv[1]), max(mv[2], mv[3])), s_w);
+    for (int r = 0; r < 4; ++r) {
+        if (b + r < ntiles) tsum[b + r] = run;
+        run += v[r];
+    }
+    if (threadIdx.x == 0) {
+        *out_n = tot;
+        if (total_slot) *total_slot = tot;
+        if (max_slot) *max_slot = m;
+    }
+}
+
+// pass 3: scan of each tile plus its offset (tsum == nullptr: single tile)
+__global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(const int32_t *in, int32_t *out, int n,
+                                                                  const int32_t *tsum, int32_t *total_slot,
+                                                                  int32_t *max_slot) {
+    __shared__ int s_w[kScanThreads / 64];
+    int v[4];
+    const int64_t b = (int64_t)blockIdx.x * kScanTile + 4 * threadIdx.x;
+    load4(in, n, b, v);
+    int tot;
+    int run = block_exclusive(v[0] + v[1] + v[2] + v[3], s_w, &tot) + (tsum ? tsum[blockIdx.x] : 0);
+    int m = 0;
+    if (!tsum) m = block_max(max(max(v[0], v[1]), max(v[2], v[3])), s_w);
+    for (int r = 0; r < 4; ++r) {
+        if (b + r < n) out[b + r] = run;
+        run += v[r];
+    }
+    if (!tsum && threadIdx.x == 0) {
+        out[n] = tot;
+        if (total_slot) *total_slot = tot;
+        if (max_slot) *max_slot = m;
     }
 }
 
 }  // namespace
 
-sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, hipStream_t s) {
+sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
+                         int32_t *scratch, hipStream_t s) {
     ProfScope ps(K_NB_SCAN, s);
-    scan_kernel<<<1, 1024, 0, s>>>(in, out, n, total_slot);
+    const int ntiles = (n + kScanTile - 1) / kScanTile;
+    if (ntiles > kScanTile) return SN_ERR_INVALID;
+    if (ntiles <= 1) {
+        scan_apply_kernel<<<1, kScanThreads, 0, s>>>(in, out, n, nullptr, total_slot, max_slot);
+        return launch_status();
+    }
+    int32_t *tsum = scratch, *tmax = scratch + kScanTile;
+    scan_tiles_kernel<<<ntiles, kScanThreads, 0, s>>>(in, n, tsum, tmax);
+    SN_TRY(launch_status());
+    scan_sums_kernel<<<1, kScanThreads, 0, s>>>(tsum, tmax, ntiles, out + n, total_slot, max_slot);
+    SN_TRY(launch_status());
+    scan_apply_kernel<<<ntiles, kScanThreads, 0, s>>>(in, out, n, tsum, nullptr, nullptr);
     return launch_status();
 }
 
@@ -366,7 +456,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         for (int c = 0; c < 3; ++c)
             if (!(sys.box[c] > 0.0f) || (int)floorf(sys.box[c] / cell_edge) < 3) return SN_ERR_BOX;
 
-    NbLayout L = nb_layout(sys, 256);
+    NbLayout L = nb_layout(sys, kWsBase);
     CellGrid *grid = reinterpret_cast<CellGrid *>(ws + L.grid);
     int *rep_of = reinterpret_cast<int *>(ws + L.rep_of);
     int *cell_of = reinterpret_cast<int *>(ws + L.cell_of);
@@ -395,7 +485,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         bin_kernel<<<(N + 255) / 256, 256, 0, s>>>(pos, N, grid, rep_of, pp, cell_of, cell_cnt);
         SN_TRY(launch_status());
     }
-    SN_TRY(scan_exclusive(cell_cnt, cell_start, (int)L.n_cells, nullptr, s));
+    SN_TRY(scan_exclusive(cell_cnt, cell_start, (int)L.n_cells, nullptr, nullptr, scan_scratch(ws), s));
     {
         ProfScope ps(K_NB_BIN, s);
         place_kernel<<<(N + 255) / 256, 256, 0, s>>>(pos, N, cell_of, cell_start, cell_fill, spos);
@@ -408,7 +498,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
                                                                row_ptr, nullptr, nullptr, status);
         SN_TRY(launch_status());
     }
-    SN_TRY(scan_exclusive(row_ptr, row_ptr, N, status + kEdgeTotal, s));
+    SN_TRY(scan_exclusive(row_ptr, row_ptr, N, status + kEdgeTotal, status + kMaxRow, scan_scratch(ws), s));
     int *host = pinned_counters();
     if (!host) return SN_ERR_HIP;
     SN_HIP(hipMemcpyAsync(host, status, 4 * 4, hipMemcpyDeviceToHost, s));

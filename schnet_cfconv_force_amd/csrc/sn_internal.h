@@ -37,12 +37,17 @@ __device__ inline void flag_status(int *status, int code) { atomicCAS(status, 0,
 
 // --------------------------------------------------------------- math
 
-// Shifted softplus ln(e^x/2 + 1/2) = max(x,0) + log1p(exp(-|x|)) - ln 2.
+// exp and log on the hardware exp2/log2 units (about 1 ulp on their own;
+// the scaling by log2(e) or ln 2 adds one rounding).
+__device__ inline float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ inline float fast_log(float x) { return __builtin_amdgcn_logf(x) * 0.69314718055994531f; }
+
+// Shifted softplus ln(e^x/2 + 1/2) = max(x,0) + ln(1 + exp(-|x|)) - ln 2.
 __device__ inline float ssp(float x) {
-    return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))) - 0.69314718055994531f;
+    return fmaxf(x, 0.0f) + fast_log(1.0f + fast_exp(-fabsf(x))) - 0.69314718055994531f;
 }
 // Its derivative, the logistic sigmoid.
-__device__ inline float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ inline float sigm(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
 
 // --------------------------------------------------------------- timing
 
@@ -64,6 +69,13 @@ struct ProfScope {
 // --------------------------------------------------------------- workspace
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace: [0, 256) status words, [256, kWsBase) scan scratch (2 x 4096
+// tile sums), then the scratch of the neighbour builder or of the
+// energy/force pipeline (they are never live at the same time).
+constexpr size_t kWsScan = 256;
+constexpr size_t kWsBase = kWsScan + 2 * 4096 * 4;
+inline int32_t *scan_scratch(char *ws) { return reinterpret_cast<int32_t *>(ws + kWsScan); }
 
 struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
     size_t grid, rep_of, cell_of, cell_cnt, cell_start, cell_fill, spos, total;
@@ -90,7 +102,10 @@ struct CellGrid {
 // neighbors.hip
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
                    int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s);
-sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, hipStream_t s);
+// Exclusive prefix sum; out[n] = total; optional device slots receive the
+// total and the maximum input; scratch = the workspace's scan scratch.
+sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
+                         int32_t *scratch, hipStream_t s);
 
 // filter.hip
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, hipStream_t s);
