@@ -52,6 +52,108 @@ def cfconv_bytes(E: int, N: int, F: int):
     return E * (4 * F + 12) + 2 * N * F * 4
 
 
+KERNEL_SOURCES = ("filter.hip", "graph.hip", "atomwise.hip", "neighbors.hip", "api.hip", "sn_internal.h")
+
+
+def source_hash() -> str:
+    """sha256 of the HIP sources: hardware counters are only valid for this code."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "schnet_cfconv_force_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+
+
+def _short_kernel(name: str) -> str:
+    import re
+    name = name.replace("void ", "").replace("sn::(anonymous namespace)::", "").replace("sn::", "")
+    return re.sub(r"[<(].*", "", name)
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, probe_mib: int, workload: str, command: str) -> str:
+    """Markdown summary of two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE).
+
+    Both counters are in KiB per dispatch.  Each is scaled by the factor that
+    makes it read the known size of the probe copy (probe_mib MiB read and
+    written by the copy kernel that runs first).
+    """
+    import collections
+    import csv
+    per = {}
+    factor = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        agg = collections.defaultdict(list)
+        probe = None
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "copyBuffer" in r["Kernel_Name"] and (probe is None or v > probe):
+                probe = v
+            agg[_short_kernel(r["Kernel_Name"])].append(v)
+        factor[counter] = (probe_mib * 1024.0) / probe if probe else 1.0
+        per[counter] = {k: sum(v) / len(v) for k, v in agg.items()}
+    rows = []
+    data = {"workload": workload, "source_hash": source_hash(), "probe_mib": probe_mib,
+            "fetch_factor": round(factor["FETCH_SIZE"], 4), "write_factor": round(factor["WRITE_SIZE"], 4),
+            "bytes_per_launch": {}}
+    for k in sorted(per["FETCH_SIZE"], key=lambda k: -per["FETCH_SIZE"][k] - per["WRITE_SIZE"].get(k, 0)):
+        if k.startswith("__amd") or k.startswith("at::"):
+            continue
+        f = per["FETCH_SIZE"][k]
+        w = per["WRITE_SIZE"].get(k, 0.0)
+        b = (f * factor["FETCH_SIZE"] + w * factor["WRITE_SIZE"]) * 1024.0
+        data["bytes_per_launch"][k] = int(b)
+        rows.append(f"| {k} | {f:.1f} | {w:.1f} | {b / 1e6:.1f} |")
+    import json as _json
+    return "\n".join([
+        f"# HBM traffic per launch, {workload}",
+        "",
+        "Two `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, mean over dispatches).",
+        f"A {probe_mib} MiB device copy runs first; the counters are scaled so that it reads {probe_mib} MiB:",
+        f"FETCH_SIZE x {factor['FETCH_SIZE']:.4f}, WRITE_SIZE x {factor['WRITE_SIZE']:.4f}.",
+        "FETCH_SIZE counts L2 misses to the memory fabric, so reads served by the Infinity Cache count too.",
+        "",
+        "Commands (from the repository root):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB / launch |",
+        "|---|---|---|---|",
+        *rows,
+        "",
+        "Machine-readable (read by bench.py; ignored once the HIP sources change):",
+        "",
+        "```json",
+        _json.dumps(data),
+        "```",
+        "",
+    ])
+
+
+def load_traffic(workload: str):
+    import json as _json
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        data = _json.loads(blob)
+    except (IndexError, ValueError):
+        return None
+    if data.get("source_hash") != source_hash():
+        return None
+    return data["bytes_per_launch"]
+
+
 def cpu_baseline(cfg, seconds: float):
     """Time the CPU oracle (as it is) on a bounded sample of the same workload."""
     import numpy as np
@@ -94,7 +196,18 @@ def main():
     ap.add_argument("--filter-format", type=int, default=0, choices=[0, 1])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="first copy a buffer of this many MiB (calibrates hardware byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary of two rocprofv3 --pmc runs to profiles/ and exit")
+    ap.add_argument("--pmc-command", default="", help="command line recorded in the traffic summary")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        md = summarize_pmc(*args.summarize_pmc, args.copy_probe_mb, args.workload, args.pmc_command)
+        with open(traffic_file(args.workload), "w") as f:
+            f.write(md)
+        print(md)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not part of "
@@ -106,6 +219,13 @@ def main():
 
     import schnet_cfconv_force_amd as sn
     import synth
+
+    if args.copy_probe_mb > 0:
+        src = torch.ones(args.copy_probe_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cfg = synth.make_config(args.workload)
     h = cfg["hyper"]
@@ -190,6 +310,11 @@ def main():
         rl["cfconv"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                         "avg_launch_us": round(1e3 * ms / n, 2), "bytes_per_launch": int(byts / n)}
+    traffic = load_traffic(args.workload)
+    if traffic:
+        kname = {"filter_bwd": "filter_bwd_kernel", "filter_fwd": "filter_fwd_kernel", "cfconv": "cfconv_kernel"}
+        for name, r in rl.items():
+            r["traffic"] = traffic.get(kname[name])
     main_rl = rl.get(dominant) or rl.get("filter_bwd")
 
     out = {

@@ -65,6 +65,20 @@ __device__ inline float w2(const FilterArgs &a, int g, int f) {   // A2[g][f]
     return a.A2[g * F + f];
 }
 
+// Tiles of 16 pairs handled by this wavefront.  The grid is a multiple of
+// the XCD count; the blocks of one XCD share one contiguous range of tiles
+// (pairs are in CSR order, so the gathered atom rows of a range stay in
+// that XCD's L2), and the wavefronts of those blocks stride through it.
+__device__ inline void tile_range(int64_t P, int64_t &tile, int64_t &end, int64_t &stride) {
+    const int64_t ntiles = (P + 15) / 16;
+    const int xcd = blockIdx.x % kXcds, nxb = gridDim.x / kXcds;
+    const int64_t per = (ntiles + kXcds - 1) / kXcds;
+    const int waves = blockDim.x / 64;
+    tile = per * xcd + (int64_t)(blockIdx.x / kXcds) * waves + threadIdx.x / 64;
+    end = min(ntiles, per * (xcd + 1));
+    stride = (int64_t)nxb * waves;
+}
+
 __device__ inline float rbf(const FilterArgs &a, float d, int k) {
     if (k >= a.K) return 0.0f;
     const float t = d - (a.lo + (float)k * a.dmu);
@@ -139,10 +153,9 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     __syncthreads();
 
     const int lane = threadIdx.x % 64;
-    const int waves = blockDim.x / 64;
-    const int64_t ntiles = (a.P + 15) / 16;
-    for (int64_t tile = (int64_t)blockIdx.x * waves + threadIdx.x / 64; tile < ntiles;
-         tile += (int64_t)gridDim.x * waves) {
+    int64_t tile, tile_end, stride;
+    tile_range(a.P, tile, tile_end, stride);
+    for (; tile < tile_end; tile += stride) {
         // keep the weight-fragment LDS reads inside the loop: hoisted out of
         // it they would need hundreds of registers
         asm volatile("" ::: "memory");
@@ -213,10 +226,9 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
 
     const int lane = threadIdx.x % 64;
     const int slot = lane / 16;
-    const int waves = blockDim.x / 64;
-    const int64_t ntiles = (a.P + 15) / 16;
-    for (int64_t tile = (int64_t)blockIdx.x * waves + threadIdx.x / 64; tile < ntiles;
-         tile += (int64_t)gridDim.x * waves) {
+    int64_t tile, tile_end, stride;
+    tile_range(a.P, tile, tile_end, stride);
+    for (; tile < tile_end; tile += stride) {
         asm volatile("" ::: "memory");
         const int64_t p = tile * 16 + lane % 16;
         const bool live = p < a.P;
@@ -357,7 +369,7 @@ template <int F>
 sn_status launch_fwd(const FilterArgs &a, hipStream_t s) {
     const int64_t tiles = (a.P + 15) / 16;
     const int waves = kFwdThreads / 64;
-    const int grid = (int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves);
+    const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
     filter_fwd_kernel<F><<<grid, kFwdThreads, 0, s>>>(a);
     return launch_status();
 }
@@ -366,7 +378,7 @@ template <int F>
 sn_status launch_bwd(const FilterArgs &a, hipStream_t s) {
     const int64_t tiles = (a.P + 15) / 16;
     const int waves = kBwdThreads / 64;
-    const int grid = (int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves);
+    const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
     filter_bwd_kernel<F><<<grid, kBwdThreads, 0, s>>>(a);
     return launch_status();
 }

@@ -116,12 +116,14 @@ __global__ void pair_check_kernel(const int32_t *up_ptr, int N, int64_t P, int *
 
 // y_i = sum_{e in row i} pfc[p] * phi[p] (.) in[col(e)], LPR = F/4 lanes per row
 template <int F>
-__global__ __launch_bounds__(256) void cfconv_kernel(int N, const int32_t *row_ptr, const int32_t *col,
-                                                     const int32_t *edge_pair, const float *pfc,
+__global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const int32_t *row_ptr,
+                                                     const int32_t *col, const int32_t *edge_pair, const float *pfc,
                                                      const float *phi, const float *in, float *out) {
     constexpr int LPR = F / 4;
     const int sub = threadIdx.x % LPR;
-    const int row = (blockIdx.x * 256 + threadIdx.x) / LPR;
+    const int blk = xcd_block(nblocks);
+    if (blk < 0) return;
+    const int row = (blk * 256 + threadIdx.x) / LPR;
     if (row >= N) return;                      // whole lane group leaves together
     const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -220,11 +222,12 @@ sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const
                  const float *pfc, const float *phi, const float *in, float *out, hipStream_t s) {
     ProfScope ps(K_CFCONV, s);
     const int rows_per_block = 256 / (F / 4);
-    const int grid = (N + rows_per_block - 1) / rows_per_block;
+    const int nb = (N + rows_per_block - 1) / rows_per_block;
+    const int grid = xcd_grid(nb);
     switch (F) {
-        case 32: cfconv_kernel<32><<<grid, 256, 0, s>>>(N, row_ptr, col, edge_pair, pfc, phi, in, out); break;
-        case 64: cfconv_kernel<64><<<grid, 256, 0, s>>>(N, row_ptr, col, edge_pair, pfc, phi, in, out); break;
-        case 128: cfconv_kernel<128><<<grid, 256, 0, s>>>(N, row_ptr, col, edge_pair, pfc, phi, in, out); break;
+        case 32: cfconv_kernel<32><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi, in, out); break;
+        case 64: cfconv_kernel<64><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi, in, out); break;
+        case 128: cfconv_kernel<128><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi, in, out); break;
         default: return SN_ERR_INVALID;
     }
     return launch_status();

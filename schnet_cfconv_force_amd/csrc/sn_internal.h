@@ -49,6 +49,22 @@ __device__ inline float ssp(float x) {
 // Its derivative, the logistic sigmoid.
 __device__ inline float sigm(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
 
+// --------------------------------------------------------------- XCD mapping
+
+// MI355X places consecutive workgroup ids on its 8 XCDs in turn, and each
+// XCD has its own L2.  xcd_block() renumbers the launched blocks so that
+// each XCD gets one contiguous slab of the logical block range (rows of the
+// same replicas share an L2).  The grid must be launched with
+// xcd_grid(n) blocks; ids that map beyond n - 1 return -1.
+constexpr int kXcds = 8;
+inline int xcd_grid(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
+__device__ inline int xcd_block(int n) {
+    const int per = (n + kXcds - 1) / kXcds;
+    const int b = (int)blockIdx.x;
+    const int logical = (b % kXcds) * per + b / kXcds;
+    return logical < n ? logical : -1;
+}
+
 // --------------------------------------------------------------- timing
 
 enum KernelClass {
