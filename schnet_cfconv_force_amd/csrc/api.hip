@@ -22,7 +22,7 @@ std::mutex g_prof_mu;
 std::vector<ProfRecord> g_prof_open;   // started, not yet stopped (stack per class)
 std::vector<ProfRecord> g_prof_done;
 const char *kClassNames[K_NUM_CLASSES] = {
-    "nb_grid", "nb_bin", "nb_scan", "nb_count", "nb_fill", "nb_rev", "pairs", "embed", "dense",
+    "nb_grid", "nb_bin", "nb_scan", "nb_count", "nb_fill", "nb_rev", "pairs", "embed", "mlp",
     "filter_fwd", "cfconv", "readout", "energy", "filter_bwd", "forces", "verlet", "kinetic"};
 }  // namespace
 
@@ -66,7 +66,7 @@ void prof_end(int cls, hipStream_t s) {
 
 EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t base) {
     EfLayout L;
-    const int64_t N = sys.n_atoms, P = E / 2, F = m.n_features, I = m.n_interactions, H = F / 2;
+    const int64_t N = sys.n_atoms, P = E / 2, F = m.n_features, I = m.n_interactions;
     const int64_t B = sys.n_replicas;
     size_t o = base;
     auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
@@ -83,11 +83,9 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     L.h = take(4 * N * F);
     L.y = take(4 * N * F);
     L.gh = take(4 * N * F);
-    L.gt = take(4 * N * F);
-    L.q = take(4 * N * H);
-    L.gq = take(4 * N * H);
     L.eps = take(4 * N + 4 * B);   // eps[N], then an energy scratch [B]
     L.S = take(4 * P);
+    L.rowmax = take(8 * N);
     L.total = o;
     return L;
 }
@@ -170,7 +168,7 @@ size_t bytes_needed(const sn_model *m, const sn_system *s, int64_t E) {
 sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const float *pos, const int32_t *row_ptr,
                              const int32_t *col, const int32_t *rev, int64_t E, float *energy, float *forces,
                              char *ws, hipStream_t s) {
-    const int N = sys.n_atoms, B = sys.n_replicas, F = m.n_features, I = m.n_interactions, H = F / 2;
+    const int N = sys.n_atoms, B = sys.n_replicas, F = m.n_features, I = m.n_interactions;
     const int64_t P = E / 2;
     int *status = reinterpret_cast<int *>(ws);
     const EfLayout L = ef_layout(m, sys, E, kWsBase);
@@ -190,7 +188,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     const int2 *pair_ij = reinterpret_cast<const int2 *>(ws + L.pair_ij);
     const float4 *pgeo = reinterpret_cast<const float4 *>(ws + L.pgeo);
     const float *pfc = F32(L.pfc);
-    float *h = F32(L.h), *y = F32(L.y), *gh = F32(L.gh), *gt = F32(L.gt), *q = F32(L.q), *gq = F32(L.gq);
+    float *h = F32(L.h), *y = F32(L.y), *gh = F32(L.gh);
     float *S = F32(L.S);
     const int64_t NF = (int64_t)N * F, PF = P * F;
     auto phi_t = [&](int t) { return F32(L.phi) + PF * t; };
@@ -200,25 +198,23 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
 
     SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, E, m.cutoff, ws, L, status, s));
     SN_TRY(embed(N, F, m.n_types, sys.types, prm + off[0], h, status, s));
+    SN_TRY(mlp_x(N, F, h, blk(0, W_IN), x_t(0), s));
     for (int t = 0; t < I; ++t) {
-        SN_TRY(dense(N, F, F, h, blk(t, W_IN), 0, nullptr, PRO_NONE, EPI_STORE, nullptr, x_t(t), s));
         SN_TRY(filter_forward(m, t, pgeo, P, phi_t(t), s));
         SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, s));
-        SN_TRY(dense(N, F, F, y, blk(t, WO1), 0, blk(t, BO1), PRO_NONE, EPI_STORE, nullptr, o_t(t), s));
-        SN_TRY(dense(N, F, F, o_t(t), blk(t, WO2), 0, blk(t, BO2), PRO_SSP, EPI_ACCUM, nullptr, h, s));
+        SN_TRY(mlp_out(N, F, y, blk(t, WO1), blk(t, BO1), blk(t, WO2), blk(t, BO2), o_t(t), h, s));
+        if (t + 1 < I) SN_TRY(mlp_x(N, F, h, blk(t + 1, W_IN), x_t(t + 1), s));
     }
-    SN_TRY(dense(N, F, H, h, R1, 0, c1, PRO_NONE, EPI_STORE, nullptr, q, s));
-    SN_TRY(readout(N, H, q, R2, c2, eps, gq, s));
+    SN_TRY(mlp_readout(N, F, h, R1, c1, R2, c2, eps, gh, s));
     SN_TRY(replica_sum(B, sys.replica_ptr, eps, energy, s));
-    // backward: dE/dh, then through the interactions in reverse
-    SN_TRY(dense(N, H, F, gq, R1, 1, nullptr, PRO_NONE, EPI_STORE, nullptr, gh, s));
+    // backward through the interactions in reverse
     for (int t = I - 1; t >= 0; --t) {
-        SN_TRY(dense(N, F, F, gh, blk(t, WO2), 1, nullptr, PRO_NONE, EPI_SIGMUL, o_t(t), gt, s));
-        SN_TRY(dense(N, F, F, gt, blk(t, WO1), 1, nullptr, PRO_NONE, EPI_STORE, nullptr, gy_t(t), s));
-        SN_TRY(filter_backward(m, t, pgeo, pair_ij, P, phi_t(t), x_t(t), gy_t(t), S, t != I - 1, s));
+        SN_TRY(mlp_bwd_out(N, F, gh, blk(t, WO2), o_t(t), blk(t, WO1), gy_t(t), s));
+        SN_TRY(filter_backward(m, t, pgeo, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t),
+                               reinterpret_cast<float2 *>(ws + L.rowmax), S, t != I - 1, s));
         if (t > 0) {   // dE/dh below the first block is not needed for forces
             SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, s));
-            SN_TRY(dense(N, F, F, y, blk(t, W_IN), 1, nullptr, PRO_NONE, EPI_ACCUM, nullptr, gh, s));
+            SN_TRY(mlp_bwd_x(N, F, y, blk(t, W_IN), gh, s));
         }
     }
     return forces_rows(N, row_ptr, col, edge_pair, pgeo, S, forces, status, s);

@@ -10,29 +10,47 @@
 //   g_fc = <G, phi>,  g_phi = fc G,  g_a = (g_phi A2^T) (.) sigmoid(a),
 //   g_rbf = g_a A1^T,  S_p += sum_k g_rbf_k rbf_k'(d) + g_fc fc'(d).
 //
+// Precision.  The products run on v_mfma_f32_16x16x32_f16 in split form:
+// every fp32 operand x is held as hi = fp16(x) and lo = fp16((x - hi) 2^11),
+// and a.b is accumulated as hi.hi into one fp32 accumulator and
+// hi.lo + lo.hi into a second one that is scaled by 2^-11 at the end.  The
+// dropped lo.lo term is below 2^-22 |a||b|, so the result carries close to
+// fp32 accuracy at 3/16 of the cost of fp32 matrix instructions.  Backward
+// operands are first scaled per pair by a power of two (exact) so that no
+// value falls into the fp16 subnormal range.
+//
 // Matrix-core mapping.  Everything is computed transposed: features are the
-// M dimension and 16 pairs are the N dimension of v_mfma_f32_16x16x4f32.
-// Lane l then always owns pair l%16, and the accumulator layout of one GEMM
-// (lane l: rows 4(l/16)+r of a 16-row tile, r = 0..3) is directly a valid
-// B operand of the next GEMM (lane l: k-slot l/16) once the k index of step
-// (tile m, register r) is taken to be 16m + 4(l/16) + r.  So the three
-// chained GEMMs never leave registers; only the weights are read from LDS,
-// pre-arranged so that each lane's operands for four consecutive steps are
-// one conflict-free 16-byte read.  The radial basis values are generated in
-// registers from d (no E x K tensor exists anywhere).
+// M dimension and 16 pairs are the N dimension.  Lane l always owns pair
+// l%16; the accumulator layout of one GEMM (lane l: rows 4(l/16)+r of each
+// 16-row tile) becomes the B operand of the next one (lane l: k-slot l/16,
+// 8 values) once the k index of value j of a 32-wide step t is taken to be
+// 32t + 16(j/4) + 4(l/16) + j%4 -- two accumulator tiles make one step.  So
+// the chained GEMMs never leave registers.  The weights are pre-split and
+// pre-arranged in LDS in the order the lanes consume them: one pair of
+// 16-byte reads per lane feeds three matrix instructions.  The radial basis
+// is generated in registers from d (no E x K tensor exists anywhere).
 //
 // Work distribution: persistent blocks (one per CU, weights staged once into
 // LDS, int16 codes dequantised while staging); each wavefront loops over
-// 16-pair tiles.
+// 16-pair tiles of an XCD-contiguous range.
 #include "sn_internal.h"
 
 namespace sn {
 
 namespace {
 
-constexpr int kFwdThreads = 1024;   // 4 wavefronts per SIMD (<= 128 VGPRs)
-constexpr int kBwdThreads = 512;    // 2 wavefronts per SIMD (<= 256 VGPRs)
+constexpr int kFwdThreads = 1024;   // 4 wavefronts per SIMD
+constexpr int kBwdThreads = 512;    // 2 wavefronts per SIMD
 constexpr float kPi = 3.14159265358979323846f;
+constexpr float kLoScale = 2048.0f;        // 2^11
+constexpr float kLoUnscale = 1.0f / 2048.0f;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+// One lane's A-operand fragment of one 32-wide k step: 8 weights as hi, lo.
+struct Frag {
+    half8 hi, lo;
+};
 
 struct FilterArgs {
     int K;
@@ -50,11 +68,12 @@ struct FilterArgs {
     const float *x, *gy;         // [N][F]
     const float *phi_in;         // [P][F]
     float *S;                    // [P]
+    const float2 *rowmax;        // [N]: max_f |x_i[f]|, max_f |g_y_i[f]|
     int accumulate;
 };
 
 template <int F>
-__device__ inline float w1(const FilterArgs &a, int k, int f) {   // A1[k][f]
+__device__ inline float w1(const FilterArgs &a, int k, int f) {   // A1[k][f], 0 beyond K
     if (k >= a.K) return 0.0f;
     if (a.qA1) return (float)a.qA1[k * F + f] * a.sA1[f];
     return a.A1[k * F + f];
@@ -64,6 +83,37 @@ __device__ inline float w2(const FilterArgs &a, int g, int f) {   // A2[g][f]
     if (a.qA2) return (float)a.qA2[g * F + f] * a.sA2[f];
     return a.A2[g * F + f];
 }
+
+__device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const _Float16 h = (_Float16)v[j];
+        hi[j] = h;
+        lo[j] = (_Float16)((v[j] - (float)h) * kLoScale);
+    }
+}
+
+__device__ inline Frag make_frag(const float (&v)[8]) {
+    Frag f;
+    split8(v, f.hi, f.lo);
+    return f;
+}
+
+// acc += A.B in split form (main: hi.hi, corr: hi.lo + lo.hi)
+__device__ inline void mma3(const Frag &w, const half8 &bh, const half8 &bl, floatx4 &main, floatx4 &corr) {
+    main = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.hi, bh, main, 0, 0, 0);
+    corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.hi, bl, corr, 0, 0, 0);
+    corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.lo, bh, corr, 0, 0, 0);
+}
+
+// k index of value j of the B operand of a chained 32-wide step t (two
+// accumulator tiles 2t and 2t+1), for the lane in k-slot s
+__device__ inline int chain_k(int t, int s, int j) { return 32 * t + 16 * (j >> 2) + 4 * s + (j & 3); }
+
+// k index (into the radial basis) of row r of g_rbf tile kt for k-slot s:
+// chosen so that each lane's rows are the basis functions it generated for
+// the B operand of the first GEMM (k = 32 ks + 8 s + j).
+__device__ inline int rbf_row_k(int kt, int s, int r) { return 32 * (kt >> 1) + 8 * s + 4 * (kt & 1) + r; }
 
 // Tiles of 16 pairs handled by this wavefront.  The grid is a multiple of
 // the XCD count; the blocks of one XCD share one contiguous range of tiles
@@ -79,80 +129,79 @@ __device__ inline void tile_range(int64_t P, int64_t &tile, int64_t &end, int64_
     stride = (int64_t)nxb * waves;
 }
 
-__device__ inline float rbf(const FilterArgs &a, float d, int k) {
+__device__ inline float rbf_val(const FilterArgs &a, float d, int k) {
     if (k >= a.K) return 0.0f;
     const float t = d - (a.lo + (float)k * a.dmu);
     return fast_exp(-a.gamma * t * t);
 }
 
-// GEMM 1 shared by both passes: acc[m] = (rbf(d) A1)^T for the lane's pair.
-// s_f1 layout: [m][kq][lane] float4, component r = step 4kq + r, holding
-// A1[4 step + lane/16][16 m + lane%16].  KS = ceil(K/4) steps are issued;
-// the zero padding of the last group of four is skipped.
+// Stage A1 for the first GEMM: s_a1[(m*KS + ks)*64 + l] holds, for output
+// feature f = 16m + l%16, the weights A1[k][f], k = 32 ks + 8(l/16) + j.
 template <int F>
-__device__ inline void gemm_rbf(const FilterArgs &a, const float4 *s_f1, int KQ, int KS, float d, int lane,
-                                floatx4 (&acc)[F / 16]) {
+__device__ inline void stage_a1(const FilterArgs &a, Frag *s_a1, int KS) {
+    constexpr int MT = F / 16;
+    for (int idx = threadIdx.x; idx < MT * KS * 64; idx += blockDim.x) {
+        const int m = idx / (KS * 64), ks = (idx / 64) % KS, l = idx % 64;
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = w1<F>(a, 32 * ks + 8 * (l / 16) + j, 16 * m + l % 16);
+        s_a1[idx] = make_frag(v);
+    }
+}
+
+// First GEMM, acc = (rbf(d) A1)^T in split form; rb receives the lane's
+// basis values rbf_k, k = 32 ks + 8 s + j.
+template <int F>
+__device__ inline void gemm_rbf(const FilterArgs &a, const Frag *s_a1, int KS, float d, int lane,
+                                floatx4 (&main)[F / 16], floatx4 (&corr)[F / 16], float (&rb)[2][8]) {
     constexpr int MT = F / 16;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int kq = 0; kq < KQ; ++kq) {
-        const int nstep = min(4, KS - 4 * kq);
-        float bv[4];
+    for (int m = 0; m < MT; ++m) main[m] = corr[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bv[r] = rbf(a, d, 4 * (4 * kq + r) + lane / 16);
-        if (nstep == 4) {
+    for (int ks = 0; ks < 2; ++ks) {
+        if (ks < KS) {
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float4 w = s_f1[(m * KQ + kq) * 64 + lane];
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.x, bv[0], acc[m], 0, 0, 0);
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.y, bv[1], acc[m], 0, 0, 0);
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.z, bv[2], acc[m], 0, 0, 0);
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.w, bv[3], acc[m], 0, 0, 0);
-            }
+            for (int j = 0; j < 8; ++j) rb[ks][j] = rbf_val(a, d, 32 * ks + 8 * (lane / 16) + j);
+            half8 bh, bl;
+            split8(rb[ks], bh, bl);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) mma3(s_a1[(m * KS + ks) * 64 + lane], bh, bl, main[m], corr[m]);
         } else {
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float4 w = s_f1[(m * KQ + kq) * 64 + lane];
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.x, bv[0], acc[m], 0, 0, 0);
-                if (nstep > 1) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.y, bv[1], acc[m], 0, 0, 0);
-                if (nstep > 2) acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.z, bv[2], acc[m], 0, 0, 0);
-            }
+            for (int j = 0; j < 8; ++j) rb[ks][j] = 0.0f;
         }
     }
 }
 
-template <int F>
-__device__ inline void stage_f1(const FilterArgs &a, float4 *s_f1, int KQ) {
-    constexpr int MT = F / 16;
-    for (int idx = threadIdx.x; idx < MT * KQ * 64; idx += blockDim.x) {
-        const int m = idx / (KQ * 64), kq = (idx / 64) % KQ, l = idx % 64;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = w1<F>(a, 4 * (4 * kq + r) + l / 16, 16 * m + l % 16);
-        s_f1[idx] = make_float4(v[0], v[1], v[2], v[3]);
-    }
+// 2^e such that |x| * 2^-e <= 1 for the largest |x| of the lane's pair
+// (the pair's values are spread over the four k-slot lanes l%16 + 16 s).
+__device__ inline int pair_exponent(float amax) {
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    return amax > 0.0f ? ilogbf(amax) + 1 : 0;
 }
 
 template <int F>
 __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
-    __shared__ float4 s_f1[MT * 4 * 64];          // K <= 64: at most 4 groups of 4 steps
-    __shared__ float4 s_f2[MT * MT * 64];         // [m][m2][lane]: A2[16 m2 + 4(l/16) + r][16 m + l%16]
+    constexpr int T2 = MT / 2;                 // 32-wide k steps of the F x F GEMM
+    __shared__ Frag s_a1[MT * 2 * 64];
+    __shared__ Frag s_a2[MT * T2 * 64];        // [m][t][l]: A2[chain_k(t, l/16, j)][16 m + l%16]
     __shared__ float s_b1[F], s_b2[F];
-    const int KS = (a.K + 3) / 4;
-    const int KQ = (KS + 3) / 4;
-    stage_f1<F>(a, s_f1, KQ);
-    for (int idx = threadIdx.x; idx < MT * MT * 64; idx += blockDim.x) {
-        const int m = idx / (MT * 64), m2 = (idx / 64) % MT, l = idx % 64;
-        float v[4];
+    const int KS = (a.K + 31) / 32;
+    stage_a1<F>(a, s_a1, KS);
+    for (int idx = threadIdx.x; idx < MT * T2 * 64; idx += blockDim.x) {
+        const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
+        float v[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = w2<F>(a, 16 * m2 + 4 * (l / 16) + r, 16 * m + l % 16);
-        s_f2[idx] = make_float4(v[0], v[1], v[2], v[3]);
+        for (int j = 0; j < 8; ++j) v[j] = w2<F>(a, chain_k(t, l / 16, j), 16 * m + l % 16);
+        s_a2[idx] = make_frag(v);
     }
     for (int f = threadIdx.x; f < F; f += blockDim.x) { s_b1[f] = a.b1[f]; s_b2[f] = a.b2[f]; }
     __syncthreads();
 
     const int lane = threadIdx.x % 64;
+    const int slot = lane / 16;
     int64_t tile, tile_end, stride;
     tile_range(a.P, tile, tile_end, stride);
     for (; tile < tile_end; tile += stride) {
@@ -161,33 +210,32 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
         asm volatile("" ::: "memory");
         const int64_t p = tile * 16 + lane % 16;
         const float d = (p < a.P) ? a.dsrc[p * a.dstride + a.doff] : 0.0f;
-        floatx4 acc1[MT];
-        gemm_rbf<F>(a, s_f1, KQ, KS, d, lane, acc1);
-        float z[MT][4];
+        floatx4 am[MT], ac[MT];
+        float rb[2][8];
+        gemm_rbf<F>(a, s_a1, KS, d, lane, am, ac, rb);
+        // z = ssp(a), converted step by step into split B operands
+        half8 zh[T2], zl[T2];
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int t = 0; t < T2; ++t) {
+            float v[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) z[m][r] = ssp(acc1[m][r] + s_b1[16 * m + 4 * (lane / 16) + r]);
-        floatx4 acc2[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc2[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m2 = 0; m2 < MT; ++m2) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float4 w = s_f2[(m * MT + m2) * 64 + lane];
-                acc2[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.x, z[m2][0], acc2[m], 0, 0, 0);
-                acc2[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.y, z[m2][1], acc2[m], 0, 0, 0);
-                acc2[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.z, z[m2][2], acc2[m], 0, 0, 0);
-                acc2[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.w, z[m2][3], acc2[m], 0, 0, 0);
+            for (int j = 0; j < 8; ++j) {
+                const int m = 2 * t + (j >> 2), r = j & 3;
+                v[j] = ssp(am[m][r] + ac[m][r] * kLoUnscale + s_b1[16 * m + 4 * slot + r]);
             }
+            split8(v, zh[t], zl[t]);
         }
-        if (p < a.P) {
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int f0 = 16 * m + 4 * (lane / 16);
-                float4 v = make_float4(acc2[m][0] + s_b2[f0], acc2[m][1] + s_b2[f0 + 1], acc2[m][2] + s_b2[f0 + 2],
-                                       acc2[m][3] + s_b2[f0 + 3]);
+        for (int m = 0; m < MT; ++m) {
+            floatx4 main = {0.f, 0.f, 0.f, 0.f}, corr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < T2; ++t) mma3(s_a2[(m * T2 + t) * 64 + lane], zh[t], zl[t], main, corr);
+            if (p < a.P) {
+                const int f0 = 16 * m + 4 * slot;
+                float4 v = make_float4(main[0] + corr[0] * kLoUnscale + s_b2[f0],
+                                       main[1] + corr[1] * kLoUnscale + s_b2[f0 + 1],
+                                       main[2] + corr[2] * kLoUnscale + s_b2[f0 + 2],
+                                       main[3] + corr[3] * kLoUnscale + s_b2[f0 + 3]);
                 *reinterpret_cast<float4 *>(a.phi + p * F + f0) = v;
             }
         }
@@ -197,39 +245,42 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
 template <int F>
 __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
-    constexpr int FS = F / 4;        // features per k-slot in the g_phi GEMM
-    constexpr int SQ = FS / 4;
-    __shared__ float4 s_f1[MT * 4 * 64];
-    __shared__ float4 s_f2b[MT * SQ * 64];   // [m][sq][lane]: A2[16 m + l%16][FS (l/16) + 4 sq + r]
-    __shared__ float4 s_f1b[4 * MT * 64];    // [kt][m2][lane]: A1[16 kt + l%16][16 m2 + 4(l/16) + r]
+    constexpr int T2 = MT / 2;
+    __shared__ Frag s_a1[MT * 2 * 64];
+    __shared__ Frag s_a2b[MT * T2 * 64];   // [m][t][l]: A2[16 m + l%16][32 t + 8(l/16) + j]
+    __shared__ Frag s_a1b[4 * T2 * 64];    // [kt][t][l]: A1[rbf_row_k(kt, (l%16)/4, l%4)][chain_k(t, l/16, j)]
     __shared__ float s_b1[F];
-    const int KS = (a.K + 3) / 4;
-    const int KQ = (KS + 3) / 4;
-    const int KT = (a.K + 15) / 16;
-    stage_f1<F>(a, s_f1, KQ);
-    for (int idx = threadIdx.x; idx < MT * SQ * 64; idx += blockDim.x) {
-        const int m = idx / (SQ * 64), sq = (idx / 64) % SQ, l = idx % 64;
-        float v[4];
+    const int KS = (a.K + 31) / 32;
+    const int KT = 2 * KS;
+    stage_a1<F>(a, s_a1, KS);
+    for (int idx = threadIdx.x; idx < MT * T2 * 64; idx += blockDim.x) {
+        const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
+        float v[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = w2<F>(a, 16 * m + l % 16, FS * (l / 16) + 4 * sq + r);
-        s_f2b[idx] = make_float4(v[0], v[1], v[2], v[3]);
+        for (int j = 0; j < 8; ++j) v[j] = w2<F>(a, 16 * m + l % 16, 32 * t + 8 * (l / 16) + j);
+        s_a2b[idx] = make_frag(v);
     }
-    for (int idx = threadIdx.x; idx < KT * MT * 64; idx += blockDim.x) {
-        const int kt = idx / (MT * 64), m2 = (idx / 64) % MT, l = idx % 64;
-        float v[4];
+    for (int idx = threadIdx.x; idx < KT * T2 * 64; idx += blockDim.x) {
+        const int kt = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
+        const int row = l % 16;
+        const int k = rbf_row_k(kt, row / 4, row % 4);
+        float v[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = w1<F>(a, 16 * kt + l % 16, 16 * m2 + 4 * (l / 16) + r);
-        s_f1b[idx] = make_float4(v[0], v[1], v[2], v[3]);
+        for (int j = 0; j < 8; ++j) v[j] = w1<F>(a, k, chain_k(t, l / 16, j));
+        s_a1b[idx] = make_frag(v);
     }
     for (int f = threadIdx.x; f < F; f += blockDim.x) s_b1[f] = a.b1[f];
     __syncthreads();
 
-    const int lane = threadIdx.x % 64;
-    const int slot = lane / 16;
     int64_t tile, tile_end, stride;
     tile_range(a.P, tile, tile_end, stride);
     for (; tile < tile_end; tile += stride) {
         asm volatile("" ::: "memory");
+        // lane-derived values are recomputed per tile (opaque to the
+        // compiler) instead of being hoisted and kept live across the loop
+        int lane = threadIdx.x % 64;
+        asm volatile("" : "+v"(lane));
+        const int slot = lane / 16;
         const int64_t p = tile * 16 + lane % 16;
         const bool live = p < a.P;
         const float d = live ? a.dsrc[p * a.dstride + a.doff] : 0.0f;
@@ -241,83 +292,99 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
             fc = c * c;
             dfc = -(kPi / a.cutoff) * sn * c;
         }
-        // G = g_y_i x_j + g_y_j x_i over this lane's quarter of the features,
-        // gathered in two halves to bound the loads in flight
-        float gphi[FS];
-        float gfc = 0.0f;
+        // recompute a = rbf A1 + b1 and keep sigmoid(a) (and the lane's rbf_k)
+        float sg[MT][4];
+        float rb[2][8];
         {
-            const int64_t bi = (int64_t)ij.x * F + FS * slot, bj = (int64_t)ij.y * F + FS * slot;
-            const int64_t bp = (live ? p : 0) * F + FS * slot;
+            floatx4 am[MT], ac[MT];
+            gemm_rbf<F>(a, s_a1, KS, d, lane, am, ac, rb);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                asm volatile("" ::: "memory");
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int qq = 0; qq < SQ / 2; ++qq) {
-                    const int q = half * (SQ / 2) + qq;
-                    const float4 gyi = *reinterpret_cast<const float4 *>(a.gy + bi + 4 * q);
-                    const float4 gyj = *reinterpret_cast<const float4 *>(a.gy + bj + 4 * q);
-                    const float4 xi = *reinterpret_cast<const float4 *>(a.x + bi + 4 * q);
-                    const float4 xj = *reinterpret_cast<const float4 *>(a.x + bj + 4 * q);
-                    const float4 ph = *reinterpret_cast<const float4 *>(a.phi_in + bp + 4 * q);
+                for (int r = 0; r < 4; ++r)
+                    sg[m][r] = sigm(am[m][r] + ac[m][r] * kLoUnscale + s_b1[16 * m + 4 * slot + r]);
+        }
+        // g_z^T = A2 g_phi^T, g_phi = fc G, G = g_y_i x_j + g_y_j x_i on the
+        // features 32 t + 8 slot + j.  The pair's operands are scaled by 2^-e1,
+        // with e1 from a bound on |g_phi| (per-atom row maxima), so each
+        // 32-feature step is gathered, split and multiplied straight away.
+        int e1 = 0;
+        {
+            const float2 mi = live ? a.rowmax[ij.x] : make_float2(0.f, 0.f);
+            const float2 mj = live ? a.rowmax[ij.y] : make_float2(0.f, 0.f);
+            const float bound = fc * (mi.y * mj.x + mj.y * mi.x);
+            e1 = bound > 0.0f ? ilogbf(bound) + 1 : 0;
+        }
+        const float fs = ldexpf(fc, -e1);
+        float gfc = 0.0f;
+        floatx4 zm[MT], zc[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) zm[m] = zc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+        {
+            const int64_t bi = (int64_t)ij.x * F + 8 * slot, bj = (int64_t)ij.y * F + 8 * slot;
+            const int64_t bp = (live ? p : 0) * F + 8 * slot;
+#pragma unroll
+            for (int t = 0; t < T2; ++t) {
+                asm volatile("" ::: "memory");   // at most one step's gathers in flight
+                float v[8];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int o = 32 * t + 4 * q;
+                    const float4 gyi = *reinterpret_cast<const float4 *>(a.gy + bi + o);
+                    const float4 gyj = *reinterpret_cast<const float4 *>(a.gy + bj + o);
+                    const float4 xi = *reinterpret_cast<const float4 *>(a.x + bi + o);
+                    const float4 xj = *reinterpret_cast<const float4 *>(a.x + bj + o);
+                    const float4 ph = *reinterpret_cast<const float4 *>(a.phi_in + bp + o);
                     const float g0 = gyi.x * xj.x + gyj.x * xi.x, g1 = gyi.y * xj.y + gyj.y * xi.y;
                     const float g2 = gyi.z * xj.z + gyj.z * xi.z, g3 = gyi.w * xj.w + gyj.w * xi.w;
                     gfc += g0 * ph.x + g1 * ph.y + g2 * ph.z + g3 * ph.w;
-                    gphi[4 * q + 0] = fc * g0; gphi[4 * q + 1] = fc * g1;
-                    gphi[4 * q + 2] = fc * g2; gphi[4 * q + 3] = fc * g3;
+                    v[4 * q + 0] = fs * g0; v[4 * q + 1] = fs * g1;
+                    v[4 * q + 2] = fs * g2; v[4 * q + 3] = fs * g3;
                 }
+                half8 bh, bl;
+                split8(v, bh, bl);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) mma3(s_a2b[(m * T2 + t) * 64 + lane], bh, bl, zm[m], zc[m]);
             }
         }
-        // g_z^T = A2 g_phi^T  (k = feature f = FS slot + step)
-        floatx4 gz[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) gz[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int sq = 0; sq < SQ; ++sq) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const float4 w = s_f2b[(m * SQ + sq) * 64 + lane];
-                gz[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.x, gphi[4 * sq + 0], gz[m], 0, 0, 0);
-                gz[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.y, gphi[4 * sq + 1], gz[m], 0, 0, 0);
-                gz[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.z, gphi[4 * sq + 2], gz[m], 0, 0, 0);
-                gz[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.w, gphi[4 * sq + 3], gz[m], 0, 0, 0);
-            }
-        }
-        // recompute a = rbf A1 + b1;  g_a = g_z (.) sigmoid(a)
-        floatx4 acc1[MT];
-        gemm_rbf<F>(a, s_f1, KQ, KS, d, lane, acc1);
+        // g_a = g_z (.) sigmoid(a)
+        float ga[MT][4];
+        float amax = 0.0f;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) gz[m][r] *= sigm(acc1[m][r] + s_b1[16 * m + 4 * slot + r]);
-        // g_rbf^T = A1 g_a^T
-        floatx4 ge[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) ge[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m2 = 0; m2 < MT; ++m2) {
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                if (kt < KT) {
-                    const float4 w = s_f1b[(kt * MT + m2) * 64 + lane];
-                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.x, gz[m2][0], ge[kt], 0, 0, 0);
-                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.y, gz[m2][1], ge[kt], 0, 0, 0);
-                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.z, gz[m2][2], ge[kt], 0, 0, 0);
-                    ge[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(w.w, gz[m2][3], ge[kt], 0, 0, 0);
-                }
+            for (int r = 0; r < 4; ++r) {
+                ga[m][r] = ldexpf(zm[m][r] + zc[m][r] * kLoUnscale, e1) * sg[m][r];
+                amax = fmaxf(amax, fabsf(ga[m][r]));
             }
+        // g_rbf^T = A1 g_a^T (rows permuted to the lane's own basis functions)
+        const int e2 = pair_exponent(amax);
+        floatx4 em[4], ec[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) em[kt] = ec[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < T2; ++t) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = ldexpf(ga[2 * t + (j >> 2)][j & 3], -e2);
+            half8 bh, bl;
+            split8(v, bh, bl);
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                if (kt < KT) mma3(s_a1b[(kt * T2 + t) * 64 + lane], bh, bl, em[kt], ec[kt]);
         }
-        // S_p = sum_k g_rbf_k rbf_k'(d) + g_fc fc'(d), summed over the four k-slots
+        // S_p = sum_k g_rbf_k rbf_k'(d) + g_fc fc'(d), summed over the four k-slots;
+        // rbf_k'(d) = -2 gamma (d - mu_k) rbf_k with rbf_k kept from the recompute
         float sp = gfc * dfc;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             if (kt < KT) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int k = 16 * kt + 4 * slot + r;
-                    if (k < a.K) {
-                        const float t = d - (a.lo + (float)k * a.dmu);
-                        sp += ge[kt][r] * (-2.0f * a.gamma * t * fast_exp(-a.gamma * t * t));
-                    }
+                    const int k = rbf_row_k(kt, slot, r);
+                    const float g = ldexpf(em[kt][r] + ec[kt][r] * kLoUnscale, e2);
+                    const float tt = d - (a.lo + (float)k * a.dmu);
+                    sp += g * (-2.0f * a.gamma * tt * rb[kt >> 1][4 * (kt & 1) + r]);
                 }
             }
         }
@@ -325,6 +392,24 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         sp += __shfl_xor(sp, 32, 64);
         if (live && slot == 0) a.S[p] = a.accumulate ? a.S[p] + sp : sp;
     }
+}
+
+// per atom: max_f |x_i[f]| and max_f |g_y_i[f]| (LPR = F/4 lanes per row)
+template <int F>
+__global__ __launch_bounds__(256) void rowmax_kernel(int N, const float *x, const float *gy, float2 *out) {
+    constexpr int LPR = F / 4;
+    const int sub = threadIdx.x % LPR;
+    const int row = (blockIdx.x * 256 + threadIdx.x) / LPR;
+    if (row >= N) return;
+    const float4 a = *reinterpret_cast<const float4 *>(x + (int64_t)row * F + 4 * sub);
+    const float4 b = *reinterpret_cast<const float4 *>(gy + (int64_t)row * F + 4 * sub);
+    float mx = fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w)));
+    float mg = fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w)));
+    for (int o = LPR / 2; o > 0; o >>= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, o, LPR));
+        mg = fmaxf(mg, __shfl_xor(mg, o, LPR));
+    }
+    if (sub == 0) out[row] = make_float2(mx, mg);
 }
 
 int num_cus() {
@@ -342,7 +427,7 @@ int num_cus() {
 
 FilterArgs make_args(const sn_model &m, int t) {
     const int F = m.n_features, K = m.n_rbf, I = m.n_interactions, T = m.n_types;
-    int64_t off[3 + 9 * 16 + 2 + 1];
+    int64_t off[9 * 16 + 6];
     sn_param_offsets(T, I, F, K, off, (int32_t)(sizeof(off) / sizeof(off[0])));
     const int64_t *blk = off + 1 + 9 * t;   // W_in, A1, b1, A2, b2, Wo1, bo1, Wo2, bo2
     FilterArgs a = {};
@@ -375,7 +460,9 @@ sn_status launch_fwd(const FilterArgs &a, hipStream_t s) {
 }
 
 template <int F>
-sn_status launch_bwd(const FilterArgs &a, hipStream_t s) {
+sn_status launch_bwd(const FilterArgs &a, int N, float2 *rowmax, hipStream_t s) {
+    rowmax_kernel<F><<<(N + 256 / (F / 4) - 1) / (256 / (F / 4)), 256, 0, s>>>(N, a.x, a.gy, rowmax);
+    SN_TRY(launch_status());
     const int64_t tiles = (a.P + 15) / 16;
     const int waves = kBwdThreads / 64;
     const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
@@ -416,9 +503,9 @@ sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t
     return fwd_dispatch(a, m.n_features, s);
 }
 
-sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const int2 *pair_ij, int64_t P,
-                          const float *phi, const float *x, const float *gy, float *S, int accumulate,
-                          hipStream_t s) {
+sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const int2 *pair_ij, int64_t P, int N,
+                          const float *phi, const float *x, const float *gy, float2 *rowmax, float *S,
+                          int accumulate, hipStream_t s) {
     if (P <= 0) return SN_OK;
     FilterArgs a = make_args(m, t);
     a.dsrc = reinterpret_cast<const float *>(pgeo);
@@ -430,12 +517,13 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const in
     a.gy = gy;
     a.phi_in = phi;
     a.S = S;
+    a.rowmax = rowmax;
     a.accumulate = accumulate;
     ProfScope ps(K_FILTER_BWD, s);
     switch (m.n_features) {
-        case 32: return launch_bwd<32>(a, s);
-        case 64: return launch_bwd<64>(a, s);
-        case 128: return launch_bwd<128>(a, s);
+        case 32: return launch_bwd<32>(a, N, rowmax, s);
+        case 64: return launch_bwd<64>(a, N, rowmax, s);
+        case 128: return launch_bwd<128>(a, N, rowmax, s);
         default: return SN_ERR_INVALID;
     }
 }

@@ -69,7 +69,7 @@ __device__ inline int xcd_block(int n) {
 
 enum KernelClass {
     K_NB_GRID = 0, K_NB_BIN, K_NB_SCAN, K_NB_COUNT, K_NB_FILL, K_NB_REV,
-    K_PAIRS, K_EMBED, K_DENSE, K_FILTER_FWD, K_CFCONV, K_READOUT, K_ENERGY,
+    K_PAIRS, K_EMBED, K_MLP, K_FILTER_FWD, K_CFCONV, K_READOUT, K_ENERGY,
     K_FILTER_BWD, K_FORCES, K_VERLET, K_KINETIC, K_NUM_CLASSES
 };
 
@@ -99,7 +99,7 @@ struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
 };
 
 struct EfLayout {            // energy/force scratch (offsets from ws base)
-    size_t up_first, up_ptr, edge_pair, pair_ij, pgeo, pfc, phi, x, o, gy, h, y, gh, gt, q, gq, eps, S, total;
+    size_t up_first, up_ptr, edge_pair, pair_ij, pgeo, pfc, phi, x, o, gy, h, y, gh, eps, S, rowmax, total;
 };
 
 NbLayout nb_layout(const sn_system &sys, size_t base);
@@ -126,9 +126,9 @@ sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_
 // filter.hip
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, hipStream_t s);
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
-sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const int2 *pair_ij, int64_t P,
-                          const float *phi, const float *x, const float *gy, float *S, int accumulate,
-                          hipStream_t s);
+sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const int2 *pair_ij, int64_t P, int N,
+                          const float *phi, const float *x, const float *gy, float2 *rowmax, float *S,
+                          int accumulate, hipStream_t s);
 
 // graph.hip
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
@@ -140,15 +140,19 @@ sn_status forces_rows(int N, const int32_t *row_ptr, const int32_t *col, const i
                       const float4 *pgeo, const float *S, float *forces, int *status, hipStream_t s);
 
 // atomwise.hip
-enum Prologue { PRO_NONE = 0, PRO_SSP = 1 };
-enum Epilogue { EPI_STORE = 0, EPI_SIGMUL = 1, EPI_ACCUM = 2 };
-sn_status dense(int N, int Fi, int Fo, const float *X, const float *W, int transW, const float *bias,
-                int pro, int epi, const float *aux, float *Y, hipStream_t s);
 sn_status embed(int N, int F, int T, const int32_t *types, const float *emb, float *h, int *status,
                 hipStream_t s);
-sn_status readout(int N, int H, const float *q, const float *R2, const float *c2, float *eps, float *gq,
-                  hipStream_t s);
 sn_status replica_sum(int B, const int32_t *replica_ptr, const float *eps, float *energy, hipStream_t s);
+
+// mlp.hip (fused atom-wise layers; see the kernel comments there)
+sn_status mlp_x(int N, int F, const float *h, const float *W_in, float *x, hipStream_t s);
+sn_status mlp_out(int N, int F, const float *y, const float *Wo1, const float *bo1, const float *Wo2,
+                  const float *bo2, float *o, float *h, hipStream_t s);
+sn_status mlp_readout(int N, int F, const float *h, const float *R1, const float *c1, const float *R2,
+                      const float *c2, float *eps, float *gh, hipStream_t s);
+sn_status mlp_bwd_out(int N, int F, const float *gh, const float *Wo2, const float *o, const float *Wo1, float *gy,
+                      hipStream_t s);
+sn_status mlp_bwd_x(int N, int F, const float *gx, const float *W_in, float *gh, hipStream_t s);
 
 // verlet (api.hip)
 
