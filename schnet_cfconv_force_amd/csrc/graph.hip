@@ -114,21 +114,27 @@ __global__ void pair_check_kernel(const int32_t *up_ptr, int N, int64_t P, int *
     if (up_ptr[N] != P) flag_status(status, SN_ERR_INVALID);
 }
 
-// y_i = sum_{e in row i} pfc[p] * phi[p] (.) in[col(e)], LPR = F/4 lanes per row
+// y_i = sum_{e in row i} pfc[p] * phi[p] (.) in[col(e)].  One wavefront per
+// row: F/4 lanes cover the features (one float4 each) and the 64/(F/4) lane
+// groups take interleaved edges of the same row, so every wavefront streams
+// one row with several edges in flight and no lanes wait on a longer row.
 template <int F>
 __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const int32_t *row_ptr,
                                                      const int32_t *col, const int32_t *edge_pair, const float *pfc,
                                                      const float *phi, const float *in, float *out) {
-    constexpr int LPR = F / 4;
-    const int sub = threadIdx.x % LPR;
+    constexpr int LPR = F / 4;            // lanes per feature row
+    constexpr int G = 64 / LPR;           // edges in flight per wavefront
+    const int lane = threadIdx.x % 64;
+    const int sub = lane % LPR, grp = lane / LPR;
     const int blk = xcd_block(nblocks);
     if (blk < 0) return;
-    const int row = (blk * 256 + threadIdx.x) / LPR;
-    if (row >= N) return;                      // whole lane group leaves together
+    const int row = blk * 4 + threadIdx.x / 64;
+    if (row >= N) return;                 // whole wavefront leaves together
     const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int eb = e0; eb < e1; eb += LPR) {
-        const int k = eb + sub;
+    for (int eb = e0; eb < e1; eb += 64) {
+        // 64 edges' indices loaded once, coalesced, then broadcast
+        const int k = eb + lane;
         int cj = 0, cp = 0;
         float cw = 0.0f;
         if (k < e1) {
@@ -136,21 +142,34 @@ __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const i
             cp = edge_pair[k];
             cw = pfc[cp];
         }
-        const int n = min(LPR, e1 - eb);
+        const int n = min(64, e1 - eb);
+        const int rounds = (n + G - 1) / G;     // uniform over the wavefront
 #pragma unroll 4
-        for (int t = 0; t < n; ++t) {
-            const int j = __shfl(cj, t, LPR);
-            const int p = __shfl(cp, t, LPR);
-            const float w = __shfl(cw, t, LPR);
-            const float4 f = *reinterpret_cast<const float4 *>(phi + (int64_t)p * F + 4 * sub);
-            const float4 x = *reinterpret_cast<const float4 *>(in + (int64_t)j * F + 4 * sub);
-            acc.x += w * f.x * x.x;
-            acc.y += w * f.y * x.y;
-            acc.z += w * f.z * x.z;
-            acc.w += w * f.w * x.w;
+        for (int r = 0; r < rounds; ++r) {
+            const int t = r * G + grp;
+            const int src = t < n ? t : n - 1;  // shuffle sources are always live lanes
+            const int j = __shfl(cj, src, 64);
+            const int p = __shfl(cp, src, 64);
+            const float w = __shfl(cw, src, 64);
+            if (t < n) {
+                const float4 f = *reinterpret_cast<const float4 *>(phi + (int64_t)p * F + 4 * sub);
+                const float4 x = *reinterpret_cast<const float4 *>(in + (int64_t)j * F + 4 * sub);
+                acc.x += w * f.x * x.x;
+                acc.y += w * f.y * x.y;
+                acc.z += w * f.z * x.z;
+                acc.w += w * f.w * x.w;
+            }
         }
     }
-    *reinterpret_cast<float4 *>(out + (int64_t)row * F + 4 * sub) = acc;
+    // combine the lane groups (fixed order: deterministic)
+#pragma unroll
+    for (int o = 32; o >= LPR; o >>= 1) {
+        acc.x += __shfl_xor(acc.x, o, 64);
+        acc.y += __shfl_xor(acc.y, o, 64);
+        acc.z += __shfl_xor(acc.z, o, 64);
+        acc.w += __shfl_xor(acc.w, o, 64);
+    }
+    if (grp == 0) *reinterpret_cast<float4 *>(out + (int64_t)row * F + 4 * sub) = acc;
 }
 
 // F_i = sum_{e in row i} S[p(e)] * u_e, 16 lanes per row
@@ -221,8 +240,7 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
 sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
                  const float *pfc, const float *phi, const float *in, float *out, hipStream_t s) {
     ProfScope ps(K_CFCONV, s);
-    const int rows_per_block = 256 / (F / 4);
-    const int nb = (N + rows_per_block - 1) / rows_per_block;
+    const int nb = (N + 3) / 4;          // four rows (wavefronts) per block
     const int grid = xcd_grid(nb);
     switch (F) {
         case 32: cfconv_kernel<32><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi, in, out); break;

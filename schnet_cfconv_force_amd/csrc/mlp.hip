@@ -23,6 +23,9 @@ namespace {
 
 constexpr float kLoScale = 2048.0f;
 constexpr float kLoUnscale = 1.0f / 2048.0f;
+// 8 wavefronts (128 atoms) per block: one block per CU holds the staged
+// weights, and the grid of the largest systems fits in one pass of the CUs
+constexpr int kMlpThreads = 512;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
@@ -104,7 +107,7 @@ __device__ inline void stage(Frag *dst, const float *W, int trans, int kdim, int
 }
 
 template <int F, int MODE>
-__global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
+__global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
     using S = Shape<F, MODE>;
     constexpr int M1 = S::M1, T1 = S::T1, M2 = S::M2, T2 = S::T2;
     constexpr int TRANS1 = (MODE == MLP_BWD_OUT || MODE == MLP_BWD_X) ? 1 : 0;
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(256) void mlp_kernel(MlpArgs a) {
     __syncthreads();
 
     const int lane = threadIdx.x % 64, slot = lane / 16;
-    const int atom0 = (blockIdx.x * 4 + threadIdx.x / 64) * 16;
+    const int atom0 = (blockIdx.x * (kMlpThreads / 64) + threadIdx.x / 64) * 16;
     if (atom0 >= a.N) return;
     const int atom = atom0 + lane % 16;
     const bool live = atom < a.N;
@@ -248,11 +251,12 @@ template <int MODE>
 sn_status launch_mlp(int F, const MlpArgs &a, hipStream_t s) {
     if (a.N <= 0) return SN_OK;
     ProfScope ps(K_MLP, s);
-    const int grid = (a.N + 63) / 64;
+    const int atoms_per_block = 16 * (kMlpThreads / 64);
+    const int grid = (a.N + atoms_per_block - 1) / atoms_per_block;
     switch (F) {
-        case 32: mlp_kernel<32, MODE><<<grid, 256, 0, s>>>(a); break;
-        case 64: mlp_kernel<64, MODE><<<grid, 256, 0, s>>>(a); break;
-        case 128: mlp_kernel<128, MODE><<<grid, 256, 0, s>>>(a); break;
+        case 32: mlp_kernel<32, MODE><<<grid, kMlpThreads, 0, s>>>(a); break;
+        case 64: mlp_kernel<64, MODE><<<grid, kMlpThreads, 0, s>>>(a); break;
+        case 128: mlp_kernel<128, MODE><<<grid, kMlpThreads, 0, s>>>(a); break;
         default: return SN_ERR_INVALID;
     }
     return launch_status();
