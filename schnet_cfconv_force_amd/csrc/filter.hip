@@ -39,7 +39,7 @@ namespace sn {
 
 namespace {
 
-constexpr int kFwdThreads = 1024;   // 4 wavefronts per SIMD
+constexpr int kFwdThreads = 768;    // 3 wavefronts per SIMD
 constexpr int kBwdThreads = 512;    // 2 wavefronts per SIMD
 constexpr float kPi = 3.14159265358979323846f;
 constexpr float kLoScale = 2048.0f;        // 2^11
@@ -89,7 +89,7 @@ __device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
     for (int j = 0; j < 8; ++j) {
         const _Float16 h = (_Float16)v[j];
         hi[j] = h;
-        lo[j] = (_Float16)((v[j] - (float)h) * kLoScale);
+        lo[j] = (_Float16)fmaf((float)h, -kLoScale, v[j] * kLoScale);   // (x - hi) 2^11, exact
     }
 }
 
@@ -104,6 +104,25 @@ __device__ inline void mma3(const Frag &w, const half8 &bh, const half8 &bl, flo
     main = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.hi, bh, main, 0, 0, 0);
     corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.hi, bl, corr, 0, 0, 0);
     corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.lo, bh, corr, 0, 0, 0);
+}
+
+// The three split products for MT output tiles that share one B operand,
+// ordered so that dependent matrix instructions on the same accumulator are
+// MT instructions apart: hi.hi and hi.lo for every tile, then lo.hi.
+// Fragment of tile m at w[m * stride].
+template <int MT>
+__device__ inline void mma3_tiles(const Frag *w, int stride, const half8 &bh, const half8 &bl, floatx4 *main,
+                                  floatx4 *corr) {
+    half8 lo[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const Frag f = w[m * stride];
+        main[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.hi, bh, main[m], 0, 0, 0);
+        corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.hi, bl, corr[m], 0, 0, 0);
+        lo[m] = f.lo;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[m], bh, corr[m], 0, 0, 0);
 }
 
 // k index of value j of the B operand of a chained 32-wide step t (two
@@ -164,8 +183,10 @@ __device__ inline void gemm_rbf(const FilterArgs &a, const Frag *s_a1, int KS, f
             for (int j = 0; j < 8; ++j) rb[ks][j] = rbf_val(a, d, 32 * ks + 8 * (lane / 16) + j);
             half8 bh, bl;
             split8(rb[ks], bh, bl);
+            constexpr int MG = MT < 4 ? MT : 4;
 #pragma unroll
-            for (int m = 0; m < MT; ++m) mma3(s_a1[(m * KS + ks) * 64 + lane], bh, bl, main[m], corr[m]);
+            for (int m0 = 0; m0 < MT; m0 += MG)
+                mma3_tiles<MG>(s_a1 + (m0 * KS + ks) * 64 + lane, KS * 64, bh, bl, main + m0, corr + m0);
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) rb[ks][j] = 0.0f;
@@ -225,18 +246,24 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
             }
             split8(v, zh[t], zl[t]);
         }
+        constexpr int MG = MT < 4 ? MT : 4;    // output tiles per group
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            floatx4 main = {0.f, 0.f, 0.f, 0.f}, corr = {0.f, 0.f, 0.f, 0.f};
+        for (int m0 = 0; m0 < MT; m0 += MG) {
+            floatx4 main[MG], corr[MG];
 #pragma unroll
-            for (int t = 0; t < T2; ++t) mma3(s_a2[(m * T2 + t) * 64 + lane], zh[t], zl[t], main, corr);
+            for (int g = 0; g < MG; ++g) main[g] = corr[g] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < T2; ++t) mma3_tiles<MG>(s_a2 + (m0 * T2 + t) * 64 + lane, T2 * 64, zh[t], zl[t], main, corr);
             if (p < a.P) {
-                const int f0 = 16 * m + 4 * slot;
-                float4 v = make_float4(main[0] + corr[0] * kLoUnscale + s_b2[f0],
-                                       main[1] + corr[1] * kLoUnscale + s_b2[f0 + 1],
-                                       main[2] + corr[2] * kLoUnscale + s_b2[f0 + 2],
-                                       main[3] + corr[3] * kLoUnscale + s_b2[f0 + 3]);
-                *reinterpret_cast<float4 *>(a.phi + p * F + f0) = v;
+#pragma unroll
+                for (int g = 0; g < MG; ++g) {
+                    const int f0 = 16 * (m0 + g) + 4 * slot;
+                    float4 v = make_float4(main[g][0] + corr[g][0] * kLoUnscale + s_b2[f0],
+                                           main[g][1] + corr[g][1] * kLoUnscale + s_b2[f0 + 1],
+                                           main[g][2] + corr[g][2] * kLoUnscale + s_b2[f0 + 2],
+                                           main[g][3] + corr[g][3] * kLoUnscale + s_b2[f0 + 3]);
+                    *reinterpret_cast<float4 *>(a.phi + p * F + f0) = v;
+                }
             }
         }
     }
@@ -343,22 +370,25 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
                 }
                 half8 bh, bl;
                 split8(v, bh, bl);
+                constexpr int MG = MT < 4 ? MT : 4;
 #pragma unroll
-                for (int m = 0; m < MT; ++m) mma3(s_a2b[(m * T2 + t) * 64 + lane], bh, bl, zm[m], zc[m]);
+                for (int m0 = 0; m0 < MT; m0 += MG)
+                    mma3_tiles<MG>(s_a2b + (m0 * T2 + t) * 64 + lane, T2 * 64, bh, bl, zm + m0, zc + m0);
             }
         }
-        // g_a = g_z (.) sigmoid(a)
+        // g_a 2^-e1 = (g_z 2^-e1) (.) sigmoid(a); the 2^e1 is folded into e2
         float ga[MT][4];
         float amax = 0.0f;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                ga[m][r] = ldexpf(zm[m][r] + zc[m][r] * kLoUnscale, e1) * sg[m][r];
+                ga[m][r] = fmaf(zc[m][r], kLoUnscale, zm[m][r]) * sg[m][r];
                 amax = fmaxf(amax, fabsf(ga[m][r]));
             }
         // g_rbf^T = A1 g_a^T (rows permuted to the lane's own basis functions)
         const int e2 = pair_exponent(amax);
+        const float down2 = ldexpf(1.0f, -e2);
         floatx4 em[4], ec[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) em[kt] = ec[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -366,28 +396,32 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         for (int t = 0; t < T2; ++t) {
             float v[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = ldexpf(ga[2 * t + (j >> 2)][j & 3], -e2);
+            for (int j = 0; j < 8; ++j) v[j] = ga[2 * t + (j >> 2)][j & 3] * down2;
             half8 bh, bl;
             split8(v, bh, bl);
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-                if (kt < KT) mma3(s_a1b[(kt * T2 + t) * 64 + lane], bh, bl, em[kt], ec[kt]);
+            if (KT == 4) {
+                mma3_tiles<4>(s_a1b + t * 64 + lane, T2 * 64, bh, bl, em, ec);
+            } else {
+                mma3_tiles<2>(s_a1b + t * 64 + lane, T2 * 64, bh, bl, em, ec);
+            }
         }
         // S_p = sum_k g_rbf_k rbf_k'(d) + g_fc fc'(d), summed over the four k-slots;
-        // rbf_k'(d) = -2 gamma (d - mu_k) rbf_k with rbf_k kept from the recompute
-        float sp = gfc * dfc;
+        // rbf_k'(d) = -2 gamma (d - mu_k) rbf_k with rbf_k kept from the recompute.
+        // The accumulators hold g_rbf 2^-(e1 + e2) (g_z carried 2^-e1, g_a 2^-e2).
+        float sk = 0.0f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             if (kt < KT) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int k = rbf_row_k(kt, slot, r);
-                    const float g = ldexpf(em[kt][r] + ec[kt][r] * kLoUnscale, e2);
+                    const float g = fmaf(ec[kt][r], kLoUnscale, em[kt][r]);
                     const float tt = d - (a.lo + (float)k * a.dmu);
-                    sp += g * (-2.0f * a.gamma * tt * rb[kt >> 1][4 * (kt & 1) + r]);
+                    sk = fmaf(g, tt * rb[kt >> 1][4 * (kt & 1) + r], sk);
                 }
             }
         }
+        float sp = fmaf(ldexpf(sk, e1 + e2), -2.0f * a.gamma, gfc * dfc);
         sp += __shfl_xor(sp, 16, 64);
         sp += __shfl_xor(sp, 32, 64);
         if (live && slot == 0) a.S[p] = a.accumulate ? a.S[p] + sp : sp;

@@ -38,7 +38,7 @@ __device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
     for (int j = 0; j < 8; ++j) {
         const _Float16 h = (_Float16)v[j];
         hi[j] = h;
-        lo[j] = (_Float16)((v[j] - (float)h) * kLoScale);
+        lo[j] = (_Float16)fmaf((float)h, -kLoScale, v[j] * kLoScale);   // (x - hi) 2^11, exact
     }
 }
 
@@ -46,6 +46,23 @@ __device__ inline void mma3(const Frag &w, const half8 &bh, const half8 &bl, flo
     main = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.hi, bh, main, 0, 0, 0);
     corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.hi, bl, corr, 0, 0, 0);
     corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.lo, bh, corr, 0, 0, 0);
+}
+
+// The three split products for MT output tiles sharing one B operand, with
+// dependent instructions on one accumulator MT instructions apart.
+template <int MT>
+__device__ inline void mma3_tiles(const Frag *w, int stride, const half8 &bh, const half8 &bl, floatx4 *main,
+                                  floatx4 *corr) {
+    half8 lo[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const Frag f = w[m * stride];
+        main[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.hi, bh, main[m], 0, 0, 0);
+        corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.hi, bl, corr[m], 0, 0, 0);
+        lo[m] = f.lo;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[m], bh, corr[m], 0, 0, 0);
 }
 
 __device__ inline int chain_k(int t, int s, int j) { return 32 * t + 16 * (j >> 2) + 4 * s + (j & 3); }
@@ -148,8 +165,7 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
         for (int j = 0; j < 8; ++j) v[j] = ldexpf(xin[t][j], -e1);
         half8 bh, bl;
         split8(v, bh, bl);
-#pragma unroll
-        for (int m = 0; m < M1; ++m) mma3(s_w1[(m * T1 + t) * 64 + lane], bh, bl, am[m], ac[m]);
+        mma3_tiles<M1>(s_w1 + t * 64 + lane, T1 * 64, bh, bl, am, ac);
     }
     // first-layer result for output features 16 m + 4 slot + r
     float r1[M1][4];
@@ -226,8 +242,7 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
         }
         half8 bh, bl;
         split8(v, bh, bl);
-#pragma unroll
-        for (int m = 0; m < M2; ++m) mma3(s_w2[(m * T2 + t) * 64 + lane], bh, bl, bm[m], bc[m]);
+        mma3_tiles<M2>(s_w2 + t * 64 + lane, T2 * 64, bh, bl, bm, bc);
     }
     if (!live) return;
 #pragma unroll
