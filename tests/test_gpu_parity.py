@@ -269,3 +269,112 @@ def test_verlet_matches_oracle(sn, n_steps):
     ep_g, ek_g = epot.cpu().numpy(), ekin.cpu().numpy()
     assert np.abs(ep_g - ep).max() <= 1e-5 * np.abs(ep).max() * 10
     assert np.abs(ek_g - ek).max() <= 1e-4 * np.abs(ek).max()
+
+
+# ------------------------------------------------------------------ more shapes and edge cases
+
+def _random_system(n_rep, n_per, box_side, seed, min_d=3.0):
+    """n_rep replicas of n_per particles placed by the seeded box generator (open boundaries)."""
+    pos = np.concatenate([synth.box_rsa(n_per, box_side, min_d, synth.seed64(seed, b)) for b in range(n_rep)])
+    rp = np.arange(0, n_rep * n_per + 1, n_per, dtype=np.int32)
+    return pos.astype(np.float32), rp
+
+
+@pytest.mark.parametrize("F,K,I,T", [(64, 64, 1, 3), (32, 2, 2, 2), (64, 33, 2, 4), (128, 7, 1, 2)])
+def test_energy_forces_other_model_shapes(sn, F, K, I, T):
+    """Every supported feature width and edge values of the basis size, against the oracle."""
+    say(f"[shapes] F={F} K={K} I={I} T={T}")
+    pos, rp = _random_system(3, 90, 18.0, 1000 + F + K)
+    rc = 7.0
+    cfg = {"pos": pos, "replica_ptr": rp, "box": None,
+           "types": np.random.default_rng(F * K).integers(0, T, len(pos)).astype(np.int32),
+           "params": synth.init_params(T, I, F, K, [F, K, I]),
+           "hyper": {"n_types": T, "n_interactions": I, "n_features": F, "n_rbf": K, "cutoff": rc,
+                     **synth.rbf_hyper(K, 0.0, rc)}}
+    L = Loaded(sn, cfg)
+    E, Fo = L.eval(sn)
+    E_ref, F_ref, eps_abs, csr = oracle_full(cfg)
+    assert len(csr[1]) > 100
+    _compare(E, Fo, E_ref, F_ref, eps_abs, rp, f"F={F} K={K}")
+
+
+def test_graph_without_edges_and_single_atom_replicas(sn):
+    """No pair within the cutoff: forces are exactly zero and the energy is the readout of the
+    atom-wise layers alone; replicas of one atom and of zero atoms are allowed."""
+    params = synth.init_params(3, 2, 32, 8, 5)
+    hyper = {"n_types": 3, "n_interactions": 2, "n_features": 32, "n_rbf": 8, "cutoff": 5.0,
+             **synth.rbf_hyper(8, 0.0, 5.0)}
+    pos = np.array([[0, 0, 0], [10, 0, 0], [0, 10, 0], [3, 3, 3], [50, 50, 50]], np.float32)
+    rp = np.array([0, 3, 3, 4, 5], np.int32)
+    cfg = {"pos": pos, "replica_ptr": rp, "types": np.array([0, 1, 2, 1, 0], np.int32), "box": None,
+           "params": params, "hyper": hyper}
+    L = Loaded(sn, cfg)
+    row_ptr, col, rev, E = L.csr(sn)
+    assert E == 0
+    en, f = L.eval(sn, (row_ptr, col, rev, E))
+    assert np.all(f == 0.0)
+    E_ref, _, eps_abs, _ = oracle_full(cfg)
+    assert en[1] == 0.0                       # the empty replica
+    assert np.all(energy_errors(en, E_ref, np.maximum(eps_abs, 1e-30)) <= E_TOL)
+
+
+def test_list_radius_beyond_cutoff_changes_nothing(sn):
+    """Pairs between the cutoff and the list radius carry a zero envelope."""
+    cfg = synth.make_config("batched_replicas", n_replicas=4)
+    L = Loaded(sn, cfg)
+    E1, F1 = L.eval(sn, L.csr(sn))
+    E2, F2 = L.eval(sn, L.csr(sn, r_list=13.5))
+    assert np.abs(E1 - E2).max() <= 1e-6 * np.abs(E1).max()
+    assert np.abs(F1 - F2).max() <= 1e-5 * np.abs(F1).max()
+
+
+def test_verlet_is_deterministic_and_reports_capacity(sn):
+    import torch
+    cfg = synth.make_config("batched_replicas", n_replicas=4)
+    runs = []
+    for _ in range(2):
+        L = Loaded(sn, cfg)
+        vel, inv_mass = dev(cfg["vel"]), dev(cfg["inv_mass"])
+        row_ptr, col, rev, E = L.csr(sn)
+        _, forces = sn.energy_forces(L.model, L.system, L.pos, row_ptr, col, rev, E, L.ws)
+        sn.verlet_step(L.model, L.system, L.pos, vel, forces, inv_mass, 2.0, synth.FORCE_TO_ACCEL, 10, 12.0,
+                       L.capacity, L.ws)
+        torch.cuda.synchronize()
+        runs.append((L.pos.cpu().numpy(), vel.cpu().numpy(), forces.cpu().numpy()))
+    for a, b in zip(runs[0], runs[1]):
+        assert np.array_equal(a, b)
+    # a capacity that the first rebuild already exceeds
+    L = Loaded(sn, cfg, capacity=1000)
+    vel, inv_mass = dev(cfg["vel"]), dev(cfg["inv_mass"])
+    forces = torch.zeros_like(L.pos)
+    with pytest.raises(sn.SnError) as exc:
+        sn.verlet_step(L.model, L.system, L.pos, vel, forces, inv_mass, 2.0, synth.FORCE_TO_ACCEL, 3, 12.0,
+                       L.capacity, L.ws)
+    assert exc.value.status == sn.SN_ERR_CAPACITY and exc.value.steps_done == 0
+    assert exc.value.n_edges > 1000
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_md_100_steps_energy_drift(sn, fmt):
+    """The 100-step, 2 fs NVE run of the batched workload: total energy is conserved to the
+    integrator's accuracy (reported), for fp32 and int16 filter weights."""
+    import torch
+    cfg = synth.make_config("batched_replicas", n_replicas=8)
+    L = Loaded(sn, cfg, fmt=fmt)
+    vel, inv_mass = dev(cfg["vel"]), dev(cfg["inv_mass"])
+    row_ptr, col, rev, E = L.csr(sn)
+    e0, forces = sn.energy_forces(L.model, L.system, L.pos, row_ptr, col, rev, E, L.ws)
+    n, B = 100, 8
+    epot = torch.zeros((n, B), dtype=torch.float32, device="cuda")
+    ekin = torch.zeros((n, B), dtype=torch.float32, device="cuda")
+    sn.verlet_step(L.model, L.system, L.pos, vel, forces, inv_mass, 2.0, synth.FORCE_TO_ACCEL, n, 12.0,
+                   L.capacity, L.ws, epot, ekin)
+    torch.cuda.synchronize()
+    tot = (epot + ekin).cpu().numpy().astype(np.float64)
+    ek = ekin.cpu().numpy().astype(np.float64)
+    drift = np.abs(tot - tot[0]).max(axis=0)
+    rel = drift / ek.mean(axis=0)
+    say(f"   fmt={fmt}: max |E_tot(t) - E_tot(0)| per replica {drift.max():.3e} "
+        f"(= {rel.max():.2e} of the mean kinetic energy)")
+    assert np.all(np.isfinite(tot))
+    assert rel.max() < 0.05
