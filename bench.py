@@ -142,6 +142,59 @@ def summarize_pmc(fetch_csv: str, write_csv: str, probe_mib: int, workload: str,
     ])
 
 
+UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS",
+                 "GRBM_GUI_ACTIVE")
+
+
+def summarize_util(csv_path: str, workload: str, command: str, n_simd: int = 1024, n_xcd: int = 8) -> str:
+    """Markdown summary of one rocprofv3 --pmc pass over UTIL_COUNTERS, per kernel (mean per dispatch).
+
+    MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs); LDS bank-conflict cycles per
+    LDS-active cycle; VALU issue = SQ_ACTIVE_INST_VALU (quad-cycles) x 4 / (GRBM_GUI_ACTIVE x SIMDs).
+    """
+    import collections
+    import csv
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        vals[_short_kernel(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    rows = []
+    for k in ("filter_bwd_kernel", "filter_fwd_kernel", "cfconv_kernel", "mlp_kernel", "rows_kernel"):
+        if k not in vals:
+            continue
+        m = {c: sum(v) / len(v) for c, v in vals[k].items()}
+        # rocprofv3 sums GRBM_GUI_ACTIVE over the XCDs; the elapsed cycles are its per-XCD value
+        gui = m.get("GRBM_GUI_ACTIVE", 0.0) / n_xcd
+        if gui <= 0:
+            continue
+        mfma = 100.0 * m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * n_simd)
+        valu = 100.0 * 4.0 * m.get("SQ_ACTIVE_INST_VALU", 0.0) / (gui * n_simd)
+        lds_act = m.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        confl = m.get("SQ_LDS_BANK_CONFLICT", 0.0)
+        rows.append(f"| {k} | {gui:.0f} | {mfma:.1f} % | {valu:.1f} % | {m.get('SQ_INSTS_VALU_MFMA_MOPS_F16', 0) * 512 / 1e9:.1f} "
+                    f"| {confl / max(lds_act, 1.0):.4f} | {m.get('SQ_INSTS_LDS', 0):.0f} |")
+    return "\n".join([
+        f"# Matrix-core, VALU and LDS counters per launch, {workload}",
+        "",
+        "One `rocprofv3 --pmc` pass (mean per dispatch).  GUI-active cycles = GRBM_GUI_ACTIVE per XCD",
+        f"(the summed counter / {n_xcd}).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GUI-active x {n_simd} SIMDs);",
+        f"VALU active = 4 x SQ_ACTIVE_INST_VALU (quad-cycles) / (GUI-active x {n_simd});",
+        "F16 MFMA GFLOP = 512 x SQ_INSTS_VALU_MFMA_MOPS_F16 / 1e9;",
+        "LDS conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles per active cycle).",
+        "",
+        "Command (repository root):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| kernel | GUI-active cycles | MFMA busy | VALU active | F16 MFMA GFLOP | LDS conflict cycles / active | LDS instructions |",
+        "|---|---|---|---|---|---|---|",
+        *rows,
+        "",
+    ])
+
+
 def load_traffic(workload: str):
     import json as _json
     path = traffic_file(workload)
@@ -205,7 +258,15 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary of two rocprofv3 --pmc runs to profiles/ and exit")
     ap.add_argument("--pmc-command", default="", help="command line recorded in the traffic summary")
+    ap.add_argument("--summarize-util", metavar="CSV",
+                    help="write the MFMA/VALU/LDS counter summary of one rocprofv3 --pmc run to profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_util:
+        md = summarize_util(args.summarize_util, args.workload, args.pmc_command)
+        with open(os.path.join(ROOT, "profiles", f"mfma_lds_{args.workload}.md"), "w") as f:
+            f.write(md)
+        print(md)
+        return
     if args.summarize_pmc:
         md = summarize_pmc(*args.summarize_pmc, args.copy_probe_mb, args.workload, args.pmc_command)
         with open(traffic_file(args.workload), "w") as f:

@@ -47,11 +47,6 @@ constexpr float kLoUnscale = 1.0f / 2048.0f;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
-// One lane's A-operand fragment of one 32-wide k step: 8 weights as hi, lo.
-struct Frag {
-    half8 hi, lo;
-};
-
 struct FilterArgs {
     int K;
     float lo, dmu, gamma, cutoff;
@@ -93,33 +88,24 @@ __device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
     }
 }
 
-__device__ inline Frag make_frag(const float (&v)[8]) {
-    Frag f;
-    split8(v, f.hi, f.lo);
-    return f;
-}
 
-// acc += A.B in split form (main: hi.hi, corr: hi.lo + lo.hi)
-__device__ inline void mma3(const Frag &w, const half8 &bh, const half8 &bl, floatx4 &main, floatx4 &corr) {
-    main = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.hi, bh, main, 0, 0, 0);
-    corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.hi, bl, corr, 0, 0, 0);
-    corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.lo, bh, corr, 0, 0, 0);
-}
 
 // The three split products for MT output tiles that share one B operand,
 // ordered so that dependent matrix instructions on the same accumulator are
 // MT instructions apart: hi.hi and hi.lo for every tile, then lo.hi.
-// Fragment of tile m at w[m * stride].
+// Fragment halves of tile m at whi[m * stride], wlo[m * stride] (hi and lo
+// live in separate arrays so that a wavefront's 16-byte reads are contiguous
+// and free of LDS bank conflicts).
 template <int MT>
-__device__ inline void mma3_tiles(const Frag *w, int stride, const half8 &bh, const half8 &bl, floatx4 *main,
-                                  floatx4 *corr) {
+__device__ inline void mma3_tiles(const half8 *whi, const half8 *wlo, int stride, const half8 &bh, const half8 &bl,
+                                  floatx4 *main, floatx4 *corr) {
     half8 lo[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        const Frag f = w[m * stride];
-        main[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.hi, bh, main[m], 0, 0, 0);
-        corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.hi, bl, corr[m], 0, 0, 0);
-        lo[m] = f.lo;
+        const half8 hi = whi[m * stride];
+        main[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bh, main[m], 0, 0, 0);
+        corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bl, corr[m], 0, 0, 0);
+        lo[m] = wlo[m * stride];
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[m], bh, corr[m], 0, 0, 0);
@@ -157,21 +143,21 @@ __device__ inline float rbf_val(const FilterArgs &a, float d, int k) {
 // Stage A1 for the first GEMM: s_a1[(m*KS + ks)*64 + l] holds, for output
 // feature f = 16m + l%16, the weights A1[k][f], k = 32 ks + 8(l/16) + j.
 template <int F>
-__device__ inline void stage_a1(const FilterArgs &a, Frag *s_a1, int KS) {
+__device__ inline void stage_a1(const FilterArgs &a, half8 *s_hi, half8 *s_lo, int KS) {
     constexpr int MT = F / 16;
     for (int idx = threadIdx.x; idx < MT * KS * 64; idx += blockDim.x) {
         const int m = idx / (KS * 64), ks = (idx / 64) % KS, l = idx % 64;
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = w1<F>(a, 32 * ks + 8 * (l / 16) + j, 16 * m + l % 16);
-        s_a1[idx] = make_frag(v);
+        split8(v, s_hi[idx], s_lo[idx]);
     }
 }
 
 // First GEMM, acc = (rbf(d) A1)^T in split form; rb receives the lane's
 // basis values rbf_k, k = 32 ks + 8 s + j.
 template <int F>
-__device__ inline void gemm_rbf(const FilterArgs &a, const Frag *s_a1, int KS, float d, int lane,
+__device__ inline void gemm_rbf(const FilterArgs &a, const half8 *s_a1h, const half8 *s_a1l, int KS, float d, int lane,
                                 floatx4 (&main)[F / 16], floatx4 (&corr)[F / 16], float (&rb)[2][8]) {
     constexpr int MT = F / 16;
 #pragma unroll
@@ -186,7 +172,8 @@ __device__ inline void gemm_rbf(const FilterArgs &a, const Frag *s_a1, int KS, f
             constexpr int MG = MT < 4 ? MT : 4;
 #pragma unroll
             for (int m0 = 0; m0 < MT; m0 += MG)
-                mma3_tiles<MG>(s_a1 + (m0 * KS + ks) * 64 + lane, KS * 64, bh, bl, main + m0, corr + m0);
+                mma3_tiles<MG>(s_a1h + (m0 * KS + ks) * 64 + lane, s_a1l + (m0 * KS + ks) * 64 + lane, KS * 64, bh,
+                               bl, main + m0, corr + m0);
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) rb[ks][j] = 0.0f;
@@ -206,17 +193,17 @@ template <int F>
 __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;                 // 32-wide k steps of the F x F GEMM
-    __shared__ Frag s_a1[MT * 2 * 64];
-    __shared__ Frag s_a2[MT * T2 * 64];        // [m][t][l]: A2[chain_k(t, l/16, j)][16 m + l%16]
+    __shared__ half8 s_a1h[MT * 2 * 64], s_a1l[MT * 2 * 64];
+    __shared__ half8 s_a2h[MT * T2 * 64], s_a2l[MT * T2 * 64];   // [m][t][l]: A2[chain_k(t, l/16, j)][16 m + l%16]
     __shared__ float s_b1[F], s_b2[F];
     const int KS = (a.K + 31) / 32;
-    stage_a1<F>(a, s_a1, KS);
+    stage_a1<F>(a, s_a1h, s_a1l, KS);
     for (int idx = threadIdx.x; idx < MT * T2 * 64; idx += blockDim.x) {
         const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = w2<F>(a, chain_k(t, l / 16, j), 16 * m + l % 16);
-        s_a2[idx] = make_frag(v);
+        split8(v, s_a2h[idx], s_a2l[idx]);
     }
     for (int f = threadIdx.x; f < F; f += blockDim.x) { s_b1[f] = a.b1[f]; s_b2[f] = a.b2[f]; }
     __syncthreads();
@@ -233,7 +220,7 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
         const float d = (p < a.P) ? a.dsrc[p * a.dstride + a.doff] : 0.0f;
         floatx4 am[MT], ac[MT];
         float rb[2][8];
-        gemm_rbf<F>(a, s_a1, KS, d, lane, am, ac, rb);
+        gemm_rbf<F>(a, s_a1h, s_a1l, KS, d, lane, am, ac, rb);
         // z = ssp(a), converted step by step into split B operands
         half8 zh[T2], zl[T2];
 #pragma unroll
@@ -253,7 +240,9 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
 #pragma unroll
             for (int g = 0; g < MG; ++g) main[g] = corr[g] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < T2; ++t) mma3_tiles<MG>(s_a2 + (m0 * T2 + t) * 64 + lane, T2 * 64, zh[t], zl[t], main, corr);
+            for (int t = 0; t < T2; ++t)
+                mma3_tiles<MG>(s_a2h + (m0 * T2 + t) * 64 + lane, s_a2l + (m0 * T2 + t) * 64 + lane, T2 * 64, zh[t],
+                               zl[t], main, corr);
             if (p < a.P) {
 #pragma unroll
                 for (int g = 0; g < MG; ++g) {
@@ -273,19 +262,19 @@ template <int F>
 __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;
-    __shared__ Frag s_a1[MT * 2 * 64];
-    __shared__ Frag s_a2b[MT * T2 * 64];   // [m][t][l]: A2[16 m + l%16][32 t + 8(l/16) + j]
-    __shared__ Frag s_a1b[4 * T2 * 64];    // [kt][t][l]: A1[rbf_row_k(kt, (l%16)/4, l%4)][chain_k(t, l/16, j)]
+    __shared__ half8 s_a1h[MT * 2 * 64], s_a1l[MT * 2 * 64];
+    __shared__ half8 s_a2bh[MT * T2 * 64], s_a2bl[MT * T2 * 64];  // [m][t][l]: A2[16 m + l%16][32 t + 8(l/16) + j]
+    __shared__ half8 s_a1bh[4 * T2 * 64], s_a1bl[4 * T2 * 64];    // [kt][t][l]: A1[rbf_row_k(kt, (l%16)/4, l%4)][chain_k(t, l/16, j)]
     __shared__ float s_b1[F];
     const int KS = (a.K + 31) / 32;
     const int KT = 2 * KS;
-    stage_a1<F>(a, s_a1, KS);
+    stage_a1<F>(a, s_a1h, s_a1l, KS);
     for (int idx = threadIdx.x; idx < MT * T2 * 64; idx += blockDim.x) {
         const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = w2<F>(a, 16 * m + l % 16, 32 * t + 8 * (l / 16) + j);
-        s_a2b[idx] = make_frag(v);
+        split8(v, s_a2bh[idx], s_a2bl[idx]);
     }
     for (int idx = threadIdx.x; idx < KT * T2 * 64; idx += blockDim.x) {
         const int kt = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
@@ -294,7 +283,7 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = w1<F>(a, k, chain_k(t, l / 16, j));
-        s_a1b[idx] = make_frag(v);
+        split8(v, s_a1bh[idx], s_a1bl[idx]);
     }
     for (int f = threadIdx.x; f < F; f += blockDim.x) s_b1[f] = a.b1[f];
     __syncthreads();
@@ -324,7 +313,7 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         float rb[2][8];
         {
             floatx4 am[MT], ac[MT];
-            gemm_rbf<F>(a, s_a1, KS, d, lane, am, ac, rb);
+            gemm_rbf<F>(a, s_a1h, s_a1l, KS, d, lane, am, ac, rb);
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -373,7 +362,8 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
                 constexpr int MG = MT < 4 ? MT : 4;
 #pragma unroll
                 for (int m0 = 0; m0 < MT; m0 += MG)
-                    mma3_tiles<MG>(s_a2b + (m0 * T2 + t) * 64 + lane, T2 * 64, bh, bl, zm + m0, zc + m0);
+                    mma3_tiles<MG>(s_a2bh + (m0 * T2 + t) * 64 + lane, s_a2bl + (m0 * T2 + t) * 64 + lane, T2 * 64,
+                                   bh, bl, zm + m0, zc + m0);
             }
         }
         // g_a 2^-e1 = (g_z 2^-e1) (.) sigmoid(a); the 2^e1 is folded into e2
@@ -400,9 +390,9 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
             half8 bh, bl;
             split8(v, bh, bl);
             if (KT == 4) {
-                mma3_tiles<4>(s_a1b + t * 64 + lane, T2 * 64, bh, bl, em, ec);
+                mma3_tiles<4>(s_a1bh + t * 64 + lane, s_a1bl + t * 64 + lane, T2 * 64, bh, bl, em, ec);
             } else {
-                mma3_tiles<2>(s_a1b + t * 64 + lane, T2 * 64, bh, bl, em, ec);
+                mma3_tiles<2>(s_a1bh + t * 64 + lane, s_a1bl + t * 64 + lane, T2 * 64, bh, bl, em, ec);
             }
         }
         // S_p = sum_k g_rbf_k rbf_k'(d) + g_fc fc'(d), summed over the four k-slots;

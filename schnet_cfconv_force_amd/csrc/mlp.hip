@@ -29,10 +29,6 @@ constexpr int kMlpThreads = 512;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
-struct Frag {
-    half8 hi, lo;
-};
-
 __device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -42,24 +38,20 @@ __device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
     }
 }
 
-__device__ inline void mma3(const Frag &w, const half8 &bh, const half8 &bl, floatx4 &main, floatx4 &corr) {
-    main = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.hi, bh, main, 0, 0, 0);
-    corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.hi, bl, corr, 0, 0, 0);
-    corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(w.lo, bh, corr, 0, 0, 0);
-}
-
 // The three split products for MT output tiles sharing one B operand, with
 // dependent instructions on one accumulator MT instructions apart.
+// Weight hi and lo halves live in separate arrays, so a wavefront's 16-byte
+// reads are contiguous and free of LDS bank conflicts.
 template <int MT>
-__device__ inline void mma3_tiles(const Frag *w, int stride, const half8 &bh, const half8 &bl, floatx4 *main,
-                                  floatx4 *corr) {
+__device__ inline void mma3_tiles(const half8 *whi, const half8 *wlo, int stride, const half8 &bh, const half8 &bl,
+                                  floatx4 *main, floatx4 *corr) {
     half8 lo[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        const Frag f = w[m * stride];
-        main[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.hi, bh, main[m], 0, 0, 0);
-        corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.hi, bl, corr[m], 0, 0, 0);
-        lo[m] = f.lo;
+        const half8 hi = whi[m * stride];
+        main[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bh, main[m], 0, 0, 0);
+        corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bl, corr[m], 0, 0, 0);
+        lo[m] = wlo[m * stride];
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[m], bh, corr[m], 0, 0, 0);
@@ -108,7 +100,7 @@ __device__ inline float wval(const float *W, int trans, int kdim, int mdim, int 
 
 // Stage a layer's A fragments: [m][t][l], value j = weight(row 16m + l%16,
 // column kfn(t, l/16, j)); chained = 1 uses the accumulator-chain k order.
-__device__ inline void stage(Frag *dst, const float *W, int trans, int kdim, int mdim, int MT, int T, int chained) {
+__device__ inline void stage(half8 *dhi, half8 *dlo, const float *W, int trans, int kdim, int mdim, int MT, int T, int chained) {
     for (int idx = threadIdx.x; idx < MT * T * 64; idx += blockDim.x) {
         const int m = idx / (T * 64), t = (idx / 64) % T, l = idx % 64;
         float v[8];
@@ -117,9 +109,7 @@ __device__ inline void stage(Frag *dst, const float *W, int trans, int kdim, int
             const int k = chained ? chain_k(t, l / 16, j) : 32 * t + 8 * (l / 16) + j;
             v[j] = wval(W, trans, kdim, mdim, k, 16 * m + l % 16);
         }
-        Frag f;
-        split8(v, f.hi, f.lo);
-        dst[idx] = f;
+        split8(v, dhi[idx], dlo[idx]);
     }
 }
 
@@ -129,10 +119,10 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
     constexpr int M1 = S::M1, T1 = S::T1, M2 = S::M2, T2 = S::T2;
     constexpr int TRANS1 = (MODE == MLP_BWD_OUT || MODE == MLP_BWD_X) ? 1 : 0;
     constexpr int TRANS2 = (MODE == MLP_READOUT || MODE == MLP_BWD_OUT) ? 1 : 0;
-    __shared__ Frag s_w1[M1 * T1 * 64];
-    __shared__ Frag s_w2[S::TWO ? M2 * T2 * 64 : 1];
-    stage(s_w1, a.W1, TRANS1, S::FI1, S::FO1, M1, T1, 0);
-    if (S::TWO) stage(s_w2, a.W2, TRANS2, S::FI2, S::FO2, M2, T2, 1);
+    __shared__ half8 s_w1h[M1 * T1 * 64], s_w1l[M1 * T1 * 64];
+    __shared__ half8 s_w2h[S::TWO ? M2 * T2 * 64 : 1], s_w2l[S::TWO ? M2 * T2 * 64 : 1];
+    stage(s_w1h, s_w1l, a.W1, TRANS1, S::FI1, S::FO1, M1, T1, 0);
+    if (S::TWO) stage(s_w2h, s_w2l, a.W2, TRANS2, S::FI2, S::FO2, M2, T2, 1);
     __syncthreads();
 
     const int lane = threadIdx.x % 64, slot = lane / 16;
@@ -165,7 +155,7 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
         for (int j = 0; j < 8; ++j) v[j] = ldexpf(xin[t][j], -e1);
         half8 bh, bl;
         split8(v, bh, bl);
-        mma3_tiles<M1>(s_w1 + t * 64 + lane, T1 * 64, bh, bl, am, ac);
+        mma3_tiles<M1>(s_w1h + t * 64 + lane, s_w1l + t * 64 + lane, T1 * 64, bh, bl, am, ac);
     }
     // first-layer result for output features 16 m + 4 slot + r
     float r1[M1][4];
@@ -242,7 +232,7 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
         }
         half8 bh, bl;
         split8(v, bh, bl);
-        mma3_tiles<M2>(s_w2 + t * 64 + lane, T2 * 64, bh, bl, bm, bc);
+        mma3_tiles<M2>(s_w2h + t * 64 + lane, s_w2l + t * 64 + lane, T2 * 64, bh, bl, bm, bc);
     }
     if (!live) return;
 #pragma unroll
