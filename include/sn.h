@@ -97,7 +97,7 @@ typedef struct sn_model {
     float rbf_lo, rbf_hi;     /* first and last Gaussian centre */
     float rbf_gamma;          /* Gaussian width gamma (> 0) */
     int32_t filter_format;    /* 0 = fp32 filter weights, 1 = int16 per-output-channel */
-    const float *params;      /* device, packed fp32 (see above) */
+    const float *params;      /* device, packed fp32 (see above), 16-byte aligned */
     const int16_t *qweights;  /* device, int16 codes (filter_format 1), else NULL */
     const float *qscales;     /* device, fp32 scales (filter_format 1), else NULL */
 } sn_model;

@@ -141,7 +141,7 @@ sn_status check_system(const sn_system *sys) {
 }
 
 sn_status check_model(const sn_model *m) {
-    if (!m || !m->params) return SN_ERR_INVALID;
+    if (!m || !m->params || (reinterpret_cast<uintptr_t>(m->params) & 15) != 0) return SN_ERR_INVALID;
     const int F = m->n_features;
     if (F != 32 && F != 64 && F != 128) return SN_ERR_INVALID;
     if (m->n_rbf < 2 || m->n_rbf > 64 || m->n_interactions < 1 || m->n_interactions > 16 || m->n_types < 1)

@@ -90,6 +90,27 @@ __device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
 
 
 
+// Stage nf (<= NF) weight fragments into LDS: fragment idx holds the eight
+// weights val(idx, j), split.  A thread's global loads for all of its
+// fragments are issued before the first one is used, so the staging costs
+// one memory latency rather than one per fragment.
+template <int NF, int NT, typename Val>
+__device__ inline void stage_frags(half8 *hi, half8 *lo, int nf, Val val) {
+    constexpr int IT = (NF + NT - 1) / NT;
+    float v[IT][8];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = (int)threadIdx.x + it * NT;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[it][j] = idx < nf ? val(idx, j) : 0.0f;
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = (int)threadIdx.x + it * NT;
+        if (idx < nf) split8(v[it], hi[idx], lo[idx]);
+    }
+}
+
 // The three split products for MT output tiles that share one B operand,
 // ordered so that dependent matrix instructions on the same accumulator are
 // MT instructions apart: hi.hi and hi.lo for every tile, then lo.hi.
@@ -142,16 +163,13 @@ __device__ inline float rbf_val(const FilterArgs &a, float d, int k) {
 
 // Stage A1 for the first GEMM: s_a1[(m*KS + ks)*64 + l] holds, for output
 // feature f = 16m + l%16, the weights A1[k][f], k = 32 ks + 8(l/16) + j.
-template <int F>
+template <int F, int NT>
 __device__ inline void stage_a1(const FilterArgs &a, half8 *s_hi, half8 *s_lo, int KS) {
     constexpr int MT = F / 16;
-    for (int idx = threadIdx.x; idx < MT * KS * 64; idx += blockDim.x) {
+    stage_frags<MT * 2 * 64, NT>(s_hi, s_lo, MT * KS * 64, [&](int idx, int j) {
         const int m = idx / (KS * 64), ks = (idx / 64) % KS, l = idx % 64;
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = w1<F>(a, 32 * ks + 8 * (l / 16) + j, 16 * m + l % 16);
-        split8(v, s_hi[idx], s_lo[idx]);
-    }
+        return w1<F>(a, 32 * ks + 8 * (l / 16) + j, 16 * m + l % 16);
+    });
 }
 
 // First GEMM, acc = (rbf(d) A1)^T in split form; rb receives the lane's
@@ -197,14 +215,11 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     __shared__ half8 s_a2h[MT * T2 * 64], s_a2l[MT * T2 * 64];   // [m][t][l]: A2[chain_k(t, l/16, j)][16 m + l%16]
     __shared__ float s_b1[F], s_b2[F];
     const int KS = (a.K + 31) / 32;
-    stage_a1<F>(a, s_a1h, s_a1l, KS);
-    for (int idx = threadIdx.x; idx < MT * T2 * 64; idx += blockDim.x) {
+    stage_a1<F, kFwdThreads>(a, s_a1h, s_a1l, KS);
+    stage_frags<MT * T2 * 64, kFwdThreads>(s_a2h, s_a2l, MT * T2 * 64, [&](int idx, int j) {
         const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = w2<F>(a, chain_k(t, l / 16, j), 16 * m + l % 16);
-        split8(v, s_a2h[idx], s_a2l[idx]);
-    }
+        return w2<F>(a, chain_k(t, l / 16, j), 16 * m + l % 16);
+    });
     for (int f = threadIdx.x; f < F; f += blockDim.x) { s_b1[f] = a.b1[f]; s_b2[f] = a.b2[f]; }
     __syncthreads();
 
@@ -268,23 +283,16 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     __shared__ float s_b1[F];
     const int KS = (a.K + 31) / 32;
     const int KT = 2 * KS;
-    stage_a1<F>(a, s_a1h, s_a1l, KS);
-    for (int idx = threadIdx.x; idx < MT * T2 * 64; idx += blockDim.x) {
+    stage_a1<F, kBwdThreads>(a, s_a1h, s_a1l, KS);
+    stage_frags<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, MT * T2 * 64, [&](int idx, int j) {
         const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = w2<F>(a, 16 * m + l % 16, 32 * t + 8 * (l / 16) + j);
-        split8(v, s_a2bh[idx], s_a2bl[idx]);
-    }
-    for (int idx = threadIdx.x; idx < KT * T2 * 64; idx += blockDim.x) {
+        return w2<F>(a, 16 * m + l % 16, 32 * t + 8 * (l / 16) + j);
+    });
+    stage_frags<4 * T2 * 64, kBwdThreads>(s_a1bh, s_a1bl, KT * T2 * 64, [&](int idx, int j) {
         const int kt = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
         const int row = l % 16;
-        const int k = rbf_row_k(kt, row / 4, row % 4);
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = w1<F>(a, k, chain_k(t, l / 16, j));
-        split8(v, s_a1bh[idx], s_a1bl[idx]);
-    }
+        return w1<F>(a, rbf_row_k(kt, row / 4, row % 4), chain_k(t, l / 16, j));
+    });
     for (int f = threadIdx.x; f < F; f += blockDim.x) s_b1[f] = a.b1[f];
     __syncthreads();
 
@@ -308,22 +316,9 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
             fc = c * c;
             dfc = -(kPi / a.cutoff) * sn * c;
         }
-        // recompute a = rbf A1 + b1 and keep sigmoid(a) (and the lane's rbf_k)
-        float sg[MT][4];
-        float rb[2][8];
-        {
-            floatx4 am[MT], ac[MT];
-            gemm_rbf<F>(a, s_a1h, s_a1l, KS, d, lane, am, ac, rb);
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sg[m][r] = sigm(am[m][r] + ac[m][r] * kLoUnscale + s_b1[16 * m + 4 * slot + r]);
-        }
-        // g_z^T = A2 g_phi^T, g_phi = fc G, G = g_y_i x_j + g_y_j x_i on the
-        // features 32 t + 8 slot + j.  The pair's operands are scaled by 2^-e1,
-        // with e1 from a bound on |g_phi| (per-atom row maxima), so each
-        // 32-feature step is gathered, split and multiplied straight away.
+        // G = g_y_i x_j + g_y_j x_i on the features 32 t + 8 slot + j, times
+        // fc 2^-e1 (g_phi scaled; e1 from a bound on |g_phi| through the
+        // per-atom row maxima), split into the B operands of all k-steps.
         int e1 = 0;
         {
             const float2 mi = live ? a.rowmax[ij.x] : make_float2(0.f, 0.f);
@@ -333,9 +328,7 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         }
         const float fs = ldexpf(fc, -e1);
         float gfc = 0.0f;
-        floatx4 zm[MT], zc[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) zm[m] = zc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+        half8 gh[T2], gl[T2];
         {
             const int64_t bi = (int64_t)ij.x * F + 8 * slot, bj = (int64_t)ij.y * F + 8 * slot;
             const int64_t bp = (live ? p : 0) * F + 8 * slot;
@@ -357,25 +350,77 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
                     v[4 * q + 0] = fs * g0; v[4 * q + 1] = fs * g1;
                     v[4 * q + 2] = fs * g2; v[4 * q + 3] = fs * g3;
                 }
-                half8 bh, bl;
-                split8(v, bh, bl);
-                constexpr int MG = MT < 4 ? MT : 4;
-#pragma unroll
-                for (int m0 = 0; m0 < MT; m0 += MG)
-                    mma3_tiles<MG>(s_a2bh + (m0 * T2 + t) * 64 + lane, s_a2bl + (m0 * T2 + t) * 64 + lane, T2 * 64,
-                                   bh, bl, zm + m0, zc + m0);
+                split8(v, gh[t], gl[t]);
+                // the step is consumed before the next step's gathers issue
+                asm volatile("" : "+v"(gh[t]), "+v"(gl[t]), "+v"(gfc));
             }
         }
+        // the lane's basis functions rbf_k(d), k = 32 ks + 8 slot + j, split
+        // into B operands; rbd keeps (d - mu_k) rbf_k for S_p
+        float rbd[2][8];
+        half8 rh[2], rl[2];
+        {
+            // d goes through an opaque copy so that this is not hoisted into
+            // the gather phase (register pressure)
+            float dr = d;
+            asm volatile("" : "+v"(dr)::"memory");
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                float rb[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int k = 32 * ks + 8 * slot + j;
+                    const float tt = dr - (a.lo + (float)k * a.dmu);
+                    const float e = fast_exp(-a.gamma * tt * tt);
+                    rb[j] = k < a.K ? e : 0.0f;
+                    rbd[ks][j] = tt * rb[j];
+                }
+                split8(rb, rh[ks], rl[ks]);
+            }
+        }
+        // per group of MG output tiles (features 16 m ..): g_z^T = A2 g_phi^T,
+        // a = rbf A1 + b1 (recomputed; b1 seeds the accumulator), and
         // g_a 2^-e1 = (g_z 2^-e1) (.) sigmoid(a); the 2^e1 is folded into e2
+        constexpr int MG = MT < 4 ? MT : 4;
         float ga[MT][4];
         float amax = 0.0f;
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int m0 = 0; m0 < MT; m0 += MG) {
+            floatx4 zm[MG], zc[MG];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                ga[m][r] = fmaf(zc[m][r], kLoUnscale, zm[m][r]) * sg[m][r];
-                amax = fmaxf(amax, fabsf(ga[m][r]));
+            for (int m = 0; m < MG; ++m) zm[m] = zc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < T2; ++t)
+                mma3_tiles<MG>(s_a2bh + (m0 * T2 + t) * 64 + lane, s_a2bl + (m0 * T2 + t) * 64 + lane, T2 * 64,
+                               gh[t], gl[t], zm, zc);
+            floatx4 gz[MG];
+#pragma unroll
+            for (int m = 0; m < MG; ++m) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gz[m][r] = fmaf(zc[m][r], kLoUnscale, zm[m][r]);
+                // g_z is complete before the recompute's operands are read
+                asm volatile("" : "+v"(gz[m])::"memory");
             }
+            floatx4 am[MG], ac[MG];
+#pragma unroll
+            for (int m = 0; m < MG; ++m) {
+                am[m] = *reinterpret_cast<const floatx4 *>(s_b1 + 16 * (m0 + m) + 4 * slot);
+                ac[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                if (ks < KS)
+                    mma3_tiles<MG>(s_a1h + (m0 * KS + ks) * 64 + lane, s_a1l + (m0 * KS + ks) * 64 + lane, KS * 64,
+                                   rh[ks], rl[ks], am, ac);
+#pragma unroll
+            for (int m = 0; m < MG; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sg = sigm(fmaf(ac[m][r], kLoUnscale, am[m][r]));
+                    ga[m0 + m][r] = gz[m][r] * sg;
+                    amax = fmaxf(amax, fabsf(ga[m0 + m][r]));
+                }
+        }
         // g_rbf^T = A1 g_a^T (rows permuted to the lane's own basis functions)
         const int e2 = pair_exponent(amax);
         const float down2 = ldexpf(1.0f, -e2);
@@ -403,12 +448,8 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         for (int kt = 0; kt < 4; ++kt) {
             if (kt < KT) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int k = rbf_row_k(kt, slot, r);
-                    const float g = fmaf(ec[kt][r], kLoUnscale, em[kt][r]);
-                    const float tt = d - (a.lo + (float)k * a.dmu);
-                    sk = fmaf(g, tt * rb[kt >> 1][4 * (kt & 1) + r], sk);
-                }
+                for (int r = 0; r < 4; ++r)
+                    sk = fmaf(fmaf(ec[kt][r], kLoUnscale, em[kt][r]), rbd[kt >> 1][4 * (kt & 1) + r], sk);
             }
         }
         float sp = fmaf(ldexpf(sk, e1 + e2), -2.0f * a.gamma, gfc * dfc);

@@ -1,13 +1,15 @@
 // Atom-wise layers of the interaction blocks and the readout, fused per
-// block of 16 atoms and run on the matrix cores.
+// wavefront of 16 atoms and run on the matrix cores.
 //
 // Same mapping as the filter network: computed transposed (output features
-// are the M dimension, 16 atoms the N dimension of
-// v_mfma_f32_16x16x32_f16), operands held in split form (hi = fp16(x),
-// lo = fp16((x - hi) 2^11), accumulated as hi.hi + 2^-11 (hi.lo + lo.hi)),
-// and the accumulator layout of the first GEMM fed directly as the B operand
-// of the second.  Each atom's operands are scaled by a power of two first
-// (exact), so no value is lost to the fp16 range.
+// are the M dimension, atoms the N dimension of v_mfma_f32_16x16x32_f16),
+// operands in the split-fp16 form of split_mfma.h, and the accumulator
+// layout of the first GEMM fed directly as the B operand of the second.
+// At these sizes a launch is bound by its chain of latencies (input and
+// weight loads, the dependent matrix instructions of one tile, the stores),
+// so wavefronts stay small (one 16-atom tile; kNT > 1 would share each
+// weight fragment read between tiles) and many (two per SIMD).  Each atom's
+// operands are scaled by a power of two from the atom's own maximum.
 //
 // Kernels (one launch each):
 //   OUT      o = y Wo1 + bo1 (stored);  h += ssp(o) Wo2 + bo2
@@ -15,55 +17,24 @@
 //   READOUT  q = h R1 + c1;  eps = ssp(q) . R2 + c2;  g_h = (sigmoid(q) (.) R2) R1^T
 //   BWD_OUT  g_o = (g_h Wo2^T) (.) sigmoid(o);  g_y = g_o Wo1^T (stored)
 //   BWD_X    g_h += g_x W_in^T
-#include "sn_internal.h"
+#include "split_mfma.h"
 
 namespace sn {
 
 namespace {
 
-constexpr float kLoScale = 2048.0f;
-constexpr float kLoUnscale = 1.0f / 2048.0f;
-// 8 wavefronts (128 atoms) per block: one block per CU holds the staged
-// weights, and the grid of the largest systems fits in one pass of the CUs
-constexpr int kMlpThreads = 512;
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-
-__device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const _Float16 h = (_Float16)v[j];
-        hi[j] = h;
-        lo[j] = (_Float16)fmaf((float)h, -kLoScale, v[j] * kLoScale);   // (x - hi) 2^11, exact
-    }
-}
-
-// The three split products for MT output tiles sharing one B operand, with
-// dependent instructions on one accumulator MT instructions apart.
-// Weight hi and lo halves live in separate arrays, so a wavefront's 16-byte
-// reads are contiguous and free of LDS bank conflicts.
-template <int MT>
-__device__ inline void mma3_tiles(const half8 *whi, const half8 *wlo, int stride, const half8 &bh, const half8 &bl,
-                                  floatx4 *main, floatx4 *corr) {
-    half8 lo[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const half8 hi = whi[m * stride];
-        main[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bh, main[m], 0, 0, 0);
-        corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bl, corr[m], 0, 0, 0);
-        lo[m] = wlo[m * stride];
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[m], bh, corr[m], 0, 0, 0);
-}
+// 8 wavefronts of 16 atoms per block: one block per CU holds the staged
+// weights of both layers, and 17k-atom systems fit in one pass of the CUs
+constexpr int kMlpWaves = 8;
+constexpr int kMlpThreads = 64 * kMlpWaves;
+constexpr int kNT = 1;   // 16-atom tiles per wavefront
 
 __device__ inline int chain_k(int t, int s, int j) { return 32 * t + 16 * (j >> 2) + 4 * s + (j & 3); }
 
-// exponent e with |x| 2^-e <= 1 over the atom's values (four k-slot lanes)
-__device__ inline int atom_exponent(float amax) {
+// the atom's largest magnitude over its four k-slot lanes
+__device__ inline float atom_max(float amax) {
     amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    return amax > 0.0f ? ilogbf(amax) + 1 : 0;
+    return fmaxf(amax, __shfl_xor(amax, 32, 64));
 }
 
 enum { MLP_X = 0, MLP_OUT = 1, MLP_READOUT = 2, MLP_BWD_OUT = 3, MLP_BWD_X = 4 };
@@ -91,25 +62,29 @@ struct MlpArgs {
     float *eps;                 // READOUT: per-atom energy
 };
 
-// Weight of output row `mrow`, input column `k` for a layer y = x W
-// (W[in][out], trans = 0) or y = x W^T (W[out][in], trans = 1).
-__device__ inline float wval(const float *W, int trans, int kdim, int mdim, int k, int mrow) {
-    if (k >= kdim) return 0.0f;
-    return trans ? W[mrow * kdim + k] : W[k * mdim + mrow];
-}
-
-// Stage a layer's A fragments: [m][t][l], value j = weight(row 16m + l%16,
-// column kfn(t, l/16, j)); chained = 1 uses the accumulator-chain k order.
-__device__ inline void stage(half8 *dhi, half8 *dlo, const float *W, int trans, int kdim, int mdim, int MT, int T, int chained) {
-    for (int idx = threadIdx.x; idx < MT * T * 64; idx += blockDim.x) {
-        const int m = idx / (T * 64), t = (idx / 64) % T, l = idx % 64;
-        float v[8];
+// Weights of A fragment idx of a layer ([m][t][l]): value j = weight(row
+// 16m + l%16, column k(t, l/16, j)), k in the plain order (32t + 8s + j) or
+// the accumulator-chain order.  In both orders values 0-3 and 4-7 are runs
+// of four consecutive k, read as one 16-byte load each when W is stored
+// [out][in] (TRANS); 0 beyond kdim.
+template <int T, int TRANS, int CHAINED>
+__device__ inline void layer_frag(const float *W, int kdim, int mdim, int idx, float (&v)[8]) {
+    const int m = idx / (T * 64), t = (idx / 64) % T, l = idx % 64, s = l / 16;
+    const int mrow = 16 * m + l % 16;
+    const int k0 = CHAINED ? 32 * t + 4 * s : 32 * t + 8 * s;
+    const int k1 = CHAINED ? k0 + 16 : k0 + 4;
+    if (TRANS) {
+        float4 p = make_float4(0.f, 0.f, 0.f, 0.f), q = p;
+        if (k0 < kdim) p = *reinterpret_cast<const float4 *>(W + (int64_t)mrow * kdim + k0);
+        if (k1 < kdim) q = *reinterpret_cast<const float4 *>(W + (int64_t)mrow * kdim + k1);
+        v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+        v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+    } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int k = chained ? chain_k(t, l / 16, j) : 32 * t + 8 * (l / 16) + j;
-            v[j] = wval(W, trans, kdim, mdim, k, 16 * m + l % 16);
+            const int k = (j < 4 ? k0 : k1) + (j & 3);
+            v[j] = k < kdim ? W[(int64_t)k * mdim + mrow] : 0.0f;
         }
-        split8(v, dhi[idx], dlo[idx]);
     }
 }
 
@@ -117,137 +92,187 @@ template <int F, int MODE>
 __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
     using S = Shape<F, MODE>;
     constexpr int M1 = S::M1, T1 = S::T1, M2 = S::M2, T2 = S::T2;
+    constexpr int MG1 = M1 < 4 ? M1 : 4, MG2 = M2 < 4 ? M2 : 4;
     constexpr int TRANS1 = (MODE == MLP_BWD_OUT || MODE == MLP_BWD_X) ? 1 : 0;
     constexpr int TRANS2 = (MODE == MLP_READOUT || MODE == MLP_BWD_OUT) ? 1 : 0;
     __shared__ half8 s_w1h[M1 * T1 * 64], s_w1l[M1 * T1 * 64];
     __shared__ half8 s_w2h[S::TWO ? M2 * T2 * 64 : 1], s_w2l[S::TWO ? M2 * T2 * 64 : 1];
-    stage(s_w1h, s_w1l, a.W1, TRANS1, S::FI1, S::FO1, M1, T1, 0);
-    if (S::TWO) stage(s_w2h, s_w2l, a.W2, TRANS2, S::FI2, S::FO2, M2, T2, 1);
-    __syncthreads();
+    __shared__ unsigned s_max[2];
+    if (threadIdx.x < 2) s_max[threadIdx.x] = 0u;
 
     const int lane = threadIdx.x % 64, slot = lane / 16;
-    const int atom0 = (blockIdx.x * (kMlpThreads / 64) + threadIdx.x / 64) * 16;
-    if (atom0 >= a.N) return;
-    const int atom = atom0 + lane % 16;
-    const bool live = atom < a.N;
-
-    // first layer input: features 32 t + 8 slot + j of the lane's atom
-    float xin[T1][8];
-    float xmax = 0.0f;
+    const int base = (blockIdx.x * kMlpWaves + threadIdx.x / 64) * (16 * kNT);
+    int atom[kNT];
+    bool live[kNT];
+    // first layer input: features 32 t + 8 slot + j of the lane's atoms
+    // (loaded before the weights are staged, so that the two latencies overlap)
+    float xin[kNT][T1][8];
+    float xmax[kNT];
 #pragma unroll
-    for (int t = 0; t < T1; ++t)
+    for (int n = 0; n < kNT; ++n) {
+        atom[n] = base + 16 * n + lane % 16;
+        live[n] = atom[n] < a.N;
+        xmax[n] = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int f0 = 32 * t + 8 * slot + 4 * q;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (live && f0 < S::FI1) v = *reinterpret_cast<const float4 *>(a.in + (int64_t)atom * F + f0);
-            xin[t][4 * q + 0] = v.x; xin[t][4 * q + 1] = v.y; xin[t][4 * q + 2] = v.z; xin[t][4 * q + 3] = v.w;
-            xmax = fmaxf(xmax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        }
-    const int e1 = atom_exponent(xmax);
-    floatx4 am[M1], ac[M1];
+        for (int t = 0; t < T1; ++t)
 #pragma unroll
-    for (int m = 0; m < M1; ++m) am[m] = ac[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < T1; ++t) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = ldexpf(xin[t][j], -e1);
-        half8 bh, bl;
-        split8(v, bh, bl);
-        mma3_tiles<M1>(s_w1h + t * 64 + lane, s_w1l + t * 64 + lane, T1 * 64, bh, bl, am, ac);
+            for (int q = 0; q < 2; ++q) {
+                const int f0 = 32 * t + 8 * slot + 4 * q;
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (live[n] && f0 < S::FI1) v = *reinterpret_cast<const float4 *>(a.in + (int64_t)atom[n] * F + f0);
+                xin[n][t][4 * q + 0] = v.x; xin[n][t][4 * q + 1] = v.y;
+                xin[n][t][4 * q + 2] = v.z; xin[n][t][4 * q + 3] = v.w;
+                xmax[n] = fmaxf(xmax[n], fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
     }
-    // first-layer result for output features 16 m + 4 slot + r
-    float r1[M1][4];
+    __syncthreads();   // s_max cleared
+    const int sw1 = stage_split<M1 * T1 * 64, kMlpThreads>(s_w1h, s_w1l, M1 * T1 * 64, &s_max[0],
+        [&](int idx, float (&v)[8]) { layer_frag<T1, TRANS1, 0>(a.W1, S::FI1, S::FO1, idx, v); });
+    int sw2 = 0;
+    if (S::TWO)
+        sw2 = stage_split<M2 * T2 * 64, kMlpThreads>(s_w2h, s_w2l, M2 * T2 * 64, &s_max[1],
+            [&](int idx, float (&v)[8]) { layer_frag<T2, TRANS2, 1>(a.W2, S::FI2, S::FO2, idx, v); });
+    __syncthreads();
+    if (base >= a.N) return;
+
+    // first layer: r1 = in W1 for output features 16 m + 4 slot + r
+    float r1[kNT][M1][4];
+    {
+        int sx[kNT];
+        half8 bh[T1][kNT], bl[T1][kNT];
 #pragma unroll
-    for (int m = 0; m < M1; ++m)
+        for (int n = 0; n < kNT; ++n) {
+            sx[n] = split_scale(atom_max(xmax[n]));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) r1[m][r] = ldexpf(am[m][r] + ac[m][r] * kLoUnscale, e1);
+            for (int t = 0; t < T1; ++t) {
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = ldexpf(xin[n][t][j], sx[n]);
+                split8(v, bh[t][n], bl[t][n]);
+            }
+        }
+#pragma unroll
+        for (int m0 = 0; m0 < M1; m0 += MG1) {
+            floatx4 acc[MG1][kNT];
+#pragma unroll
+            for (int m = 0; m < MG1; ++m)
+#pragma unroll
+                for (int n = 0; n < kNT; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < T1; ++t)
+                mma_split<MG1, kNT>(s_w1h + (m0 * T1 + t) * 64 + lane, s_w1l + (m0 * T1 + t) * 64 + lane, T1 * 64,
+                                    bh[t], bl[t], acc);
+#pragma unroll
+            for (int m = 0; m < MG1; ++m)
+#pragma unroll
+                for (int n = 0; n < kNT; ++n)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) r1[n][m0 + m][r] = ldexpf(acc[m][n][r], -(sw1 + sx[n]));
+        }
+    }
 
     if (MODE == MLP_X || MODE == MLP_BWD_X) {
-        if (!live) return;
 #pragma unroll
-        for (int m = 0; m < M1; ++m) {
-            float4 *dst = reinterpret_cast<float4 *>(a.out + (int64_t)atom * F + 16 * m + 4 * slot);
-            float4 v = make_float4(r1[m][0], r1[m][1], r1[m][2], r1[m][3]);
-            if (MODE == MLP_BWD_X) {
-                const float4 o = *dst;
-                v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+        for (int n = 0; n < kNT; ++n) {
+            if (!live[n]) continue;
+#pragma unroll
+            for (int m = 0; m < M1; ++m) {
+                float4 *dst = reinterpret_cast<float4 *>(a.out + (int64_t)atom[n] * F + 16 * m + 4 * slot);
+                float4 v = make_float4(r1[n][m][0], r1[n][m][1], r1[n][m][2], r1[n][m][3]);
+                if (MODE == MLP_BWD_X) {
+                    const float4 o = *dst;
+                    v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+                }
+                *dst = v;
             }
-            *dst = v;
         }
         return;
     }
 
-    // activation between the layers -> B operand of the second GEMM
-    float z[M1][4];
-    float zmax = 0.0f;
-    float eps_part = 0.0f;
+    // activation between the layers -> B operands of the second GEMM
+    half8 bh[T2][kNT], bl[T2][kNT];
+    int sz[kNT];
 #pragma unroll
-    for (int m = 0; m < M1; ++m) {
-        const int n0 = 16 * m + 4 * slot;
-        if (MODE == MLP_OUT) {
-            float o[4];
+    for (int n = 0; n < kNT; ++n) {
+        float z[M1][4];
+        float zmax = 0.0f;
+        float eps_part = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                o[r] = r1[m][r] + a.b1[n0 + r];
-                z[m][r] = ssp(o[r]);
+        for (int m = 0; m < M1; ++m) {
+            const int n0 = 16 * m + 4 * slot;
+            if (MODE == MLP_OUT) {
+                float o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    o[r] = r1[n][m][r] + a.b1[n0 + r];
+                    z[m][r] = ssp(o[r]);
+                }
+                if (live[n])
+                    *reinterpret_cast<float4 *>(a.mid + (int64_t)atom[n] * F + n0) = make_float4(o[0], o[1], o[2], o[3]);
+            } else if (MODE == MLP_READOUT) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float q = r1[n][m][r] + a.b1[n0 + r];
+                    eps_part += ssp(q) * a.R2[n0 + r];
+                    z[m][r] = sigm(q) * a.R2[n0 + r];
+                }
+            } else {   // MLP_BWD_OUT
+                float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (live[n]) o = *reinterpret_cast<const float4 *>(a.aux + (int64_t)atom[n] * F + n0);
+                z[m][0] = r1[n][m][0] * sigm(o.x);
+                z[m][1] = r1[n][m][1] * sigm(o.y);
+                z[m][2] = r1[n][m][2] * sigm(o.z);
+                z[m][3] = r1[n][m][3] * sigm(o.w);
             }
-            if (live)
-                *reinterpret_cast<float4 *>(a.mid + (int64_t)atom * F + n0) = make_float4(o[0], o[1], o[2], o[3]);
-        } else if (MODE == MLP_READOUT) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float q = r1[m][r] + a.b1[n0 + r];
-                eps_part += ssp(q) * a.R2[n0 + r];
-                z[m][r] = sigm(q) * a.R2[n0 + r];
+            for (int r = 0; r < 4; ++r) zmax = fmaxf(zmax, fabsf(z[m][r]));
+        }
+        if (MODE == MLP_READOUT) {
+            eps_part += __shfl_xor(eps_part, 16, 64);
+            eps_part += __shfl_xor(eps_part, 32, 64);
+            if (live[n] && slot == 0) a.eps[atom[n]] = eps_part + a.c2[0];
+        }
+        sz[n] = split_scale(atom_max(zmax));
+#pragma unroll
+        for (int t = 0; t < T2; ++t) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int m = 2 * t + (j >> 2);
+                v[j] = m < M1 ? ldexpf(z[m < M1 ? m : 0][j & 3], sz[n]) : 0.0f;
             }
-        } else {   // MLP_BWD_OUT
-            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (live) o = *reinterpret_cast<const float4 *>(a.aux + (int64_t)atom * F + n0);
-            z[m][0] = r1[m][0] * sigm(o.x);
-            z[m][1] = r1[m][1] * sigm(o.y);
-            z[m][2] = r1[m][2] * sigm(o.z);
-            z[m][3] = r1[m][3] * sigm(o.w);
+            split8(v, bh[t][n], bl[t][n]);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) zmax = fmaxf(zmax, fabsf(z[m][r]));
     }
-    if (MODE == MLP_READOUT) {
-        eps_part += __shfl_xor(eps_part, 16, 64);
-        eps_part += __shfl_xor(eps_part, 32, 64);
-        if (live && slot == 0) a.eps[atom] = eps_part + a.c2[0];
-    }
-    const int e2 = atom_exponent(zmax);
-    floatx4 bm[M2], bc[M2];
 #pragma unroll
-    for (int m = 0; m < M2; ++m) bm[m] = bc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int m0 = 0; m0 < M2; m0 += MG2) {
+        floatx4 acc[MG2][kNT];
 #pragma unroll
-    for (int t = 0; t < T2; ++t) {
-        float v[8];
+        for (int m = 0; m < MG2; ++m)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int m = 2 * t + (j >> 2);
-            v[j] = m < M1 ? ldexpf(z[m < M1 ? m : 0][j & 3], -e2) : 0.0f;
-        }
-        half8 bh, bl;
-        split8(v, bh, bl);
-        mma3_tiles<M2>(s_w2h + t * 64 + lane, s_w2l + t * 64 + lane, T2 * 64, bh, bl, bm, bc);
-    }
-    if (!live) return;
+            for (int n = 0; n < kNT; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < M2; ++m) {
-        const int n0 = 16 * m + 4 * slot;
-        float v[4];
+        for (int t = 0; t < T2; ++t)
+            mma_split<MG2, kNT>(s_w2h + (m0 * T2 + t) * 64 + lane, s_w2l + (m0 * T2 + t) * 64 + lane, T2 * 64,
+                                bh[t], bl[t], acc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = ldexpf(bm[m][r] + bc[m][r] * kLoUnscale, e2);
-        float4 *dst = reinterpret_cast<float4 *>(a.out + (int64_t)atom * F + n0);
-        if (MODE == MLP_OUT) {
-            const float4 h = *dst;
-            *dst = make_float4(h.x + v[0] + a.b2[n0], h.y + v[1] + a.b2[n0 + 1], h.z + v[2] + a.b2[n0 + 2],
-                               h.w + v[3] + a.b2[n0 + 3]);
-        } else {
-            *dst = make_float4(v[0], v[1], v[2], v[3]);
+        for (int n = 0; n < kNT; ++n) {
+            if (!live[n]) continue;
+#pragma unroll
+            for (int m = 0; m < MG2; ++m) {
+                const int n0 = 16 * (m0 + m) + 4 * slot;
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = ldexpf(acc[m][n][r], -(sw2 + sz[n]));
+                float4 *dst = reinterpret_cast<float4 *>(a.out + (int64_t)atom[n] * F + n0);
+                if (MODE == MLP_OUT) {
+                    const float4 h = *dst;
+                    *dst = make_float4(h.x + v[0] + a.b2[n0], h.y + v[1] + a.b2[n0 + 1], h.z + v[2] + a.b2[n0 + 2],
+                                       h.w + v[3] + a.b2[n0 + 3]);
+                } else {
+                    *dst = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
         }
     }
 }
@@ -256,7 +281,7 @@ template <int MODE>
 sn_status launch_mlp(int F, const MlpArgs &a, hipStream_t s) {
     if (a.N <= 0) return SN_OK;
     ProfScope ps(K_MLP, s);
-    const int atoms_per_block = 16 * (kMlpThreads / 64);
+    const int atoms_per_block = 16 * kNT * kMlpWaves;
     const int grid = (a.N + atoms_per_block - 1) / atoms_per_block;
     switch (F) {
         case 32: mlp_kernel<32, MODE><<<grid, kMlpThreads, 0, s>>>(a); break;
