@@ -56,7 +56,8 @@ def cfconv_bytes(E: int, N: int, F: int):
     return E * (4 * F + 12) + 2 * N * F * 4
 
 
-KERNEL_SOURCES = ("filter.hip", "graph.hip", "atomwise.hip", "neighbors.hip", "api.hip", "sn_internal.h")
+KERNEL_SOURCES = ("filter.hip", "graph.hip", "atomwise.hip", "mlp.hip", "neighbors.hip", "api.hip", "sn_internal.h",
+                  "split_mfma.h")
 
 
 def source_hash() -> str:
