@@ -164,6 +164,43 @@ size_t bytes_needed(const sn_model *m, const sn_system *s, int64_t E) {
     return std::max(nb, ef);
 }
 
+// Auxiliary stream of a device for the filter kernels, which run beside the
+// atom-wise chain of the caller's stream: the filter network depends only on
+// the pair distances, so every interaction's forward filter can start as
+// soon as the pairs are set up, and each backward filter (the only writer of
+// S, in interaction order) overlaps the next CFConv and atom-wise layers.
+// Fork and join go through events; the stream keeps the default priority.
+// Enqueueing holds the device's lock, so calls from several host threads
+// stay correctly ordered (their kernels still overlap on the device).
+struct Aux {
+    std::mutex mu;
+    hipStream_t s = nullptr;
+    hipEvent_t ev[2 * 16 + 3] = {};
+    bool tried = false, ok = false;
+};
+
+Aux &aux_for_current_device() {
+    static Aux aux[64];
+    static std::mutex init_mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    Aux &a = aux[dev & 63];
+    std::lock_guard<std::mutex> g(init_mu);
+    if (!a.tried) {
+        a.tried = true;
+        a.ok = hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) == hipSuccess;
+        for (auto &e : a.ev) a.ok = a.ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+    }
+    return a;
+}
+
+// `to` waits for the work enqueued so far on `from`
+sn_status stream_wait(hipEvent_t e, hipStream_t from, hipStream_t to) {
+    if (from == to) return SN_OK;
+    if (hipEventRecord(e, from) != hipSuccess || hipStreamWaitEvent(to, e, 0) != hipSuccess) return SN_ERR_HIP;
+    return SN_OK;
+}
+
 // The pipeline itself; arguments already checked, status not cleared.
 sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const float *pos, const int32_t *row_ptr,
                              const int32_t *col, const int32_t *rev, int64_t E, float *energy, float *forces,
@@ -196,27 +233,48 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     auto o_t = [&](int t) { return F32(L.o) + NF * t; };
     auto gy_t = [&](int t) { return F32(L.gy) + NF * t; };
 
-    SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, E, m.cutoff, ws, L, status, s));
-    SN_TRY(embed(N, F, m.n_types, sys.types, prm + off[0], h, status, s));
-    SN_TRY(mlp_x(N, F, h, blk(0, W_IN), x_t(0), s));
-    for (int t = 0; t < I; ++t) {
-        SN_TRY(filter_forward(m, t, pgeo, P, phi_t(t), s));
-        SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, s));
-        SN_TRY(mlp_out(N, F, y, blk(t, WO1), blk(t, BO1), blk(t, WO2), blk(t, BO2), o_t(t), h, s));
-        if (t + 1 < I) SN_TRY(mlp_x(N, F, h, blk(t + 1, W_IN), x_t(t + 1), s));
-    }
-    SN_TRY(mlp_readout(N, F, h, R1, c1, R2, c2, eps, gh, s));
-    SN_TRY(replica_sum(B, sys.replica_ptr, eps, energy, s));
-    // backward through the interactions in reverse
-    for (int t = I - 1; t >= 0; --t) {
-        SN_TRY(mlp_bwd_out(N, F, gh, blk(t, WO2), o_t(t), blk(t, WO1), gy_t(t), s));
-        SN_TRY(filter_backward(m, t, pgeo, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t),
-                               reinterpret_cast<float2 *>(ws + L.rowmax), S, t != I - 1, s));
-        if (t > 0) {   // dE/dh below the first block is not needed for forces
-            SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, s));
-            SN_TRY(mlp_bwd_x(N, F, y, blk(t, W_IN), gh, s));
+    Aux &ax = aux_for_current_device();
+    std::lock_guard<std::mutex> lock(ax.mu);
+    hipStream_t s2 = ax.ok ? ax.s : s;
+    hipEvent_t *ev = ax.ev;   // [0] fork, [1 + t] phi_t ready, [1 + I + t] g_y_t ready, [2 + 2I] join
+
+    auto run = [&]() -> sn_status {
+        SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, E, m.cutoff, ws, L, status, s));
+        SN_TRY(stream_wait(ev[0], s, s2));
+        for (int t = 0; t < I; ++t) {
+            SN_TRY(filter_forward(m, t, pgeo, P, phi_t(t), s2));
+            if (s2 != s && hipEventRecord(ev[1 + t], s2) != hipSuccess) return SN_ERR_HIP;
         }
-    }
+        SN_TRY(embed(N, F, m.n_types, sys.types, prm + off[0], h, status, s));
+        SN_TRY(mlp_x(N, F, h, blk(0, W_IN), x_t(0), s));
+        for (int t = 0; t < I; ++t) {
+            if (s2 != s && hipStreamWaitEvent(s, ev[1 + t], 0) != hipSuccess) return SN_ERR_HIP;
+            SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, s));
+            SN_TRY(mlp_out(N, F, y, blk(t, WO1), blk(t, BO1), blk(t, WO2), blk(t, BO2), o_t(t), h, s));
+            if (t + 1 < I) SN_TRY(mlp_x(N, F, h, blk(t + 1, W_IN), x_t(t + 1), s));
+        }
+        SN_TRY(mlp_readout(N, F, h, R1, c1, R2, c2, eps, gh, s));
+        SN_TRY(replica_sum(B, sys.replica_ptr, eps, energy, s));
+        // backward through the interactions in reverse; the filter backward of
+        // interaction t runs beside the CFConv and layers that lead to t - 1
+        for (int t = I - 1; t >= 0; --t) {
+            SN_TRY(mlp_bwd_out(N, F, gh, blk(t, WO2), o_t(t), blk(t, WO1), gy_t(t), s));
+            SN_TRY(stream_wait(ev[1 + I + t], s, s2));
+            SN_TRY(filter_backward(m, t, pgeo, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t),
+                                   reinterpret_cast<float2 *>(ws + L.rowmax), S, t != I - 1, s2));
+            if (t > 0) {   // dE/dh below the first block is not needed for forces
+                SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, s));
+                SN_TRY(mlp_bwd_x(N, F, y, blk(t, W_IN), gh, s));
+            }
+        }
+        return SN_OK;
+    };
+    const sn_status st = run();
+    // join: everything enqueued on the auxiliary stream precedes what follows
+    // on the caller's stream (also after an error)
+    const sn_status js = stream_wait(ev[2 + 2 * I], s2, s);
+    SN_TRY(st);
+    SN_TRY(js);
     return forces_rows(N, row_ptr, col, edge_pair, pgeo, S, forces, status, s);
 }
 
