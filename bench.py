@@ -212,6 +212,40 @@ def load_traffic(workload: str):
     return data["bytes_per_launch"]
 
 
+def event_times(fn, n: int):
+    """Per-call milliseconds of fn() from HIP events on the current stream."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def measured_peaks(torch):
+    """Device rates to set the datasheet peaks beside: a 1 GiB device-to-device
+    copy (read + write bytes / time) and a large fp16 GEMM in the vendor
+    library (divided by three for the split-fp16 product rate)."""
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    ms = event_times(lambda: b.copy_(a), 10)
+    copy = 2 * 4 * n / (min(ms) * 1e-3) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, dtype=torch.float16, device="cuda")
+    y = torch.randn(m, m, dtype=torch.float16, device="cuda")
+    torch.matmul(x, y)
+    ms = event_times(lambda: torch.matmul(x, y), 10)
+    gemm = 2 * m ** 3 / (min(ms) * 1e-3) / 1e12
+    return {"hbm_copy_GBs": round(copy, 1), "f16_gemm_TFLOPs": round(gemm, 1),
+            "split_f16_mfma_TFLOPs_via_gemm": round(gemm / 3, 1),
+            "how": "1 GiB float32 device copy (2 x 4 B per element); 8192^3 fp16 torch.matmul; best of 10"}
+
+
 def cpu_baseline(cfg, seconds: float):
     """Time the CPU oracle (as it is) on a bounded sample of the same workload."""
     import numpy as np
@@ -254,6 +288,8 @@ def main():
     ap.add_argument("--filter-format", type=int, default=0, choices=[0, 1])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-measure-peaks", dest="measure_peaks", action="store_false",
+                    help="skip the device-copy and fp16-GEMM rate measurements (fractions of measured rates)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first copy a buffer of this many MiB (calibrates hardware byte counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -354,13 +390,18 @@ def main():
     for _ in range(3):
         sn.energy_forces(model, system, pos, row_ptr, col, rev, E_last, ws, forces=forces)
     torch.cuda.synchronize()
-    n_fixed = max(10, args.steps)
+    n_fixed = max(20, args.steps)
     t2 = time.perf_counter()
     for _ in range(n_fixed):
         sn.energy_forces(model, system, pos, row_ptr, col, rev, E_last, ws, forces=forces)
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     fixed_evals_per_s = n_fixed / (t3 - t2)
+    eval_ms = event_times(lambda: sn.energy_forces(model, system, pos, row_ptr, col, rev, E_last, ws,
+                                                   forces=forces), n_fixed)
+    # the neighbour build alone (cell list + CSR), same positions
+    nb_ms = event_times(lambda: sn.build_csr_neighbors(system, pos, h["cutoff"], capacity, ws), n_fixed)
+    peaks = measured_peaks(torch) if args.measure_peaks else None
 
     fwd_pp, bwd_pp = filter_flops_per_pair(F, K)
     kernels = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps,
@@ -412,12 +453,23 @@ def main():
         "ns_per_day": round(ns_per_day, 1),
         "evals_per_s_fixed_csr": round(fixed_evals_per_s, 2),
         "edges_per_s_fixed_csr": round(E_last * fixed_evals_per_s, 1),
+        "eval_ms_fixed_csr": {"median": round(float(np.median(eval_ms)), 4), "min": round(float(np.min(eval_ms)), 4),
+                              "n": len(eval_ms)},
+        "neighbour_build_ms": {"median": round(float(np.median(nb_ms)), 4), "min": round(float(np.min(nb_ms)), 4),
+                               "n": len(nb_ms)},
+        "peak_device_memory_bytes": int(torch.cuda.max_memory_allocated()),
+        "workspace_bytes": int(ws.numel()),
         "roofline": main_rl,
         "roofline_kernels": rl,
         "dominant_kernel": dominant,
         "kernels": kernels,
         "context": {"pages_ns_per_day": 1000, "pages_hardware": "1x NVIDIA RTX PRO 6000, 64 x 269-bead 1ENH"},
     }
+    if peaks:
+        out["measured_peaks"] = peaks
+        for r in rl.values():
+            ref = peaks["hbm_copy_GBs"] if r["unit"] == "GB/s" else peaks["split_f16_mfma_TFLOPs_via_gemm"]
+            r["frac_vs_measured"] = round(r["achieved"] / ref, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(out))

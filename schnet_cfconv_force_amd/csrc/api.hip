@@ -2,6 +2,7 @@
 // energy/force pipeline, the velocity-Verlet driver and per-kernel timing.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -194,6 +195,14 @@ Aux &aux_for_current_device() {
     return a;
 }
 
+bool serial_requested() {
+    static const bool v = [] {
+        const char *e = std::getenv("SN_SERIAL");
+        return e && e[0] == '1';
+    }();
+    return v;
+}
+
 // `to` waits for the work enqueued so far on `from`
 sn_status stream_wait(hipEvent_t e, hipStream_t from, hipStream_t to) {
     if (from == to) return SN_OK;
@@ -235,7 +244,10 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
 
     Aux &ax = aux_for_current_device();
     std::lock_guard<std::mutex> lock(ax.mu);
-    hipStream_t s2 = ax.ok ? ax.s : s;
+    // with per-kernel timing on (or SN_SERIAL=1 in the environment) every
+    // kernel runs on the caller's stream, so that its timing events or a
+    // kernel trace bracket that kernel alone
+    hipStream_t s2 = (ax.ok && !g_prof_on && !serial_requested()) ? ax.s : s;
     hipEvent_t *ev = ax.ev;   // [0] fork, [1 + t] phi_t ready, [1 + I + t] g_y_t ready, [2 + 2I] join
 
     auto run = [&]() -> sn_status {
