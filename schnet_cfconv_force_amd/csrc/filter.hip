@@ -39,7 +39,8 @@ namespace sn {
 
 namespace {
 
-constexpr int kFwdThreads = 768;    // 3 wavefronts per SIMD
+constexpr int kFwdThreads = 1024;   // 4 wavefronts per SIMD
+constexpr int kFwdNT = 1;           // 16-pair tiles per forward wavefront (2 measured slower)
 constexpr int kBwdThreads = 512;    // 2 wavefronts per SIMD
 constexpr float kPi = 3.14159265358979323846f;
 constexpr float kLoScale = 2048.0f;        // 2^11
@@ -132,6 +133,29 @@ __device__ inline void mma3_tiles(const half8 *whi, const half8 *wlo, int stride
     for (int m = 0; m < MT; ++m) corr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[m], bh, corr[m], 0, 0, 0);
 }
 
+// The split products for MG weight tiles and NT B operands (16-pair tiles)
+// sharing one pair of fragment reads: main[m][n] += hi.hi, corr[m][n] +=
+// hi.lo + lo.hi; dependent instructions on one accumulator are MG*NT apart.
+template <int MG, int NT>
+__device__ inline void mma3_tiles_nt(const half8 *whi, const half8 *wlo, int stride, const half8 (&bh)[NT],
+                                     const half8 (&bl)[NT], floatx4 (&main)[MG][NT], floatx4 (&corr)[MG][NT]) {
+    half8 lo[MG];
+#pragma unroll
+    for (int m = 0; m < MG; ++m) {
+        const half8 hi = whi[m * stride];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            main[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bh[n], main[m][n], 0, 0, 0);
+            corr[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bl[n], corr[m][n], 0, 0, 0);
+        }
+        lo[m] = wlo[m * stride];
+    }
+#pragma unroll
+    for (int m = 0; m < MG; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) corr[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[m], bh[n], corr[m][n], 0, 0, 0);
+}
+
 // k index of value j of the B operand of a chained 32-wide step t (two
 // accumulator tiles 2t and 2t+1), for the lane in k-slot s
 __device__ inline int chain_k(int t, int s, int j) { return 32 * t + 16 * (j >> 2) + 4 * s + (j & 3); }
@@ -145,8 +169,8 @@ __device__ inline int rbf_row_k(int kt, int s, int r) { return 32 * (kt >> 1) + 
 // the XCD count; the blocks of one XCD share one contiguous range of tiles
 // (pairs are in CSR order, so the gathered atom rows of a range stay in
 // that XCD's L2), and the wavefronts of those blocks stride through it.
-__device__ inline void tile_range(int64_t P, int64_t &tile, int64_t &end, int64_t &stride) {
-    const int64_t ntiles = (P + 15) / 16;
+__device__ inline void tile_range(int64_t P, int64_t &tile, int64_t &end, int64_t &stride, int tile_pairs = 16) {
+    const int64_t ntiles = (P + tile_pairs - 1) / tile_pairs;
     const int xcd = blockIdx.x % kXcds, nxb = gridDim.x / kXcds;
     const int64_t per = (ntiles + kXcds - 1) / kXcds;
     const int waves = blockDim.x / 64;
@@ -172,33 +196,6 @@ __device__ inline void stage_a1(const FilterArgs &a, half8 *s_hi, half8 *s_lo, i
     });
 }
 
-// First GEMM, acc = (rbf(d) A1)^T in split form; rb receives the lane's
-// basis values rbf_k, k = 32 ks + 8 s + j.
-template <int F>
-__device__ inline void gemm_rbf(const FilterArgs &a, const half8 *s_a1h, const half8 *s_a1l, int KS, float d, int lane,
-                                floatx4 (&main)[F / 16], floatx4 (&corr)[F / 16], float (&rb)[2][8]) {
-    constexpr int MT = F / 16;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) main[m] = corr[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        if (ks < KS) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) rb[ks][j] = rbf_val(a, d, 32 * ks + 8 * (lane / 16) + j);
-            half8 bh, bl;
-            split8(rb[ks], bh, bl);
-            constexpr int MG = MT < 4 ? MT : 4;
-#pragma unroll
-            for (int m0 = 0; m0 < MT; m0 += MG)
-                mma3_tiles<MG>(s_a1h + (m0 * KS + ks) * 64 + lane, s_a1l + (m0 * KS + ks) * 64 + lane, KS * 64, bh,
-                               bl, main + m0, corr + m0);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) rb[ks][j] = 0.0f;
-        }
-    }
-}
-
 // 2^e such that |x| * 2^-e <= 1 for the largest |x| of the lane's pair
 // (the pair's values are spread over the four k-slot lanes l%16 + 16 s).
 __device__ inline int pair_exponent(float amax) {
@@ -211,6 +208,8 @@ template <int F>
 __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;                 // 32-wide k steps of the F x F GEMM
+    constexpr int NT = kFwdNT;                 // 16-pair tiles per wavefront
+    constexpr int MG = MT < 4 ? MT : 4;        // output tiles per group
     __shared__ half8 s_a1h[MT * 2 * 64], s_a1l[MT * 2 * 64];
     __shared__ half8 s_a2h[MT * T2 * 64], s_a2l[MT * T2 * 64];   // [m][t][l]: A2[chain_k(t, l/16, j)][16 m + l%16]
     __shared__ float s_b1[F], s_b2[F];
@@ -223,50 +222,88 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     for (int f = threadIdx.x; f < F; f += blockDim.x) { s_b1[f] = a.b1[f]; s_b2[f] = a.b2[f]; }
     __syncthreads();
 
-    const int lane = threadIdx.x % 64;
-    const int slot = lane / 16;
     int64_t tile, tile_end, stride;
-    tile_range(a.P, tile, tile_end, stride);
+    tile_range(a.P, tile, tile_end, stride, 16 * NT);
     for (; tile < tile_end; tile += stride) {
         // keep the weight-fragment LDS reads inside the loop: hoisted out of
         // it they would need hundreds of registers
         asm volatile("" ::: "memory");
-        const int64_t p = tile * 16 + lane % 16;
-        const float d = (p < a.P) ? a.dsrc[p * a.dstride + a.doff] : 0.0f;
-        floatx4 am[MT], ac[MT];
-        float rb[2][8];
-        gemm_rbf<F>(a, s_a1h, s_a1l, KS, d, lane, am, ac, rb);
-        // z = ssp(a), converted step by step into split B operands
-        half8 zh[T2], zl[T2];
+        int lane = threadIdx.x % 64;
+        asm volatile("" : "+v"(lane));
+        const int slot = lane / 16;
+        int64_t p[NT];
+        half8 rh[2][NT], rl[2][NT];
 #pragma unroll
-        for (int t = 0; t < T2; ++t) {
-            float v[8];
+        for (int n = 0; n < NT; ++n) {
+            p[n] = tile * (16 * NT) + 16 * n + lane % 16;
+            const float d = (p[n] < a.P) ? a.dsrc[p[n] * a.dstride + a.doff] : 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int m = 2 * t + (j >> 2), r = j & 3;
-                v[j] = ssp(am[m][r] + ac[m][r] * kLoUnscale + s_b1[16 * m + 4 * slot + r]);
+            for (int ks = 0; ks < 2; ++ks) {
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = ks < KS ? rbf_val(a, d, 32 * ks + 8 * slot + j) : 0.0f;
+                split8(v, rh[ks][n], rl[ks][n]);
             }
-            split8(v, zh[t], zl[t]);
         }
-        constexpr int MG = MT < 4 ? MT : 4;    // output tiles per group
+        // z = ssp(rbf A1 + b1) on features 16 m + 4 slot + r, in groups of MG tiles
+        float z[NT][MT][4];
 #pragma unroll
         for (int m0 = 0; m0 < MT; m0 += MG) {
-            floatx4 main[MG], corr[MG];
+            floatx4 am[MG][NT], ac[MG][NT];
 #pragma unroll
-            for (int g = 0; g < MG; ++g) main[g] = corr[g] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int g = 0; g < MG; ++g)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) am[g][n] = ac[g][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                if (ks < KS)
+                    mma3_tiles_nt<MG, NT>(s_a1h + (m0 * KS + ks) * 64 + lane, s_a1l + (m0 * KS + ks) * 64 + lane,
+                                          KS * 64, rh[ks], rl[ks], am, ac);
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+                const float4 b = *reinterpret_cast<const float4 *>(s_b1 + 16 * (m0 + g) + 4 * slot);
+                const float bb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) z[n][m0 + g][r] = ssp(am[g][n][r] + ac[g][n][r] * kLoUnscale + bb[r]);
+            }
+        }
+        // chained B operands of the second GEMM
+        half8 zh[T2][NT], zl[T2][NT];
+#pragma unroll
+        for (int t = 0; t < T2; ++t)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = z[n][2 * t + (j >> 2)][j & 3];
+                split8(v, zh[t][n], zl[t][n]);
+            }
+#pragma unroll
+        for (int m0 = 0; m0 < MT; m0 += MG) {
+            floatx4 main[MG][NT], corr[MG][NT];
+#pragma unroll
+            for (int g = 0; g < MG; ++g)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) main[g][n] = corr[g][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < T2; ++t)
-                mma3_tiles<MG>(s_a2h + (m0 * T2 + t) * 64 + lane, s_a2l + (m0 * T2 + t) * 64 + lane, T2 * 64, zh[t],
-                               zl[t], main, corr);
-            if (p < a.P) {
+                mma3_tiles_nt<MG, NT>(s_a2h + (m0 * T2 + t) * 64 + lane, s_a2l + (m0 * T2 + t) * 64 + lane,
+                                      T2 * 64, zh[t], zl[t], main, corr);
 #pragma unroll
-                for (int g = 0; g < MG; ++g) {
-                    const int f0 = 16 * (m0 + g) + 4 * slot;
-                    float4 v = make_float4(main[g][0] + corr[g][0] * kLoUnscale + s_b2[f0],
-                                           main[g][1] + corr[g][1] * kLoUnscale + s_b2[f0 + 1],
-                                           main[g][2] + corr[g][2] * kLoUnscale + s_b2[f0 + 2],
-                                           main[g][3] + corr[g][3] * kLoUnscale + s_b2[f0 + 3]);
-                    *reinterpret_cast<float4 *>(a.phi + p * F + f0) = v;
+            for (int n = 0; n < NT; ++n) {
+                if (p[n] < a.P) {
+#pragma unroll
+                    for (int g = 0; g < MG; ++g) {
+                        const int f0 = 16 * (m0 + g) + 4 * slot;
+                        const float4 b = *reinterpret_cast<const float4 *>(s_b2 + f0);
+                        const float4 v = make_float4(main[g][n][0] + corr[g][n][0] * kLoUnscale + b.x,
+                                                     main[g][n][1] + corr[g][n][1] * kLoUnscale + b.y,
+                                                     main[g][n][2] + corr[g][n][2] * kLoUnscale + b.z,
+                                                     main[g][n][3] + corr[g][n][3] * kLoUnscale + b.w);
+                        *reinterpret_cast<float4 *>(a.phi + p[n] * F + f0) = v;
+                    }
                 }
             }
         }
@@ -517,7 +554,7 @@ FilterArgs make_args(const sn_model &m, int t) {
 
 template <int F>
 sn_status launch_fwd(const FilterArgs &a, hipStream_t s) {
-    const int64_t tiles = (a.P + 15) / 16;
+    const int64_t tiles = (a.P + 16 * kFwdNT - 1) / (16 * kFwdNT);
     const int waves = kFwdThreads / 64;
     const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
     filter_fwd_kernel<F><<<grid, kFwdThreads, 0, s>>>(a);
