@@ -86,7 +86,8 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     L.gh = take(4 * N * F);
     L.eps = take(4 * N + 4 * B);   // eps[N], then an energy scratch [B]
     L.S = take(4 * P);
-    L.rowmax = take(8 * N);
+    L.xmax = take(4 * I * N);
+    L.gmax = take(4 * I * N);
     L.total = o;
     return L;
 }
@@ -241,6 +242,8 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     auto x_t = [&](int t) { return F32(L.x) + NF * t; };
     auto o_t = [&](int t) { return F32(L.o) + NF * t; };
     auto gy_t = [&](int t) { return F32(L.gy) + NF * t; };
+    auto xmax_t = [&](int t) { return F32(L.xmax) + (int64_t)N * t; };
+    auto gmax_t = [&](int t) { return F32(L.gmax) + (int64_t)N * t; };
 
     Aux &ax = aux_for_current_device();
     std::lock_guard<std::mutex> lock(ax.mu);
@@ -258,22 +261,22 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
             if (s2 != s && hipEventRecord(ev[1 + t], s2) != hipSuccess) return SN_ERR_HIP;
         }
         SN_TRY(embed(N, F, m.n_types, sys.types, prm + off[0], h, status, s));
-        SN_TRY(mlp_x(N, F, h, blk(0, W_IN), x_t(0), s));
+        SN_TRY(mlp_x(N, F, h, blk(0, W_IN), x_t(0), xmax_t(0), s));
         for (int t = 0; t < I; ++t) {
             if (s2 != s && hipStreamWaitEvent(s, ev[1 + t], 0) != hipSuccess) return SN_ERR_HIP;
             SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, s));
             SN_TRY(mlp_out(N, F, y, blk(t, WO1), blk(t, BO1), blk(t, WO2), blk(t, BO2), o_t(t), h, s));
-            if (t + 1 < I) SN_TRY(mlp_x(N, F, h, blk(t + 1, W_IN), x_t(t + 1), s));
+            if (t + 1 < I) SN_TRY(mlp_x(N, F, h, blk(t + 1, W_IN), x_t(t + 1), xmax_t(t + 1), s));
         }
         SN_TRY(mlp_readout(N, F, h, R1, c1, R2, c2, eps, gh, s));
         SN_TRY(replica_sum(B, sys.replica_ptr, eps, energy, s));
         // backward through the interactions in reverse; the filter backward of
         // interaction t runs beside the CFConv and layers that lead to t - 1
         for (int t = I - 1; t >= 0; --t) {
-            SN_TRY(mlp_bwd_out(N, F, gh, blk(t, WO2), o_t(t), blk(t, WO1), gy_t(t), s));
+            SN_TRY(mlp_bwd_out(N, F, gh, blk(t, WO2), o_t(t), blk(t, WO1), gy_t(t), gmax_t(t), s));
             SN_TRY(stream_wait(ev[1 + I + t], s, s2));
-            SN_TRY(filter_backward(m, t, pgeo, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t),
-                                   reinterpret_cast<float2 *>(ws + L.rowmax), S, t != I - 1, s2));
+            SN_TRY(filter_backward(m, t, pgeo, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
+                                   t != I - 1, s2));
             if (t > 0) {   // dE/dh below the first block is not needed for forces
                 SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, s));
                 SN_TRY(mlp_bwd_x(N, F, y, blk(t, W_IN), gh, s));

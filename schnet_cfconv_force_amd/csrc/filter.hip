@@ -64,7 +64,7 @@ struct FilterArgs {
     const float *x, *gy;         // [N][F]
     const float *phi_in;         // [P][F]
     float *S;                    // [P]
-    const float2 *rowmax;        // [N]: max_f |x_i[f]|, max_f |g_y_i[f]|
+    const float *xmax, *gmax;    // [N]: max_f |x_i[f]|, max_f |g_y_i[f]|
     int accumulate;
 };
 
@@ -358,8 +358,8 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         // per-atom row maxima), split into the B operands of all k-steps.
         int e1 = 0;
         {
-            const float2 mi = live ? a.rowmax[ij.x] : make_float2(0.f, 0.f);
-            const float2 mj = live ? a.rowmax[ij.y] : make_float2(0.f, 0.f);
+            const float2 mi = live ? make_float2(a.xmax[ij.x], a.gmax[ij.x]) : make_float2(0.f, 0.f);
+            const float2 mj = live ? make_float2(a.xmax[ij.y], a.gmax[ij.y]) : make_float2(0.f, 0.f);
             const float bound = fc * (mi.y * mj.x + mj.y * mi.x);
             e1 = bound > 0.0f ? ilogbf(bound) + 1 : 0;
         }
@@ -496,24 +496,6 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     }
 }
 
-// per atom: max_f |x_i[f]| and max_f |g_y_i[f]| (LPR = F/4 lanes per row)
-template <int F>
-__global__ __launch_bounds__(256) void rowmax_kernel(int N, const float *x, const float *gy, float2 *out) {
-    constexpr int LPR = F / 4;
-    const int sub = threadIdx.x % LPR;
-    const int row = (blockIdx.x * 256 + threadIdx.x) / LPR;
-    if (row >= N) return;
-    const float4 a = *reinterpret_cast<const float4 *>(x + (int64_t)row * F + 4 * sub);
-    const float4 b = *reinterpret_cast<const float4 *>(gy + (int64_t)row * F + 4 * sub);
-    float mx = fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w)));
-    float mg = fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w)));
-    for (int o = LPR / 2; o > 0; o >>= 1) {
-        mx = fmaxf(mx, __shfl_xor(mx, o, LPR));
-        mg = fmaxf(mg, __shfl_xor(mg, o, LPR));
-    }
-    if (sub == 0) out[row] = make_float2(mx, mg);
-}
-
 int num_cus() {
     static int n = 0;
     if (n == 0) {
@@ -562,9 +544,7 @@ sn_status launch_fwd(const FilterArgs &a, hipStream_t s) {
 }
 
 template <int F>
-sn_status launch_bwd(const FilterArgs &a, int N, float2 *rowmax, hipStream_t s) {
-    rowmax_kernel<F><<<(N + 256 / (F / 4) - 1) / (256 / (F / 4)), 256, 0, s>>>(N, a.x, a.gy, rowmax);
-    SN_TRY(launch_status());
+sn_status launch_bwd(const FilterArgs &a, hipStream_t s) {
     const int64_t tiles = (a.P + 15) / 16;
     const int waves = kBwdThreads / 64;
     const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
@@ -606,9 +586,10 @@ sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t
 }
 
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const int2 *pair_ij, int64_t P, int N,
-                          const float *phi, const float *x, const float *gy, float2 *rowmax, float *S,
-                          int accumulate, hipStream_t s) {
+                          const float *phi, const float *x, const float *gy, const float *xmax, const float *gmax,
+                          float *S, int accumulate, hipStream_t s) {
     if (P <= 0) return SN_OK;
+    (void)N;
     FilterArgs a = make_args(m, t);
     a.dsrc = reinterpret_cast<const float *>(pgeo);
     a.dstride = 4;
@@ -619,13 +600,14 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const in
     a.gy = gy;
     a.phi_in = phi;
     a.S = S;
-    a.rowmax = rowmax;
+    a.xmax = xmax;
+    a.gmax = gmax;
     a.accumulate = accumulate;
     ProfScope ps(K_FILTER_BWD, s);
     switch (m.n_features) {
-        case 32: return launch_bwd<32>(a, N, rowmax, s);
-        case 64: return launch_bwd<64>(a, N, rowmax, s);
-        case 128: return launch_bwd<128>(a, N, rowmax, s);
+        case 32: return launch_bwd<32>(a, s);
+        case 64: return launch_bwd<64>(a, s);
+        case 128: return launch_bwd<128>(a, s);
         default: return SN_ERR_INVALID;
     }
 }

@@ -60,6 +60,7 @@ struct MlpArgs {
     float *mid;                 // OUT: o is stored here
     float *out;                 // X: x;  OUT: h (+=);  READOUT: g_h;  BWD_OUT: g_y;  BWD_X: g_h (+=)
     float *eps;                 // READOUT: per-atom energy
+    float *rmax;                // X: max_f |x|;  BWD_OUT: max_f |g_y| (per atom; optional)
 };
 
 // Weights of A fragment idx of a layer ([m][t][l]): value j = weight(row
@@ -172,6 +173,18 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
     }
 
     if (MODE == MLP_X || MODE == MLP_BWD_X) {
+        if (MODE == MLP_X && a.rmax) {   // the per-atom row maximum of x, for the filter backward's scales
+#pragma unroll
+            for (int n = 0; n < kNT; ++n) {
+                float mx = 0.0f;
+#pragma unroll
+                for (int m = 0; m < M1; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(r1[n][m][r]));
+                mx = atom_max(mx);
+                if (live[n] && slot == 0) a.rmax[atom[n]] = mx;
+            }
+        }
 #pragma unroll
         for (int n = 0; n < kNT; ++n) {
             if (!live[n]) continue;
@@ -244,6 +257,9 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
             split8(v, bh[t][n], bl[t][n]);
         }
     }
+    float omax[kNT];
+#pragma unroll
+    for (int n = 0; n < kNT; ++n) omax[n] = 0.0f;
 #pragma unroll
     for (int m0 = 0; m0 < M2; m0 += MG2) {
         floatx4 acc[MG2][kNT];
@@ -272,7 +288,16 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
                 } else {
                     *dst = make_float4(v[0], v[1], v[2], v[3]);
                 }
+                if (MODE == MLP_BWD_OUT)
+                    omax[n] = fmaxf(omax[n], fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
             }
+        }
+    }
+    if (MODE == MLP_BWD_OUT && a.rmax) {   // the per-atom row maximum of g_y
+#pragma unroll
+        for (int n = 0; n < kNT; ++n) {
+            const float mx = atom_max(omax[n]);
+            if (live[n] && slot == 0) a.rmax[atom[n]] = mx;
         }
     }
 }
@@ -294,9 +319,9 @@ sn_status launch_mlp(int F, const MlpArgs &a, hipStream_t s) {
 
 }  // namespace
 
-sn_status mlp_x(int N, int F, const float *h, const float *W_in, float *x, hipStream_t s) {
+sn_status mlp_x(int N, int F, const float *h, const float *W_in, float *x, float *xmax, hipStream_t s) {
     MlpArgs a = {};
-    a.N = N; a.in = h; a.W1 = W_in; a.out = x;
+    a.N = N; a.in = h; a.W1 = W_in; a.out = x; a.rmax = xmax;
     return launch_mlp<MLP_X>(F, a, s);
 }
 
@@ -315,9 +340,9 @@ sn_status mlp_readout(int N, int F, const float *h, const float *R1, const float
 }
 
 sn_status mlp_bwd_out(int N, int F, const float *gh, const float *Wo2, const float *o, const float *Wo1, float *gy,
-                      hipStream_t s) {
+                      float *gymax, hipStream_t s) {
     MlpArgs a = {};
-    a.N = N; a.in = gh; a.W1 = Wo2; a.aux = o; a.W2 = Wo1; a.out = gy;
+    a.N = N; a.in = gh; a.W1 = Wo2; a.aux = o; a.W2 = Wo1; a.out = gy; a.rmax = gymax;
     return launch_mlp<MLP_BWD_OUT>(F, a, s);
 }
 

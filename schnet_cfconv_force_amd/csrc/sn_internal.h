@@ -99,7 +99,7 @@ struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
 };
 
 struct EfLayout {            // energy/force scratch (offsets from ws base)
-    size_t up_first, up_ptr, edge_pair, pair_ij, pgeo, pfc, phi, x, o, gy, h, y, gh, eps, S, rowmax, total;
+    size_t up_first, up_ptr, edge_pair, pair_ij, pgeo, pfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, total;
 };
 
 NbLayout nb_layout(const sn_system &sys, size_t base);
@@ -126,9 +126,10 @@ sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_
 // filter.hip
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, hipStream_t s);
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
+// xmax / gmax: per-atom max_f |x[i][f]| and max_f |g_y[i][f]| of interaction t
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const int2 *pair_ij, int64_t P, int N,
-                          const float *phi, const float *x, const float *gy, float2 *rowmax, float *S,
-                          int accumulate, hipStream_t s);
+                          const float *phi, const float *x, const float *gy, const float *xmax, const float *gmax,
+                          float *S, int accumulate, hipStream_t s);
 
 // graph.hip
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
@@ -145,13 +146,15 @@ sn_status embed(int N, int F, int T, const int32_t *types, const float *emb, flo
 sn_status replica_sum(int B, const int32_t *replica_ptr, const float *eps, float *energy, hipStream_t s);
 
 // mlp.hip (fused atom-wise layers; see the kernel comments there)
-sn_status mlp_x(int N, int F, const float *h, const float *W_in, float *x, hipStream_t s);
+// xmax (optional): per-atom max_f |x|
+sn_status mlp_x(int N, int F, const float *h, const float *W_in, float *x, float *xmax, hipStream_t s);
 sn_status mlp_out(int N, int F, const float *y, const float *Wo1, const float *bo1, const float *Wo2,
                   const float *bo2, float *o, float *h, hipStream_t s);
 sn_status mlp_readout(int N, int F, const float *h, const float *R1, const float *c1, const float *R2,
                       const float *c2, float *eps, float *gh, hipStream_t s);
+// gymax (optional): per-atom max_f |g_y|
 sn_status mlp_bwd_out(int N, int F, const float *gh, const float *Wo2, const float *o, const float *Wo1, float *gy,
-                      hipStream_t s);
+                      float *gymax, hipStream_t s);
 sn_status mlp_bwd_x(int N, int F, const float *gx, const float *W_in, float *gh, hipStream_t s);
 
 // verlet (api.hip)
