@@ -42,6 +42,7 @@ namespace {
 constexpr int kFwdThreads = 1024;   // 4 wavefronts per SIMD
 constexpr int kFwdNT = 1;           // 16-pair tiles per forward wavefront (2 measured slower)
 constexpr int kBwdThreads = 512;    // 2 wavefronts per SIMD
+constexpr int kBwdMG = 4;           // backward output tiles per group           // backward output tiles per group
 constexpr float kPi = 3.14159265358979323846f;
 constexpr float kLoScale = 2048.0f;        // 2^11
 constexpr float kLoUnscale = 1.0f / 2048.0f;
@@ -156,14 +157,34 @@ __device__ inline void mma3_tiles_nt(const half8 *whi, const half8 *wlo, int str
         for (int n = 0; n < NT; ++n) corr[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[m], bh[n], corr[m][n], 0, 0, 0);
 }
 
+// Two B operands sharing their A fragments: (main0, corr0) += A B0 and
+// (main1, corr1) += A B1 in split form -- one pair of fragment reads for six
+// matrix instructions.
+template <int MT>
+__device__ inline void mma3_tiles2(const half8 *whi, const half8 *wlo, int stride, const half8 &bh0,
+                                   const half8 &bl0, floatx4 *main0, floatx4 *corr0, const half8 &bh1,
+                                   const half8 &bl1, floatx4 *main1, floatx4 *corr1) {
+    half8 lo[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const half8 hi = whi[m * stride];
+        main0[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bh0, main0[m], 0, 0, 0);
+        corr0[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bl0, corr0[m], 0, 0, 0);
+        main1[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bh1, main1[m], 0, 0, 0);
+        corr1[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bl1, corr1[m], 0, 0, 0);
+        lo[m] = wlo[m * stride];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        corr0[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[m], bh0, corr0[m], 0, 0, 0);
+        corr1[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[m], bh1, corr1[m], 0, 0, 0);
+    }
+}
+
 // k index of value j of the B operand of a chained 32-wide step t (two
 // accumulator tiles 2t and 2t+1), for the lane in k-slot s
 __device__ inline int chain_k(int t, int s, int j) { return 32 * t + 16 * (j >> 2) + 4 * s + (j & 3); }
 
-// k index (into the radial basis) of row r of g_rbf tile kt for k-slot s:
-// chosen so that each lane's rows are the basis functions it generated for
-// the B operand of the first GEMM (k = 32 ks + 8 s + j).
-__device__ inline int rbf_row_k(int kt, int s, int r) { return 32 * (kt >> 1) + 8 * s + 4 * (kt & 1) + r; }
 
 // Tiles of 16 pairs handled by this wavefront.  The grid is a multiple of
 // the XCD count; the blocks of one XCD share one contiguous range of tiles
@@ -314,21 +335,15 @@ template <int F>
 __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;
-    __shared__ half8 s_a1h[MT * 2 * 64], s_a1l[MT * 2 * 64];
+    constexpr int MG = MT < kBwdMG ? MT : kBwdMG;
+    __shared__ half8 s_a1h[MT * 2 * 64], s_a1l[MT * 2 * 64];      // [m][ks][l] as in the forward pass
     __shared__ half8 s_a2bh[MT * T2 * 64], s_a2bl[MT * T2 * 64];  // [m][t][l]: A2[16 m + l%16][32 t + 8(l/16) + j]
-    __shared__ half8 s_a1bh[4 * T2 * 64], s_a1bl[4 * T2 * 64];    // [kt][t][l]: A1[rbf_row_k(kt, (l%16)/4, l%4)][chain_k(t, l/16, j)]
     __shared__ float s_b1[F];
     const int KS = (a.K + 31) / 32;
-    const int KT = 2 * KS;
     stage_a1<F, kBwdThreads>(a, s_a1h, s_a1l, KS);
     stage_frags<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, MT * T2 * 64, [&](int idx, int j) {
         const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
         return w2<F>(a, 16 * m + l % 16, 32 * t + 8 * (l / 16) + j);
-    });
-    stage_frags<4 * T2 * 64, kBwdThreads>(s_a1bh, s_a1bl, KT * T2 * 64, [&](int idx, int j) {
-        const int kt = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
-        const int row = l % 16;
-        return w1<F>(a, rbf_row_k(kt, row / 4, row % 4), chain_k(t, l / 16, j));
     });
     for (int f = threadIdx.x; f < F; f += blockDim.x) s_b1[f] = a.b1[f];
     __syncthreads();
@@ -392,35 +407,44 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
                 asm volatile("" : "+v"(gh[t]), "+v"(gl[t]), "+v"(gfc));
             }
         }
-        // the lane's basis functions rbf_k(d), k = 32 ks + 8 slot + j, split
-        // into B operands; rbd keeps (d - mu_k) rbf_k for S_p
-        float rbd[2][8];
-        half8 rh[2], rl[2];
+        // the lane's basis values rbf_k(d) and derivatives rbf_k'(d) =
+        // -2 gamma (d - mu_k) rbf_k, k = 32 ks + 8 slot + j, split into the B
+        // operands of the recomputed first layer and of its distance tangent
+        // (the derivatives scaled by 2^-ep, ep from the pair's largest |rbf'|)
+        half8 rh[2], rl[2], qh[2], ql[2];
+        int ep;
         {
             // d goes through an opaque copy so that this is not hoisted into
             // the gather phase (register pressure)
             float dr = d;
             asm volatile("" : "+v"(dr)::"memory");
+            float rb[2][8], rd[2][8];
+            float dmax = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                float rb[8];
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int k = 32 * ks + 8 * slot + j;
                     const float tt = dr - (a.lo + (float)k * a.dmu);
-                    const float e = fast_exp(-a.gamma * tt * tt);
-                    rb[j] = k < a.K ? e : 0.0f;
-                    rbd[ks][j] = tt * rb[j];
+                    const float e = k < a.K ? fast_exp(-a.gamma * tt * tt) : 0.0f;
+                    rb[ks][j] = e;
+                    rd[ks][j] = -2.0f * a.gamma * tt * e;
+                    dmax = fmaxf(dmax, fabsf(rd[ks][j]));
                 }
-                split8(rb, rh[ks], rl[ks]);
+            ep = pair_exponent(dmax);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) rd[ks][j] = ldexpf(rd[ks][j], -ep);
+                split8(rb[ks], rh[ks], rl[ks]);
+                split8(rd[ks], qh[ks], ql[ks]);
             }
         }
-        // per group of MG output tiles (features 16 m ..): g_z^T = A2 g_phi^T,
-        // a = rbf A1 + b1 (recomputed; b1 seeds the accumulator), and
-        // g_a 2^-e1 = (g_z 2^-e1) (.) sigmoid(a); the 2^e1 is folded into e2
-        constexpr int MG = MT < 4 ? MT : 4;
-        float ga[MT][4];
-        float amax = 0.0f;
+        // per group of MG output tiles (features 16 m ..): g_z = A2 g_phi
+        // (2^-e1), the recomputed a = rbf A1 + b1 and its tangent
+        // a' = rbf' A1 (2^-ep), then sum_g g_z sigmoid(a) a' -- which is
+        // sum_k g_rbf_k rbf_k', the RBF part of dE/dd, without forming g_rbf
+        float sk = 0.0f;
 #pragma unroll
         for (int m0 = 0; m0 < MT; m0 += MG) {
             floatx4 zm[MG], zc[MG];
@@ -438,58 +462,27 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
                 // g_z is complete before the recompute's operands are read
                 asm volatile("" : "+v"(gz[m])::"memory");
             }
-            floatx4 am[MG], ac[MG];
+            floatx4 am[MG], ac[MG], tm[MG], tc[MG];
 #pragma unroll
             for (int m = 0; m < MG; ++m) {
                 am[m] = *reinterpret_cast<const floatx4 *>(s_b1 + 16 * (m0 + m) + 4 * slot);
-                ac[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+                ac[m] = tm[m] = tc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 if (ks < KS)
-                    mma3_tiles<MG>(s_a1h + (m0 * KS + ks) * 64 + lane, s_a1l + (m0 * KS + ks) * 64 + lane, KS * 64,
-                                   rh[ks], rl[ks], am, ac);
+                    mma3_tiles2<MG>(s_a1h + (m0 * KS + ks) * 64 + lane, s_a1l + (m0 * KS + ks) * 64 + lane, KS * 64,
+                                    rh[ks], rl[ks], am, ac, qh[ks], ql[ks], tm, tc);
 #pragma unroll
             for (int m = 0; m < MG; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float sg = sigm(fmaf(ac[m][r], kLoUnscale, am[m][r]));
-                    ga[m0 + m][r] = gz[m][r] * sg;
-                    amax = fmaxf(amax, fabsf(ga[m0 + m][r]));
+                    sk = fmaf(gz[m][r] * sg, fmaf(tc[m][r], kLoUnscale, tm[m][r]), sk);
                 }
         }
-        // g_rbf^T = A1 g_a^T (rows permuted to the lane's own basis functions)
-        const int e2 = pair_exponent(amax);
-        const float down2 = ldexpf(1.0f, -e2);
-        floatx4 em[4], ec[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) em[kt] = ec[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < T2; ++t) {
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = ga[2 * t + (j >> 2)][j & 3] * down2;
-            half8 bh, bl;
-            split8(v, bh, bl);
-            if (KT == 4) {
-                mma3_tiles<4>(s_a1bh + t * 64 + lane, s_a1bl + t * 64 + lane, T2 * 64, bh, bl, em, ec);
-            } else {
-                mma3_tiles<2>(s_a1bh + t * 64 + lane, s_a1bl + t * 64 + lane, T2 * 64, bh, bl, em, ec);
-            }
-        }
-        // S_p = sum_k g_rbf_k rbf_k'(d) + g_fc fc'(d), summed over the four k-slots;
-        // rbf_k'(d) = -2 gamma (d - mu_k) rbf_k with rbf_k kept from the recompute.
-        // The accumulators hold g_rbf 2^-(e1 + e2) (g_z carried 2^-e1, g_a 2^-e2).
-        float sk = 0.0f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            if (kt < KT) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sk = fmaf(fmaf(ec[kt][r], kLoUnscale, em[kt][r]), rbd[kt >> 1][4 * (kt & 1) + r], sk);
-            }
-        }
-        float sp = fmaf(ldexpf(sk, e1 + e2), -2.0f * a.gamma, gfc * dfc);
+        // S_p = sum_k g_rbf_k rbf_k' + g_fc fc'(d), summed over the four k-slot lanes
+        float sp = fmaf(ldexpf(sk, e1 + ep), 1.0f, gfc * dfc);
         sp += __shfl_xor(sp, 16, 64);
         sp += __shfl_xor(sp, 32, 64);
         if (live && slot == 0) a.S[p] = a.accumulate ? a.S[p] + sp : sp;
