@@ -41,8 +41,8 @@ namespace {
 
 constexpr int kFwdThreads = 1024;   // 4 wavefronts per SIMD
 constexpr int kFwdNT = 1;           // 16-pair tiles per forward wavefront (2 measured slower)
-constexpr int kBwdThreads = 512;    // 2 wavefronts per SIMD
-constexpr int kBwdMG = 4;           // backward output tiles per group           // backward output tiles per group
+constexpr int kBwdThreads = 1024;   // 4 wavefronts per SIMD
+constexpr int kBwdMG = 1;           // backward output tiles per group (register budget of 4 wavefronts)
 constexpr float kPi = 3.14159265358979323846f;
 constexpr float kLoScale = 2048.0f;        // 2^11
 constexpr float kLoUnscale = 1.0f / 2048.0f;
@@ -480,6 +480,8 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
                     const float sg = sigm(fmaf(ac[m][r], kLoUnscale, am[m][r]));
                     sk = fmaf(gz[m][r] * sg, fmaf(tc[m][r], kLoUnscale, tm[m][r]), sk);
                 }
+            // the group is finished before the next group's fragments are read
+            asm volatile("" : "+v"(sk)::"memory");
         }
         // S_p = sum_k g_rbf_k rbf_k' + g_fc fc'(d), summed over the four k-slot lanes
         float sp = fmaf(ldexpf(sk, e1 + ep), 1.0f, gfc * dfc);
