@@ -41,6 +41,7 @@ namespace {
 
 constexpr int kFwdThreads = 1024;   // 4 wavefronts per SIMD
 constexpr int kFwdNT = 1;           // 16-pair tiles per forward wavefront (2 measured slower)
+constexpr int kFwdMG = 4;           // forward output tiles per product group
 constexpr int kBwdThreads = 1024;   // 4 wavefronts per SIMD
 constexpr int kBwdMG = 1;           // backward output tiles per group (register budget of 4 wavefronts)
 constexpr float kPi = 3.14159265358979323846f;
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;                 // 32-wide k steps of the F x F GEMM
     constexpr int NT = kFwdNT;                 // 16-pair tiles per wavefront
-    constexpr int MG = MT < 4 ? MT : 4;        // output tiles per group
+    constexpr int MG = MT < kFwdMG ? MT : kFwdMG;   // output tiles per group
     __shared__ half8 s_a1h[MT * 2 * 64], s_a1l[MT * 2 * 64];
     __shared__ half8 s_a2h[MT * T2 * 64], s_a2l[MT * T2 * 64];   // [m][t][l]: A2[chain_k(t, l/16, j)][16 m + l%16]
     __shared__ float s_b1[F], s_b2[F];
