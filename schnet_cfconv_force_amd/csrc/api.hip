@@ -77,6 +77,7 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     L.pair_ij = take(8 * P);
     L.pgeo = take(16 * P);
     L.pfc = take(4 * P);
+    L.pdfc = take(4 * P);
     L.phi = take(4 * I * P * F);
     L.x = take(4 * I * N * F);
     L.o = take(4 * I * N * F);
@@ -235,6 +236,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     const int2 *pair_ij = reinterpret_cast<const int2 *>(ws + L.pair_ij);
     const float4 *pgeo = reinterpret_cast<const float4 *>(ws + L.pgeo);
     const float *pfc = F32(L.pfc);
+    const float *pdfc = F32(L.pdfc);
     float *h = F32(L.h), *y = F32(L.y), *gh = F32(L.gh);
     float *S = F32(L.S);
     const int64_t NF = (int64_t)N * F, PF = P * F;
@@ -275,7 +277,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
         for (int t = I - 1; t >= 0; --t) {
             SN_TRY(mlp_bwd_out(N, F, gh, blk(t, WO2), o_t(t), blk(t, WO1), gy_t(t), gmax_t(t), s));
             SN_TRY(stream_wait(ev[1 + I + t], s, s2));
-            SN_TRY(filter_backward(m, t, pgeo, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
+            SN_TRY(filter_backward(m, t, pgeo, pfc, pdfc, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
                                    t != I - 1, s2));
             if (t > 0) {   // dE/dh below the first block is not needed for forces
                 SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, s));

@@ -47,7 +47,7 @@ struct PairArgs {
     int32_t *edge_pair;
     int2 *pair_ij;
     float4 *pgeo;
-    float *pfc;
+    float *pfc, *pdfc;
     int periodic;
     float L[3], invL[3];
     float cutoff;
@@ -88,13 +88,17 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
             const float d = sqrtf(dx * dx + dy * dy + dz * dz);
             const float inv = 1.0f / d;
             a.pgeo[p] = make_float4(dx * inv, dy * inv, dz * inv, d);
-            float fc = 0.0f;
+            float fc = 0.0f, dfc = 0.0f;
             if (d < a.cutoff) {
-                // (cos(pi d/rc) + 1)/2 written as cos^2(pi d/(2 rc)): no cancellation near rc
-                float c = cosf(0.5f * kPi * d / a.cutoff);
+                // (cos(pi d/rc) + 1)/2 written as cos^2(pi d/(2 rc)): no cancellation near rc;
+                // its derivative -(pi/(2 rc)) sin(pi d/rc) = -(pi/rc) sin cos of the half angle
+                const float th = 0.5f * kPi * d / a.cutoff;
+                const float c = cosf(th);
                 fc = c * c;
+                dfc = -(kPi / a.cutoff) * sinf(th) * c;
             }
             a.pfc[p] = fc;
+            a.pdfc[p] = dfc;
         } else {
             // the reverse edge (j, i) is an upper edge of row j
             const int r = a.rev[e];
@@ -224,6 +228,7 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
     a.pair_ij = reinterpret_cast<int2 *>(ws + L.pair_ij);
     a.pgeo = reinterpret_cast<float4 *>(ws + L.pgeo);
     a.pfc = reinterpret_cast<float *>(ws + L.pfc);
+    a.pdfc = reinterpret_cast<float *>(ws + L.pdfc);
     a.periodic = sys.periodic ? 1 : 0;
     for (int c = 0; c < 3; ++c) {
         a.L[c] = sys.periodic ? sys.box[c] : 1.0f;

@@ -99,7 +99,7 @@ struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
 };
 
 struct EfLayout {            // energy/force scratch (offsets from ws base)
-    size_t up_first, up_ptr, edge_pair, pair_ij, pgeo, pfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, total;
+    size_t up_first, up_ptr, edge_pair, pair_ij, pgeo, pfc, pdfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, total;
 };
 
 NbLayout nb_layout(const sn_system &sys, size_t base);
@@ -127,9 +127,10 @@ sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, hipStream_t s);
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
 // xmax / gmax: per-atom max_f |x[i][f]| and max_f |g_y[i][f]| of interaction t
-sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const int2 *pair_ij, int64_t P, int N,
-                          const float *phi, const float *x, const float *gy, const float *xmax, const float *gmax,
-                          float *S, int accumulate, hipStream_t s);
+// pfc / pdfc: per-pair envelope fc(d) and its derivative fc'(d)
+sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
+                          const int2 *pair_ij, int64_t P, int N, const float *phi, const float *x, const float *gy,
+                          const float *xmax, const float *gmax, float *S, int accumulate, hipStream_t s);
 
 // graph.hip
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,

@@ -28,12 +28,28 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 constexpr int kSplitTop = 14;
 
 __device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
+    // The values are opaque to the compiler: otherwise it may fuse the
+    // product that made one into its conversion to hi at one use but not at
+    // another, and hi would then differ between them by a rounding.
+    float x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const _Float16 h = (_Float16)v[j];
-        hi[j] = h;
-        lo[j] = (_Float16)(v[j] - (float)h);
+        x[j] = v[j];
+        asm("" : "+v"(x[j]));
     }
+    half8 h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = (_Float16)x[j];
+    // hi is converted once (packed pairs); lo = x - hi (exact) is one
+    // mixed-precision fma per value that reads hi from its packed half, for
+    // which -1 is kept opaque too (folded, x - hi would become a conversion
+    // back to fp32 and a subtraction)
+    asm("" : "+v"(h));
+    float m1 = -1.0f;
+    asm("" : "+s"(m1));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lo[j] = (_Float16)fmaf((float)h[j], m1, x[j]);
+    hi = h;
 }
 
 // Power-of-two exponent s with amax 2^s in [2^(kSplitTop-1), 2^kSplitTop)
