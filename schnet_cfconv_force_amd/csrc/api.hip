@@ -24,7 +24,7 @@ std::vector<ProfRecord> g_prof_open;   // started, not yet stopped (stack per cl
 std::vector<ProfRecord> g_prof_done;
 const char *kClassNames[K_NUM_CLASSES] = {
     "nb_grid", "nb_bin", "nb_scan", "nb_count", "nb_fill", "nb_rev", "pairs", "embed", "mlp",
-    "filter_fwd", "cfconv", "readout", "energy", "filter_bwd", "forces", "verlet", "kinetic"};
+    "filter_fwd", "cfconv", "readout", "energy", "filter_bwd", "forces", "verlet", "kinetic", "pack"};
 }  // namespace
 
 std::vector<hipEvent_t> g_event_pool;     // reused events (creating events is slow)
@@ -89,6 +89,7 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     L.S = take(4 * P);
     L.xmax = take(4 * I * N);
     L.gmax = take(4 * I * N);
+    L.pack = take(pack_bytes((int)I));
     L.total = o;
     return L;
 }
@@ -178,7 +179,7 @@ size_t bytes_needed(const sn_model *m, const sn_system *s, int64_t E) {
 struct Aux {
     std::mutex mu;
     hipStream_t s = nullptr;
-    hipEvent_t ev[2 * 16 + 3] = {};
+    hipEvent_t ev[2 * 16 + 4] = {};
     bool tried = false, ok = false;
 };
 
@@ -253,35 +254,45 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     // kernel runs on the caller's stream, so that its timing events or a
     // kernel trace bracket that kernel alone
     hipStream_t s2 = (ax.ok && !g_prof_on && !serial_requested()) ? ax.s : s;
-    hipEvent_t *ev = ax.ev;   // [0] fork, [1 + t] phi_t ready, [1 + I + t] g_y_t ready, [2 + 2I] join
+    // [0] pairs ready, [1 + t] phi_t ready, [1 + I + t] g_y_t ready, [2 + 2I] join, [3 + 2I] start
+    hipEvent_t *ev = ax.ev;
+    char *pack = ws + L.pack;
+    auto pk = [&](int t, int kind) { return pack_ref(pack, I, pack_slot(t, kind)); };
+    auto pr = [&](int k) { return pack_ref(pack, I, pack_readout_slot(I, k)); };
 
     auto run = [&]() -> sn_status {
+        // the weight pack: the filter's part on the auxiliary stream (after
+        // the caller's earlier work), beside the atom-wise part and the pair
+        // setup on the caller's stream
+        SN_TRY(stream_wait(ev[3 + 2 * I], s, s2));
+        SN_TRY(filter_pack(m, pack, s2));
+        SN_TRY(mlp_pack(m, pack, s));
         SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, E, m.cutoff, ws, L, status, s));
         SN_TRY(stream_wait(ev[0], s, s2));
         for (int t = 0; t < I; ++t) {
-            SN_TRY(filter_forward(m, t, pgeo, P, phi_t(t), s2));
+            SN_TRY(filter_forward(m, t, pgeo, P, phi_t(t), pack, s2));
             if (s2 != s && hipEventRecord(ev[1 + t], s2) != hipSuccess) return SN_ERR_HIP;
         }
         SN_TRY(embed(N, F, m.n_types, sys.types, prm + off[0], h, status, s));
-        SN_TRY(mlp_x(N, F, h, blk(0, W_IN), x_t(0), xmax_t(0), s));
+        SN_TRY(mlp_x(N, F, h, pk(0, PK_XW), x_t(0), xmax_t(0), s));
         for (int t = 0; t < I; ++t) {
             if (s2 != s && hipStreamWaitEvent(s, ev[1 + t], 0) != hipSuccess) return SN_ERR_HIP;
             SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, s));
-            SN_TRY(mlp_out(N, F, y, blk(t, WO1), blk(t, BO1), blk(t, WO2), blk(t, BO2), o_t(t), h, s));
-            if (t + 1 < I) SN_TRY(mlp_x(N, F, h, blk(t + 1, W_IN), x_t(t + 1), xmax_t(t + 1), s));
+            SN_TRY(mlp_out(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), o_t(t), h, s));
+            if (t + 1 < I) SN_TRY(mlp_x(N, F, h, pk(t + 1, PK_XW), x_t(t + 1), xmax_t(t + 1), s));
         }
-        SN_TRY(mlp_readout(N, F, h, R1, c1, R2, c2, eps, gh, s));
+        SN_TRY(mlp_readout(N, F, h, pr(0), c1, pr(1), R2, c2, eps, gh, s));
         SN_TRY(replica_sum(B, sys.replica_ptr, eps, energy, s));
         // backward through the interactions in reverse; the filter backward of
         // interaction t runs beside the CFConv and layers that lead to t - 1
         for (int t = I - 1; t >= 0; --t) {
-            SN_TRY(mlp_bwd_out(N, F, gh, blk(t, WO2), o_t(t), blk(t, WO1), gy_t(t), gmax_t(t), s));
+            SN_TRY(mlp_bwd_out(N, F, gh, pk(t, PK_BOW1), o_t(t), pk(t, PK_BOW2), gy_t(t), gmax_t(t), s));
             SN_TRY(stream_wait(ev[1 + I + t], s, s2));
             SN_TRY(filter_backward(m, t, pgeo, pfc, pdfc, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
-                                   t != I - 1, s2));
+                                   t != I - 1, pack, s2));
             if (t > 0) {   // dE/dh below the first block is not needed for forces
                 SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, s));
-                SN_TRY(mlp_bwd_x(N, F, y, blk(t, W_IN), gh, s));
+                SN_TRY(mlp_bwd_x(N, F, y, pk(t, PK_BXW), gh, s));
             }
         }
         return SN_OK;

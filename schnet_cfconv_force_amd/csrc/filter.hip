@@ -70,6 +70,10 @@ struct FilterArgs {
     float *S;                    // [P]
     const float *xmax, *gmax;    // [N]: max_f |x_i[f]|, max_f |g_y_i[f]|
     int accumulate;
+    // weight pack (or null): the first layer, the pass's second layer, and
+    // their scales (first layer: {sa1, sz}; second layer: {sa2, -})
+    const half8 *pa1h, *pa1l, *pa2h, *pa2l;
+    const int *psc1, *psc2;
 };
 
 template <int F>
@@ -159,6 +163,35 @@ __device__ inline int stage_a1(const FilterArgs &a, half8 *s_hi, half8 *s_lo, in
     });
 }
 
+// The largest |a_f| bound over the features, into *s_max (0 on entry; read
+// after a barrier): |a_f| <= sum_k |A1[k][f]| + |b1[f]| since 0 <= rbf <= 1.
+// z = ssp(a) / ln 2 then satisfies |z| <= bound log2(e) + 1.
+template <int F>
+__device__ inline void first_layer_bound(const FilterArgs &a, unsigned *s_max) {
+    for (int f = threadIdx.x; f < F; f += blockDim.x) {
+        float s = fabsf(a.b1[f]);
+        for (int k = 0; k < a.K; ++k) s += fabsf(w1<F>(a, k, f));
+        atomicMax(s_max, __float_as_uint(s));
+    }
+}
+// Second-layer fragments ([m][t][l]).  Forward: value j = ln 2 A2[chain_k(t,
+// l/16, j)][16 m + l%16] (the activation is computed in base 2 and the layer
+// absorbs the ln 2).  Backward: A2[16 m + l%16][32 t + 8(l/16) + j].
+template <int F>
+__device__ inline void a2_fwd_frag(const FilterArgs &a, int idx, float (&v)[8]) {
+    constexpr int T2 = F / 32;
+    const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = kLn2 * w2<F>(a, chain_k(t, l / 16, j), 16 * m + l % 16);
+}
+template <int F>
+__device__ inline void a2_bwd_frag(const FilterArgs &a, int idx, float (&v)[8]) {
+    constexpr int T2 = F / 32;
+    const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = w2<F>(a, 16 * m + l % 16, 32 * t + 8 * (l / 16) + j);
+}
+
 // acc0 += A B0 and acc1 += A B1 in split form for MG weight tiles: one pair
 // of fragment reads per tile for six matrix instructions; dependent
 // instructions on one accumulator are 2 MG apart.
@@ -198,24 +231,22 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     __shared__ float s_b1[F], s_b2[F];
     __shared__ unsigned s_max[3];
     const int KS = (a.K + 31) / 32;
-    if (threadIdx.x < 3) s_max[threadIdx.x] = 0u;
-    __syncthreads();
-    // |a_f| <= sum_k |A1[k][f]| + |b1[f]| since 0 <= rbf <= 1
-    for (int f = threadIdx.x; f < F; f += blockDim.x) {
-        float s = fabsf(a.b1[f]);
-        for (int k = 0; k < a.K; ++k) s += fabsf(w1<F>(a, k, f));
-        atomicMax(&s_max[2], __float_as_uint(s));
+    int sa1, sa2, sz;
+    if (a.pa1h) {
+        copy_frags<MT * 2 * 64, kFwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * KS * 64);
+        copy_frags<MT * T2 * 64, kFwdThreads>(s_a2h, s_a2l, a.pa2h, a.pa2l, MT * T2 * 64);
+        sa1 = a.psc1[0];
+        sz = a.psc1[1];
+        sa2 = a.psc2[0];
+    } else {
+        if (threadIdx.x < 3) s_max[threadIdx.x] = 0u;
+        __syncthreads();
+        first_layer_bound<F>(a, &s_max[2]);
+        sa1 = stage_a1<F, kFwdThreads>(a, s_a1h, s_a1l, KS, &s_max[0]);
+        sa2 = stage_split<MT * T2 * 64, kFwdThreads>(s_a2h, s_a2l, MT * T2 * 64, &s_max[1],
+                                                     [&](int idx, float (&v)[8]) { a2_fwd_frag<F>(a, idx, v); });
+        sz = split_scale(__uint_as_float(s_max[2]) * kLog2e + 1.0f);
     }
-    const int sa1 = stage_a1<F, kFwdThreads>(a, s_a1h, s_a1l, KS, &s_max[0]);
-    // the second layer absorbs the ln 2 of the activation (computed in base 2)
-    const int sa2 = stage_split<MT * T2 * 64, kFwdThreads>(s_a2h, s_a2l, MT * T2 * 64, &s_max[1],
-                                                           [&](int idx, float (&v)[8]) {
-        const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = kLn2 * w2<F>(a, chain_k(t, l / 16, j), 16 * m + l % 16);
-    });
-    // z = ssp(a) / ln 2 satisfies |z| <= |a| log2(e) + 1; it is held as z 2^sz
-    const int sz = split_scale(__uint_as_float(s_max[2]) * kLog2e + 1.0f);
     for (int f = threadIdx.x; f < F; f += blockDim.x) {
         s_b1[f] = ldexpf(a.b1[f], sa1);
         s_b2[f] = ldexpf(a.b2[f], sz + sa2);
@@ -319,15 +350,19 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     __shared__ float s_b1[F];
     __shared__ unsigned s_max[2];
     const int KS = (a.K + 31) / 32;
-    if (threadIdx.x < 2) s_max[threadIdx.x] = 0u;
-    __syncthreads();
-    const int sa1 = stage_a1<F, kBwdThreads>(a, s_a1h, s_a1l, KS, &s_max[0]);
-    const int sa2 = stage_split<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, MT * T2 * 64, &s_max[1],
-                                                           [&](int idx, float (&v)[8]) {
-        const int m = idx / (T2 * 64), t = (idx / 64) % T2, l = idx % 64;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = w2<F>(a, 16 * m + l % 16, 32 * t + 8 * (l / 16) + j);
-    });
+    int sa1, sa2;
+    if (a.pa1h) {
+        copy_frags<MT * 2 * 64, kBwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * KS * 64);
+        copy_frags<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, a.pa2h, a.pa2l, MT * T2 * 64);
+        sa1 = a.psc1[0];
+        sa2 = a.psc2[0];
+    } else {
+        if (threadIdx.x < 2) s_max[threadIdx.x] = 0u;
+        __syncthreads();
+        sa1 = stage_a1<F, kBwdThreads>(a, s_a1h, s_a1l, KS, &s_max[0]);
+        sa2 = stage_split<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, MT * T2 * 64, &s_max[1],
+                                                     [&](int idx, float (&v)[8]) { a2_bwd_frag<F>(a, idx, v); });
+    }
     for (int f = threadIdx.x; f < F; f += blockDim.x) s_b1[f] = ldexpf(a.b1[f], sa1);
     __syncthreads();
     const Basis bs = make_basis(a);
@@ -454,6 +489,58 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
 }
 
 
+// The filter's slots of the weight pack: one block per (interaction,
+// matrix), each staging one matrix exactly as the kernels above would, but
+// into the pack.
+struct FilterWeights {
+    const float *A1, *A2, *b1;
+    const int16_t *qA1, *qA2;
+    const float *sA1, *sA2;
+};
+struct FilterPackArgs {
+    FilterWeights w[16];
+    char *pack;
+    int I, K;
+};
+
+template <int F>
+__global__ __launch_bounds__(kFwdThreads) void filter_pack_kernel(FilterPackArgs pa) {
+    constexpr int MT = F / 16, T2 = MT / 2;
+    __shared__ unsigned s_max[2];
+    if (threadIdx.x < 2) s_max[threadIdx.x] = 0u;
+    __syncthreads();
+    const int t = blockIdx.x / 3, kind = blockIdx.x % 3;
+    FilterArgs a = {};
+    a.K = pa.K;
+    a.A1 = pa.w[t].A1;
+    a.A2 = pa.w[t].A2;
+    a.b1 = pa.w[t].b1;
+    a.qA1 = pa.w[t].qA1;
+    a.qA2 = pa.w[t].qA2;
+    a.sA1 = pa.w[t].sA1;
+    a.sA2 = pa.w[t].sA2;
+    const PackRef r = pack_ref(pa.pack, pa.I, pack_slot(t, kind));
+    half8 *hi = const_cast<half8 *>(static_cast<const half8 *>(r.hi));
+    half8 *lo = const_cast<half8 *>(static_cast<const half8 *>(r.lo));
+    int sc0 = 0, sc1 = 0;
+    if (kind == PK_FA1) {
+        first_layer_bound<F>(a, &s_max[1]);
+        sc0 = stage_a1<F, kFwdThreads>(a, hi, lo, (a.K + 31) / 32, &s_max[0]);   // its barrier completes s_max[1]
+        sc1 = split_scale(__uint_as_float(s_max[1]) * kLog2e + 1.0f);
+    } else if (kind == PK_FA2) {
+        sc0 = stage_split<MT * T2 * 64, kFwdThreads>(hi, lo, MT * T2 * 64, &s_max[0],
+                                                     [&](int idx, float (&v)[8]) { a2_fwd_frag<F>(a, idx, v); });
+    } else {
+        sc0 = stage_split<MT * T2 * 64, kFwdThreads>(hi, lo, MT * T2 * 64, &s_max[0],
+                                                     [&](int idx, float (&v)[8]) { a2_bwd_frag<F>(a, idx, v); });
+    }
+    if (threadIdx.x == 0) {
+        int *sc = const_cast<int *>(r.sc);
+        sc[0] = sc0;
+        sc[1] = sc1;
+    }
+}
+
 int num_cus() {
     static int n = 0;
     if (n == 0) {
@@ -521,10 +608,45 @@ sn_status fwd_dispatch(const FilterArgs &a, int F, hipStream_t s) {
     }
 }
 
+void attach_pack(FilterArgs &a, const sn_model &m, int t, const char *pack, int second) {
+    if (!pack) return;
+    const PackRef r1 = pack_ref(pack, m.n_interactions, pack_slot(t, PK_FA1));
+    const PackRef r2 = pack_ref(pack, m.n_interactions, pack_slot(t, second));
+    a.pa1h = static_cast<const half8 *>(r1.hi);
+    a.pa1l = static_cast<const half8 *>(r1.lo);
+    a.psc1 = r1.sc;
+    a.pa2h = static_cast<const half8 *>(r2.hi);
+    a.pa2l = static_cast<const half8 *>(r2.lo);
+    a.psc2 = r2.sc;
+}
+
 }  // namespace
 
-sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, hipStream_t s) {
+sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s) {
+    const int I = m.n_interactions;
+    if (I < 1 || I > 16) return SN_ERR_INVALID;
+    FilterPackArgs pa = {};
+    pa.pack = pack;
+    pa.I = I;
+    pa.K = m.n_rbf;
+    for (int t = 0; t < I; ++t) {
+        const FilterArgs a = make_args(m, t);
+        pa.w[t] = FilterWeights{a.A1, a.A2, a.b1, a.qA1, a.qA2, a.sA1, a.sA2};
+    }
+    ProfScope ps(K_PACK, s);
+    switch (m.n_features) {
+        case 32: filter_pack_kernel<32><<<3 * I, kFwdThreads, 0, s>>>(pa); break;
+        case 64: filter_pack_kernel<64><<<3 * I, kFwdThreads, 0, s>>>(pa); break;
+        case 128: filter_pack_kernel<128><<<3 * I, kFwdThreads, 0, s>>>(pa); break;
+        default: return SN_ERR_INVALID;
+    }
+    return launch_status();
+}
+
+sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, const char *pack,
+                         hipStream_t s) {
     FilterArgs a = make_args(m, t);
+    attach_pack(a, m, t, pack, PK_FA2);
     a.dsrc = reinterpret_cast<const float *>(pgeo);
     a.dstride = 4;
     a.doff = 3;
@@ -545,10 +667,12 @@ sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t
 
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
                           const int2 *pair_ij, int64_t P, int N, const float *phi, const float *x, const float *gy,
-                          const float *xmax, const float *gmax, float *S, int accumulate, hipStream_t s) {
+                          const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
+                          hipStream_t s) {
     if (P <= 0) return SN_OK;
     (void)N;
     FilterArgs a = make_args(m, t);
+    attach_pack(a, m, t, pack, PK_FA2B);
     a.dsrc = reinterpret_cast<const float *>(pgeo);
     a.dstride = 4;
     a.doff = 3;

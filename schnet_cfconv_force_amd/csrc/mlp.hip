@@ -48,13 +48,18 @@ struct Shape {
     static constexpr int FO2 = F;
     static constexpr int M1 = FO1 / 16, T1 = (FI1 + 31) / 32;
     static constexpr int M2 = FO2 / 16, T2 = (FI2 + 31) / 32;
+    // weights stored [out][in] (read transposed)
+    static constexpr int TR1 = (MODE == MLP_BWD_OUT || MODE == MLP_BWD_X) ? 1 : 0;
+    static constexpr int TR2 = (MODE == MLP_READOUT || MODE == MLP_BWD_OUT) ? 1 : 0;
 };
 
 struct MlpArgs {
     int N;
     const float *in;            // [N][F] input of the first layer
-    const float *W1, *b1;       // first layer weights (layout depends on the mode) and bias
-    const float *W2, *b2;       // second layer
+    const half8 *w1h, *w1l;     // first layer, pre-split (weight-pack slot)
+    const half8 *w2h, *w2l;     // second layer
+    const int *sc1, *sc2;       // their split scales
+    const float *b1, *b2;       // biases
     const float *aux;           // BWD_OUT: the stored pre-activation o
     const float *R2, *c2;       // READOUT
     float *mid;                 // OUT: o is stored here
@@ -94,12 +99,8 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
     using S = Shape<F, MODE>;
     constexpr int M1 = S::M1, T1 = S::T1, M2 = S::M2, T2 = S::T2;
     constexpr int MG1 = M1 < 4 ? M1 : 4, MG2 = M2 < 4 ? M2 : 4;
-    constexpr int TRANS1 = (MODE == MLP_BWD_OUT || MODE == MLP_BWD_X) ? 1 : 0;
-    constexpr int TRANS2 = (MODE == MLP_READOUT || MODE == MLP_BWD_OUT) ? 1 : 0;
     __shared__ half8 s_w1h[M1 * T1 * 64], s_w1l[M1 * T1 * 64];
     __shared__ half8 s_w2h[S::TWO ? M2 * T2 * 64 : 1], s_w2l[S::TWO ? M2 * T2 * 64 : 1];
-    __shared__ unsigned s_max[2];
-    if (threadIdx.x < 2) s_max[threadIdx.x] = 0u;
 
     const int lane = threadIdx.x % 64, slot = lane / 16;
     const int base = (blockIdx.x * kMlpWaves + threadIdx.x / 64) * (16 * kNT);
@@ -126,13 +127,10 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
                 xmax[n] = fmaxf(xmax[n], fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
             }
     }
-    __syncthreads();   // s_max cleared
-    const int sw1 = stage_split<M1 * T1 * 64, kMlpThreads>(s_w1h, s_w1l, M1 * T1 * 64, &s_max[0],
-        [&](int idx, float (&v)[8]) { layer_frag<T1, TRANS1, 0>(a.W1, S::FI1, S::FO1, idx, v); });
-    int sw2 = 0;
-    if (S::TWO)
-        sw2 = stage_split<M2 * T2 * 64, kMlpThreads>(s_w2h, s_w2l, M2 * T2 * 64, &s_max[1],
-            [&](int idx, float (&v)[8]) { layer_frag<T2, TRANS2, 1>(a.W2, S::FI2, S::FO2, idx, v); });
+    copy_frags<M1 * T1 * 64, kMlpThreads>(s_w1h, s_w1l, a.w1h, a.w1l, M1 * T1 * 64);
+    if (S::TWO) copy_frags<M2 * T2 * 64, kMlpThreads>(s_w2h, s_w2l, a.w2h, a.w2l, M2 * T2 * 64);
+    const int sw1 = a.sc1[0];
+    const int sw2 = S::TWO ? a.sc2[0] : 0;
     __syncthreads();
     if (base >= a.N) return;
 
@@ -302,6 +300,55 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
     }
 }
 
+// Pre-split one layer of a mode into a weight-pack slot (as the kernel's
+// staging would into LDS); returns the split scale.
+template <int F, int MODE, int LAYER>
+__device__ inline int pack_layer(const float *W, half8 *hi, half8 *lo, unsigned *s_max) {
+    using S = Shape<F, MODE>;
+    if (LAYER == 1)
+        return stage_split<S::M1 * S::T1 * 64, kMlpThreads>(hi, lo, S::M1 * S::T1 * 64, s_max,
+            [&](int idx, float (&v)[8]) { layer_frag<S::T1, S::TR1, 0>(W, S::FI1, S::FO1, idx, v); });
+    return stage_split<S::M2 * S::T2 * 64, kMlpThreads>(hi, lo, S::M2 * S::T2 * 64, s_max,
+        [&](int idx, float (&v)[8]) { layer_frag<S::T2, S::TR2, 1>(W, S::FI2, S::FO2, idx, v); });
+}
+
+struct MlpPackArgs {
+    const float *W_in[16], *Wo1[16], *Wo2[16];
+    const float *R1;
+    char *pack;
+    int I;
+};
+
+// The atom-wise slots of the weight pack: one block per matrix (six per
+// interaction, then the two readout layers).
+template <int F>
+__global__ __launch_bounds__(kMlpThreads) void mlp_pack_kernel(MlpPackArgs pa) {
+    __shared__ unsigned s_max;
+    if (threadIdx.x == 0) s_max = 0u;
+    __syncthreads();
+    const int b = blockIdx.x;
+    const int t = b / 6, k = b % 6;
+    const int slot = b < 6 * pa.I ? pack_slot(t, PK_XW + k) : pack_readout_slot(pa.I, b - 6 * pa.I);
+    const PackRef r = pack_ref(pa.pack, pa.I, slot);
+    half8 *hi = const_cast<half8 *>(static_cast<const half8 *>(r.hi));
+    half8 *lo = const_cast<half8 *>(static_cast<const half8 *>(r.lo));
+    int sc = 0;
+    if (b >= 6 * pa.I) {
+        sc = b == 6 * pa.I ? pack_layer<F, MLP_READOUT, 1>(pa.R1, hi, lo, &s_max)
+                           : pack_layer<F, MLP_READOUT, 2>(pa.R1, hi, lo, &s_max);
+    } else {
+        switch (PK_XW + k) {
+            case PK_XW: sc = pack_layer<F, MLP_X, 1>(pa.W_in[t], hi, lo, &s_max); break;
+            case PK_OW1: sc = pack_layer<F, MLP_OUT, 1>(pa.Wo1[t], hi, lo, &s_max); break;
+            case PK_OW2: sc = pack_layer<F, MLP_OUT, 2>(pa.Wo2[t], hi, lo, &s_max); break;
+            case PK_BOW1: sc = pack_layer<F, MLP_BWD_OUT, 1>(pa.Wo2[t], hi, lo, &s_max); break;
+            case PK_BOW2: sc = pack_layer<F, MLP_BWD_OUT, 2>(pa.Wo1[t], hi, lo, &s_max); break;
+            default: sc = pack_layer<F, MLP_BWD_X, 1>(pa.W_in[t], hi, lo, &s_max); break;
+        }
+    }
+    if (threadIdx.x == 0) const_cast<int *>(r.sc)[0] = sc;
+}
+
 template <int MODE>
 sn_status launch_mlp(int F, const MlpArgs &a, hipStream_t s) {
     if (a.N <= 0) return SN_OK;
@@ -317,38 +364,80 @@ sn_status launch_mlp(int F, const MlpArgs &a, hipStream_t s) {
     return launch_status();
 }
 
+void set_layers(MlpArgs &a, PackRef w1, const PackRef *w2) {
+    a.w1h = static_cast<const half8 *>(w1.hi);
+    a.w1l = static_cast<const half8 *>(w1.lo);
+    a.sc1 = w1.sc;
+    if (w2) {
+        a.w2h = static_cast<const half8 *>(w2->hi);
+        a.w2l = static_cast<const half8 *>(w2->lo);
+        a.sc2 = w2->sc;
+    }
+}
+
 }  // namespace
 
-sn_status mlp_x(int N, int F, const float *h, const float *W_in, float *x, float *xmax, hipStream_t s) {
+sn_status mlp_pack(const sn_model &m, char *pack, hipStream_t s) {
+    const int T = m.n_types, I = m.n_interactions, F = m.n_features, K = m.n_rbf;
+    if (I < 1 || I > 16) return SN_ERR_INVALID;
+    int64_t off[9 * 16 + 6];
+    sn_param_offsets(T, I, F, K, off, (int32_t)(sizeof(off) / sizeof(off[0])));
+    MlpPackArgs pa = {};
+    pa.pack = pack;
+    pa.I = I;
+    for (int t = 0; t < I; ++t) {
+        const int64_t *blk = off + 1 + 9 * t;   // W_in, A1, b1, A2, b2, Wo1, bo1, Wo2, bo2
+        pa.W_in[t] = m.params + blk[0];
+        pa.Wo1[t] = m.params + blk[5];
+        pa.Wo2[t] = m.params + blk[7];
+    }
+    pa.R1 = m.params + off[1 + 9 * I];
+    ProfScope ps(K_PACK, s);
+    const int grid = 6 * I + 2;
+    switch (F) {
+        case 32: mlp_pack_kernel<32><<<grid, kMlpThreads, 0, s>>>(pa); break;
+        case 64: mlp_pack_kernel<64><<<grid, kMlpThreads, 0, s>>>(pa); break;
+        case 128: mlp_pack_kernel<128><<<grid, kMlpThreads, 0, s>>>(pa); break;
+        default: return SN_ERR_INVALID;
+    }
+    return launch_status();
+}
+
+sn_status mlp_x(int N, int F, const float *h, PackRef W_in, float *x, float *xmax, hipStream_t s) {
     MlpArgs a = {};
-    a.N = N; a.in = h; a.W1 = W_in; a.out = x; a.rmax = xmax;
+    a.N = N; a.in = h; a.out = x; a.rmax = xmax;
+    set_layers(a, W_in, nullptr);
     return launch_mlp<MLP_X>(F, a, s);
 }
 
-sn_status mlp_out(int N, int F, const float *y, const float *Wo1, const float *bo1, const float *Wo2,
-                  const float *bo2, float *o, float *h, hipStream_t s) {
+sn_status mlp_out(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
+                  float *o, float *h, hipStream_t s) {
     MlpArgs a = {};
-    a.N = N; a.in = y; a.W1 = Wo1; a.b1 = bo1; a.W2 = Wo2; a.b2 = bo2; a.mid = o; a.out = h;
+    a.N = N; a.in = y; a.b1 = bo1; a.b2 = bo2; a.mid = o; a.out = h;
+    set_layers(a, Wo1, &Wo2);
     return launch_mlp<MLP_OUT>(F, a, s);
 }
 
-sn_status mlp_readout(int N, int F, const float *h, const float *R1, const float *c1, const float *R2,
+sn_status mlp_readout(int N, int F, const float *h, PackRef R1, const float *c1, PackRef R1t, const float *R2,
                       const float *c2, float *eps, float *gh, hipStream_t s) {
     MlpArgs a = {};
-    a.N = N; a.in = h; a.W1 = R1; a.b1 = c1; a.W2 = R1; a.R2 = R2; a.c2 = c2; a.eps = eps; a.out = gh;
+    a.N = N; a.in = h; a.b1 = c1; a.R2 = R2; a.c2 = c2; a.eps = eps; a.out = gh;
+    set_layers(a, R1, &R1t);
     return launch_mlp<MLP_READOUT>(F, a, s);
 }
 
-sn_status mlp_bwd_out(int N, int F, const float *gh, const float *Wo2, const float *o, const float *Wo1, float *gy,
+sn_status mlp_bwd_out(int N, int F, const float *gh, PackRef Wo2t, const float *o, PackRef Wo1t, float *gy,
                       float *gymax, hipStream_t s) {
     MlpArgs a = {};
-    a.N = N; a.in = gh; a.W1 = Wo2; a.aux = o; a.W2 = Wo1; a.out = gy; a.rmax = gymax;
+    a.N = N; a.in = gh; a.aux = o; a.out = gy; a.rmax = gymax;
+    set_layers(a, Wo2t, &Wo1t);
     return launch_mlp<MLP_BWD_OUT>(F, a, s);
 }
 
-sn_status mlp_bwd_x(int N, int F, const float *gx, const float *W_in, float *gh, hipStream_t s) {
+sn_status mlp_bwd_x(int N, int F, const float *gx, PackRef W_int, float *gh, hipStream_t s) {
     MlpArgs a = {};
-    a.N = N; a.in = gx; a.W1 = W_in; a.out = gh;
+    a.N = N; a.in = gx; a.out = gh;
+    set_layers(a, W_int, nullptr);
     return launch_mlp<MLP_BWD_X>(F, a, s);
 }
 

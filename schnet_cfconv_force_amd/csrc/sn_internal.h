@@ -70,7 +70,7 @@ __device__ inline int xcd_block(int n) {
 enum KernelClass {
     K_NB_GRID = 0, K_NB_BIN, K_NB_SCAN, K_NB_COUNT, K_NB_FILL, K_NB_REV,
     K_PAIRS, K_EMBED, K_MLP, K_FILTER_FWD, K_CFCONV, K_READOUT, K_ENERGY,
-    K_FILTER_BWD, K_FORCES, K_VERLET, K_KINETIC, K_NUM_CLASSES
+    K_FILTER_BWD, K_FORCES, K_VERLET, K_KINETIC, K_PACK, K_NUM_CLASSES
 };
 
 void prof_begin(int cls, hipStream_t s);
@@ -99,8 +99,46 @@ struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
 };
 
 struct EfLayout {            // energy/force scratch (offsets from ws base)
-    size_t up_first, up_ptr, edge_pair, pair_ij, pgeo, pfc, pdfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, total;
+    size_t up_first, up_ptr, edge_pair, pair_ij, pgeo, pfc, pdfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, pack,
+        total;
 };
+
+// Weight pack: every weight matrix of the model pre-split into fp16 hi / lo
+// halves and pre-arranged in the fragment order in which a kernel stages it
+// into LDS, written once per evaluation so that each block's staging is a
+// straight copy.  One slot per matrix: hi [kPackSlotFrags] then lo
+// [kPackSlotFrags] 16-byte fragments; after all slots, two ints per slot
+// (the power-of-two scale of the split, and one more scale where a kernel
+// needs it).
+enum PackKind {
+    PK_FA1 = 0,   // filter first layer (both passes)
+    PK_FA2,       // filter second layer, forward (chained order, times ln 2)
+    PK_FA2B,      // filter second layer, backward (transposed)
+    PK_XW,        // atom-wise W_in
+    PK_OW1,       // Wo1
+    PK_OW2,       // Wo2 (chained)
+    PK_BOW1,      // Wo2 transposed
+    PK_BOW2,      // Wo1 transposed (chained)
+    PK_BXW,       // W_in transposed
+    PK_PER_T
+};
+constexpr int kPackSlotFrags = 2048;
+constexpr size_t kPackSlotBytes = 2 * size_t(kPackSlotFrags) * 16;
+__host__ __device__ inline int pack_slot(int t, int kind) { return t * PK_PER_T + kind; }
+__host__ __device__ inline int pack_readout_slot(int I, int k) { return I * PK_PER_T + k; }   // k = 0: R1, 1: R1 transposed (chained)
+__host__ __device__ inline int pack_slots(int I) { return I * PK_PER_T + 2; }
+inline size_t pack_bytes(int I) { return pack_slots(I) * kPackSlotBytes + align256(8 * size_t(pack_slots(I))); }
+struct PackRef {             // device pointers of one slot
+    const void *hi, *lo;
+    const int *sc;
+};
+__host__ __device__ inline PackRef pack_ref(const char *pack, int I, int slot) {
+    PackRef r;
+    r.hi = pack + slot * kPackSlotBytes;
+    r.lo = pack + slot * kPackSlotBytes + kPackSlotBytes / 2;
+    r.sc = reinterpret_cast<const int *>(pack + pack_slots(I) * kPackSlotBytes) + 2 * slot;
+    return r;
+}
 
 NbLayout nb_layout(const sn_system &sys, size_t base);
 EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t n_edges, size_t base);
@@ -124,13 +162,18 @@ sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_
                          int32_t *scratch, hipStream_t s);
 
 // filter.hip
-sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, hipStream_t s);
+// Writes the filter slots of the weight pack (all interactions).
+sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s);
+// pack: the weight pack written by filter_pack, or null (the kernels then stage from the weights)
+sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, const char *pack,
+                         hipStream_t s);
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
 // xmax / gmax: per-atom max_f |x[i][f]| and max_f |g_y[i][f]| of interaction t
 // pfc / pdfc: per-pair envelope fc(d) and its derivative fc'(d)
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
                           const int2 *pair_ij, int64_t P, int N, const float *phi, const float *x, const float *gy,
-                          const float *xmax, const float *gmax, float *S, int accumulate, hipStream_t s);
+                          const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
+                          hipStream_t s);
 
 // graph.hip
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
@@ -146,17 +189,19 @@ sn_status embed(int N, int F, int T, const int32_t *types, const float *emb, flo
                 hipStream_t s);
 sn_status replica_sum(int B, const int32_t *replica_ptr, const float *eps, float *energy, hipStream_t s);
 
-// mlp.hip (fused atom-wise layers; see the kernel comments there)
+// mlp.hip (fused atom-wise layers; see the kernel comments there).  The
+// weights come from the weight pack (slots written by mlp_pack).
+sn_status mlp_pack(const sn_model &m, char *pack, hipStream_t s);
 // xmax (optional): per-atom max_f |x|
-sn_status mlp_x(int N, int F, const float *h, const float *W_in, float *x, float *xmax, hipStream_t s);
-sn_status mlp_out(int N, int F, const float *y, const float *Wo1, const float *bo1, const float *Wo2,
-                  const float *bo2, float *o, float *h, hipStream_t s);
-sn_status mlp_readout(int N, int F, const float *h, const float *R1, const float *c1, const float *R2,
+sn_status mlp_x(int N, int F, const float *h, PackRef W_in, float *x, float *xmax, hipStream_t s);
+sn_status mlp_out(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
+                  float *o, float *h, hipStream_t s);
+sn_status mlp_readout(int N, int F, const float *h, PackRef R1, const float *c1, PackRef R1t, const float *R2,
                       const float *c2, float *eps, float *gh, hipStream_t s);
 // gymax (optional): per-atom max_f |g_y|
-sn_status mlp_bwd_out(int N, int F, const float *gh, const float *Wo2, const float *o, const float *Wo1, float *gy,
+sn_status mlp_bwd_out(int N, int F, const float *gh, PackRef Wo2t, const float *o, PackRef Wo1t, float *gy,
                       float *gymax, hipStream_t s);
-sn_status mlp_bwd_x(int N, int F, const float *gx, const float *W_in, float *gh, hipStream_t s);
+sn_status mlp_bwd_x(int N, int F, const float *gx, PackRef W_int, float *gh, hipStream_t s);
 
 // verlet (api.hip)
 

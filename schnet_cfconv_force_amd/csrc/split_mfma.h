@@ -47,9 +47,11 @@ __device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
     asm("" : "+v"(h));
     float m1 = -1.0f;
     asm("" : "+s"(m1));
+    half8 l;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lo[j] = (_Float16)fmaf((float)h[j], m1, x[j]);
+    for (int j = 0; j < 8; ++j) l[j] = (_Float16)fmaf((float)h[j], m1, x[j]);
     hi = h;
+    lo = l;
 }
 
 // Power-of-two exponent s with amax 2^s in [2^(kSplitTop-1), 2^kSplitTop)
@@ -99,6 +101,30 @@ __device__ inline int stage_split(half8 *hi, half8 *lo, int nf, unsigned *s_max,
         }
     }
     return sc;
+}
+
+// Copy nf (<= NF) pre-split fragments (a weight-pack slot) into LDS; all of
+// a thread's loads are issued before the first store.
+template <int NF, int NTHR>
+__device__ inline void copy_frags(half8 *hi, half8 *lo, const half8 *src_hi, const half8 *src_lo, int nf) {
+    constexpr int IT = (NF + NTHR - 1) / NTHR;
+    half8 vh[IT], vl[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = (int)threadIdx.x + it * NTHR;
+        if (idx < nf) {
+            vh[it] = src_hi[idx];
+            vl[it] = src_lo[idx];
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = (int)threadIdx.x + it * NTHR;
+        if (idx < nf) {
+            hi[idx] = vh[it];
+            lo[idx] = vl[it];
+        }
+    }
 }
 
 // acc[m][n] += A_m B_n in split form for MG weight tiles (fragments at
