@@ -179,13 +179,18 @@ def _f64(params):
 #    (forward and backward); FS-abs (2), (3)]
 # ---------------------------------------------------------------------------
 
-def energy_forces(params, hyper, types, pos, replica_ptr, csr, box=None, return_intermediates=False):
+def energy_forces(params, hyper, types, pos, replica_ptr, csr, box=None, return_intermediates=False,
+                  phi_store=None):
     """Per-replica energies E_b and forces F = -dE/dr, all in fp64.
 
     params: named weights (float32 arrays are promoted to fp64).
     hyper:  n_rbf, cutoff, rbf_lo, rbf_hi, rbf_gamma.
     csr:    (row_ptr, col, rev) -- only row_ptr and col are used; the edge
             set is taken as given (the full directed list).
+    phi_store: optional function applied to each interaction's filter rows
+            phi before they are used (forward and backward alike), to measure
+            what a storage format for them costs; None (the default) is the
+            exact computation.
 
     Forward, then the analytic gradient written out by the chain rule.  The
     CFConv is a plain scatter over the directed edges, y_i += W_e * x_j, and
@@ -207,6 +212,8 @@ def energy_forces(params, hyper, types, pos, replica_ptr, csr, box=None, return_
         x = h @ blk["W_in"]
         a = e @ blk["A1"] + blk["b1"]
         phi = ssp(a) @ blk["A2"] + blk["b2"]
+        if phi_store is not None:
+            phi = phi_store(phi)
         W = fc[:, None] * phi
         y = np.zeros_like(x)
         np.add.at(y, ei, W * x[ej])

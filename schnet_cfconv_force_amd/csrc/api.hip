@@ -78,7 +78,7 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     L.pgeo = take(16 * P);
     L.pfc = take(4 * P);
     L.pdfc = take(4 * P);
-    L.phi = take(4 * I * P * F);
+    L.phi = take(4 * I * P * fp24_words((int)F));   // 24-bit filter rows
     L.x = take(4 * I * N * F);
     L.o = take(4 * I * N * F);
     L.gy = take(4 * I * N * F);
@@ -240,8 +240,8 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     const float *pdfc = F32(L.pdfc);
     float *h = F32(L.h), *y = F32(L.y), *gh = F32(L.gh);
     float *S = F32(L.S);
-    const int64_t NF = (int64_t)N * F, PF = P * F;
-    auto phi_t = [&](int t) { return F32(L.phi) + PF * t; };
+    const int64_t NF = (int64_t)N * F;
+    auto phi_t = [&](int t) { return reinterpret_cast<uint32_t *>(ws + L.phi) + P * fp24_words(F) * t; };
     auto x_t = [&](int t) { return F32(L.x) + NF * t; };
     auto o_t = [&](int t) { return F32(L.o) + NF * t; };
     auto gy_t = [&](int t) { return F32(L.gy) + NF * t; };

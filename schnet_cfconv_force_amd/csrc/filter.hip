@@ -61,12 +61,13 @@ struct FilterArgs {
     const float *dsrc;           // distance of pair p at dsrc[p * dstride + doff]
     int dstride, doff;
     int64_t P;
-    float *phi;                  // forward output [P][F]
+    float *phi;                  // forward output [P][F] (fp32), or
+    uint32_t *phi24;             // forward output [P][3F/4] (the 24-bit row format)
     // backward
     const int2 *pair_ij;
     const float *fc, *dfc;       // [P]: envelope fc(d_p) and its derivative fc'(d_p)
     const float *x, *gy;         // [N][F]
-    const float *phi_in;         // [P][F]
+    const uint32_t *phi24_in;    // [P][3F/4] (the 24-bit row format)
     float *S;                    // [P]
     const float *xmax, *gmax;    // [N]: max_f |x_i[f]|, max_f |g_y_i[f]|
     int accumulate;
@@ -333,7 +334,13 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
 #pragma unroll
                 for (int g = 0; g < MG; ++g) {
                     const floatx4 v = acc[g][0] * os;
-                    *reinterpret_cast<floatx4 *>(a.phi + p * F + 16 * (m0 + g) + 4 * slot) = v;
+                    if (a.phi24) {
+                        const Packed4 w = pack_fp24(v[0], v[1], v[2], v[3]);
+                        *reinterpret_cast<uint3 *>(a.phi24 + p * fp24_words(F) + 3 * (4 * (m0 + g) + slot)) =
+                            make_uint3(w.w0, w.w1, w.w2);
+                    } else {
+                        *reinterpret_cast<floatx4 *>(a.phi + p * F + 16 * (m0 + g) + 4 * slot) = v;
+                    }
                 }
             }
         }
@@ -400,7 +407,7 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         half8 gh[T2], gl[T2];
         {
             const int64_t bi = (int64_t)ij.x * F + 8 * slot, bj = (int64_t)ij.y * F + 8 * slot;
-            const int64_t bp = (live ? p : 0) * F + 8 * slot;
+            const int64_t bp = (live ? p : 0) * fp24_words(F) + 6 * slot;   // features 8 slot ..
 #pragma unroll
             for (int t = 0; t < T2; ++t) {
                 asm volatile("" ::: "memory");   // at most one step's gathers in flight
@@ -412,7 +419,8 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
                     const float4 gyj = *reinterpret_cast<const float4 *>(a.gy + bj + o);
                     const float4 xi = *reinterpret_cast<const float4 *>(a.x + bi + o);
                     const float4 xj = *reinterpret_cast<const float4 *>(a.x + bj + o);
-                    const float4 ph = *reinterpret_cast<const float4 *>(a.phi_in + bp + o);
+                    const uint3 pw = *reinterpret_cast<const uint3 *>(a.phi24_in + bp + 3 * (o / 4));
+                    const float4 ph = unpack_fp24(pw.x, pw.y, pw.z);
                     const float g0 = gyi.x * xj.x + gyj.x * xi.x, g1 = gyi.y * xj.y + gyj.y * xi.y;
                     const float g2 = gyi.z * xj.z + gyj.z * xi.z, g3 = gyi.w * xj.w + gyj.w * xi.w;
                     gfc += g0 * ph.x + g1 * ph.y + g2 * ph.z + g3 * ph.w;
@@ -643,15 +651,15 @@ sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s) {
     return launch_status();
 }
 
-sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, const char *pack,
-                         hipStream_t s) {
+sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, uint32_t *phi24,
+                         const char *pack, hipStream_t s) {
     FilterArgs a = make_args(m, t);
     attach_pack(a, m, t, pack, PK_FA2);
     a.dsrc = reinterpret_cast<const float *>(pgeo);
     a.dstride = 4;
     a.doff = 3;
     a.P = P;
-    a.phi = phi;
+    a.phi24 = phi24;
     return fwd_dispatch(a, m.n_features, s);
 }
 
@@ -666,7 +674,7 @@ sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t
 }
 
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
-                          const int2 *pair_ij, int64_t P, int N, const float *phi, const float *x, const float *gy,
+                          const int2 *pair_ij, int64_t P, int N, const uint32_t *phi24, const float *x, const float *gy,
                           const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
                           hipStream_t s) {
     if (P <= 0) return SN_OK;
@@ -682,7 +690,7 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
     a.dfc = pdfc;
     a.x = x;
     a.gy = gy;
-    a.phi_in = phi;
+    a.phi24_in = phi24;
     a.S = S;
     a.xmax = xmax;
     a.gmax = gmax;

@@ -118,14 +118,15 @@ __global__ void pair_check_kernel(const int32_t *up_ptr, int N, int64_t P, int *
     if (up_ptr[N] != P) flag_status(status, SN_ERR_INVALID);
 }
 
-// y_i = sum_{e in row i} pfc[p] * phi[p] (.) in[col(e)].  One wavefront per
+// y_i = sum_{e in row i} pfc[p] * phi[p] (.) in[col(e)], phi in the 24-bit
+// row format (three words per four features).  One wavefront per
 // row: F/4 lanes cover the features (one float4 each) and the 64/(F/4) lane
 // groups take interleaved edges of the same row, so every wavefront streams
 // one row with several edges in flight and no lanes wait on a longer row.
 template <int F>
 __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const int32_t *row_ptr,
                                                      const int32_t *col, const int32_t *edge_pair, const float *pfc,
-                                                     const float *phi, const float *in, float *out) {
+                                                     const uint32_t *phi24, const float *in, float *out) {
     constexpr int LPR = F / 4;            // lanes per feature row
     constexpr int G = 64 / LPR;           // edges in flight per wavefront
     const int lane = threadIdx.x % 64;
@@ -156,7 +157,8 @@ __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const i
             const int p = __shfl(cp, src, 64);
             const float w = __shfl(cw, src, 64);
             if (t < n) {
-                const float4 f = *reinterpret_cast<const float4 *>(phi + (int64_t)p * F + 4 * sub);
+                const uint3 fw = *reinterpret_cast<const uint3 *>(phi24 + (int64_t)p * fp24_words(F) + 3 * sub);
+                const float4 f = unpack_fp24(fw.x, fw.y, fw.z);
                 const float4 x = *reinterpret_cast<const float4 *>(in + (int64_t)j * F + 4 * sub);
                 acc.x += w * f.x * x.x;
                 acc.y += w * f.y * x.y;
@@ -243,14 +245,14 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
 }
 
 sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
-                 const float *pfc, const float *phi, const float *in, float *out, hipStream_t s) {
+                 const float *pfc, const uint32_t *phi24, const float *in, float *out, hipStream_t s) {
     ProfScope ps(K_CFCONV, s);
     const int nb = (N + 3) / 4;          // four rows (wavefronts) per block
     const int grid = xcd_grid(nb);
     switch (F) {
-        case 32: cfconv_kernel<32><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi, in, out); break;
-        case 64: cfconv_kernel<64><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi, in, out); break;
-        case 128: cfconv_kernel<128><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi, in, out); break;
+        case 32: cfconv_kernel<32><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out); break;
+        case 64: cfconv_kernel<64><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out); break;
+        case 128: cfconv_kernel<128><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out); break;
         default: return SN_ERR_INVALID;
     }
     return launch_status();

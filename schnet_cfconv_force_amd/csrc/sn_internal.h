@@ -49,6 +49,39 @@ __device__ inline float ssp(float x) {
 // Its derivative, the logistic sigmoid.
 __device__ inline float sigm(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
 
+// --------------------------------------------------------------- filter-row storage
+
+// The filter rows that the pipeline keeps in HBM between its kernels are
+// stored in a 24-bit float: an fp32 value rounded to its upper three bytes
+// (sign, exponent, 15 mantissa bits; the magnitude rounded half up), so the
+// relative error of a stored value is at most 2^-16.  Four consecutive
+// features pack into three 32-bit words.
+struct Packed4 {
+    uint32_t w0, w1, w2;
+};
+__device__ inline Packed4 pack_fp24(float a, float b, float c, float d) {
+    // adding half of the dropped byte's weight to the bit pattern rounds the
+    // magnitude (a carry runs into the exponent as it should)
+    const uint32_t r0 = __float_as_uint(a) + 0x80u, r1 = __float_as_uint(b) + 0x80u;
+    const uint32_t r2 = __float_as_uint(c) + 0x80u, r3 = __float_as_uint(d) + 0x80u;
+    // v_perm_b32 selector: byte k of the result = byte sel_k of {src0 : src1}
+    // (src1 bytes 0-3, src0 bytes 4-7)
+    Packed4 p;
+    p.w0 = __builtin_amdgcn_perm(r1, r0, 0x05030201u);   // r0.b1 r0.b2 r0.b3 r1.b1
+    p.w1 = __builtin_amdgcn_perm(r2, r1, 0x06050302u);   // r1.b2 r1.b3 r2.b1 r2.b2
+    p.w2 = __builtin_amdgcn_perm(r3, r2, 0x07060503u);   // r2.b3 r3.b1 r3.b2 r3.b3
+    return p;
+}
+__device__ inline float4 unpack_fp24(uint32_t w0, uint32_t w1, uint32_t w2) {
+    // selector byte 0x0c gives a zero byte
+    return make_float4(__uint_as_float(__builtin_amdgcn_perm(w1, w0, 0x0201000cu)),
+                       __uint_as_float(__builtin_amdgcn_perm(w1, w0, 0x0504030cu)),
+                       __uint_as_float(__builtin_amdgcn_perm(w2, w1, 0x0403020cu)),
+                       __uint_as_float(__builtin_amdgcn_perm(w2, w2, 0x0302010cu)));
+}
+// 32-bit words per stored filter row of F features
+__host__ __device__ constexpr int fp24_words(int F) { return 3 * F / 4; }
+
 // --------------------------------------------------------------- XCD mapping
 
 // MI355X places consecutive workgroup ids on its 8 XCDs in turn, and each
@@ -164,14 +197,15 @@ sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_
 // filter.hip
 // Writes the filter slots of the weight pack (all interactions).
 sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s);
-// pack: the weight pack written by filter_pack, or null (the kernels then stage from the weights)
-sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, float *phi, const char *pack,
-                         hipStream_t s);
+// pack: the weight pack written by filter_pack, or null (the kernels then stage from the weights).
+// phi24: the filter rows [P][3F/4] in the 24-bit row format (see pack_fp24).
+sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, uint32_t *phi24,
+                         const char *pack, hipStream_t s);
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
 // xmax / gmax: per-atom max_f |x[i][f]| and max_f |g_y[i][f]| of interaction t
 // pfc / pdfc: per-pair envelope fc(d) and its derivative fc'(d)
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
-                          const int2 *pair_ij, int64_t P, int N, const float *phi, const float *x, const float *gy,
+                          const int2 *pair_ij, int64_t P, int N, const uint32_t *phi24, const float *x, const float *gy,
                           const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
                           hipStream_t s);
 
@@ -179,8 +213,9 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
                       const int32_t *rev, int64_t E, float cutoff, char *ws, const EfLayout &L, int *status,
                       hipStream_t s);
+// phi24: the filter rows in the 24-bit row format
 sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
-                 const float *pfc, const float *phi, const float *in, float *out, hipStream_t s);
+                 const float *pfc, const uint32_t *phi24, const float *in, float *out, hipStream_t s);
 sn_status forces_rows(int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
                       const float4 *pgeo, const float *S, float *forces, int *status, hipStream_t s);
 
