@@ -179,7 +179,7 @@ size_t bytes_needed(const sn_model *m, const sn_system *s, int64_t E) {
 struct Aux {
     std::mutex mu;
     hipStream_t s = nullptr;
-    hipEvent_t ev[2 * 16 + 4] = {};
+    hipEvent_t ev[3 * 16 + 4] = {};
     bool tried = false, ok = false;
 };
 
@@ -254,7 +254,8 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     // kernel runs on the caller's stream, so that its timing events or a
     // kernel trace bracket that kernel alone
     hipStream_t s2 = (ax.ok && !g_prof_on && !serial_requested()) ? ax.s : s;
-    // [0] pairs ready, [1 + t] phi_t ready, [1 + I + t] g_y_t ready, [2 + 2I] join, [3 + 2I] start
+    // [0] pairs ready, [1 + t] phi_t ready, [1 + I + t] g_y_t ready, [2 + 2I] join, [3 + 2I] start,
+    // [4 + 2I + t] the forward CFConv of t done
     hipEvent_t *ev = ax.ev;
     char *pack = ws + L.pack;
     auto pk = [&](int t, int kind) { return pack_ref(pack, I, pack_slot(t, kind)); };
@@ -269,15 +270,22 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
         SN_TRY(mlp_pack(m, pack, s));
         SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, E, m.cutoff, ws, L, status, s));
         SN_TRY(stream_wait(ev[0], s, s2));
-        for (int t = 0; t < I; ++t) {
-            SN_TRY(filter_forward(m, t, pgeo, P, phi_t(t), pack, s2));
-            if (s2 != s && hipEventRecord(ev[1 + t], s2) != hipSuccess) return SN_ERR_HIP;
-        }
+        SN_TRY(filter_forward(m, 0, pgeo, P, phi_t(0), pack, s2));
+        if (s2 != s && hipEventRecord(ev[1], s2) != hipSuccess) return SN_ERR_HIP;
         SN_TRY(embed(N, F, m.n_types, sys.types, prm + off[0], h, status, s));
         SN_TRY(mlp_x(N, F, h, pk(0, PK_XW), x_t(0), xmax_t(0), s));
         for (int t = 0; t < I; ++t) {
             if (s2 != s && hipStreamWaitEvent(s, ev[1 + t], 0) != hipSuccess) return SN_ERR_HIP;
             SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, s));
+            if (t + 1 < I) {
+                // the next filter rows are written only after this CFConv has
+                // read phi_t: one interaction's rows (24-bit, about 200 MB for
+                // 64 replicas) then stay in the Infinity Cache from their write
+                // to their read
+                SN_TRY(stream_wait(ev[4 + 2 * I + t], s, s2));
+                SN_TRY(filter_forward(m, t + 1, pgeo, P, phi_t(t + 1), pack, s2));
+                if (s2 != s && hipEventRecord(ev[2 + t], s2) != hipSuccess) return SN_ERR_HIP;
+            }
             SN_TRY(mlp_out(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), o_t(t), h, s));
             if (t + 1 < I) SN_TRY(mlp_x(N, F, h, pk(t + 1, PK_XW), x_t(t + 1), xmax_t(t + 1), s));
         }
