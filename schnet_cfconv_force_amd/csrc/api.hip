@@ -72,6 +72,7 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     size_t o = base;
     auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
     L.up_first = take(4 * N);
+    L.up_cnt = take(4 * N);
     L.up_ptr = take(4 * (N + 1));
     L.edge_pair = take(4 * E);
     L.pair_ij = take(8 * P);

@@ -216,10 +216,11 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
     const int N = sys.n_atoms;
     ProfScope ps(K_PAIRS, s);
     int32_t *up_first = reinterpret_cast<int32_t *>(ws + L.up_first);
+    int32_t *up_cnt = reinterpret_cast<int32_t *>(ws + L.up_cnt);
     int32_t *up_ptr = reinterpret_cast<int32_t *>(ws + L.up_ptr);
-    pair_count_kernel<<<(N + 255) / 256, 256, 0, s>>>(N, row_ptr, col, up_first, up_ptr);
+    pair_count_kernel<<<(N + 255) / 256, 256, 0, s>>>(N, row_ptr, col, up_first, up_cnt);
     SN_TRY(launch_status());
-    SN_TRY(scan_exclusive(up_ptr, up_ptr, N, nullptr, nullptr, scan_scratch(ws), s));
+    SN_TRY(scan_exclusive(up_cnt, up_ptr, N, nullptr, nullptr, s));
     pair_check_kernel<<<1, 1, 0, s>>>(up_ptr, N, E / 2, status);
     SN_TRY(launch_status());
     PairArgs a;

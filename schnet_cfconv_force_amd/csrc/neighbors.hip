@@ -326,84 +326,52 @@ __device__ inline void load4(const int32_t *in, int n, int64_t b, int v[4]) {
     for (int r = 0; r < 4; ++r) v[r] = (b + r < n) ? in[b + r] : 0;
 }
 
-// pass 1: per-tile sum and max
-__global__ __launch_bounds__(kScanThreads) void scan_tiles_kernel(const int32_t *in, int n, int32_t *tsum,
-                                                                  int32_t *tmax) {
+// Exclusive scan in one launch.  Block b scans tile b (kScanTile values) and
+// finds the sum of all earlier tiles by reading them itself: at the sizes
+// used here (up to a few hundred thousand values) that redundant read from
+// L2 costs less than the launches of a multi-pass scan.  The last block also
+// writes out[n] (the total) and the optional total and maximum slots.  in and
+// out must not overlap; in must be 16-byte aligned.
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t *in, int32_t *out, int n,
+                                                            int32_t *total_slot, int32_t *max_slot) {
     __shared__ int s_w[kScanThreads / 64];
-    int v[4];
-    load4(in, n, (int64_t)blockIdx.x * kScanTile + 4 * threadIdx.x, v);
-    int tot;
-    block_exclusive(v[0] + v[1] + v[2] + v[3], s_w, &tot);
-    const int m = block_max(max(max(v[0], v[1]), max(v[2], v[3])), s_w);
-    if (threadIdx.x == 0) {
-        tsum[blockIdx.x] = tot;
-        tmax[blockIdx.x] = m;
+    const int64_t t0 = (int64_t)blockIdx.x * kScanTile;   // a multiple of 4 * kScanThreads
+    const bool last = blockIdx.x == gridDim.x - 1;
+    int pre = 0, mx = 0;
+#pragma unroll 4
+    for (int64_t b = 4 * (int64_t)threadIdx.x; b < t0; b += 4 * kScanThreads) {
+        const int4 v = *reinterpret_cast<const int4 *>(in + b);
+        pre += (v.x + v.y) + (v.z + v.w);
+        mx = max(mx, max(max(v.x, v.y), max(v.z, v.w)));
     }
-}
-
-// pass 2 (one block): exclusive scan of the tile sums in place; total and max
-__global__ __launch_bounds__(kScanThreads) void scan_sums_kernel(int32_t *tsum, const int32_t *tmax, int ntiles,
-                                                                 int32_t *out_n, int32_t *total_slot,
-                                                                 int32_t *max_slot) {
-    __shared__ int s_w[kScanThreads / 64];
-    int v[4], mv[4];
-    const int64_t b = 4 * threadIdx.x;
-    load4(tsum, ntiles, b, v);
-    load4(tmax, ntiles, b, mv);
+    int before;
+    block_exclusive(pre, s_w, &before);   // the block-wide sum of the earlier tiles
+    int v[4];
+    load4(in, n, t0 + 4 * threadIdx.x, v);
     int tot;
-    int run = block_exclusive(v[0] + v[1] + v[2] + v[3], s_w, &tot);
-    const int m = block_max(max(max(mv[0], mv[1]), max(mv[2], mv[3])), s_w);
+    int run = before + block_exclusive(v[0] + v[1] + v[2] + v[3], s_w, &tot);
     for (int r = 0; r < 4; ++r) {
-        if (b + r < ntiles) tsum[b + r] = run;
+        if (t0 + 4 * threadIdx.x + r < n) out[t0 + 4 * threadIdx.x + r] = run;
         run += v[r];
     }
-    if (threadIdx.x == 0) {
-        *out_n = tot;
-        if (total_slot) *total_slot = tot;
-        if (max_slot) *max_slot = m;
-    }
-}
-
-// pass 3: scan of each tile plus its offset (tsum == nullptr: single tile)
-__global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(const int32_t *in, int32_t *out, int n,
-                                                                  const int32_t *tsum, int32_t *total_slot,
-                                                                  int32_t *max_slot) {
-    __shared__ int s_w[kScanThreads / 64];
-    int v[4];
-    const int64_t b = (int64_t)blockIdx.x * kScanTile + 4 * threadIdx.x;
-    load4(in, n, b, v);
-    int tot;
-    int run = block_exclusive(v[0] + v[1] + v[2] + v[3], s_w, &tot) + (tsum ? tsum[blockIdx.x] : 0);
-    int m = 0;
-    if (!tsum) m = block_max(max(max(v[0], v[1]), max(v[2], v[3])), s_w);
-    for (int r = 0; r < 4; ++r) {
-        if (b + r < n) out[b + r] = run;
-        run += v[r];
-    }
-    if (!tsum && threadIdx.x == 0) {
-        out[n] = tot;
-        if (total_slot) *total_slot = tot;
-        if (max_slot) *max_slot = m;
+    if (last) {
+        const int m = block_max(max(mx, max(max(v[0], v[1]), max(v[2], v[3]))), s_w);
+        if (threadIdx.x == 0) {
+            out[n] = before + tot;
+            if (total_slot) *total_slot = before + tot;
+            if (max_slot) *max_slot = m;
+        }
     }
 }
 
 }  // namespace
 
 sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
-                         int32_t *scratch, hipStream_t s) {
+                         hipStream_t s) {
     ProfScope ps(K_NB_SCAN, s);
-    const int ntiles = (n + kScanTile - 1) / kScanTile;
-    if (ntiles > kScanTile) return SN_ERR_INVALID;
-    if (ntiles <= 1) {
-        scan_apply_kernel<<<1, kScanThreads, 0, s>>>(in, out, n, nullptr, total_slot, max_slot);
-        return launch_status();
-    }
-    int32_t *tsum = scratch, *tmax = scratch + kScanTile;
-    scan_tiles_kernel<<<ntiles, kScanThreads, 0, s>>>(in, n, tsum, tmax);
-    SN_TRY(launch_status());
-    scan_sums_kernel<<<1, kScanThreads, 0, s>>>(tsum, tmax, ntiles, out + n, total_slot, max_slot);
-    SN_TRY(launch_status());
-    scan_apply_kernel<<<ntiles, kScanThreads, 0, s>>>(in, out, n, tsum, nullptr, nullptr);
+    if (n < 0 || in == out) return SN_ERR_INVALID;
+    const int ntiles = n > 0 ? (n + kScanTile - 1) / kScanTile : 1;
+    scan_kernel<<<ntiles, kScanThreads, 0, s>>>(in, out, n, total_slot, max_slot);
     return launch_status();
 }
 
@@ -425,6 +393,7 @@ NbLayout nb_layout(const sn_system &sys, size_t base) {
     L.cell_start = o; o = align256(o + 4 * (L.n_cells + 1));
     L.cell_fill = o;  o = align256(o + 4 * (L.n_cells + 1));
     L.spos = o;       o = align256(o + 16 * N);
+    L.row_cnt = o;    o = align256(o + 4 * N);
     L.total = o;
     return L;
 }
@@ -464,6 +433,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
     int *cell_start = reinterpret_cast<int *>(ws + L.cell_start);
     int *cell_fill = reinterpret_cast<int *>(ws + L.cell_fill);
     float4 *spos = reinterpret_cast<float4 *>(ws + L.spos);
+    int *row_cnt = reinterpret_cast<int *>(ws + L.row_cnt);
 
     // reset the counters but keep the status word: an error flagged by earlier
     // work on this workspace (e.g. a non-finite force) is reported below
@@ -485,7 +455,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         bin_kernel<<<(N + 255) / 256, 256, 0, s>>>(pos, N, grid, rep_of, pp, cell_of, cell_cnt);
         SN_TRY(launch_status());
     }
-    SN_TRY(scan_exclusive(cell_cnt, cell_start, (int)L.n_cells, nullptr, nullptr, scan_scratch(ws), s));
+    SN_TRY(scan_exclusive(cell_cnt, cell_start, (int)L.n_cells, nullptr, nullptr, s));
     {
         ProfScope ps(K_NB_BIN, s);
         place_kernel<<<(N + 255) / 256, 256, 0, s>>>(pos, N, cell_of, cell_start, cell_fill, spos);
@@ -495,10 +465,10 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
     {
         ProfScope ps(K_NB_COUNT, s);
         rows_kernel<false><<<blocks, kWave * kNbWaves, 0, s>>>(pos, N, grid, rep_of, cell_start, spos, pp,
-                                                               row_ptr, nullptr, nullptr, status);
+                                                               row_cnt, nullptr, nullptr, status);
         SN_TRY(launch_status());
     }
-    SN_TRY(scan_exclusive(row_ptr, row_ptr, N, status + kEdgeTotal, status + kMaxRow, scan_scratch(ws), s));
+    SN_TRY(scan_exclusive(row_cnt, row_ptr, N, status + kEdgeTotal, status + kMaxRow, s));
     int *host = pinned_counters();
     if (!host) return SN_ERR_HIP;
     SN_HIP(hipMemcpyAsync(host, status, 4 * 4, hipMemcpyDeviceToHost, s));

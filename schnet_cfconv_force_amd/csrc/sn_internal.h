@@ -119,20 +119,18 @@ struct ProfScope {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: [0, 256) status words, [256, kWsBase) scan scratch (2 x 4096
-// tile sums), then the scratch of the neighbour builder or of the
-// energy/force pipeline (they are never live at the same time).
-constexpr size_t kWsScan = 256;
-constexpr size_t kWsBase = kWsScan + 2 * 4096 * 4;
-inline int32_t *scan_scratch(char *ws) { return reinterpret_cast<int32_t *>(ws + kWsScan); }
+// Workspace: [0, 256) status words, then the scratch of the neighbour
+// builder or of the energy/force pipeline (they are never live at the same
+// time).
+constexpr size_t kWsBase = 256;
 
 struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
-    size_t grid, rep_of, cell_of, cell_cnt, cell_start, cell_fill, spos, total;
+    size_t grid, rep_of, cell_of, cell_cnt, cell_start, cell_fill, spos, row_cnt, total;
     int64_t n_cells;         // capacity of the cell table
 };
 
 struct EfLayout {            // energy/force scratch (offsets from ws base)
-    size_t up_first, up_ptr, edge_pair, pair_ij, pgeo, pfc, pdfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, pack,
+    size_t up_first, up_cnt, up_ptr, edge_pair, pair_ij, pgeo, pfc, pdfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, pack,
         total;
 };
 
@@ -189,10 +187,10 @@ struct CellGrid {
 // neighbors.hip
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
                    int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s);
-// Exclusive prefix sum; out[n] = total; optional device slots receive the
-// total and the maximum input; scratch = the workspace's scan scratch.
+// Exclusive prefix sum (one launch); out[n] = total; optional device slots
+// receive the total and the maximum input.  in and out must not overlap.
 sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
-                         int32_t *scratch, hipStream_t s);
+                         hipStream_t s);
 
 // filter.hip
 // Writes the filter slots of the weight pack (all interactions).
