@@ -353,12 +353,13 @@ def main():
     csr = (row_ptr, col, rev)
 
     def md(n):
-        edges = []
-        for _ in range(n):
-            _, _, _, E = sn.verlet_step(model, system, pos, vel, forces, inv_mass, dt_fs, synth.FORCE_TO_ACCEL, 1,
-                                        h["cutoff"], capacity, ws, csr=csr)
-            edges.append(E)
-        return edges
+        # one call runs all n steps (the library synchronises once, at its end)
+        if n <= 0:
+            return []
+        elog = torch.zeros(n, dtype=torch.int32, device="cuda")
+        sn.verlet_step(model, system, pos, vel, forces, inv_mass, dt_fs, synth.FORCE_TO_ACCEL, n,
+                       h["cutoff"], capacity, ws, csr=csr, edge_log=elog)
+        return [int(e) for e in elog.cpu().tolist()]
 
     md(args.warmup)
     torch.cuda.synchronize()

@@ -192,14 +192,20 @@ sn_status sn_energy_forces(const sn_model *model, const sn_system *sys, const fl
  * inv_mass[N].  row_ptr/col_idx/rev_idx (capacity as above) receive the
  * last neighbour list and *n_edges its size (host).  epot_log and ekin_log,
  * if not NULL, receive per step and replica the potential energy and
- * 0.5 sum m v^2 / force_to_accel ([n_steps][B]).  Synchronises once per step
- * (neighbour count); returns SN_ERR_CAPACITY / SN_ERR_NONFINITE at the
- * first failing step, with *n_steps_done (host, may be NULL) = steps done. */
+ * 0.5 sum m v^2 / force_to_accel ([n_steps][B], device); edge_log, if not
+ * NULL, the edge count of each step's neighbour list ([n_steps], device).
+ * The steps run without host synchronisation: the edge and pair counts stay
+ * on the device, the capacity and row-length checks run there, and the
+ * call synchronises once, at its end.  After the first error (for example
+ * SN_ERR_CAPACITY, SN_ERR_ROW or SN_ERR_NONFINITE) no atom moves again and
+ * every later neighbour list is empty; the call returns that error, with
+ * *n_steps_done (host, may be NULL) = the steps completed before it; pos,
+ * vel and forces then hold the state of the failing step, not a valid one. */
 sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos, float *vel, float *forces,
                          const float *inv_mass, float dt, float force_to_accel, int32_t n_steps,
                          float r_list, int32_t *row_ptr, int32_t *col_idx, int32_t *rev_idx,
                          int64_t capacity, int64_t *n_edges, float *epot_log, float *ekin_log,
-                         int32_t *n_steps_done, void *ws, size_t ws_bytes, void *stream);
+                         int32_t *edge_log, int32_t *n_steps_done, void *ws, size_t ws_bytes, void *stream);
 
 /* Filter network alone ("How", flash radial basis and the filter network,
  * FlashSchNet summary page): phi[p][F] = ssp(rbf(d_p) A1 + b1) A2 + b2 of

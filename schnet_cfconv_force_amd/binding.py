@@ -76,7 +76,7 @@ def lib() -> ctypes.CDLL:
         "sn_version": (i32, []),
         "sn_build_csr_neighbors": (i32, [PS, vp, f32, vp, vp, vp, i64, P64, vp, sz, vp]),
         "sn_energy_forces": (i32, [PM, PS, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]),
-        "sn_verlet_step": (i32, [PM, PS, vp, vp, vp, vp, f32, f32, i32, f32, vp, vp, vp, i64, P64, vp, vp,
+        "sn_verlet_step": (i32, [PM, PS, vp, vp, vp, vp, f32, f32, i32, f32, vp, vp, vp, i64, P64, vp, vp, vp,
                                  ctypes.POINTER(ctypes.c_int32), vp, sz, vp]),
         "sn_filter_forward": (i32, [PM, i32, vp, i64, vp, vp]),
         "sn_read_status": (i32, [vp, vp]),
@@ -258,8 +258,9 @@ def energy_forces(model: Model, system: System, pos, row_ptr, col, rev, n_edges:
 
 def verlet_step(model: Model, system: System, pos, vel, forces, inv_mass, dt: float, force_to_accel: float,
                 n_steps: int, r_list: float, capacity: int, ws, epot_log=None, ekin_log=None, csr=None,
-                stream=None):
-    """sn_verlet_step; pos, vel, forces are updated in place.  Returns (row_ptr, col, rev, n_edges)."""
+                stream=None, edge_log=None):
+    """sn_verlet_step; pos, vel, forces are updated in place.  Returns (row_ptr, col, rev, n_edges).
+    edge_log (optional int32 device tensor [n_steps]) receives each step's edge count."""
     torch = _torch()
     dev = pos.device
     if csr is None:
@@ -273,7 +274,7 @@ def verlet_step(model: Model, system: System, pos, vel, forces, inv_mass, dt: fl
     st = lib().sn_verlet_step(ctypes.byref(model.c), ctypes.byref(system.c), pos.data_ptr(), vel.data_ptr(),
                               forces.data_ptr(), inv_mass.data_ptr(), float(dt), float(force_to_accel),
                               int(n_steps), float(r_list), row_ptr.data_ptr(), col.data_ptr(), rev.data_ptr(),
-                              int(capacity), ctypes.byref(ne), _ptr(epot_log), _ptr(ekin_log),
+                              int(capacity), ctypes.byref(ne), _ptr(epot_log), _ptr(ekin_log), _ptr(edge_log),
                               ctypes.byref(done), ws.data_ptr(), ws.numel(), _stream(stream))
     if st != SN_OK:
         err = SnError(st, "sn_verlet_step")

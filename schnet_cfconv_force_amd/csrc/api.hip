@@ -106,10 +106,15 @@ sn_status clear_status(void *ws, hipStream_t s) {
     return launch_status();
 }
 
-// v += dt/2 c F / m ; if drift: r += dt v
+// v += dt/2 c F / m ; if drift: r += dt v.  Nothing moves once an error is
+// flagged; steps_done (if set) counts the completed steps, and edge_slot (if
+// set) receives the step's edge count.
 __global__ void verlet_kernel(int N, float *pos, float *vel, const float *forces, const float *inv_mass, float half_dt_c,
-                              float dt, int drift) {
+                              float dt, int drift, int *status, int *edge_slot) {
     int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (edge_slot && idx == 0) *edge_slot = status[kEdgeTotal];
+    if (*status != 0) return;
+    if (!drift && idx == 0) status[kStepsDone] += 1;
     if (idx >= 3 * N) return;
     int i = idx / 3;
     float v = vel[idx] + half_dt_c * forces[idx] * inv_mass[i];
@@ -215,9 +220,12 @@ sn_status stream_wait(hipEvent_t e, hipStream_t from, hipStream_t to) {
 }
 
 // The pipeline itself; arguments already checked, status not cleared.
+// device_edges: E is only the edge capacity (workspace layout and launch
+// sizes); the edge and pair counts are taken on the device (row_ptr[N]), so
+// nothing is read back to the host.
 sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const float *pos, const int32_t *row_ptr,
                              const int32_t *col, const int32_t *rev, int64_t E, float *energy, float *forces,
-                             char *ws, hipStream_t s) {
+                             char *ws, hipStream_t s, bool device_edges = false) {
     const int N = sys.n_atoms, B = sys.n_replicas, F = m.n_features, I = m.n_interactions;
     const int64_t P = E / 2;
     int *status = reinterpret_cast<int *>(ws);
@@ -259,6 +267,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     // [4 + 2I + t] the forward CFConv of t done
     hipEvent_t *ev = ax.ev;
     char *pack = ws + L.pack;
+    const int *p_dev = status + kPairTotal;   // the pair count, written by the pair setup
     auto pk = [&](int t, int kind) { return pack_ref(pack, I, pack_slot(t, kind)); };
     auto pr = [&](int k) { return pack_ref(pack, I, pack_readout_slot(I, k)); };
 
@@ -269,9 +278,9 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
         SN_TRY(stream_wait(ev[3 + 2 * I], s, s2));
         SN_TRY(filter_pack(m, pack, s2));
         SN_TRY(mlp_pack(m, pack, s));
-        SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, E, m.cutoff, ws, L, status, s));
+        SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, device_edges ? -1 : E, m.cutoff, ws, L, status, s));
         SN_TRY(stream_wait(ev[0], s, s2));
-        SN_TRY(filter_forward(m, 0, pgeo, P, phi_t(0), pack, s2));
+        SN_TRY(filter_forward(m, 0, pgeo, P, phi_t(0), pack, p_dev, s2));
         if (s2 != s && hipEventRecord(ev[1], s2) != hipSuccess) return SN_ERR_HIP;
         SN_TRY(embed(N, F, m.n_types, sys.types, prm + off[0], h, status, s));
         SN_TRY(mlp_x(N, F, h, pk(0, PK_XW), x_t(0), xmax_t(0), s));
@@ -284,7 +293,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
                 // 64 replicas) then stay in the Infinity Cache from their write
                 // to their read
                 SN_TRY(stream_wait(ev[4 + 2 * I + t], s, s2));
-                SN_TRY(filter_forward(m, t + 1, pgeo, P, phi_t(t + 1), pack, s2));
+                SN_TRY(filter_forward(m, t + 1, pgeo, P, phi_t(t + 1), pack, p_dev, s2));
                 if (s2 != s && hipEventRecord(ev[2 + t], s2) != hipSuccess) return SN_ERR_HIP;
             }
             SN_TRY(mlp_out(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), o_t(t), h, s));
@@ -298,7 +307,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
             SN_TRY(mlp_bwd_out(N, F, gh, pk(t, PK_BOW1), o_t(t), pk(t, PK_BOW2), gy_t(t), gmax_t(t), s));
             SN_TRY(stream_wait(ev[1 + I + t], s, s2));
             SN_TRY(filter_backward(m, t, pgeo, pfc, pdfc, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
-                                   t != I - 1, pack, s2));
+                                   t != I - 1, pack, p_dev, s2));
             if (t > 0) {   // dE/dh below the first block is not needed for forces
                 SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, s));
                 SN_TRY(mlp_bwd_x(N, F, y, pk(t, PK_BXW), gh, s));
@@ -435,8 +444,8 @@ sn_status sn_energy_forces(const sn_model *model, const sn_system *sys, const fl
 sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos, float *vel, float *forces,
                          const float *inv_mass, float dt, float force_to_accel, int32_t n_steps, float r_list,
                          int32_t *row_ptr, int32_t *col_idx, int32_t *rev_idx, int64_t capacity, int64_t *n_edges,
-                         float *epot_log, float *ekin_log, int32_t *n_steps_done, void *ws, size_t ws_bytes,
-                         void *stream) {
+                         float *epot_log, float *ekin_log, int32_t *edge_log, int32_t *n_steps_done, void *ws,
+                         size_t ws_bytes, void *stream) {
     if (n_steps_done) *n_steps_done = 0;
     SN_TRY(check_system(sys));
     SN_TRY(check_model(model));
@@ -449,23 +458,28 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char *w = reinterpret_cast<char *>(ws);
     SN_TRY(clear_status(ws, s));
+    int *status = reinterpret_cast<int *>(w);
     const float half = 0.5f * dt * force_to_accel;
+    // no host synchronisation inside the loop: the neighbour build and the
+    // pipeline take the edge and pair counts on the device, errors are
+    // flagged in the status word (after which nothing moves and every later
+    // neighbour list is empty), and the counters are read once at the end
+    float *eps_scratch = reinterpret_cast<float *>(w + ef_layout(*model, *sys, capacity, kWsBase).eps) + N;
     for (int32_t step = 0; step < n_steps; ++step) {
         if (N > 0) {
             ProfScope ps(K_VERLET, s);
-            verlet_kernel<<<(3 * N + 255) / 256, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, 1);
+            verlet_kernel<<<(3 * N + 255) / 256, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, 1, status,
+                                                              nullptr);
             SN_TRY(launch_status());
         }
-        int64_t E = 0;
-        sn_status st = nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, &E, w, s);
-        *n_edges = E;
-        if (st != SN_OK) return st;   // includes a non-finite force flagged in the previous step
-        float *eout = epot_log ? epot_log + (int64_t)step * B
-                               : reinterpret_cast<float *>(w + ef_layout(*model, *sys, E, kWsBase).eps) + N;
-        SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, E, eout, forces, w, s));
-        if (N > 0) {
+        int64_t E_unused = 0;
+        SN_TRY(nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, &E_unused, w, s, false));
+        float *eout = epot_log ? epot_log + (int64_t)step * B : eps_scratch;
+        SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, capacity, eout, forces, w, s, true));
+        {
             ProfScope ps(K_VERLET, s);
-            verlet_kernel<<<(3 * N + 255) / 256, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, 0);
+            verlet_kernel<<<(3 * N + 255) / 256 + 1, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, 0, status,
+                                                                  edge_log ? edge_log + step : nullptr);
             SN_TRY(launch_status());
         }
         if (ekin_log) {
@@ -474,11 +488,14 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
                                              ekin_log + (int64_t)step * B);
             SN_TRY(launch_status());
         }
-        if (n_steps_done) *n_steps_done = step + 1;
     }
-    sn_status st = sn_read_status(ws, stream);
-    if (st != SN_OK && n_steps_done && *n_steps_done > 0) *n_steps_done -= 1;
-    return st;
+    int host[kStepsDone + 1] = {};
+    SN_HIP(hipMemcpyAsync(host, status, sizeof(host), hipMemcpyDeviceToHost, s));
+    SN_HIP(hipStreamSynchronize(s));
+    *n_edges = host[kEdgeTotal];
+    if (n_steps_done) *n_steps_done = host[kStepsDone];
+    SN_TRY(clear_status(ws, s));
+    return host[kStatusWord];
 }
 
 sn_status sn_filter_forward(const sn_model *model, int32_t interaction, const float *d, int64_t n, float *phi,

@@ -60,7 +60,8 @@ struct FilterArgs {
     const float *b1, *b2;
     const float *dsrc;           // distance of pair p at dsrc[p * dstride + doff]
     int dstride, doff;
-    int64_t P;
+    int64_t P;                   // pair count, or the capacity when P_dev is set
+    const int *P_dev;            // (may be null) the pair count on the device
     float *phi;                  // forward output [P][F] (fp32), or
     uint32_t *phi24;             // forward output [P][3F/4] (the 24-bit row format)
     // backward
@@ -224,6 +225,7 @@ __device__ inline void mma_split2(const half8 *whi, const half8 *wlo, int stride
 
 template <int F>
 __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
+    const int64_t P = a.P_dev ? (int64_t)*a.P_dev : a.P;
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;                      // 32-wide k steps of the F x F GEMM
     constexpr int MG = MT < kFwdMG ? MT : kFwdMG;   // output tiles per group
@@ -259,13 +261,13 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     const float os = ldexpf(1.0f, -(sz + sa2));   // second accumulator -> phi
 
     int64_t tile, tile_end, stride;
-    tile_range(a.P, tile, tile_end, stride);
+    tile_range(P, tile, tile_end, stride);
     // the distance of the wavefront's next tile is loaded one tile ahead, so
     // that its latency (and the wait for the earlier tile's stores, which the
     // same counter tracks) is not paid at the start of every tile
     auto load_d = [&](int64_t t) {
         const int64_t q = t * 16 + (threadIdx.x % 16);
-        return (t < tile_end && q < a.P) ? a.dsrc[q * a.dstride + a.doff] : 0.0f;
+        return (t < tile_end && q < P) ? a.dsrc[q * a.dstride + a.doff] : 0.0f;
     };
     float d_next = load_d(tile);
     asm volatile("" : "+v"(d_next));
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
             // the next distance has arrived long before; taking it here keeps
             // the loop's first wait from also waiting for these stores
             asm volatile("" : "+v"(d_next));
-            if (p < a.P) {
+            if (p < P) {
 #pragma unroll
                 for (int g = 0; g < MG; ++g) {
                     const floatx4 v = acc[g][0] * os;
@@ -349,6 +351,7 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
 
 template <int F>
 __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
+    const int64_t P = a.P_dev ? (int64_t)*a.P_dev : a.P;
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;
     constexpr int MG = MT < kBwdMG ? MT : kBwdMG;
@@ -378,7 +381,7 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     const int es = -(kSplitTop - 1) - sa2 - sa1;         // with e1: the scales of g_z and a'
 
     int64_t tile, tile_end, stride;
-    tile_range(a.P, tile, tile_end, stride);
+    tile_range(P, tile, tile_end, stride);
     for (; tile < tile_end; tile += stride) {
         asm volatile("" ::: "memory");
         // lane-derived values are recomputed per tile (opaque to the
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         asm volatile("" : "+v"(lane));
         const int slot = lane / 16;
         const int64_t p = tile * 16 + lane % 16;
-        const bool live = p < a.P;
+        const bool live = p < P;
         const float d = live ? a.dsrc[p * a.dstride + a.doff] : 0.0f;
         const int2 ij = live ? a.pair_ij[p] : make_int2(0, 0);
         const float fc = live ? a.fc[p] : 0.0f;
@@ -652,13 +655,14 @@ sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s) {
 }
 
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, uint32_t *phi24,
-                         const char *pack, hipStream_t s) {
+                         const char *pack, const int *p_dev, hipStream_t s) {
     FilterArgs a = make_args(m, t);
     attach_pack(a, m, t, pack, PK_FA2);
     a.dsrc = reinterpret_cast<const float *>(pgeo);
     a.dstride = 4;
     a.doff = 3;
     a.P = P;
+    a.P_dev = p_dev;
     a.phi24 = phi24;
     return fwd_dispatch(a, m.n_features, s);
 }
@@ -676,7 +680,7 @@ sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
                           const int2 *pair_ij, int64_t P, int N, const uint32_t *phi24, const float *x, const float *gy,
                           const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
-                          hipStream_t s) {
+                          const int *p_dev, hipStream_t s) {
     if (P <= 0) return SN_OK;
     (void)N;
     FilterArgs a = make_args(m, t);
@@ -686,6 +690,7 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
     a.doff = 3;
     a.P = P;
     a.pair_ij = pair_ij;
+    a.P_dev = p_dev;
     a.fc = pfc;
     a.dfc = pdfc;
     a.x = x;

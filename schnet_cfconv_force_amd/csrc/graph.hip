@@ -51,7 +51,7 @@ struct PairArgs {
     int periodic;
     float L[3], invL[3];
     float cutoff;
-    int64_t E, P;
+    int64_t E;
     int *status;
 };
 
@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
     const int lane = threadIdx.x % 64;
     const int i = blockIdx.x * 4 + threadIdx.x / 64;
     if (i >= a.N) return;
+    const int64_t P = a.status[kPairTotal];   // written by pair_check_kernel
     const int e0 = a.row_ptr[i], e1 = a.row_ptr[i + 1];
     const int uf = a.up_first[i], up = a.up_ptr[i];
     const float xi = a.pos[3 * i], yi = a.pos[3 * i + 1], zi = a.pos[3 * i + 2];
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
         }
         if (j > i) {
             const int p = up + (e - uf);
-            if (p >= a.P) {                       // more upper edges than E/2: not symmetric
+            if (p >= P) {                         // more upper edges than E/2: not symmetric
                 flag_status(a.status, SN_ERR_INVALID);
                 a.edge_pair[e] = 0;
                 continue;
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
             const int r = a.rev[e];
             const int p = (r >= a.up_first[j] && r < a.row_ptr[j + 1] && a.col[r] == i)
                               ? a.up_ptr[j] + (r - a.up_first[j]) : -1;
-            if (p < 0 || p >= a.P) {
+            if (p < 0 || p >= P) {
                 flag_status(a.status, SN_ERR_INVALID);
                 a.edge_pair[e] = 0;
                 continue;
@@ -114,8 +115,14 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
     }
 }
 
-__global__ void pair_check_kernel(const int32_t *up_ptr, int N, int64_t P, int *status) {
-    if (up_ptr[N] != P) flag_status(status, SN_ERR_INVALID);
+// The pair count is E / 2 (E from the host, or row_ptr[N] when E < 0) and
+// must equal the number of upper edges; it goes to the status slot
+// kPairTotal, or 0 if the check fails.
+__global__ void pair_check_kernel(const int32_t *up_ptr, const int32_t *row_ptr, int N, int64_t E, int *status) {
+    const int64_t P = (E >= 0 ? E : (int64_t)row_ptr[N]) / 2;
+    const bool ok = up_ptr[N] == P;
+    if (!ok) flag_status(status, SN_ERR_INVALID);
+    status[kPairTotal] = ok ? (int)P : 0;
 }
 
 // y_i = sum_{e in row i} pfc[p] * phi[p] (.) in[col(e)], phi in the 24-bit
@@ -221,7 +228,7 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
     pair_count_kernel<<<(N + 255) / 256, 256, 0, s>>>(N, row_ptr, col, up_first, up_cnt);
     SN_TRY(launch_status());
     SN_TRY(scan_exclusive(up_cnt, up_ptr, N, nullptr, nullptr, s));
-    pair_check_kernel<<<1, 1, 0, s>>>(up_ptr, N, E / 2, status);
+    pair_check_kernel<<<1, 1, 0, s>>>(up_ptr, row_ptr, N, E, status);
     SN_TRY(launch_status());
     PairArgs a;
     a.N = N;
@@ -239,7 +246,6 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
     }
     a.cutoff = cutoff;
     a.E = E;
-    a.P = E / 2;
     a.status = status;
     pair_fill_kernel<<<(N + 3) / 4, 256, 0, s>>>(a);
     return launch_status();

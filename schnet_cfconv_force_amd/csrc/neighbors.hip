@@ -170,7 +170,8 @@ template <bool FILL>
 __global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos, int n_atoms, const CellGrid *grid,
                                                                const int *rep_of, const int *cell_start,
                                                                const float4 *spos, PredParams pp, int *cnt,
-                                                               const int32_t *row_ptr, int32_t *col, int *status) {
+                                                               const int32_t *row_ptr, int32_t *col, int64_t capacity,
+                                                               int *status) {
     __shared__ int s_start[kNbWaves][28];
     __shared__ int s_pre[kNbWaves][28];
     __shared__ int s_buf[FILL ? kNbWaves : 1][FILL ? SN_MAX_ROW : 1];
@@ -244,8 +245,11 @@ __global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos
     }
     const int r0 = row_ptr[i];
     const int n = row_ptr[i + 1] - r0;
-    if (n != base || n > SN_MAX_ROW) {
-        if (lane == 0) flag_status(status, SN_ERR_INVALID);
+    if ((int64_t)row_ptr[n_atoms] > capacity || n > SN_MAX_ROW || n != base) {
+        if (lane == 0)
+            flag_status(status, (int64_t)row_ptr[n_atoms] > capacity ? SN_ERR_CAPACITY
+                                : n > SN_MAX_ROW                    ? SN_ERR_ROW
+                                                                    : SN_ERR_INVALID);
         return;
     }
     wave_sync();
@@ -255,6 +259,12 @@ __global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos
         for (int m = 0; m < n; ++m) rank += (s_buf[FILL ? wv : 0][FILL ? m : 0] < v);
         col[r0 + rank] = v;
     }
+}
+
+// After a flagged error: an empty CSR (every row_ptr entry zero).
+__global__ void csr_guard_kernel(int32_t *row_ptr, int n_atoms, const int *status) {
+    if (*status == 0) return;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= n_atoms; i += gridDim.x * blockDim.x) row_ptr[i] = 0;
 }
 
 // One wavefront per row: rev[e] = index of (j, i) in row j.
@@ -408,7 +418,7 @@ static int *pinned_counters() {
 }
 
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
-                   int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s) {
+                   int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync) {
     const int N = sys.n_atoms, B = sys.n_replicas;
     int *status = reinterpret_cast<int *>(ws);
     PredParams pp;
@@ -437,7 +447,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
 
     // reset the counters but keep the status word: an error flagged by earlier
     // work on this workspace (e.g. a non-finite force) is reported below
-    SN_TRY(fill_int(status + 1, 0, kStatusSlots - 1, s));
+    SN_TRY(fill_int(status + kMaxRow, 0, 2, s));   // kMaxRow, kEdgeTotal
     if (N == 0) {
         SN_TRY(fill_int(row_ptr, 0, 1, s));
         *n_edges = 0;
@@ -465,25 +475,31 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
     {
         ProfScope ps(K_NB_COUNT, s);
         rows_kernel<false><<<blocks, kWave * kNbWaves, 0, s>>>(pos, N, grid, rep_of, cell_start, spos, pp,
-                                                               row_cnt, nullptr, nullptr, status);
+                                                               row_cnt, nullptr, nullptr, capacity, status);
         SN_TRY(launch_status());
     }
     SN_TRY(scan_exclusive(row_cnt, row_ptr, N, status + kEdgeTotal, status + kMaxRow, s));
-    int *host = pinned_counters();
-    if (!host) return SN_ERR_HIP;
-    SN_HIP(hipMemcpyAsync(host, status, 4 * 4, hipMemcpyDeviceToHost, s));
-    SN_HIP(hipStreamSynchronize(s));
-    const int st = host[kStatusWord], max_row = host[kMaxRow];
-    const int64_t E = host[kEdgeTotal];
-    *n_edges = E;
-    if (st != 0) return st;
-    if (max_row > SN_MAX_ROW) return SN_ERR_ROW;
-    if (E > capacity) return SN_ERR_CAPACITY;
+    if (sync) {
+        int *host = pinned_counters();
+        if (!host) return SN_ERR_HIP;
+        SN_HIP(hipMemcpyAsync(host, status, 4 * 4, hipMemcpyDeviceToHost, s));
+        SN_HIP(hipStreamSynchronize(s));
+        const int st = host[kStatusWord], max_row = host[kMaxRow];
+        const int64_t E = host[kEdgeTotal];
+        *n_edges = E;
+        if (st != 0) return st;
+        if (max_row > SN_MAX_ROW) return SN_ERR_ROW;
+        if (E > capacity) return SN_ERR_CAPACITY;
+    }
     {
         ProfScope ps(K_NB_FILL, s);
         rows_kernel<true><<<blocks, kWave * kNbWaves, 0, s>>>(pos, N, grid, rep_of, cell_start, spos, pp, nullptr,
-                                                              row_ptr, col, status);
+                                                              row_ptr, col, capacity, status);
         SN_TRY(launch_status());
+        if (!sync) {
+            csr_guard_kernel<<<(N + 256) / 256, 256, 0, s>>>(row_ptr, N, status);
+            SN_TRY(launch_status());
+        }
     }
     {
         ProfScope ps(K_NB_REV, s);

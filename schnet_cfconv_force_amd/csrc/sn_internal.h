@@ -15,7 +15,10 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // --------------------------------------------------------------- status
 
 // Device status word slots (int32, in the first 256 bytes of the workspace).
-enum StatusSlot { kStatusWord = 0, kMaxRow = 1, kEdgeTotal = 2, kStatusSlots = 64 };
+// Device status words at the head of the workspace: the first error code
+// (0 = none), the longest row and the edge total of the last neighbour
+// build, the pair count of the last pair setup, and the MD steps completed.
+enum StatusSlot { kStatusWord = 0, kMaxRow = 1, kEdgeTotal = 2, kPairTotal = 3, kStepsDone = 4, kStatusSlots = 64 };
 
 #define SN_TRY(expr)                               \
     do {                                           \
@@ -185,8 +188,13 @@ struct CellGrid {
 // --------------------------------------------------------------- launchers
 
 // neighbors.hip
+// sync: read the edge count back (into *n_edges) and check it on the host
+// before the rows are filled.  Otherwise nothing is read back: the fill
+// checks the capacity and row lengths on the device, and after any flagged
+// error the CSR is left empty (row_ptr all zero) so that later kernels stay
+// in bounds.
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
-                   int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s);
+                   int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync = true);
 // Exclusive prefix sum (one launch); out[n] = total; optional device slots
 // receive the total and the maximum input.  in and out must not overlap.
 sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
@@ -197,17 +205,20 @@ sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_
 sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s);
 // pack: the weight pack written by filter_pack, or null (the kernels then stage from the weights).
 // phi24: the filter rows [P][3F/4] in the 24-bit row format (see pack_fp24).
+// P: the pair capacity (launch size); p_dev (may be null): the device pair count.
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, uint32_t *phi24,
-                         const char *pack, hipStream_t s);
+                         const char *pack, const int *p_dev, hipStream_t s);
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
 // xmax / gmax: per-atom max_f |x[i][f]| and max_f |g_y[i][f]| of interaction t
 // pfc / pdfc: per-pair envelope fc(d) and its derivative fc'(d)
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
                           const int2 *pair_ij, int64_t P, int N, const uint32_t *phi24, const float *x, const float *gy,
                           const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
-                          hipStream_t s);
+                          const int *p_dev, hipStream_t s);
 
 // graph.hip
+// E: the edge count, or -1 to take it from row_ptr[N] on the device.  Writes
+// the pair count to the status slot kPairTotal (0 after a failed check).
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
                       const int32_t *rev, int64_t E, float cutoff, char *ws, const EfLayout &L, int *status,
                       hipStream_t s);

@@ -337,9 +337,13 @@ def test_verlet_is_deterministic_and_reports_capacity(sn):
         vel, inv_mass = dev(cfg["vel"]), dev(cfg["inv_mass"])
         row_ptr, col, rev, E = L.csr(sn)
         _, forces = sn.energy_forces(L.model, L.system, L.pos, row_ptr, col, rev, E, L.ws)
-        sn.verlet_step(L.model, L.system, L.pos, vel, forces, inv_mass, 2.0, synth.FORCE_TO_ACCEL, 10, 12.0,
-                       L.capacity, L.ws)
+        elog = torch.zeros(10, dtype=torch.int32, device="cuda")
+        rp, _, _, ne = sn.verlet_step(L.model, L.system, L.pos, vel, forces, inv_mass, 2.0, synth.FORCE_TO_ACCEL,
+                                      10, 12.0, L.capacity, L.ws, edge_log=elog)
         torch.cuda.synchronize()
+        # the per-step edge log ends with the edge count of the returned list
+        el = elog.cpu().numpy()
+        assert el[-1] == ne == int(rp[-1].item()) and np.all(el > 0)
         runs.append((L.pos.cpu().numpy(), vel.cpu().numpy(), forces.cpu().numpy()))
     for a, b in zip(runs[0], runs[1]):
         assert np.array_equal(a, b)
