@@ -198,9 +198,10 @@ sn_status sn_energy_forces(const sn_model *model, const sn_system *sys, const fl
  * on the device, the capacity and row-length checks run there, and the
  * call synchronises once, at its end.  After the first error (for example
  * SN_ERR_CAPACITY, SN_ERR_ROW or SN_ERR_NONFINITE) no atom moves again and
- * every later neighbour list is empty; the call returns that error, with
- * *n_steps_done (host, may be NULL) = the steps completed before it; pos,
- * vel and forces then hold the state of the failing step, not a valid one. */
+ * the kernels that read a neighbour list do nothing; the call returns that
+ * error, with *n_steps_done (host, may be NULL) = the steps completed before
+ * it; pos, vel, forces and the neighbour-list outputs then hold the state of
+ * the failing step, not a valid one. */
 sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos, float *vel, float *forces,
                          const float *inv_mass, float dt, float force_to_accel, int32_t n_steps,
                          float r_list, int32_t *row_ptr, int32_t *col_idx, int32_t *rev_idx,

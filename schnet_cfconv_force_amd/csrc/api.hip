@@ -106,20 +106,18 @@ sn_status clear_status(void *ws, hipStream_t s) {
     return launch_status();
 }
 
-// v += dt/2 c F / m ; if drift: r += dt v.  Nothing moves once an error is
-// flagged; steps_done (if set) counts the completed steps, and edge_slot (if
-// set) receives the step's edge count.
-__global__ void verlet_kernel(int N, float *pos, float *vel, const float *forces, const float *inv_mass, float half_dt_c,
-                              float dt, int drift, int *status, int *edge_slot) {
+// The closing half kick of a step, v += dt/2 c F / m (the opening one and
+// the drift run in the neighbour build).  Nothing moves once an error is
+// flagged; otherwise the step is counted in kStepsDone.  edge_slot (if set)
+// receives the step's edge count.
+__global__ void half_kick_kernel(int N, float *vel, const float *forces, const float *inv_mass, float half_dt_c,
+                                 int *status, int *edge_slot) {
     int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (edge_slot && idx == 0) *edge_slot = status[kEdgeTotal];
     if (*status != 0) return;
-    if (!drift && idx == 0) status[kStepsDone] += 1;
+    if (idx == 0) status[kStepsDone] += 1;
     if (idx >= 3 * N) return;
-    int i = idx / 3;
-    float v = vel[idx] + half_dt_c * forces[idx] * inv_mass[i];
-    vel[idx] = v;
-    if (drift) pos[idx] += dt * v;
+    vel[idx] += half_dt_c * forces[idx] * inv_mass[idx / 3];
 }
 
 __global__ __launch_bounds__(256) void kinetic_kernel(const int32_t *rptr, const float *vel, const float *inv_mass,
@@ -222,10 +220,13 @@ sn_status stream_wait(hipEvent_t e, hipStream_t from, hipStream_t to) {
 // The pipeline itself; arguments already checked, status not cleared.
 // device_edges: E is only the edge capacity (workspace layout and launch
 // sizes); the edge and pair counts are taken on the device (row_ptr[N]), so
-// nothing is read back to the host.
+// nothing is read back to the host, and the kernels that read the CSR do
+// nothing once an error is flagged (the neighbour build may then have left
+// the rows unfilled).  packed: the weight pack in the workspace is current
+// (written by filter_pack and mlp_pack since the weights last changed).
 sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const float *pos, const int32_t *row_ptr,
                              const int32_t *col, const int32_t *rev, int64_t E, float *energy, float *forces,
-                             char *ws, hipStream_t s, bool device_edges = false) {
+                             char *ws, hipStream_t s, bool device_edges = false, bool packed = false) {
     const int N = sys.n_atoms, B = sys.n_replicas, F = m.n_features, I = m.n_interactions;
     const int64_t P = E / 2;
     int *status = reinterpret_cast<int *>(ws);
@@ -268,6 +269,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     hipEvent_t *ev = ax.ev;
     char *pack = ws + L.pack;
     const int *p_dev = status + kPairTotal;   // the pair count, written by the pair setup
+    const int *guard = device_edges ? status : nullptr;
     auto pk = [&](int t, int kind) { return pack_ref(pack, I, pack_slot(t, kind)); };
     auto pr = [&](int k) { return pack_ref(pack, I, pack_readout_slot(I, k)); };
 
@@ -275,10 +277,12 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
         // the weight pack: the filter's part on the auxiliary stream (after
         // the caller's earlier work), beside the atom-wise part and the pair
         // setup on the caller's stream
-        SN_TRY(stream_wait(ev[3 + 2 * I], s, s2));
-        SN_TRY(filter_pack(m, pack, s2));
-        SN_TRY(mlp_pack(m, pack, s));
-        SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, device_edges ? -1 : E, m.cutoff, ws, L, status, s));
+        if (!packed) {
+            SN_TRY(stream_wait(ev[3 + 2 * I], s, s2));
+            SN_TRY(filter_pack(m, pack, s2));
+            SN_TRY(mlp_pack(m, pack, s));
+        }
+        SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, device_edges ? -1 : E, m.cutoff, ws, L, status, guard, s));
         SN_TRY(stream_wait(ev[0], s, s2));
         SN_TRY(filter_forward(m, 0, pgeo, P, phi_t(0), pack, p_dev, s2));
         if (s2 != s && hipEventRecord(ev[1], s2) != hipSuccess) return SN_ERR_HIP;
@@ -286,7 +290,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
         SN_TRY(mlp_x(N, F, h, pk(0, PK_XW), x_t(0), xmax_t(0), s));
         for (int t = 0; t < I; ++t) {
             if (s2 != s && hipStreamWaitEvent(s, ev[1 + t], 0) != hipSuccess) return SN_ERR_HIP;
-            SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, s));
+            SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, guard, s));
             if (t + 1 < I) {
                 // the next filter rows are written only after this CFConv has
                 // read phi_t: one interaction's rows (24-bit, about 200 MB for
@@ -309,7 +313,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
             SN_TRY(filter_backward(m, t, pgeo, pfc, pdfc, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
                                    t != I - 1, pack, p_dev, s2));
             if (t > 0) {   // dE/dh below the first block is not needed for forces
-                SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, s));
+                SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, guard, s));
                 SN_TRY(mlp_bwd_x(N, F, y, pk(t, PK_BXW), gh, s));
             }
         }
@@ -321,7 +325,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     const sn_status js = stream_wait(ev[2 + 2 * I], s2, s);
     SN_TRY(st);
     SN_TRY(js);
-    return forces_rows(N, row_ptr, col, edge_pair, pgeo, S, forces, status, s);
+    return forces_rows(N, row_ptr, col, edge_pair, pgeo, S, forces, status, guard, s);
 }
 
 }  // namespace
@@ -462,24 +466,30 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
     const float half = 0.5f * dt * force_to_accel;
     // no host synchronisation inside the loop: the neighbour build and the
     // pipeline take the edge and pair counts on the device, errors are
-    // flagged in the status word (after which nothing moves and every later
-    // neighbour list is empty), and the counters are read once at the end
-    float *eps_scratch = reinterpret_cast<float *>(w + ef_layout(*model, *sys, capacity, kWsBase).eps) + N;
+    // flagged in the status word (after which nothing moves and the kernels
+    // that read the neighbour list do nothing), and the counters are read
+    // once at the end
+    const EfLayout L = ef_layout(*model, *sys, capacity, kWsBase);
+    float *eps_scratch = reinterpret_cast<float *>(w + L.eps) + N;
+    // the weights do not change during the call: one weight pack serves every
+    // step, unless the neighbour build's scratch reaches into it
+    const bool pack_once = nb_layout(*sys, kWsBase).total <= L.pack;
+    if (pack_once) {
+        SN_TRY(filter_pack(*model, w + L.pack, s));
+        SN_TRY(mlp_pack(*model, w + L.pack, s));
+    }
+    // the first half kick and the drift run inside the neighbour build's first kernel
+    const KickArgs kick{vel, forces, inv_mass, half, dt};
     for (int32_t step = 0; step < n_steps; ++step) {
-        if (N > 0) {
-            ProfScope ps(K_VERLET, s);
-            verlet_kernel<<<(3 * N + 255) / 256, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, 1, status,
-                                                              nullptr);
-            SN_TRY(launch_status());
-        }
         int64_t E_unused = 0;
-        SN_TRY(nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, &E_unused, w, s, false));
+        SN_TRY(nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, &E_unused, w, s, false, &kick));
         float *eout = epot_log ? epot_log + (int64_t)step * B : eps_scratch;
-        SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, capacity, eout, forces, w, s, true));
+        SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, capacity, eout, forces, w, s, true,
+                                  pack_once));
         {
             ProfScope ps(K_VERLET, s);
-            verlet_kernel<<<(3 * N + 255) / 256 + 1, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, 0, status,
-                                                                  edge_log ? edge_log + step : nullptr);
+            half_kick_kernel<<<(3 * N + 255) / 256 + 1, 256, 0, s>>>(N, vel, forces, inv_mass, half, status,
+                                                                     edge_log ? edge_log + step : nullptr);
             SN_TRY(launch_status());
         }
         if (ekin_log) {

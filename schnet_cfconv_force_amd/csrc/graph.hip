@@ -27,9 +27,13 @@ constexpr float kPi = 3.14159265358979323846f;
 
 // thread per row: first upper edge and number of upper edges
 __global__ void pair_count_kernel(int N, const int32_t *row_ptr, const int32_t *col, int32_t *up_first,
-                                  int32_t *up_cnt) {
+                                  int32_t *up_cnt, const int *guard) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= N) return;
+    if (guard && *guard) {               // the pair count is then 0: nothing reads these
+        up_cnt[i] = 0;
+        return;
+    }
     int lo = row_ptr[i], hi = row_ptr[i + 1];
     const int end = hi;
     while (lo < hi) {                     // first e with col[e] > i
@@ -53,14 +57,15 @@ struct PairArgs {
     float cutoff;
     int64_t E;
     int *status;
+    const int *guard;
 };
 
 // one wavefront per row: pair index of every edge; geometry of upper edges
 __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
     const int lane = threadIdx.x % 64;
     const int i = blockIdx.x * 4 + threadIdx.x / 64;
-    if (i >= a.N) return;
-    const int64_t P = a.status[kPairTotal];   // written by pair_check_kernel
+    if (i >= a.N || (a.guard && *a.guard)) return;
+    const int64_t P = a.status[kPairTotal];   // written by the pair count check
     const int e0 = a.row_ptr[i], e1 = a.row_ptr[i + 1];
     const int uf = a.up_first[i], up = a.up_ptr[i];
     const float xi = a.pos[3 * i], yi = a.pos[3 * i + 1], zi = a.pos[3 * i + 2];
@@ -115,16 +120,6 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
     }
 }
 
-// The pair count is E / 2 (E from the host, or row_ptr[N] when E < 0) and
-// must equal the number of upper edges; it goes to the status slot
-// kPairTotal, or 0 if the check fails.
-__global__ void pair_check_kernel(const int32_t *up_ptr, const int32_t *row_ptr, int N, int64_t E, int *status) {
-    const int64_t P = (E >= 0 ? E : (int64_t)row_ptr[N]) / 2;
-    const bool ok = up_ptr[N] == P;
-    if (!ok) flag_status(status, SN_ERR_INVALID);
-    status[kPairTotal] = ok ? (int)P : 0;
-}
-
 // y_i = sum_{e in row i} pfc[p] * phi[p] (.) in[col(e)], phi in the 24-bit
 // row format (three words per four features).  One wavefront per
 // row: F/4 lanes cover the features (one float4 each) and the 64/(F/4) lane
@@ -133,7 +128,8 @@ __global__ void pair_check_kernel(const int32_t *up_ptr, const int32_t *row_ptr,
 template <int F>
 __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const int32_t *row_ptr,
                                                      const int32_t *col, const int32_t *edge_pair, const float *pfc,
-                                                     const uint32_t *phi24, const float *in, float *out) {
+                                                     const uint32_t *phi24, const float *in, float *out,
+                                                     const int *guard) {
     constexpr int LPR = F / 4;            // lanes per feature row
     constexpr int G = 64 / LPR;           // edges in flight per wavefront
     const int lane = threadIdx.x % 64;
@@ -141,7 +137,7 @@ __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const i
     const int blk = xcd_block(nblocks);
     if (blk < 0) return;
     const int row = blk * 4 + threadIdx.x / 64;
-    if (row >= N) return;                 // whole wavefront leaves together
+    if (row >= N || (guard && *guard)) return;   // whole wavefront leaves together
     const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int eb = e0; eb < e1; eb += 64) {
@@ -188,10 +184,10 @@ __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const i
 // F_i = sum_{e in row i} S[p(e)] * u_e, 16 lanes per row
 __global__ __launch_bounds__(256) void forces_kernel(int N, const int32_t *row_ptr, const int32_t *col,
                                                      const int32_t *edge_pair, const float4 *pgeo, const float *S,
-                                                     float *forces, int *status) {
+                                                     float *forces, int *status, const int *guard) {
     const int sub = threadIdx.x % 16;
     const int i = (blockIdx.x * 256 + threadIdx.x) / 16;
-    if (i >= N) return;
+    if (i >= N || (guard && *guard)) return;
     const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
     float fx = 0.f, fy = 0.f, fz = 0.f;
     for (int e = e0 + sub; e < e1; e += 16) {
@@ -219,17 +215,15 @@ __global__ __launch_bounds__(256) void forces_kernel(int N, const int32_t *row_p
 
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
                       const int32_t *rev, int64_t E, float cutoff, char *ws, const EfLayout &L, int *status,
-                      hipStream_t s) {
+                      const int *guard, hipStream_t s) {
     const int N = sys.n_atoms;
     ProfScope ps(K_PAIRS, s);
     int32_t *up_first = reinterpret_cast<int32_t *>(ws + L.up_first);
     int32_t *up_cnt = reinterpret_cast<int32_t *>(ws + L.up_cnt);
     int32_t *up_ptr = reinterpret_cast<int32_t *>(ws + L.up_ptr);
-    pair_count_kernel<<<(N + 255) / 256, 256, 0, s>>>(N, row_ptr, col, up_first, up_cnt);
+    pair_count_kernel<<<(N + 255) / 256, 256, 0, s>>>(N, row_ptr, col, up_first, up_cnt, guard);
     SN_TRY(launch_status());
-    SN_TRY(scan_exclusive(up_cnt, up_ptr, N, nullptr, nullptr, s));
-    pair_check_kernel<<<1, 1, 0, s>>>(up_ptr, row_ptr, N, E, status);
-    SN_TRY(launch_status());
+    SN_TRY(scan_exclusive(up_cnt, up_ptr, N, nullptr, nullptr, s, PairCountCheck{status, row_ptr, N, E, guard != nullptr}));
     PairArgs a;
     a.N = N;
     a.row_ptr = row_ptr; a.col = col; a.rev = rev; a.up_first = up_first; a.up_ptr = up_ptr;
@@ -247,28 +241,31 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
     a.cutoff = cutoff;
     a.E = E;
     a.status = status;
+    a.guard = guard;
     pair_fill_kernel<<<(N + 3) / 4, 256, 0, s>>>(a);
     return launch_status();
 }
 
 sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
-                 const float *pfc, const uint32_t *phi24, const float *in, float *out, hipStream_t s) {
+                 const float *pfc, const uint32_t *phi24, const float *in, float *out, const int *guard,
+                 hipStream_t s) {
     ProfScope ps(K_CFCONV, s);
     const int nb = (N + 3) / 4;          // four rows (wavefronts) per block
     const int grid = xcd_grid(nb);
     switch (F) {
-        case 32: cfconv_kernel<32><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out); break;
-        case 64: cfconv_kernel<64><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out); break;
-        case 128: cfconv_kernel<128><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out); break;
+        case 32: cfconv_kernel<32><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out, guard); break;
+        case 64: cfconv_kernel<64><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out, guard); break;
+        case 128: cfconv_kernel<128><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out, guard); break;
         default: return SN_ERR_INVALID;
     }
     return launch_status();
 }
 
 sn_status forces_rows(int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
-                      const float4 *pgeo, const float *S, float *forces, int *status, hipStream_t s) {
+                      const float4 *pgeo, const float *S, float *forces, int *status, const int *guard,
+                      hipStream_t s) {
     ProfScope ps(K_FORCES, s);
-    forces_kernel<<<(N + 15) / 16, 256, 0, s>>>(N, row_ptr, col, edge_pair, pgeo, S, forces, status);
+    forces_kernel<<<(N + 15) / 16, 256, 0, s>>>(N, row_ptr, col, edge_pair, pgeo, S, forces, status, guard);
     return launch_status();
 }
 

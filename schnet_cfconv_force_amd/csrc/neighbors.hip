@@ -43,13 +43,38 @@ __global__ void fill_int_kernel(int *p, int v, int64_t n) {
     if (i < n) p[i] = v;
 }
 
-// One block per replica: atom -> replica map, bounding box, cell grid.
-__global__ __launch_bounds__(256) void grid_kernel(const float *pos, const int32_t *rptr, int periodic,
-                                                   PredParams pp, float cell_edge, CellGrid *grid,
-                                                   int *rep_of, int *status) {
+// One block per replica: atom -> replica map, bounding box, cell grid.  It
+// also clears the replica's slice of the cell counters (cells [8 s + 64 b,
+// 8 e + 64 (b + 1)) belong to replica b; the last block clears the final
+// entry) and the builder's status slots, and, when `kick` is set and no
+// error is flagged, first applies the integrator's half kick and drift to
+// the replica's atoms (v += kick->half F / m; r += kick->dt v).
+__global__ __launch_bounds__(256) void grid_kernel(float *pos, const int32_t *rptr, int periodic, PredParams pp,
+                                                   float cell_edge, CellGrid *grid, int *rep_of, int *cell_cnt,
+                                                   int *cell_fill, int64_t n_cells, KickArgs kick, int *status) {
     __shared__ float red[6][256];
     const int b = blockIdx.x;
     const int s = rptr[b], e = rptr[b + 1];
+    for (int64_t c = 8 * (int64_t)s + 64 * b + threadIdx.x; c < 8 * (int64_t)e + 64 * (b + 1); c += blockDim.x) {
+        cell_cnt[c] = 0;
+        cell_fill[c] = 0;
+    }
+    if (b == gridDim.x - 1 && threadIdx.x == 0) {
+        cell_cnt[n_cells] = 0;
+        cell_fill[n_cells] = 0;
+    }
+    if (b == 0 && threadIdx.x == 0) {
+        status[kMaxRow] = 0;
+        status[kEdgeTotal] = 0;
+    }
+    if (kick.vel && *status == 0) {
+        for (int k = 3 * s + threadIdx.x; k < 3 * e; k += blockDim.x) {
+            const float v = kick.vel[k] + kick.half * kick.forces[k] * kick.inv_mass[k / 3];
+            kick.vel[k] = v;
+            pos[k] += kick.dt * v;
+        }
+        __syncthreads();   // the positions below are read by other threads of the block
+    }
     float lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
     bool bad = false;
     for (int i = s + threadIdx.x; i < e; i += blockDim.x) {
@@ -261,18 +286,12 @@ __global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos
     }
 }
 
-// After a flagged error: an empty CSR (every row_ptr entry zero).
-__global__ void csr_guard_kernel(int32_t *row_ptr, int n_atoms, const int *status) {
-    if (*status == 0) return;
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= n_atoms; i += gridDim.x * blockDim.x) row_ptr[i] = 0;
-}
-
 // One wavefront per row: rev[e] = index of (j, i) in row j.
 __global__ __launch_bounds__(256) void rev_kernel(int n_atoms, const int32_t *row_ptr, const int32_t *col,
                                                   int32_t *rev, int *status) {
     const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int i = blockIdx.x * 4 + wv;
-    if (i >= n_atoms) return;
+    if (i >= n_atoms || *status != 0) return;   // after an error the rows may not be filled
     const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
     for (int e = e0 + lane; e < e1; e += kWave) {
         const int j = col[e];
@@ -343,7 +362,8 @@ __device__ inline void load4(const int32_t *in, int n, int64_t b, int v[4]) {
 // writes out[n] (the total) and the optional total and maximum slots.  in and
 // out must not overlap; in must be 16-byte aligned.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t *in, int32_t *out, int n,
-                                                            int32_t *total_slot, int32_t *max_slot) {
+                                                            int32_t *total_slot, int32_t *max_slot,
+                                                            PairCountCheck chk) {
     __shared__ int s_w[kScanThreads / 64];
     const int64_t t0 = (int64_t)blockIdx.x * kScanTile;   // a multiple of 4 * kScanThreads
     const bool last = blockIdx.x == gridDim.x - 1;
@@ -370,6 +390,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t *in, i
             out[n] = before + tot;
             if (total_slot) *total_slot = before + tot;
             if (max_slot) *max_slot = m;
+            if (chk.status) {
+                const int64_t P = (chk.E >= 0 ? chk.E : (int64_t)chk.row_ptr[chk.N]) / 2;
+                const bool flagged = chk.guard && chk.status[kStatusWord] != 0;
+                const bool ok = !flagged && before + tot == P;
+                if (!ok && !flagged) flag_status(chk.status, SN_ERR_INVALID);
+                chk.status[kPairTotal] = ok ? (int)P : 0;
+            }
         }
     }
 }
@@ -377,11 +404,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t *in, i
 }  // namespace
 
 sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
-                         hipStream_t s) {
+                         hipStream_t s, PairCountCheck chk) {
     ProfScope ps(K_NB_SCAN, s);
     if (n < 0 || in == out) return SN_ERR_INVALID;
     const int ntiles = n > 0 ? (n + kScanTile - 1) / kScanTile : 1;
-    scan_kernel<<<ntiles, kScanThreads, 0, s>>>(in, out, n, total_slot, max_slot);
+    scan_kernel<<<ntiles, kScanThreads, 0, s>>>(in, out, n, total_slot, max_slot, chk);
     return launch_status();
 }
 
@@ -418,7 +445,8 @@ static int *pinned_counters() {
 }
 
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
-                   int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync) {
+                   int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync,
+                   const KickArgs *kick) {
     const int N = sys.n_atoms, B = sys.n_replicas;
     int *status = reinterpret_cast<int *>(ws);
     PredParams pp;
@@ -447,17 +475,15 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
 
     // reset the counters but keep the status word: an error flagged by earlier
     // work on this workspace (e.g. a non-finite force) is reported below
-    SN_TRY(fill_int(status + kMaxRow, 0, 2, s));   // kMaxRow, kEdgeTotal
     if (N == 0) {
         SN_TRY(fill_int(row_ptr, 0, 1, s));
         *n_edges = 0;
         return SN_OK;
     }
-    SN_TRY(fill_int(cell_cnt, 0, L.n_cells + 1, s));
-    SN_TRY(fill_int(cell_fill, 0, L.n_cells + 1, s));
     {
         ProfScope ps(K_NB_GRID, s);
-        grid_kernel<<<B, 256, 0, s>>>(pos, sys.replica_ptr, pp.periodic, pp, cell_edge, grid, rep_of, status);
+        grid_kernel<<<B, 256, 0, s>>>(const_cast<float *>(pos), sys.replica_ptr, pp.periodic, pp, cell_edge, grid,
+                                      rep_of, cell_cnt, cell_fill, L.n_cells, kick ? *kick : KickArgs{}, status);
         SN_TRY(launch_status());
     }
     {
@@ -496,10 +522,6 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         rows_kernel<true><<<blocks, kWave * kNbWaves, 0, s>>>(pos, N, grid, rep_of, cell_start, spos, pp, nullptr,
                                                               row_ptr, col, capacity, status);
         SN_TRY(launch_status());
-        if (!sync) {
-            csr_guard_kernel<<<(N + 256) / 256, 256, 0, s>>>(row_ptr, N, status);
-            SN_TRY(launch_status());
-        }
     }
     {
         ProfScope ps(K_NB_REV, s);

@@ -188,17 +188,38 @@ struct CellGrid {
 // --------------------------------------------------------------- launchers
 
 // neighbors.hip
+// The integrator's first half kick and drift, applied by the neighbour
+// build's first kernel (vel == nullptr: none).
+struct KickArgs {
+    float *vel;
+    const float *forces, *inv_mass;
+    float half, dt;
+};
 // sync: read the edge count back (into *n_edges) and check it on the host
 // before the rows are filled.  Otherwise nothing is read back: the fill
-// checks the capacity and row lengths on the device, and after any flagged
-// error the CSR is left empty (row_ptr all zero) so that later kernels stay
-// in bounds.
+// checks the capacity and row lengths on the device and flags errors; every
+// kernel that reads the CSR afterwards returns at once when the status word
+// is set (the rows may then be unfilled).  kick (optional): see KickArgs;
+// pos is then updated in place.
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
-                   int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync = true);
+                   int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync = true,
+                   const KickArgs *kick = nullptr);
+// Check run by the scan's last block once the total is known: the pair
+// count is E / 2 (E >= 0), or row_ptr[N] / 2 (E < 0), and must equal the
+// total (the number of upper edges).  status[kPairTotal] receives it, or 0
+// when the check fails (flagged SN_ERR_INVALID) or when `guard` is set and
+// an error is already flagged.
+struct PairCountCheck {
+    int *status;                 // null: no check
+    const int32_t *row_ptr;
+    int N;
+    int64_t E;
+    bool guard;
+};
 // Exclusive prefix sum (one launch); out[n] = total; optional device slots
 // receive the total and the maximum input.  in and out must not overlap.
 sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
-                         hipStream_t s);
+                         hipStream_t s, PairCountCheck chk = PairCountCheck{});
 
 // filter.hip
 // Writes the filter slots of the weight pack (all interactions).
@@ -219,14 +240,19 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
 // graph.hip
 // E: the edge count, or -1 to take it from row_ptr[N] on the device.  Writes
 // the pair count to the status slot kPairTotal (0 after a failed check).
+// guard (here and below; may be null): the kernels return at once while
+// *guard is non-zero, for a CSR that a flagged neighbour build may have left
+// unfilled (the pair count is then 0).
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
                       const int32_t *rev, int64_t E, float cutoff, char *ws, const EfLayout &L, int *status,
-                      hipStream_t s);
+                      const int *guard, hipStream_t s);
 // phi24: the filter rows in the 24-bit row format
 sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
-                 const float *pfc, const uint32_t *phi24, const float *in, float *out, hipStream_t s);
+                 const float *pfc, const uint32_t *phi24, const float *in, float *out, const int *guard,
+                 hipStream_t s);
 sn_status forces_rows(int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
-                      const float4 *pgeo, const float *S, float *forces, int *status, hipStream_t s);
+                      const float4 *pgeo, const float *S, float *forces, int *status, const int *guard,
+                      hipStream_t s);
 
 // atomwise.hip
 sn_status embed(int N, int F, int T, const int32_t *types, const float *emb, float *h, int *status,
