@@ -91,6 +91,8 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     L.xmax = take(4 * I * N);
     L.gmax = take(4 * I * N);
     L.pack = take(pack_bytes((int)I));
+    L.rep = take(8 * kTileMaxSplit * B);   // the tile neighbour build's per-block counts
+    L.mask = take(8 * (kRepMaxAtoms / 64) * N);   // and its row masks
     L.total = o;
     return L;
 }
@@ -106,18 +108,27 @@ sn_status clear_status(void *ws, hipStream_t s) {
     return launch_status();
 }
 
-// The closing half kick of a step, v += dt/2 c F / m (the opening one and
-// the drift run in the neighbour build).  Nothing moves once an error is
-// flagged; otherwise the step is counted in kStepsDone.  edge_slot (if set)
-// receives the step's edge count.
-__global__ void half_kick_kernel(int N, float *vel, const float *forces, const float *inv_mass, float half_dt_c,
-                                 int *status, int *edge_slot) {
-    int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (edge_slot && idx == 0) *edge_slot = status[kEdgeTotal];
+// Velocity Verlet around a force evaluation.  close: the step's closing
+// half kick v += dt/2 c F / m, the step counted in kStepsDone and its edge
+// count written to edge_slot (if set).  open: the next step's opening half
+// kick with the same forces, then the drift r += dt v.  Both in one launch
+// give the same bits as one after the other.  Nothing moves once an error is
+// flagged.
+__global__ void verlet_kernel(int N, float *pos, float *vel, const float *forces, const float *inv_mass,
+                              float half_dt_c, float dt, int close, int open, int *status, int *edge_slot) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (close && edge_slot && idx == 0) *edge_slot = status[kEdgeTotal];
     if (*status != 0) return;
-    if (idx == 0) status[kStepsDone] += 1;
+    if (close && idx == 0) status[kStepsDone] += 1;
     if (idx >= 3 * N) return;
-    vel[idx] += half_dt_c * forces[idx] * inv_mass[idx / 3];
+    const float a = forces[idx], im = inv_mass[idx / 3];
+    float v = vel[idx];
+    if (close) v = v + half_dt_c * a * im;
+    if (open) {
+        v = v + half_dt_c * a * im;
+        pos[idx] += dt * v;
+    }
+    vel[idx] = v;
 }
 
 __global__ __launch_bounds__(256) void kinetic_kernel(const int32_t *rptr, const float *vel, const float *inv_mass,
@@ -224,9 +235,11 @@ sn_status stream_wait(hipEvent_t e, hipStream_t from, hipStream_t to) {
 // nothing once an error is flagged (the neighbour build may then have left
 // the rows unfilled).  packed: the weight pack in the workspace is current
 // (written by filter_pack and mlp_pack since the weights last changed).
+// pairs_ready: the neighbour build has written the pair arrays and count.
 sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const float *pos, const int32_t *row_ptr,
                              const int32_t *col, const int32_t *rev, int64_t E, float *energy, float *forces,
-                             char *ws, hipStream_t s, bool device_edges = false, bool packed = false) {
+                             char *ws, hipStream_t s, bool device_edges = false, bool packed = false,
+                             bool pairs_ready = false) {
     const int N = sys.n_atoms, B = sys.n_replicas, F = m.n_features, I = m.n_interactions;
     const int64_t P = E / 2;
     int *status = reinterpret_cast<int *>(ws);
@@ -282,9 +295,10 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
             SN_TRY(filter_pack(m, pack, s2));
             SN_TRY(mlp_pack(m, pack, s));
         }
-        SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, device_edges ? -1 : E, m.cutoff, ws, L, status, guard, s));
+        if (!pairs_ready)
+            SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, device_edges ? -1 : E, m.cutoff, ws, L, status, guard, s));
         SN_TRY(stream_wait(ev[0], s, s2));
-        SN_TRY(filter_forward(m, 0, pgeo, P, phi_t(0), pack, p_dev, s2));
+        SN_TRY(filter_forward(m, 0, pgeo, P, phi_t(0), pack, p_dev, guard, s2));
         if (s2 != s && hipEventRecord(ev[1], s2) != hipSuccess) return SN_ERR_HIP;
         SN_TRY(embed(N, F, m.n_types, sys.types, prm + off[0], h, status, s));
         SN_TRY(mlp_x(N, F, h, pk(0, PK_XW), x_t(0), xmax_t(0), s));
@@ -297,7 +311,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
                 // 64 replicas) then stay in the Infinity Cache from their write
                 // to their read
                 SN_TRY(stream_wait(ev[4 + 2 * I + t], s, s2));
-                SN_TRY(filter_forward(m, t + 1, pgeo, P, phi_t(t + 1), pack, p_dev, s2));
+                SN_TRY(filter_forward(m, t + 1, pgeo, P, phi_t(t + 1), pack, p_dev, guard, s2));
                 if (s2 != s && hipEventRecord(ev[2 + t], s2) != hipSuccess) return SN_ERR_HIP;
             }
             SN_TRY(mlp_out(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), o_t(t), h, s));
@@ -311,7 +325,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
             SN_TRY(mlp_bwd_out(N, F, gh, pk(t, PK_BOW1), o_t(t), pk(t, PK_BOW2), gy_t(t), gmax_t(t), s));
             SN_TRY(stream_wait(ev[1 + I + t], s, s2));
             SN_TRY(filter_backward(m, t, pgeo, pfc, pdfc, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
-                                   t != I - 1, pack, p_dev, s2));
+                                   t != I - 1, pack, p_dev, guard, s2));
             if (t > 0) {   // dE/dh below the first block is not needed for forces
                 SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, guard, s));
                 SN_TRY(mlp_bwd_x(N, F, y, pk(t, PK_BXW), gh, s));
@@ -427,7 +441,9 @@ sn_status sn_build_csr_neighbors(const sn_system *sys, const float *pos, float r
     SN_TRY(check_ws(ws, ws_bytes, nb_layout(*sys, kWsBase).total));
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     SN_TRY(clear_status(ws, s));
-    return nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, n_edges, reinterpret_cast<char *>(ws), s);
+    const int max_rep = sys->n_atoms > 0 ? max_replica_atoms(*sys, s) : -1;
+    return nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, n_edges, reinterpret_cast<char *>(ws), s,
+                    true, max_rep);
 }
 
 sn_status sn_energy_forces(const sn_model *model, const sn_system *sys, const float *pos, const int32_t *row_ptr,
@@ -478,25 +494,45 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
         SN_TRY(filter_pack(*model, w + L.pack, s));
         SN_TRY(mlp_pack(*model, w + L.pack, s));
     }
-    // the first half kick and the drift run inside the neighbour build's first kernel
-    const KickArgs kick{vel, forces, inv_mass, half, dt};
+    // small replicas: the neighbour build also writes the pair arrays
+    const int max_rep = N > 0 && n_steps > 0 ? max_replica_atoms(*sys, s) : -1;
+    NbPairOut pairs;
+    pairs.edge_pair = reinterpret_cast<int32_t *>(w + L.edge_pair);
+    pairs.pair_ij = reinterpret_cast<int2 *>(w + L.pair_ij);
+    pairs.pgeo = reinterpret_cast<float4 *>(w + L.pgeo);
+    pairs.pfc = reinterpret_cast<float *>(w + L.pfc);
+    pairs.pdfc = reinterpret_cast<float *>(w + L.pdfc);
+    pairs.cutoff = model->cutoff;
+    pairs.mask = reinterpret_cast<uint64_t *>(w + L.mask);
+    pairs.rep = reinterpret_cast<int32_t *>(w + L.rep);
+    const unsigned vblocks = (3 * N + 255) / 256 + 1;   // one more: the step counter at N = 0
+    auto verlet = [&](int close, int open, int32_t step) -> sn_status {
+        ProfScope ps(K_VERLET, s);
+        verlet_kernel<<<vblocks, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, close, open, status,
+                                              edge_log && close ? edge_log + step : nullptr);
+        return launch_status();
+    };
+    // the first step's opening kick and drift; each later one runs with the
+    // previous step's closing kick (unless the kinetic energy is logged between)
+    if (n_steps > 0) SN_TRY(verlet(0, 1, 0));
     for (int32_t step = 0; step < n_steps; ++step) {
         int64_t E_unused = 0;
-        SN_TRY(nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, &E_unused, w, s, false, &kick));
+        bool pairs_done = false;
+        SN_TRY(nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, &E_unused, w, s, false, max_rep,
+                        &pairs, &pairs_done));
         float *eout = epot_log ? epot_log + (int64_t)step * B : eps_scratch;
         SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, capacity, eout, forces, w, s, true,
-                                  pack_once));
-        {
-            ProfScope ps(K_VERLET, s);
-            half_kick_kernel<<<(3 * N + 255) / 256 + 1, 256, 0, s>>>(N, vel, forces, inv_mass, half, status,
-                                                                     edge_log ? edge_log + step : nullptr);
-            SN_TRY(launch_status());
-        }
+                                  pack_once, pairs_done));
+        const int open_next = step + 1 < n_steps;
+        SN_TRY(verlet(1, open_next && !ekin_log, step));
         if (ekin_log) {
-            ProfScope ps(K_KINETIC, s);
-            kinetic_kernel<<<B, 256, 0, s>>>(sys->replica_ptr, vel, inv_mass, 0.5f / force_to_accel,
-                                             ekin_log + (int64_t)step * B);
-            SN_TRY(launch_status());
+            {
+                ProfScope ps(K_KINETIC, s);
+                kinetic_kernel<<<B, 256, 0, s>>>(sys->replica_ptr, vel, inv_mass, 0.5f / force_to_accel,
+                                                 ekin_log + (int64_t)step * B);
+                SN_TRY(launch_status());
+            }
+            if (open_next) SN_TRY(verlet(0, 1, step + 1));
         }
     }
     int host[kStepsDone + 1] = {};

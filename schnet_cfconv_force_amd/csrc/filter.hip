@@ -62,6 +62,7 @@ struct FilterArgs {
     int dstride, doff;
     int64_t P;                   // pair count, or the capacity when P_dev is set
     const int *P_dev;            // (may be null) the pair count on the device
+    const int *guard;            // (may be null) no pairs while *guard is non-zero
     float *phi;                  // forward output [P][F] (fp32), or
     uint32_t *phi24;             // forward output [P][3F/4] (the 24-bit row format)
     // backward
@@ -225,7 +226,7 @@ __device__ inline void mma_split2(const half8 *whi, const half8 *wlo, int stride
 
 template <int F>
 __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
-    const int64_t P = a.P_dev ? (int64_t)*a.P_dev : a.P;
+    const int64_t P = (a.guard && *a.guard) ? 0 : a.P_dev ? (int64_t)*a.P_dev : a.P;
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;                      // 32-wide k steps of the F x F GEMM
     constexpr int MG = MT < kFwdMG ? MT : kFwdMG;   // output tiles per group
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
 
 template <int F>
 __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
-    const int64_t P = a.P_dev ? (int64_t)*a.P_dev : a.P;
+    const int64_t P = (a.guard && *a.guard) ? 0 : a.P_dev ? (int64_t)*a.P_dev : a.P;
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;
     constexpr int MG = MT < kBwdMG ? MT : kBwdMG;
@@ -655,7 +656,7 @@ sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s) {
 }
 
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, uint32_t *phi24,
-                         const char *pack, const int *p_dev, hipStream_t s) {
+                         const char *pack, const int *p_dev, const int *guard, hipStream_t s) {
     FilterArgs a = make_args(m, t);
     attach_pack(a, m, t, pack, PK_FA2);
     a.dsrc = reinterpret_cast<const float *>(pgeo);
@@ -663,6 +664,7 @@ sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P
     a.doff = 3;
     a.P = P;
     a.P_dev = p_dev;
+    a.guard = guard;
     a.phi24 = phi24;
     return fwd_dispatch(a, m.n_features, s);
 }
@@ -680,7 +682,7 @@ sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
                           const int2 *pair_ij, int64_t P, int N, const uint32_t *phi24, const float *x, const float *gy,
                           const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
-                          const int *p_dev, hipStream_t s) {
+                          const int *p_dev, const int *guard, hipStream_t s) {
     if (P <= 0) return SN_OK;
     (void)N;
     FilterArgs a = make_args(m, t);
@@ -691,6 +693,7 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
     a.P = P;
     a.pair_ij = pair_ij;
     a.P_dev = p_dev;
+    a.guard = guard;
     a.fc = pfc;
     a.dfc = pdfc;
     a.x = x;

@@ -23,8 +23,6 @@ namespace sn {
 
 namespace {
 
-constexpr float kPi = 3.14159265358979323846f;
-
 // thread per row: first upper edge and number of upper edges
 __global__ void pair_count_kernel(int N, const int32_t *row_ptr, const int32_t *col, int32_t *up_first,
                                   int32_t *up_cnt, const int *guard) {
@@ -68,7 +66,6 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
     const int64_t P = a.status[kPairTotal];   // written by the pair count check
     const int e0 = a.row_ptr[i], e1 = a.row_ptr[i + 1];
     const int uf = a.up_first[i], up = a.up_ptr[i];
-    const float xi = a.pos[3 * i], yi = a.pos[3 * i + 1], zi = a.pos[3 * i + 2];
     for (int e = e0 + lane; e < e1; e += 64) {
         const int j = a.col[e];
         if (j < 0 || j >= a.N || j == i) {
@@ -85,24 +82,10 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
             }
             a.edge_pair[e] = p;
             a.pair_ij[p] = make_int2(i, j);
-            float dx = a.pos[3 * j] - xi, dy = a.pos[3 * j + 1] - yi, dz = a.pos[3 * j + 2] - zi;
-            if (a.periodic) {
-                dx -= a.L[0] * rintf(dx * a.invL[0]);
-                dy -= a.L[1] * rintf(dy * a.invL[1]);
-                dz -= a.L[2] * rintf(dz * a.invL[2]);
-            }
-            const float d = sqrtf(dx * dx + dy * dy + dz * dz);
-            const float inv = 1.0f / d;
-            a.pgeo[p] = make_float4(dx * inv, dy * inv, dz * inv, d);
-            float fc = 0.0f, dfc = 0.0f;
-            if (d < a.cutoff) {
-                // (cos(pi d/rc) + 1)/2 written as cos^2(pi d/(2 rc)): no cancellation near rc;
-                // its derivative -(pi/(2 rc)) sin(pi d/rc) = -(pi/rc) sin cos of the half angle
-                const float th = 0.5f * kPi * d / a.cutoff;
-                const float c = cosf(th);
-                fc = c * c;
-                dfc = -(kPi / a.cutoff) * sinf(th) * c;
-            }
+            float4 g;
+            float fc, dfc;
+            pair_geometry(a.pos + 3 * i, a.pos + 3 * j, a.periodic, a.L, a.invL, a.cutoff, g, fc, dfc);
+            a.pgeo[p] = g;
             a.pfc[p] = fc;
             a.pdfc[p] = dfc;
         } else {

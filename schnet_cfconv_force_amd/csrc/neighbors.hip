@@ -22,6 +22,9 @@
 // sorted rows do not, so the output is deterministic.
 #pragma clang fp contract(off)
 
+#include <algorithm>
+#include <vector>
+
 #include "sn_internal.h"
 
 namespace sn {
@@ -43,16 +46,88 @@ __global__ void fill_int_kernel(int *p, int v, int64_t n) {
     if (i < n) p[i] = v;
 }
 
+// The cell grid of one replica of n atoms from its bounding box lo..hi
+// (`bad`: some coordinate of the replica is not finite; the box is then
+// ignored).  At most 8 n + 64 cells, each edge at least cell_edge.
+__device__ inline CellGrid make_grid(const float (&lo)[3], const float (&hi)[3], bool bad, int n,
+                                     const PredParams &pp, float cell_edge, int offset) {
+    const long cap = 8L * n + 64;
+    CellGrid g;
+    if (pp.periodic) {
+        int m[3];
+        for (int c = 0; c < 3; ++c) m[c] = (int)floorf(pp.L[c] / cell_edge);
+        while ((long)m[0] * m[1] * m[2] > cap) {           // coarser cells for sparse replicas
+            int c = (m[0] >= m[1] && m[0] >= m[2]) ? 0 : (m[1] >= m[2] ? 1 : 2);
+            if (m[c] <= 3) break;
+            m[c] = max(3, (m[c] * 4) / 5);
+        }
+        for (int c = 0; c < 3; ++c) {
+            g.lo[c] = 0.0f;
+            g.n[c] = m[c];
+            g.inv[c] = (float)m[c] / pp.L[c];
+        }
+    } else {
+        const bool use = n > 0 && !bad;
+        float ext[3];
+        for (int c = 0; c < 3; ++c) {
+            ext[c] = use ? hi[c] - lo[c] : 0.0f;
+            if (!(ext[c] >= 0.0f && ext[c] <= 1.0e30f)) ext[c] = 0.0f;   // overflowed extent: one cell
+        }
+        float ce = cell_edge;
+        int m[3];
+        for (;;) {                       // ends: the extents are finite, and ce grows
+            for (int c = 0; c < 3; ++c) m[c] = (int)fminf(floorf(ext[c] / ce) + 1.0f, 1048576.0f);
+            if ((double)m[0] * m[1] * m[2] <= (double)cap) break;
+            ce *= 1.25f;
+        }
+        for (int c = 0; c < 3; ++c) {
+            g.lo[c] = use ? lo[c] : 0.0f;
+            g.n[c] = m[c];
+            g.inv[c] = 1.0f / ce;
+        }
+    }
+    g.offset = offset;
+    return g;
+}
+
+// Bounding box of atoms [s, e) over a block of NT threads: the result in
+// lo / hi of thread 0; the return value (every thread) tells whether any
+// coordinate is not finite.  red: 6 x (NT / 64) floats of LDS.
+template <int NT>
+__device__ inline bool block_bbox(const float *pos, int s, int e, float (*red)[NT / 64], float (&lo)[3],
+                                  float (&hi)[3]) {
+    const int lane = threadIdx.x % 64, wv = threadIdx.x / 64;
+    bool bad = false;
+    for (int c = 0; c < 3; ++c) { lo[c] = INFINITY; hi[c] = -INFINITY; }
+    for (int i = s + threadIdx.x; i < e; i += NT)
+        for (int c = 0; c < 3; ++c) {
+            const float v = pos[3 * i + c];
+            if (!isfinite(v)) bad = true;
+            lo[c] = fminf(lo[c], v);
+            hi[c] = fmaxf(hi[c], v);
+        }
+    for (int c = 0; c < 3; ++c)
+        for (int o = 32; o > 0; o >>= 1) {
+            lo[c] = fminf(lo[c], __shfl_xor(lo[c], o, 64));
+            hi[c] = fmaxf(hi[c], __shfl_xor(hi[c], o, 64));
+        }
+    if (lane == 0)
+        for (int c = 0; c < 3; ++c) { red[c][wv] = lo[c]; red[3 + c][wv] = hi[c]; }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0)
+        for (int w = 1; w < NT / 64; ++w)
+            for (int c = 0; c < 3; ++c) { lo[c] = fminf(lo[c], red[c][w]); hi[c] = fmaxf(hi[c], red[3 + c][w]); }
+    return bad;
+}
+
 // One block per replica: atom -> replica map, bounding box, cell grid.  It
 // also clears the replica's slice of the cell counters (cells [8 s + 64 b,
 // 8 e + 64 (b + 1)) belong to replica b; the last block clears the final
-// entry) and the builder's status slots, and, when `kick` is set and no
-// error is flagged, first applies the integrator's half kick and drift to
-// the replica's atoms (v += kick->half F / m; r += kick->dt v).
-__global__ __launch_bounds__(256) void grid_kernel(float *pos, const int32_t *rptr, int periodic, PredParams pp,
+// entry) and the builder's status slots.
+__global__ __launch_bounds__(256) void grid_kernel(const float *pos, const int32_t *rptr, PredParams pp,
                                                    float cell_edge, CellGrid *grid, int *rep_of, int *cell_cnt,
-                                                   int *cell_fill, int64_t n_cells, KickArgs kick, int *status) {
-    __shared__ float red[6][256];
+                                                   int *cell_fill, int64_t n_cells, int *status) {
+    __shared__ float red[6][4];
     const int b = blockIdx.x;
     const int s = rptr[b], e = rptr[b + 1];
     for (int64_t c = 8 * (int64_t)s + 64 * b + threadIdx.x; c < 8 * (int64_t)e + 64 * (b + 1); c += blockDim.x) {
@@ -67,71 +142,12 @@ __global__ __launch_bounds__(256) void grid_kernel(float *pos, const int32_t *rp
         status[kMaxRow] = 0;
         status[kEdgeTotal] = 0;
     }
-    if (kick.vel && *status == 0) {
-        for (int k = 3 * s + threadIdx.x; k < 3 * e; k += blockDim.x) {
-            const float v = kick.vel[k] + kick.half * kick.forces[k] * kick.inv_mass[k / 3];
-            kick.vel[k] = v;
-            pos[k] += kick.dt * v;
-        }
-        __syncthreads();   // the positions below are read by other threads of the block
-    }
-    float lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
-    bool bad = false;
-    for (int i = s + threadIdx.x; i < e; i += blockDim.x) {
-        rep_of[i] = b;
-        for (int c = 0; c < 3; ++c) {
-            float v = pos[3 * i + c];
-            if (!isfinite(v)) bad = true;
-            lo[c] = fminf(lo[c], v);
-            hi[c] = fmaxf(hi[c], v);
-        }
-    }
-    if (bad) flag_status(status, SN_ERR_NONFINITE);
-    for (int c = 0; c < 3; ++c) { red[c][threadIdx.x] = lo[c]; red[3 + c][threadIdx.x] = hi[c]; }
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w)
-            for (int c = 0; c < 3; ++c) {
-                red[c][threadIdx.x] = fminf(red[c][threadIdx.x], red[c][threadIdx.x + w]);
-                red[3 + c][threadIdx.x] = fmaxf(red[3 + c][threadIdx.x], red[3 + c][threadIdx.x + w]);
-            }
-        __syncthreads();
-    }
+    for (int i = s + threadIdx.x; i < e; i += 256) rep_of[i] = b;
+    float lo[3], hi[3];
+    const bool bad = block_bbox<256>(pos, s, e, red, lo, hi);
     if (threadIdx.x != 0) return;
-    const long cap = 8L * (e - s) + 64;
-    CellGrid g;
-    if (periodic) {
-        int n[3];
-        for (int c = 0; c < 3; ++c) n[c] = (int)floorf(pp.L[c] / cell_edge);
-        while ((long)n[0] * n[1] * n[2] > cap) {           // coarser cells for sparse replicas
-            int c = (n[0] >= n[1] && n[0] >= n[2]) ? 0 : (n[1] >= n[2] ? 1 : 2);
-            if (n[c] <= 3) break;
-            n[c] = max(3, (n[c] * 4) / 5);
-        }
-        for (int c = 0; c < 3; ++c) {
-            g.lo[c] = 0.0f;
-            g.n[c] = n[c];
-            g.inv[c] = (float)n[c] / pp.L[c];
-        }
-    } else {
-        float ce = cell_edge;
-        int n[3];
-        for (;;) {
-            for (int c = 0; c < 3; ++c) {
-                float ext = (e > s && !bad) ? red[3 + c][0] - red[c][0] : 0.0f;
-                n[c] = (int)fminf(floorf(ext / ce) + 1.0f, 1048576.0f);
-            }
-            if ((double)n[0] * n[1] * n[2] <= (double)cap) break;
-            ce *= 1.25f;
-        }
-        for (int c = 0; c < 3; ++c) {
-            g.lo[c] = (e > s && !bad) ? red[c][0] : 0.0f;
-            g.n[c] = n[c];
-            g.inv[c] = 1.0f / ce;
-        }
-    }
-    g.offset = 8 * s + 64 * b;
-    grid[b] = g;
+    if (bad) flag_status(status, SN_ERR_NONFINITE);
+    grid[b] = make_grid(lo, hi, bad, e - s, pp, cell_edge, 8 * s + 64 * b);
 }
 
 __device__ inline int cell_coord(float x, int c, const CellGrid &g, const PredParams &pp) {
@@ -401,6 +417,215 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t *in, i
     }
 }
 
+// ------------------------------------------------------------- tile build
+// Replicas of at most kRepMaxAtoms atoms: each block holds its replica's
+// positions in LDS and tests every ordered pair of its rows, 64 columns (one
+// wavefront ballot) at a time, so that each row's neighbours form a bit mask
+// over the replica's atoms.  A replica this small spans about three cells of
+// r_list per dimension, so cells would not thin out the candidates much; the
+// masks instead give everything else by population counts: a bit's position
+// in its row (sorted order for free), the reverse edge (the position of i in
+// row j), the first upper edge of a row and the pair numbers.  R blocks per
+// replica (R = split) share its rows; two launches:
+//   count  row masks -> mask; per block, edge count and longest row -> rep
+//   fill   offsets of the earlier blocks (from rep), row_ptr, col, rev and
+//          optionally the pair arrays (one pair per upper edge, numbered
+//          replica by replica and row by row, as the pair setup numbers them)
+// Each fill block reads the masks of its whole replica.  The predicate is
+// the cell-list path's, so both give the same CSR.
+
+constexpr int kTileThreads = kScanThreads;   // the block size block_exclusive assumes
+constexpr int kTileWaves = kTileThreads / kWave;
+constexpr int kTileWords = kRepMaxAtoms / 64;
+
+struct TileArgs {
+    const float *pos;
+    const int32_t *rptr;
+    int B, N, R;                 // R blocks per replica
+    PredParams pp;
+    uint64_t *mask;              // [N][kTileWords] row masks
+    int32_t *rep;                // [2 B R]: edge count, then longest row, per block
+    int32_t *row_ptr, *col, *rev;
+    int64_t capacity;
+    int flag;                    // flag SN_ERR_ROW / SN_ERR_CAPACITY in the status word
+    NbPairOut pr;                // pr.edge_pair null: no pair arrays
+    int *status;
+};
+
+__device__ inline uint64_t below_mask(int bit) { return (1ull << bit) - 1ull; }
+
+// The replica's positions into LDS (sp[3 q + c]); returns whether any is not
+// finite (block-wide, after a barrier).
+__device__ inline bool tile_positions(const float *pos, int s, int n, float *sp) {
+    bool bad = false;
+    for (int k = threadIdx.x; k < 3 * n; k += kTileThreads) {
+        const float v = pos[3 * (int64_t)s + k];
+        bad |= !isfinite(v);
+        sp[k] = v;
+    }
+    return __syncthreads_or(bad);
+}
+
+__global__ __launch_bounds__(kTileThreads) void tile_count_kernel(TileArgs a) {
+    __shared__ float sp[3 * kRepMaxAtoms];
+    __shared__ int s_sum, s_max;
+    const int b = blockIdx.x / a.R, part = blockIdx.x % a.R;
+    const int s = a.rptr[b], e = a.rptr[b + 1], n = e - s;
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    if (threadIdx.x == 0) {
+        s_sum = 0;
+        s_max = 0;
+    }
+    if (tile_positions(a.pos, s, n, sp)) {       // the fill pass sees the flag and writes nothing
+        if (threadIdx.x == 0) flag_status(a.status, SN_ERR_NONFINITE);
+        return;
+    }
+    const int W = (n + kWave - 1) / kWave;
+    const int per = (n + a.R - 1) / a.R, q0 = part * per, q1 = min(n, q0 + per);
+    int sum = 0, mx = 0;
+    for (int q = q0 + wv; q < q1; q += kTileWaves) {
+        const float xi = sp[3 * q], yi = sp[3 * q + 1], zi = sp[3 * q + 2];
+        uint64_t mine = 0;
+        int cnt = 0;
+#pragma unroll
+        for (int w = 0; w < kTileWords; ++w) {
+            if (w >= W) break;
+            const int j = kWave * w + lane, jj = j < n ? j : 0;
+            const float4 pj = make_float4(sp[3 * jj], sp[3 * jj + 1], sp[3 * jj + 2], 0.0f);
+            const bool pass = j < n && j != q && within(xi, yi, zi, pj, a.pp);
+            const uint64_t m = __ballot(pass);
+            cnt += __popcll(m);
+            if (lane == w) mine = m;
+        }
+        if (lane < W) a.mask[(int64_t)(s + q) * kTileWords + lane] = mine;
+        sum += cnt;
+        mx = max(mx, cnt);
+    }
+    if (lane == 0) {
+        atomicAdd(&s_sum, sum);
+        atomicMax(&s_max, mx);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        a.rep[blockIdx.x] = s_sum;
+        a.rep[a.B * a.R + blockIdx.x] = s_max;
+    }
+}
+
+__global__ __launch_bounds__(kTileThreads, 8) void tile_fill_kernel(TileArgs a) {
+    __shared__ uint64_t sm[kRepMaxAtoms][kTileWords];
+    __shared__ int wpre[kRepMaxAtoms][kTileWords];   // set bits of the row's earlier words
+    __shared__ int s_rptr[kRepMaxAtoms + 1], s_upf[kRepMaxAtoms], s_upp[kRepMaxAtoms];
+    __shared__ float sp[3 * kRepMaxAtoms];
+    __shared__ int s_sw[kTileWaves];
+    __shared__ unsigned long long s_before, s_total;
+    __shared__ int s_max, s_st;
+    const int b = blockIdx.x / a.R, part = blockIdx.x % a.R;
+    const int s = a.rptr[b], e = a.rptr[b + 1], n = e - s;
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int W = (n + kWave - 1) / kWave;
+    if (threadIdx.x == 0) {
+        s_before = 0;
+        s_total = 0;
+        s_max = 0;
+        s_st = *a.status;                         // read before this kernel flags anything
+    }
+    __syncthreads();
+    {
+        const int first = b * a.R;                // this replica's first block: "before" = earlier replicas
+        unsigned long long before = 0, total = 0;
+        int mx = 0;
+        for (int r = threadIdx.x; r < a.B * a.R; r += kTileThreads) {
+            const unsigned long long v = (unsigned)a.rep[r];
+            total += v;
+            if (r < first) before += v;
+            mx = max(mx, a.rep[a.B * a.R + r]);
+        }
+        if (total) atomicAdd(&s_total, total);
+        if (before) atomicAdd(&s_before, before);
+        if (mx) atomicMax(&s_max, mx);
+    }
+    __syncthreads();
+    if (s_st != 0) return;                        // uniform: nothing is written after an error
+    const int64_t before = (int64_t)s_before, total = (int64_t)s_total;
+    const int max_row = s_max;
+    const bool fail = max_row > SN_MAX_ROW || total > a.capacity || total > INT32_MAX;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.status[kEdgeTotal] = (int)min(total, (int64_t)INT32_MAX);
+        a.status[kMaxRow] = max_row;
+        if (a.flag && fail) flag_status(a.status, max_row > SN_MAX_ROW ? SN_ERR_ROW : SN_ERR_CAPACITY);
+        if (a.pr.edge_pair) a.status[kPairTotal] = fail ? 0 : (int)(total / 2);
+    }
+    for (int k = threadIdx.x; k < n * kTileWords; k += kTileThreads)
+        (&sm[0][0])[k] = a.mask[(int64_t)s * kTileWords + k];
+    for (int k = threadIdx.x; k < 3 * n; k += kTileThreads) sp[k] = a.pos[3 * (int64_t)s + k];
+    __syncthreads();
+    // per row (one thread each): prefix counts of the words, length, first upper edge
+    const int q = threadIdx.x;
+    int cnt = 0, upf = 0;
+    if (q < n) {
+        for (int w = 0; w < W; ++w) {
+            wpre[q][w] = cnt;
+            cnt += __popcll(sm[q][w]);
+        }
+        upf = wpre[q][q / kWave] + __popcll(sm[q][q / kWave] & below_mask(q % kWave));
+        s_upf[q] = upf;
+    }
+    int tot_edges, tot_upper;
+    const int pre = block_exclusive(cnt, s_sw, &tot_edges);
+    const int pup = block_exclusive(cnt - upf, s_sw, &tot_upper);
+    const int per = (n + a.R - 1) / a.R, q0 = part * per, q1 = min(n, q0 + per);
+    if (q < n) {
+        s_rptr[q] = pre;
+        s_upp[q] = pup;
+        if (q >= q0 && q < q1) a.row_ptr[s + q] = (int)(before + pre);
+    }
+    if (q == 0) s_rptr[n] = tot_edges;
+    if (blockIdx.x == gridDim.x - 1 && q == 0) a.row_ptr[a.N] = (int)min(total, (int64_t)INT32_MAX);
+    if (fail) return;                             // uniform
+    if (2 * tot_upper != tot_edges) {             // not symmetric: the pair numbering would not fit
+        if (q == 0) flag_status(a.status, SN_ERR_INVALID);
+        return;                                   // uniform
+    }
+    __syncthreads();
+
+    const int64_t pbase = before / 2;           // pairs of the earlier replicas
+    for (int r = q0 + wv; r < q1; r += kTileWaves) {
+        const int i = s + r;
+        const int64_t rbase = before + s_rptr[r];
+#pragma unroll
+        for (int w = 0; w < kTileWords; ++w) {
+            if (w >= W) break;
+            const uint64_t m = sm[r][w];
+            if (!((m >> lane) & 1ull)) continue;
+            const int c = kWave * w + lane;       // column, local index
+            const int k = wpre[r][w] + __popcll(m & below_mask(lane));
+            const int64_t ed = rbase + k;
+            a.col[ed] = s + c;
+            // position of r in row c (present when the predicate is symmetric)
+            const uint64_t mc = sm[c][r / kWave];
+            const int kc = wpre[c][r / kWave] + __popcll(mc & below_mask(r % kWave));
+            const bool sym = (mc >> (r % kWave)) & 1ull;
+            if (!sym) flag_status(a.status, SN_ERR_INVALID);
+            a.rev[ed] = sym ? (int)(before + s_rptr[c] + kc) : -1;
+            if (!a.pr.edge_pair) continue;
+            if (c > r) {
+                const int64_t p = pbase + s_upp[r] + (k - s_upf[r]);
+                a.pr.edge_pair[ed] = (int)p;
+                a.pr.pair_ij[p] = make_int2(i, s + c);
+                float4 g;
+                float fc, dfc;
+                pair_geometry(sp + 3 * r, sp + 3 * c, a.pp.periodic, a.pp.L, a.pp.invL, a.pr.cutoff, g, fc, dfc);
+                a.pr.pgeo[p] = g;
+                a.pr.pfc[p] = fc;
+                a.pr.pdfc[p] = dfc;
+            } else {
+                a.pr.edge_pair[ed] = sym ? (int)(pbase + s_upp[c] + (kc - s_upf[c])) : 0;
+            }
+        }
+    }
+}
+
 }  // namespace
 
 sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
@@ -431,8 +656,25 @@ NbLayout nb_layout(const sn_system &sys, size_t base) {
     L.cell_fill = o;  o = align256(o + 4 * (L.n_cells + 1));
     L.spos = o;       o = align256(o + 16 * N);
     L.row_cnt = o;    o = align256(o + 4 * N);
+    L.rep = o;        o = align256(o + 8 * kTileMaxSplit * B);
+    L.mask = o;       o = align256(o + 8 * kTileWords * N);
     L.total = o;
     return L;
+}
+
+int max_replica_atoms(const sn_system &sys, hipStream_t s) {
+    const int B = sys.n_replicas;
+    std::vector<int32_t> h((size_t)B + 1);
+    if (hipMemcpyAsync(h.data(), sys.replica_ptr, 4 * ((size_t)B + 1), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return -1;
+    if (h[0] != 0 || h[B] != sys.n_atoms) return -1;
+    int m = 0;
+    for (int b = 0; b < B; ++b) {
+        if (h[b + 1] < h[b]) return -1;
+        m = std::max(m, h[b + 1] - h[b]);
+    }
+    return m;
 }
 
 // Host-pinned landing slot for the counters read back once per build.
@@ -446,7 +688,8 @@ static int *pinned_counters() {
 
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
                    int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync,
-                   const KickArgs *kick) {
+                   int max_rep, const NbPairOut *pairs, bool *pairs_done) {
+    if (pairs_done) *pairs_done = false;
     const int N = sys.n_atoms, B = sys.n_replicas;
     int *status = reinterpret_cast<int *>(ws);
     PredParams pp;
@@ -480,10 +723,52 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         *n_edges = 0;
         return SN_OK;
     }
+    if (max_rep >= 0 && max_rep <= kRepMaxAtoms && B <= kRepMaxReplicas) {
+        TileArgs a;
+        a.pos = pos;
+        a.rptr = sys.replica_ptr;
+        a.B = B;
+        a.N = N;
+        // blocks per replica: about two per CU over the launch
+        a.R = std::min(kTileMaxSplit, std::max(1, (512 + B - 1) / B));
+        a.pp = pp;
+        a.mask = pairs ? pairs->mask : reinterpret_cast<uint64_t *>(ws + L.mask);
+        a.rep = pairs ? pairs->rep : reinterpret_cast<int32_t *>(ws + L.rep);
+        a.row_ptr = row_ptr;
+        a.col = col;
+        a.rev = rev;
+        a.capacity = capacity;
+        a.flag = sync ? 0 : 1;
+        a.pr = pairs ? *pairs : NbPairOut{};
+        a.status = status;
+        {
+            ProfScope ps(K_NB_COUNT, s);
+            tile_count_kernel<<<B * a.R, kTileThreads, 0, s>>>(a);
+            SN_TRY(launch_status());
+        }
+        {
+            ProfScope ps(K_NB_FILL, s);
+            tile_fill_kernel<<<B * a.R, kTileThreads, 0, s>>>(a);
+            SN_TRY(launch_status());
+        }
+        if (pairs_done) *pairs_done = pairs != nullptr;
+        if (sync) {
+            int *host = pinned_counters();
+            if (!host) return SN_ERR_HIP;
+            SN_HIP(hipMemcpyAsync(host, status, 4 * 4, hipMemcpyDeviceToHost, s));
+            SN_HIP(hipStreamSynchronize(s));
+            const int st = host[kStatusWord], max_row = host[kMaxRow];
+            *n_edges = host[kEdgeTotal];
+            if (st != 0) return st;
+            if (max_row > SN_MAX_ROW) return SN_ERR_ROW;
+            if (*n_edges > capacity) return SN_ERR_CAPACITY;
+        }
+        return SN_OK;
+    }
     {
         ProfScope ps(K_NB_GRID, s);
-        grid_kernel<<<B, 256, 0, s>>>(const_cast<float *>(pos), sys.replica_ptr, pp.periodic, pp, cell_edge, grid,
-                                      rep_of, cell_cnt, cell_fill, L.n_cells, kick ? *kick : KickArgs{}, status);
+        grid_kernel<<<B, 256, 0, s>>>(pos, sys.replica_ptr, pp, cell_edge, grid, rep_of, cell_cnt, cell_fill,
+                                      L.n_cells, status);
         SN_TRY(launch_status());
     }
     {

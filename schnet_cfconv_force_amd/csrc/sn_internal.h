@@ -128,13 +128,13 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t kWsBase = 256;
 
 struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
-    size_t grid, rep_of, cell_of, cell_cnt, cell_start, cell_fill, spos, row_cnt, total;
+    size_t grid, rep_of, cell_of, cell_cnt, cell_start, cell_fill, spos, row_cnt, rep, mask, total;
     int64_t n_cells;         // capacity of the cell table
 };
 
 struct EfLayout {            // energy/force scratch (offsets from ws base)
     size_t up_first, up_cnt, up_ptr, edge_pair, pair_ij, pgeo, pfc, pdfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, pack,
-        total;
+        rep, mask, total;
 };
 
 // Weight pack: every weight matrix of the model pre-split into fp16 hi / lo
@@ -185,25 +185,89 @@ struct CellGrid {
     int offset;        // first cell of this replica in the global cell table
 };
 
+// sin and cos of th in [0, pi/2]: Taylor polynomials about 0 (through x^9
+// for sin, x^10 for cos; the first omitted terms are below 3e-9 relative on
+// [0, pi/4]) on u = th, or on u = pi/2 - th above pi/4 (sin and cos then
+// swap).  pi/2 is split in two floats, so u = pi/2 - th is exact to the
+// rounding of the last addition.
+__host__ __device__ inline void sincos_quadrant(float th, float &sn, float &cs) {
+    const float kPio2Hi = 1.57079637050628662109375f;   // float(pi/2)
+    const float kPio2Lo = -4.37113900018624283e-8f;     // pi/2 - kPio2Hi
+    const bool flip = th > 0.785398163397448309616f;    // pi/4
+    const float u = flip ? (kPio2Hi - th) + kPio2Lo : th;
+    const float u2 = u * u;
+    const float ps = fmaf(fmaf(fmaf(u2, 1.0f / 362880.0f, -1.0f / 5040.0f), u2, 1.0f / 120.0f), u2, -1.0f / 6.0f);
+    const float s_u = fmaf(u * u2, ps, u);
+    const float pc = fmaf(fmaf(fmaf(fmaf(u2, -1.0f / 3628800.0f, 1.0f / 40320.0f), u2, -1.0f / 720.0f), u2,
+                               1.0f / 24.0f), u2, -0.5f);
+    const float c_u = fmaf(u2, pc, 1.0f);
+    sn = flip ? c_u : s_u;
+    cs = flip ? s_u : c_u;
+}
+
+// Geometry of the pair (i, j) at positions ri, rj (three floats each): unit
+// vector from i to j and distance in pgeo, the cosine envelope
+// (cos(pi d / rc) + 1) / 2 in fc and its derivative in dfc (0 at and beyond
+// rc).  Every fused multiply-add is written out, so the bits do not depend
+// on a file's contraction setting.
+__device__ inline void pair_geometry(const float *ri, const float *rj, int periodic, const float (&L)[3],
+                                     const float (&invL)[3], float cutoff, float4 &pgeo, float &fc, float &dfc) {
+    float dx = rj[0] - ri[0], dy = rj[1] - ri[1], dz = rj[2] - ri[2];
+    if (periodic) {
+        dx = fmaf(-L[0], rintf(dx * invL[0]), dx);
+        dy = fmaf(-L[1], rintf(dy * invL[1]), dy);
+        dz = fmaf(-L[2], rintf(dz * invL[2]), dz);
+    }
+    const float d = sqrtf(fmaf(dz, dz, fmaf(dy, dy, dx * dx)));
+    const float inv = 1.0f / d;
+    pgeo = make_float4(dx * inv, dy * inv, dz * inv, d);
+    fc = 0.0f;
+    dfc = 0.0f;
+    if (d < cutoff) {
+        // written as cos^2(pi d / (2 rc)): no cancellation near rc; the
+        // derivative -(pi / (2 rc)) sin(pi d / rc) = -(pi / rc) sin cos of the half angle
+        constexpr float kPi = 3.14159265358979323846f;
+        const float th = (0.5f * kPi) * d / cutoff;
+        float sn, c;
+        sincos_quadrant(th, sn, c);
+        fc = c * c;
+        dfc = -(kPi / cutoff) * sn * c;
+    }
+}
+
 // --------------------------------------------------------------- launchers
 
 // neighbors.hip
-// The integrator's first half kick and drift, applied by the neighbour
-// build's first kernel (vel == nullptr: none).
-struct KickArgs {
-    float *vel;
-    const float *forces, *inv_mass;
-    float half, dt;
+// Pair outputs of the neighbour build (the arrays the pair setup writes),
+// plus scratch that must not overlap them: mask [N][kRepMaxAtoms / 64]
+// words and rep [2 kTileMaxSplit B] ints.
+struct NbPairOut {
+    int32_t *edge_pair;
+    int2 *pair_ij;
+    float4 *pgeo;
+    float *pfc, *pdfc;
+    float cutoff;
+    uint64_t *mask;
+    int32_t *rep;
 };
+// Largest replica (atoms), read from the device (synchronises `s`); -1 on error.
+int max_replica_atoms(const sn_system &sys, hipStream_t s);
+// Replicas of at most this many atoms are built by one block each from
+// all-pairs bit masks in LDS (two launches for the whole build).
+constexpr int kRepMaxAtoms = 512;
+constexpr int kRepMaxReplicas = 4096;   // each block of that build reads every replica's count
+constexpr int kTileMaxSplit = 16;       // blocks per replica in that build
 // sync: read the edge count back (into *n_edges) and check it on the host
 // before the rows are filled.  Otherwise nothing is read back: the fill
 // checks the capacity and row lengths on the device and flags errors; every
 // kernel that reads the CSR afterwards returns at once when the status word
-// is set (the rows may then be unfilled).  kick (optional): see KickArgs;
-// pos is then updated in place.
+// is set (the rows may then be unfilled).  max_rep: the largest replica's atom count
+// (-1: unknown); when it is at most kRepMaxAtoms the replica-local build
+// runs, and with `pairs` set it also writes the pair arrays and the pair
+// count (status slot kPairTotal; 0 after an error) and sets *pairs_done.
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
                    int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync = true,
-                   const KickArgs *kick = nullptr);
+                   int max_rep = -1, const NbPairOut *pairs = nullptr, bool *pairs_done = nullptr);
 // Check run by the scan's last block once the total is known: the pair
 // count is E / 2 (E >= 0), or row_ptr[N] / 2 (E < 0), and must equal the
 // total (the number of upper edges).  status[kPairTotal] receives it, or 0
@@ -226,16 +290,17 @@ sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_
 sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s);
 // pack: the weight pack written by filter_pack, or null (the kernels then stage from the weights).
 // phi24: the filter rows [P][3F/4] in the 24-bit row format (see pack_fp24).
-// P: the pair capacity (launch size); p_dev (may be null): the device pair count.
+// P: the pair capacity (launch size); p_dev (may be null): the device pair
+// count; guard (may be null): no pairs are processed while *guard is set.
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, uint32_t *phi24,
-                         const char *pack, const int *p_dev, hipStream_t s);
+                         const char *pack, const int *p_dev, const int *guard, hipStream_t s);
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
 // xmax / gmax: per-atom max_f |x[i][f]| and max_f |g_y[i][f]| of interaction t
 // pfc / pdfc: per-pair envelope fc(d) and its derivative fc'(d)
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
                           const int2 *pair_ij, int64_t P, int N, const uint32_t *phi24, const float *x, const float *gy,
                           const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
-                          const int *p_dev, hipStream_t s);
+                          const int *p_dev, const int *guard, hipStream_t s);
 
 // graph.hip
 // E: the edge count, or -1 to take it from row_ptr[N] on the device.  Writes
