@@ -1,0 +1,124 @@
+"""GPU: both neighbour-build paths against the oracle.
+
+Replicas of at most 512 atoms are built from all-pairs row bit masks (one
+block per replica slice, two launches, pair arrays included on the MD path);
+larger ones by the cell list.  The library picks the path from the largest
+replica, so systems just below and just above that size run each path on
+the same kind of input: the CSR must be bit-identical to the oracle's either
+way, and a few Verlet steps must follow the oracle's trajectory.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from helpers import force_errors
+
+pytestmark = pytest.mark.gpu
+
+TILE_MAX = 512   # the largest replica the mask path builds
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sn():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import schnet_cfconv_force_amd as sn
+    sn.lib()
+    return sn
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _system(sizes, side, seed, min_d=2.5):
+    pos = np.concatenate([synth.box_rsa(n, side, min_d, synth.seed64(seed, b)) for b, n in enumerate(sizes)])
+    rp = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    return pos.astype(np.float32), rp
+
+
+def _model(F=32, K=8, I=1, T=3, rc=7.0, seed=11):
+    return synth.init_params(T, I, F, K, seed), {"n_types": T, "n_interactions": I, "n_features": F, "n_rbf": K,
+                                                  "cutoff": rc, **synth.rbf_hyper(K, 0.0, rc)}
+
+
+@pytest.mark.parametrize("sizes,periodic", [
+    ([TILE_MAX, TILE_MAX], False),         # mask path at its largest replica
+    ([TILE_MAX, TILE_MAX + 1], False),     # one atom more: the cell list
+    ([300, 0, 1, 2, 211], False),          # empty and tiny replicas on the mask path
+    ([400], True),                         # periodic, mask path
+    ([TILE_MAX + 88], True),               # periodic, cell list
+])
+def test_csr_bit_exact_on_both_paths(sn, sizes, periodic):
+    say(f"[build paths] sizes={sizes} periodic={periodic}")
+    side = 26.0
+    pos, rp = _system(sizes, side, 7 + len(sizes) + int(periodic))
+    box = np.array([side] * 3, np.float32) if periodic else None
+    params, hyper = _model(rc=6.5)
+    model = sn.Model(params, hyper)
+    system = sn.System(rp, np.zeros(len(pos), np.int32), box)
+    cap = max(64, 200 * len(pos))
+    ws = sn.workspace(model, system, cap)
+    for r_list in (6.5, 8.0):
+        row_ptr, col, rev, E = sn.build_csr_neighbors(system, dev(pos), r_list, cap, ws)
+        ref = O.neighbors_bruteforce(pos, rp, r_list, box)
+        say(f"   r_list={r_list}: E={E}")
+        assert E == len(ref[1]) and E > 0
+        assert np.array_equal(row_ptr.cpu().numpy(), ref[0])
+        assert np.array_equal(col.cpu().numpy()[:E], ref[1])
+        assert np.array_equal(rev.cpu().numpy()[:E], ref[2])
+
+
+def test_capacity_error_on_the_mask_path(sn):
+    pos, rp = _system([200, 200], 20.0, 3)
+    params, hyper = _model()
+    model = sn.Model(params, hyper)
+    system = sn.System(rp, np.zeros(len(pos), np.int32))
+    ws = sn.workspace(model, system, 50_000)
+    ref = O.neighbors_bruteforce(pos, rp, 7.0)
+    st, ne = sn.build_csr_status(system, dev(pos), 7.0, 100, ws)
+    assert st == sn.SN_ERR_CAPACITY and ne == len(ref[1])
+    st, ne = sn.build_csr_status(system, dev(pos), 7.0, 50_000, ws)
+    assert st == sn.SN_OK and ne == len(ref[1])
+
+
+@pytest.mark.parametrize("sizes", [[250, 250], [TILE_MAX + 100]])
+def test_verlet_on_both_paths_matches_oracle(sn, sizes):
+    """Three steps: the mask path also writes the pair arrays; the cell path runs the pair setup."""
+    import torch
+    say(f"[build paths] verlet sizes={sizes}")
+    pos, rp = _system(sizes, 24.0 if len(sizes) > 1 else 28.0, 21)
+    params, hyper = _model(F=32, K=8, I=2, rc=7.0)
+    types = np.random.default_rng(5).integers(0, 3, len(pos)).astype(np.int32)
+    inv_mass = np.full(len(pos), 1.0 / 110.0, np.float32)
+    vel = synth.maxwell_boltzmann(len(pos), rp, 110.0, 300.0, 9).astype(np.float32)
+    model = sn.Model(params, hyper)
+    system = sn.System(rp, types)
+    cap = 200 * len(pos)
+    ws = sn.workspace(model, system, cap)
+    p, v, im = dev(pos), dev(vel), dev(inv_mass)
+    row_ptr, col, rev, E = sn.build_csr_neighbors(system, p, 7.0, cap, ws)
+    _, forces = sn.energy_forces(model, system, p, row_ptr, col, rev, E, ws)
+    n = 3
+    B = len(sizes)
+    epot = torch.zeros((n, B), dtype=torch.float32, device="cuda")
+    sn.verlet_step(model, system, p, v, forces, im, 2.0, synth.FORCE_TO_ACCEL, n, 7.0, cap, ws, epot)
+    torch.cuda.synchronize()
+    r_ref, v_ref, f_ref, ep_ref, _ = O.verlet(params, hyper, types, pos, vel, inv_mass, rp, 2.0,
+                                              synth.FORCE_TO_ACCEL, n, 7.0)
+    dr = np.abs(p.cpu().numpy() - r_ref).max()
+    dv = np.abs(v.cpu().numpy() - v_ref).max() / np.abs(v_ref).max()
+    say(f"   max |dr| {dr:.2e} A, max rel dv {dv:.2e}")
+    assert dr < 1e-4 and dv < 1e-4
+    assert force_errors(forces.cpu().numpy(), f_ref, rp).max() < 1e-3
+    ep = epot.cpu().numpy()
+    assert np.abs(ep - ep_ref).max() <= 1e-4 * np.abs(ep_ref).max()
