@@ -300,8 +300,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
         SN_TRY(stream_wait(ev[0], s, s2));
         SN_TRY(filter_forward(m, 0, pgeo, P, phi_t(0), pack, p_dev, guard, s2));
         if (s2 != s && hipEventRecord(ev[1], s2) != hipSuccess) return SN_ERR_HIP;
-        SN_TRY(embed(N, F, m.n_types, sys.types, prm + off[0], h, status, s));
-        SN_TRY(mlp_x(N, F, h, pk(0, PK_XW), x_t(0), xmax_t(0), s));
+        SN_TRY(mlp_embed_x(N, F, m.n_types, sys.types, prm + off[0], pk(0, PK_XW), h, x_t(0), xmax_t(0), status, s));
         for (int t = 0; t < I; ++t) {
             if (s2 != s && hipStreamWaitEvent(s, ev[1 + t], 0) != hipSuccess) return SN_ERR_HIP;
             SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, guard, s));
@@ -314,21 +313,25 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
                 SN_TRY(filter_forward(m, t + 1, pgeo, P, phi_t(t + 1), pack, p_dev, guard, s2));
                 if (s2 != s && hipEventRecord(ev[2 + t], s2) != hipSuccess) return SN_ERR_HIP;
             }
-            SN_TRY(mlp_out(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), o_t(t), h, s));
-            if (t + 1 < I) SN_TRY(mlp_x(N, F, h, pk(t + 1, PK_XW), x_t(t + 1), xmax_t(t + 1), s));
+            if (t + 1 < I)
+                SN_TRY(mlp_out_x(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), pk(t + 1, PK_XW),
+                                 o_t(t), h, x_t(t + 1), xmax_t(t + 1), s));
+            else   // the last interaction, the readout and the first backward block
+                SN_TRY(mlp_tail(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), h, pr(0), c1, pr(1),
+                                R2, c2, pk(t, PK_BOW1), pk(t, PK_BOW2), eps, gh, gy_t(t), gmax_t(t), s));
         }
-        SN_TRY(mlp_readout(N, F, h, pr(0), c1, pr(1), R2, c2, eps, gh, s));
         SN_TRY(replica_sum(B, sys.replica_ptr, eps, energy, s));
-        // backward through the interactions in reverse; the filter backward of
-        // interaction t runs beside the CFConv and layers that lead to t - 1
+        // backward through the interactions in reverse (g_y of t is ready); the
+        // filter backward of interaction t runs beside the CFConv and layers
+        // that lead to t - 1
         for (int t = I - 1; t >= 0; --t) {
-            SN_TRY(mlp_bwd_out(N, F, gh, pk(t, PK_BOW1), o_t(t), pk(t, PK_BOW2), gy_t(t), gmax_t(t), s));
             SN_TRY(stream_wait(ev[1 + I + t], s, s2));
             SN_TRY(filter_backward(m, t, pgeo, pfc, pdfc, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
                                    t != I - 1, pack, p_dev, guard, s2));
             if (t > 0) {   // dE/dh below the first block is not needed for forces
                 SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, guard, s));
-                SN_TRY(mlp_bwd_x(N, F, y, pk(t, PK_BXW), gh, s));
+                SN_TRY(mlp_bx_bo(N, F, y, pk(t, PK_BXW), pk(t - 1, PK_BOW1), o_t(t - 1), pk(t - 1, PK_BOW2), gh,
+                                 gy_t(t - 1), gmax_t(t - 1), s));
             }
         }
         return SN_OK;

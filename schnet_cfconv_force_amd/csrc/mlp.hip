@@ -1,35 +1,51 @@
 // Atom-wise layers of the interaction blocks and the readout, fused per
 // wavefront of 16 atoms and run on the matrix cores.
 //
-// Same mapping as the filter network: computed transposed (output features
-// are the M dimension, atoms the N dimension of v_mfma_f32_16x16x32_f16),
-// operands in the split-fp16 form of split_mfma.h, and the accumulator
-// layout of the first GEMM fed directly as the B operand of the second.
-// At these sizes a launch is bound by its chain of latencies (input and
-// weight loads, the dependent matrix instructions of one tile, the stores),
-// so wavefronts stay small (one 16-atom tile; kNT > 1 would share each
-// weight fragment read between tiles) and many (two per SIMD).  Each atom's
+// Computed transposed (output features are the M dimension, atoms the N
+// dimension of v_mfma_f32_16x16x32_f16), with operands in the split-fp16
+// form of split_mfma.h.  Every layer's weights sit in the weight pack in
+// the accumulator-chained order, so a layer's input is always held the way
+// an accumulator leaves it (lane = atom l%16, features 16 m + 4 (l/16) + r):
+// rows load with one float4 per tile, and a layer's output feeds the next
+// layer as its B operand without leaving the registers.  Each atom's
 // operands are scaled by a power of two from the atom's own maximum.
 //
-// Kernels (one launch each):
-//   OUT      o = y Wo1 + bo1 (stored);  h += ssp(o) Wo2 + bo2
-//   X        x = h W_in
-//   READOUT  q = h R1 + c1;  eps = ssp(q) . R2 + c2;  g_h = (sigmoid(q) (.) R2) R1^T
-//   BWD_OUT  g_o = (g_h Wo2^T) (.) sigmoid(o);  g_y = g_o Wo1^T (stored)
-//   BWD_X    g_h += g_x W_in^T
+// One launch runs a chain of layers between two CFConvs:
+//   EMBED_X   h = Emb[type];  x_0 = h W_in
+//   OUT_X     o = y Wo1 + bo1 (stored);  h += ssp(o) Wo2 + bo2;  x_{t+1} = h W_in
+//   TAIL      the last interaction's OUT, then the readout
+//             q = h R1 + c1, eps = ssp(q) . R2 + c2, g_h = (sigmoid(q) (.) R2) R1^T,
+//             then the first backward block g_o = (g_h Wo2^T) (.) sigmoid(o),
+//             g_y = g_o Wo1^T
+//   BX_BO     g_h += g_x W_in^T (interaction t), then for t - 1:
+//             g_o = (g_h Wo2^T) (.) sigmoid(o), g_y = g_o Wo1^T
+// x and g_y also get their per-atom row maxima (the filter backward's
+// scales).  A block stages its chain's weights in two LDS buffers: while one
+// layer runs, the next layer's fragments are already loaded into registers
+// and go to the freed buffer after a block barrier.
 #include "split_mfma.h"
 
 namespace sn {
 
 namespace {
 
-// 8 wavefronts of 16 atoms per block: one block per CU holds the staged
-// weights of both layers, and 17k-atom systems fit in one pass of the CUs
+// 8 wavefronts of 16 atoms per block: a 17k-atom system fits in one pass
+// of the CUs, and two buffers of F x F weights fit in LDS
 constexpr int kMlpWaves = 8;
 constexpr int kMlpThreads = 64 * kMlpWaves;
-constexpr int kNT = 1;   // 16-atom tiles per wavefront
 
-__device__ inline int chain_k(int t, int s, int j) { return 32 * t + 16 * (j >> 2) + 4 * s + (j & 3); }
+template <int F>
+struct Dims {
+    static constexpr int M = F / 16;                 // 16-feature tiles of a row
+    static constexpr int MR = F / 32;                // tiles of the readout's hidden layer (F / 2)
+    static constexpr int T = (F + 31) / 32;          // 32-wide k steps over F inputs
+    static constexpr int TR = (F / 2 + 31) / 32;     // ... over F / 2 inputs
+    static constexpr int LAYER = M * T * 64;         // fragments of an F x F layer
+    static constexpr int R1F = MR * T * 64;          // readout first layer (F -> F / 2)
+    static constexpr int R2F = M * TR * 64;          // readout second layer (F / 2 -> F)
+    static constexpr int BUF = LAYER > R1F + R2F ? LAYER : R1F + R2F;
+    static constexpr int IT = (BUF + kMlpThreads - 1) / kMlpThreads;   // fragments per thread
+};
 
 // the atom's largest magnitude over its four k-slot lanes
 __device__ inline float atom_max(float amax) {
@@ -37,48 +53,16 @@ __device__ inline float atom_max(float amax) {
     return fmaxf(amax, __shfl_xor(amax, 32, 64));
 }
 
-enum { MLP_X = 0, MLP_OUT = 1, MLP_READOUT = 2, MLP_BWD_OUT = 3, MLP_BWD_X = 4 };
-
-template <int F, int MODE>
-struct Shape {
-    static constexpr int FI1 = F;
-    static constexpr int FO1 = MODE == MLP_READOUT ? F / 2 : F;
-    static constexpr bool TWO = MODE == MLP_OUT || MODE == MLP_READOUT || MODE == MLP_BWD_OUT;
-    static constexpr int FI2 = FO1;
-    static constexpr int FO2 = F;
-    static constexpr int M1 = FO1 / 16, T1 = (FI1 + 31) / 32;
-    static constexpr int M2 = FO2 / 16, T2 = (FI2 + 31) / 32;
-    // weights stored [out][in] (read transposed)
-    static constexpr int TR1 = (MODE == MLP_BWD_OUT || MODE == MLP_BWD_X) ? 1 : 0;
-    static constexpr int TR2 = (MODE == MLP_READOUT || MODE == MLP_BWD_OUT) ? 1 : 0;
-};
-
-struct MlpArgs {
-    int N;
-    const float *in;            // [N][F] input of the first layer
-    const half8 *w1h, *w1l;     // first layer, pre-split (weight-pack slot)
-    const half8 *w2h, *w2l;     // second layer
-    const int *sc1, *sc2;       // their split scales
-    const float *b1, *b2;       // biases
-    const float *aux;           // BWD_OUT: the stored pre-activation o
-    const float *R2, *c2;       // READOUT
-    float *mid;                 // OUT: o is stored here
-    float *out;                 // X: x;  OUT: h (+=);  READOUT: g_h;  BWD_OUT: g_y;  BWD_X: g_h (+=)
-    float *eps;                 // READOUT: per-atom energy
-    float *rmax;                // X: max_f |x|;  BWD_OUT: max_f |g_y| (per atom; optional)
-};
-
-// Weights of A fragment idx of a layer ([m][t][l]): value j = weight(row
-// 16m + l%16, column k(t, l/16, j)), k in the plain order (32t + 8s + j) or
-// the accumulator-chain order.  In both orders values 0-3 and 4-7 are runs
-// of four consecutive k, read as one 16-byte load each when W is stored
-// [out][in] (TRANS); 0 beyond kdim.
-template <int T, int TRANS, int CHAINED>
+// Weights of fragment idx of a layer ([m][t][l], T k steps) in the
+// accumulator-chained order: value j = weight(row 16 m + l%16, column
+// 32 t + 16 (j / 4) + 4 (l / 16) + j % 4); 0 beyond kdim.  W is [kdim][mdim]
+// (row-vector convention) or, with TRANS, [mdim][kdim]; runs of four
+// consecutive k are then one 16-byte load.
+template <int T, int TRANS>
 __device__ inline void layer_frag(const float *W, int kdim, int mdim, int idx, float (&v)[8]) {
     const int m = idx / (T * 64), t = (idx / 64) % T, l = idx % 64, s = l / 16;
     const int mrow = 16 * m + l % 16;
-    const int k0 = CHAINED ? 32 * t + 4 * s : 32 * t + 8 * s;
-    const int k1 = CHAINED ? k0 + 16 : k0 + 4;
+    const int k0 = 32 * t + 4 * s, k1 = k0 + 16;
     if (TRANS) {
         float4 p = make_float4(0.f, 0.f, 0.f, 0.f), q = p;
         if (k0 < kdim) p = *reinterpret_cast<const float4 *>(W + (int64_t)mrow * kdim + k0);
@@ -94,222 +78,336 @@ __device__ inline void layer_frag(const float *W, int kdim, int mdim, int idx, f
     }
 }
 
-template <int F, int MODE>
-__global__ __launch_bounds__(kMlpThreads) void mlp_kernel(MlpArgs a) {
-    using S = Shape<F, MODE>;
-    constexpr int M1 = S::M1, T1 = S::T1, M2 = S::M2, T2 = S::T2;
-    constexpr int MG1 = M1 < 4 ? M1 : 4, MG2 = M2 < 4 ? M2 : 4;
-    __shared__ half8 s_w1h[M1 * T1 * 64], s_w1l[M1 * T1 * 64];
-    __shared__ half8 s_w2h[S::TWO ? M2 * T2 * 64 : 1], s_w2l[S::TWO ? M2 * T2 * 64 : 1];
+// One wavefront's 16 atoms.
+struct Wave {
+    int lane, slot, atom;
+    bool live;
+};
 
-    const int lane = threadIdx.x % 64, slot = lane / 16;
-    const int base = (blockIdx.x * kMlpWaves + threadIdx.x / 64) * (16 * kNT);
-    int atom[kNT];
-    bool live[kNT];
-    // first layer input: features 32 t + 8 slot + j of the lane's atoms
-    // (loaded before the weights are staged, so that the two latencies overlap)
-    float xin[kNT][T1][8];
-    float xmax[kNT];
+template <int M>
+__device__ inline void load_rows(const float *src, int F, const Wave &w, float (&v)[M][4]) {
 #pragma unroll
-    for (int n = 0; n < kNT; ++n) {
-        atom[n] = base + 16 * n + lane % 16;
-        live[n] = atom[n] < a.N;
-        xmax[n] = 0.0f;
-#pragma unroll
-        for (int t = 0; t < T1; ++t)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int f0 = 32 * t + 8 * slot + 4 * q;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (live[n] && f0 < S::FI1) v = *reinterpret_cast<const float4 *>(a.in + (int64_t)atom[n] * F + f0);
-                xin[n][t][4 * q + 0] = v.x; xin[n][t][4 * q + 1] = v.y;
-                xin[n][t][4 * q + 2] = v.z; xin[n][t][4 * q + 3] = v.w;
-                xmax[n] = fmaxf(xmax[n], fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-            }
+    for (int m = 0; m < M; ++m) {
+        float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (w.live) q = *reinterpret_cast<const float4 *>(src + (int64_t)w.atom * F + 16 * m + 4 * w.slot);
+        v[m][0] = q.x; v[m][1] = q.y; v[m][2] = q.z; v[m][3] = q.w;
     }
-    copy_frags<M1 * T1 * 64, kMlpThreads>(s_w1h, s_w1l, a.w1h, a.w1l, M1 * T1 * 64);
-    if (S::TWO) copy_frags<M2 * T2 * 64, kMlpThreads>(s_w2h, s_w2l, a.w2h, a.w2l, M2 * T2 * 64);
-    const int sw1 = a.sc1[0];
-    const int sw2 = S::TWO ? a.sc2[0] : 0;
-    __syncthreads();
-    if (base >= a.N) return;
+}
 
-    // first layer: r1 = in W1 for output features 16 m + 4 slot + r
-    float r1[kNT][M1][4];
-    {
-        int sx[kNT];
-        half8 bh[T1][kNT], bl[T1][kNT];
+template <int M>
+__device__ inline void store_rows(float *dst, int F, const Wave &w, const float (&v)[M][4]) {
+    if (!w.live) return;
 #pragma unroll
-        for (int n = 0; n < kNT; ++n) {
-            sx[n] = split_scale(atom_max(xmax[n]));
-#pragma unroll
-            for (int t = 0; t < T1; ++t) {
-                float v[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = ldexpf(xin[n][t][j], sx[n]);
-                split8(v, bh[t][n], bl[t][n]);
-            }
-        }
-#pragma unroll
-        for (int m0 = 0; m0 < M1; m0 += MG1) {
-            floatx4 acc[MG1][kNT];
-#pragma unroll
-            for (int m = 0; m < MG1; ++m)
-#pragma unroll
-                for (int n = 0; n < kNT; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < T1; ++t)
-                mma_split<MG1, kNT>(s_w1h + (m0 * T1 + t) * 64 + lane, s_w1l + (m0 * T1 + t) * 64 + lane, T1 * 64,
-                                    bh[t], bl[t], acc);
-#pragma unroll
-            for (int m = 0; m < MG1; ++m)
-#pragma unroll
-                for (int n = 0; n < kNT; ++n)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) r1[n][m0 + m][r] = ldexpf(acc[m][n][r], -(sw1 + sx[n]));
-        }
-    }
+    for (int m = 0; m < M; ++m)
+        *reinterpret_cast<float4 *>(dst + (int64_t)w.atom * F + 16 * m + 4 * w.slot) =
+            make_float4(v[m][0], v[m][1], v[m][2], v[m][3]);
+}
 
-    if (MODE == MLP_X || MODE == MLP_BWD_X) {
-        if (MODE == MLP_X && a.rmax) {   // the per-atom row maximum of x, for the filter backward's scales
+// per-atom max_f |v| (every lane of the atom gets it)
+template <int M>
+__device__ inline float row_absmax(const float (&v)[M][4]) {
+    float mx = 0.0f;
 #pragma unroll
-            for (int n = 0; n < kNT; ++n) {
-                float mx = 0.0f;
+    for (int m = 0; m < M; ++m)
 #pragma unroll
-                for (int m = 0; m < M1; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(r1[n][m][r]));
-                mx = atom_max(mx);
-                if (live[n] && slot == 0) a.rmax[atom[n]] = mx;
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < kNT; ++n) {
-            if (!live[n]) continue;
-#pragma unroll
-            for (int m = 0; m < M1; ++m) {
-                float4 *dst = reinterpret_cast<float4 *>(a.out + (int64_t)atom[n] * F + 16 * m + 4 * slot);
-                float4 v = make_float4(r1[n][m][0], r1[n][m][1], r1[n][m][2], r1[n][m][3]);
-                if (MODE == MLP_BWD_X) {
-                    const float4 o = *dst;
-                    v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-                }
-                *dst = v;
-            }
-        }
-        return;
-    }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(v[m][r]));
+    return atom_max(mx);
+}
 
-    // activation between the layers -> B operands of the second GEMM
-    half8 bh[T2][kNT], bl[T2][kNT];
-    int sz[kNT];
+// out = in W for 16 atoms: MI input tiles, MO output tiles; W as fragments
+// [m][t][l] in LDS (hi at wh, lo at wl) with split scale sw.
+template <int MI, int MO>
+__device__ inline void layer(const float (&in)[MI][4], const half8 *wh, const half8 *wl, int sw, int lane,
+                             float (&out)[MO][4]) {
+    constexpr int T = (16 * MI + 31) / 32;
+    constexpr int MG = MO < 4 ? MO : 4;
+    const int sx = split_scale(row_absmax(in));
+    half8 bh[T], bl[T];
 #pragma unroll
-    for (int n = 0; n < kNT; ++n) {
-        float z[M1][4];
-        float zmax = 0.0f;
-        float eps_part = 0.0f;
+    for (int t = 0; t < T; ++t) {
+        float v[8];
 #pragma unroll
-        for (int m = 0; m < M1; ++m) {
-            const int n0 = 16 * m + 4 * slot;
-            if (MODE == MLP_OUT) {
-                float o[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    o[r] = r1[n][m][r] + a.b1[n0 + r];
-                    z[m][r] = ssp(o[r]);
-                }
-                if (live[n])
-                    *reinterpret_cast<float4 *>(a.mid + (int64_t)atom[n] * F + n0) = make_float4(o[0], o[1], o[2], o[3]);
-            } else if (MODE == MLP_READOUT) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float q = r1[n][m][r] + a.b1[n0 + r];
-                    eps_part += ssp(q) * a.R2[n0 + r];
-                    z[m][r] = sigm(q) * a.R2[n0 + r];
-                }
-            } else {   // MLP_BWD_OUT
-                float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (live[n]) o = *reinterpret_cast<const float4 *>(a.aux + (int64_t)atom[n] * F + n0);
-                z[m][0] = r1[n][m][0] * sigm(o.x);
-                z[m][1] = r1[n][m][1] * sigm(o.y);
-                z[m][2] = r1[n][m][2] * sigm(o.z);
-                z[m][3] = r1[n][m][3] * sigm(o.w);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) zmax = fmaxf(zmax, fabsf(z[m][r]));
+        for (int j = 0; j < 8; ++j) {
+            const int m = 2 * t + (j >> 2);
+            v[j] = m < MI ? ldexpf(in[m < MI ? m : 0][j & 3], sx) : 0.0f;
         }
-        if (MODE == MLP_READOUT) {
-            eps_part += __shfl_xor(eps_part, 16, 64);
-            eps_part += __shfl_xor(eps_part, 32, 64);
-            if (live[n] && slot == 0) a.eps[atom[n]] = eps_part + a.c2[0];
-        }
-        sz[n] = split_scale(atom_max(zmax));
-#pragma unroll
-        for (int t = 0; t < T2; ++t) {
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int m = 2 * t + (j >> 2);
-                v[j] = m < M1 ? ldexpf(z[m < M1 ? m : 0][j & 3], sz[n]) : 0.0f;
-            }
-            split8(v, bh[t][n], bl[t][n]);
-        }
+        split8(v, bh[t], bl[t]);
     }
-    float omax[kNT];
 #pragma unroll
-    for (int n = 0; n < kNT; ++n) omax[n] = 0.0f;
+    for (int m0 = 0; m0 < MO; m0 += MG) {
+        floatx4 acc[MG][1];
 #pragma unroll
-    for (int m0 = 0; m0 < M2; m0 += MG2) {
-        floatx4 acc[MG2][kNT];
+        for (int m = 0; m < MG; ++m) acc[m][0] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < MG2; ++m)
+        for (int t = 0; t < T; ++t)
+            mma_split<MG, 1>(wh + (m0 * T + t) * 64 + lane, wl + (m0 * T + t) * 64 + lane, T * 64, &bh[t], &bl[t],
+                             acc);
 #pragma unroll
-            for (int n = 0; n < kNT; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < MG; ++m)
 #pragma unroll
-        for (int t = 0; t < T2; ++t)
-            mma_split<MG2, kNT>(s_w2h + (m0 * T2 + t) * 64 + lane, s_w2l + (m0 * T2 + t) * 64 + lane, T2 * 64,
-                                bh[t], bl[t], acc);
-#pragma unroll
-        for (int n = 0; n < kNT; ++n) {
-            if (!live[n]) continue;
-#pragma unroll
-            for (int m = 0; m < MG2; ++m) {
-                const int n0 = 16 * (m0 + m) + 4 * slot;
-                float v[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = ldexpf(acc[m][n][r], -(sw2 + sz[n]));
-                float4 *dst = reinterpret_cast<float4 *>(a.out + (int64_t)atom[n] * F + n0);
-                if (MODE == MLP_OUT) {
-                    const float4 h = *dst;
-                    *dst = make_float4(h.x + v[0] + a.b2[n0], h.y + v[1] + a.b2[n0 + 1], h.z + v[2] + a.b2[n0 + 2],
-                                       h.w + v[3] + a.b2[n0 + 3]);
-                } else {
-                    *dst = make_float4(v[0], v[1], v[2], v[3]);
-                }
-                if (MODE == MLP_BWD_OUT)
-                    omax[n] = fmaxf(omax[n], fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-            }
-        }
+            for (int r = 0; r < 4; ++r) out[m0 + m][r] = ldexpf(acc[m][0][r], -(sw + sx));
     }
-    if (MODE == MLP_BWD_OUT && a.rmax) {   // the per-atom row maximum of g_y
+}
+
+// A weight slot's fragments on their way from the pack to an LDS buffer:
+// loaded into registers before a layer runs, stored after the barrier that
+// frees the buffer.
+template <int F>
+struct Prefetch {
+    half8 h[Dims<F>::IT], l[Dims<F>::IT];
+};
+
+// (fragments 0..nf-1 of slot r go to buffer positions at..at+nf-1)
+template <int F>
+__device__ inline void prefetch_load(Prefetch<F> &p, const PackRef &r, int nf, int at = 0) {
 #pragma unroll
-        for (int n = 0; n < kNT; ++n) {
-            const float mx = atom_max(omax[n]);
-            if (live[n] && slot == 0) a.rmax[atom[n]] = mx;
+    for (int it = 0; it < Dims<F>::IT; ++it) {
+        const int idx = (int)threadIdx.x + it * kMlpThreads - at;
+        if (idx >= 0 && idx < nf) {
+            p.h[it] = static_cast<const half8 *>(r.hi)[idx];
+            p.l[it] = static_cast<const half8 *>(r.lo)[idx];
         }
     }
 }
 
-// Pre-split one layer of a mode into a weight-pack slot (as the kernel's
-// staging would into LDS); returns the split scale.
-template <int F, int MODE, int LAYER>
+template <int F>
+__device__ inline void prefetch_store(const Prefetch<F> &p, half8 *dh, half8 *dl, int nf) {
+#pragma unroll
+    for (int it = 0; it < Dims<F>::IT; ++it) {
+        const int idx = (int)threadIdx.x + it * kMlpThreads;
+        if (idx < nf) {
+            dh[idx] = p.h[it];
+            dl[idx] = p.l[it];
+        }
+    }
+}
+
+enum Prog { P_EMBED_X = 0, P_OUT_X, P_TAIL, P_BX_BO };
+
+struct ChainArgs {
+    int N;
+    const float *in;             // OUT_X, TAIL: y;  BX_BO: g_x
+    const int32_t *types;        // EMBED_X
+    const float *emb;
+    int n_types;
+    int *status;
+    PackRef w[6];                // the chain's weight slots, in layer order
+    const float *bo1, *bo2;      // OUT biases
+    const float *c1, *R2, *c2;   // readout
+    float *o;                    // OUT_X: o (stored)
+    const float *o_prev;         // BX_BO: o of interaction t - 1
+    float *h;                    // EMBED_X: written; OUT_X: updated; TAIL: read
+    float *x, *xmax;             // x_{t+1} and its row maxima
+    float *eps;                  // TAIL
+    float *gh;                   // TAIL: written; BX_BO: updated
+    float *gy, *gmax;            // TAIL, BX_BO: g_y and its row maxima
+};
+
+template <int F, int PROG>
+__global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
+    using D = Dims<F>;
+    constexpr int M = D::M, MR = D::MR;
+    __shared__ half8 s_ah[D::BUF], s_al[D::BUF], s_bh[D::BUF], s_bl[D::BUF];
+    Wave w;
+    w.lane = threadIdx.x % 64;
+    w.slot = w.lane / 16;
+    const int base = (blockIdx.x * kMlpWaves + threadIdx.x / 64) * 16;
+    w.atom = base + w.lane % 16;
+    w.live = w.atom < a.N;
+    const bool active = base < a.N;   // the wavefront has atoms (all waves join the barriers)
+    const int lane = w.lane;
+    Prefetch<F> pf;
+
+    if (PROG == P_EMBED_X) {
+        copy_frags<D::BUF, kMlpThreads>(s_ah, s_al, static_cast<const half8 *>(a.w[0].hi),
+                                        static_cast<const half8 *>(a.w[0].lo), D::LAYER);
+        const int sw0 = a.w[0].sc[0];
+        float h[M][4];
+        if (active) {
+            int z = w.live ? a.types[w.atom] : 0;
+            if (z < 0 || z >= a.n_types) {
+                if (w.slot == 0) flag_status(a.status, SN_ERR_INVALID);
+                z = 0;
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float4 q = *reinterpret_cast<const float4 *>(a.emb + (int64_t)z * F + 16 * m + 4 * w.slot);
+                h[m][0] = q.x; h[m][1] = q.y; h[m][2] = q.z; h[m][3] = q.w;
+            }
+            store_rows<M>(a.h, F, w, h);
+        }
+        __syncthreads();
+        if (!active) return;
+        float x[M][4];
+        layer<M, M>(h, s_ah, s_al, sw0, lane, x);
+        store_rows<M>(a.x, F, w, x);
+        const float mx = row_absmax(x);
+        if (w.live && w.slot == 0) a.xmax[w.atom] = mx;
+        return;
+    }
+
+    // the first two layers' weights; the first layer's input
+    copy_frags<D::BUF, kMlpThreads>(s_ah, s_al, static_cast<const half8 *>(a.w[0].hi),
+                                    static_cast<const half8 *>(a.w[0].lo), D::LAYER);
+    copy_frags<D::BUF, kMlpThreads>(s_bh, s_bl, static_cast<const half8 *>(a.w[1].hi),
+                                    static_cast<const half8 *>(a.w[1].lo), D::LAYER);
+    const int sw0 = a.w[0].sc[0], sw1 = a.w[1].sc[0];
+    float in[M][4];
+    if (active) load_rows<M>(a.in, F, w, in);
+    __syncthreads();
+
+    if (PROG == P_OUT_X) {
+        prefetch_load<F>(pf, a.w[2], D::LAYER);
+        const int sw2 = a.w[2].sc[0];
+        float o[M][4], z[M][4];
+        if (active) {
+            layer<M, M>(in, s_ah, s_al, sw0, lane, o);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    o[m][r] += a.bo1[16 * m + 4 * w.slot + r];
+                    z[m][r] = ssp(o[m][r]);
+                }
+            store_rows<M>(a.o, F, w, o);
+        }
+        __syncthreads();                                  // buffer A is free
+        prefetch_store<F>(pf, s_ah, s_al, D::LAYER);
+        float h[M][4];
+        if (active) {
+            float d[M][4];
+            layer<M, M>(z, s_bh, s_bl, sw1, lane, d);
+            load_rows<M>(a.h, F, w, h);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) h[m][r] = h[m][r] + d[m][r] + a.bo2[16 * m + 4 * w.slot + r];
+            store_rows<M>(a.h, F, w, h);
+        }
+        __syncthreads();                                  // W_in is in buffer A
+        if (!active) return;
+        float x[M][4];
+        layer<M, M>(h, s_ah, s_al, sw2, lane, x);
+        store_rows<M>(a.x, F, w, x);
+        const float mx = row_absmax(x);
+        if (w.live && w.slot == 0) a.xmax[w.atom] = mx;
+        return;
+    }
+
+    if (PROG == P_TAIL) {
+        // layers: Wo1 (A), Wo2 (B), R1 and R1^T (A), Wo2^T (B), Wo1^T (A)
+        prefetch_load<F>(pf, a.w[2], D::R1F);
+        prefetch_load<F>(pf, a.w[3], D::R2F, D::R1F);
+        const int sw2 = a.w[2].sc[0], sw3 = a.w[3].sc[0], sw4 = a.w[4].sc[0], sw5 = a.w[5].sc[0];
+        float o[M][4], z[M][4];
+        if (active) {
+            layer<M, M>(in, s_ah, s_al, sw0, lane, o);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    o[m][r] += a.bo1[16 * m + 4 * w.slot + r];
+                    z[m][r] = ssp(o[m][r]);
+                }
+        }
+        __syncthreads();                                  // buffer A is free
+        prefetch_store<F>(pf, s_ah, s_al, D::R1F + D::R2F);
+        float h[M][4];
+        if (active) {
+            float d[M][4];
+            layer<M, M>(z, s_bh, s_bl, sw1, lane, d);
+            load_rows<M>(a.h, F, w, h);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) h[m][r] = h[m][r] + d[m][r] + a.bo2[16 * m + 4 * w.slot + r];
+        }
+        prefetch_load<F>(pf, a.w[4], D::LAYER);
+        __syncthreads();                                  // R1, R1^T in A; buffer B is free
+        prefetch_store<F>(pf, s_bh, s_bl, D::LAYER);
+        float gh[M][4];
+        if (active) {
+            float q[MR][4], zq[MR][4];
+            layer<M, MR>(h, s_ah, s_al, sw2, lane, q);
+            float eps_part = 0.0f;
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n0 = 16 * m + 4 * w.slot + r;
+                    const float qq = q[m][r] + a.c1[n0];
+                    eps_part += ssp(qq) * a.R2[n0];
+                    zq[m][r] = sigm(qq) * a.R2[n0];
+                }
+            eps_part += __shfl_xor(eps_part, 16, 64);
+            eps_part += __shfl_xor(eps_part, 32, 64);
+            if (w.live && w.slot == 0) a.eps[w.atom] = eps_part + a.c2[0];
+            layer<MR, M>(zq, s_ah + D::R1F, s_al + D::R1F, sw3, lane, gh);
+            store_rows<M>(a.gh, F, w, gh);
+        }
+        prefetch_load<F>(pf, a.w[5], D::LAYER);
+        __syncthreads();                                  // Wo2^T in B; buffer A is free
+        prefetch_store<F>(pf, s_ah, s_al, D::LAYER);
+        float go[M][4];
+        if (active) {
+            layer<M, M>(gh, s_bh, s_bl, sw4, lane, go);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) go[m][r] *= sigm(o[m][r]);
+        }
+        __syncthreads();                                  // Wo1^T in A
+        if (!active) return;
+        float gy[M][4];
+        layer<M, M>(go, s_ah, s_al, sw5, lane, gy);
+        store_rows<M>(a.gy, F, w, gy);
+        const float mx = row_absmax(gy);
+        if (w.live && w.slot == 0) a.gmax[w.atom] = mx;
+        return;
+    }
+
+    // P_BX_BO: layers W_in^T (A), Wo2^T (B), Wo1^T (A)
+    prefetch_load<F>(pf, a.w[2], D::LAYER);
+    const int sw2 = a.w[2].sc[0];
+    float gh[M][4];
+    if (active) {
+        float d[M][4];
+        layer<M, M>(in, s_ah, s_al, sw0, lane, d);
+        load_rows<M>(a.gh, F, w, gh);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gh[m][r] += d[m][r];
+        store_rows<M>(a.gh, F, w, gh);
+    }
+    __syncthreads();                                      // buffer A is free
+    prefetch_store<F>(pf, s_ah, s_al, D::LAYER);
+    float go[M][4];
+    if (active) {
+        float op[M][4];
+        layer<M, M>(gh, s_bh, s_bl, sw1, lane, go);
+        load_rows<M>(a.o_prev, F, w, op);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) go[m][r] *= sigm(op[m][r]);
+    }
+    __syncthreads();                                      // Wo1^T in A
+    if (!active) return;
+    float gy[M][4];
+    layer<M, M>(go, s_ah, s_al, sw2, lane, gy);
+    store_rows<M>(a.gy, F, w, gy);
+    const float mx = row_absmax(gy);
+    if (w.live && w.slot == 0) a.gmax[w.atom] = mx;
+}
+
+// Pre-split one matrix into a weight-pack slot (as a block's staging would
+// into LDS); returns the split scale.  TRANS: W is read transposed.
+template <int F, int KDIM, int MDIM, int TRANS>
 __device__ inline int pack_layer(const float *W, half8 *hi, half8 *lo, unsigned *s_max) {
-    using S = Shape<F, MODE>;
-    if (LAYER == 1)
-        return stage_split<S::M1 * S::T1 * 64, kMlpThreads>(hi, lo, S::M1 * S::T1 * 64, s_max,
-            [&](int idx, float (&v)[8]) { layer_frag<S::T1, S::TR1, 0>(W, S::FI1, S::FO1, idx, v); });
-    return stage_split<S::M2 * S::T2 * 64, kMlpThreads>(hi, lo, S::M2 * S::T2 * 64, s_max,
-        [&](int idx, float (&v)[8]) { layer_frag<S::T2, S::TR2, 1>(W, S::FI2, S::FO2, idx, v); });
+    constexpr int T = (KDIM + 31) / 32, NF = (MDIM / 16) * T * 64;
+    return stage_split<NF, kMlpThreads>(hi, lo, NF, s_max,
+                                        [&](int idx, float (&v)[8]) { layer_frag<T, TRANS>(W, KDIM, MDIM, idx, v); });
 }
 
 struct MlpPackArgs {
@@ -334,45 +432,34 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_pack_kernel(MlpPackArgs pa) {
     half8 *lo = const_cast<half8 *>(static_cast<const half8 *>(r.lo));
     int sc = 0;
     if (b >= 6 * pa.I) {
-        sc = b == 6 * pa.I ? pack_layer<F, MLP_READOUT, 1>(pa.R1, hi, lo, &s_max)
-                           : pack_layer<F, MLP_READOUT, 2>(pa.R1, hi, lo, &s_max);
+        sc = b == 6 * pa.I ? pack_layer<F, F, F / 2, 0>(pa.R1, hi, lo, &s_max)     // q = h R1
+                           : pack_layer<F, F / 2, F, 1>(pa.R1, hi, lo, &s_max);    // g_h = g_q R1^T
     } else {
         switch (PK_XW + k) {
-            case PK_XW: sc = pack_layer<F, MLP_X, 1>(pa.W_in[t], hi, lo, &s_max); break;
-            case PK_OW1: sc = pack_layer<F, MLP_OUT, 1>(pa.Wo1[t], hi, lo, &s_max); break;
-            case PK_OW2: sc = pack_layer<F, MLP_OUT, 2>(pa.Wo2[t], hi, lo, &s_max); break;
-            case PK_BOW1: sc = pack_layer<F, MLP_BWD_OUT, 1>(pa.Wo2[t], hi, lo, &s_max); break;
-            case PK_BOW2: sc = pack_layer<F, MLP_BWD_OUT, 2>(pa.Wo1[t], hi, lo, &s_max); break;
-            default: sc = pack_layer<F, MLP_BWD_X, 1>(pa.W_in[t], hi, lo, &s_max); break;
+            case PK_XW: sc = pack_layer<F, F, F, 0>(pa.W_in[t], hi, lo, &s_max); break;
+            case PK_OW1: sc = pack_layer<F, F, F, 0>(pa.Wo1[t], hi, lo, &s_max); break;
+            case PK_OW2: sc = pack_layer<F, F, F, 0>(pa.Wo2[t], hi, lo, &s_max); break;
+            case PK_BOW1: sc = pack_layer<F, F, F, 1>(pa.Wo2[t], hi, lo, &s_max); break;
+            case PK_BOW2: sc = pack_layer<F, F, F, 1>(pa.Wo1[t], hi, lo, &s_max); break;
+            default: sc = pack_layer<F, F, F, 1>(pa.W_in[t], hi, lo, &s_max); break;
         }
     }
     if (threadIdx.x == 0) const_cast<int *>(r.sc)[0] = sc;
 }
 
-template <int MODE>
-sn_status launch_mlp(int F, const MlpArgs &a, hipStream_t s) {
+template <int PROG>
+sn_status launch_chain(int F, const ChainArgs &a, hipStream_t s) {
     if (a.N <= 0) return SN_OK;
     ProfScope ps(K_MLP, s);
-    const int atoms_per_block = 16 * kNT * kMlpWaves;
+    const int atoms_per_block = 16 * kMlpWaves;
     const int grid = (a.N + atoms_per_block - 1) / atoms_per_block;
     switch (F) {
-        case 32: mlp_kernel<32, MODE><<<grid, kMlpThreads, 0, s>>>(a); break;
-        case 64: mlp_kernel<64, MODE><<<grid, kMlpThreads, 0, s>>>(a); break;
-        case 128: mlp_kernel<128, MODE><<<grid, kMlpThreads, 0, s>>>(a); break;
+        case 32: chain_kernel<32, PROG><<<grid, kMlpThreads, 0, s>>>(a); break;
+        case 64: chain_kernel<64, PROG><<<grid, kMlpThreads, 0, s>>>(a); break;
+        case 128: chain_kernel<128, PROG><<<grid, kMlpThreads, 0, s>>>(a); break;
         default: return SN_ERR_INVALID;
     }
     return launch_status();
-}
-
-void set_layers(MlpArgs &a, PackRef w1, const PackRef *w2) {
-    a.w1h = static_cast<const half8 *>(w1.hi);
-    a.w1l = static_cast<const half8 *>(w1.lo);
-    a.sc1 = w1.sc;
-    if (w2) {
-        a.w2h = static_cast<const half8 *>(w2->hi);
-        a.w2l = static_cast<const half8 *>(w2->lo);
-        a.sc2 = w2->sc;
-    }
 }
 
 }  // namespace
@@ -403,42 +490,41 @@ sn_status mlp_pack(const sn_model &m, char *pack, hipStream_t s) {
     return launch_status();
 }
 
-sn_status mlp_x(int N, int F, const float *h, PackRef W_in, float *x, float *xmax, hipStream_t s) {
-    MlpArgs a = {};
-    a.N = N; a.in = h; a.out = x; a.rmax = xmax;
-    set_layers(a, W_in, nullptr);
-    return launch_mlp<MLP_X>(F, a, s);
+sn_status mlp_embed_x(int N, int F, int T, const int32_t *types, const float *emb, PackRef W_in, float *h, float *x,
+                      float *xmax, int *status, hipStream_t s) {
+    ChainArgs a = {};
+    a.N = N; a.types = types; a.emb = emb; a.n_types = T; a.status = status;
+    a.w[0] = W_in;
+    a.h = h; a.x = x; a.xmax = xmax;
+    return launch_chain<P_EMBED_X>(F, a, s);
 }
 
-sn_status mlp_out(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
-                  float *o, float *h, hipStream_t s) {
-    MlpArgs a = {};
-    a.N = N; a.in = y; a.b1 = bo1; a.b2 = bo2; a.mid = o; a.out = h;
-    set_layers(a, Wo1, &Wo2);
-    return launch_mlp<MLP_OUT>(F, a, s);
+sn_status mlp_out_x(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
+                    PackRef W_in, float *o, float *h, float *x, float *xmax, hipStream_t s) {
+    ChainArgs a = {};
+    a.N = N; a.in = y; a.bo1 = bo1; a.bo2 = bo2;
+    a.w[0] = Wo1; a.w[1] = Wo2; a.w[2] = W_in;
+    a.o = o; a.h = h; a.x = x; a.xmax = xmax;
+    return launch_chain<P_OUT_X>(F, a, s);
 }
 
-sn_status mlp_readout(int N, int F, const float *h, PackRef R1, const float *c1, PackRef R1t, const float *R2,
-                      const float *c2, float *eps, float *gh, hipStream_t s) {
-    MlpArgs a = {};
-    a.N = N; a.in = h; a.b1 = c1; a.R2 = R2; a.c2 = c2; a.eps = eps; a.out = gh;
-    set_layers(a, R1, &R1t);
-    return launch_mlp<MLP_READOUT>(F, a, s);
+sn_status mlp_tail(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
+                   const float *h, PackRef R1, const float *c1, PackRef R1t, const float *R2, const float *c2,
+                   PackRef Wo2t, PackRef Wo1t, float *eps, float *gh, float *gy, float *gymax, hipStream_t s) {
+    ChainArgs a = {};
+    a.N = N; a.in = y; a.bo1 = bo1; a.bo2 = bo2; a.c1 = c1; a.R2 = R2; a.c2 = c2;
+    a.w[0] = Wo1; a.w[1] = Wo2; a.w[2] = R1; a.w[3] = R1t; a.w[4] = Wo2t; a.w[5] = Wo1t;
+    a.h = const_cast<float *>(h); a.eps = eps; a.gh = gh; a.gy = gy; a.gmax = gymax;
+    return launch_chain<P_TAIL>(F, a, s);
 }
 
-sn_status mlp_bwd_out(int N, int F, const float *gh, PackRef Wo2t, const float *o, PackRef Wo1t, float *gy,
-                      float *gymax, hipStream_t s) {
-    MlpArgs a = {};
-    a.N = N; a.in = gh; a.aux = o; a.out = gy; a.rmax = gymax;
-    set_layers(a, Wo2t, &Wo1t);
-    return launch_mlp<MLP_BWD_OUT>(F, a, s);
-}
-
-sn_status mlp_bwd_x(int N, int F, const float *gx, PackRef W_int, float *gh, hipStream_t s) {
-    MlpArgs a = {};
-    a.N = N; a.in = gx; a.out = gh;
-    set_layers(a, W_int, nullptr);
-    return launch_mlp<MLP_BWD_X>(F, a, s);
+sn_status mlp_bx_bo(int N, int F, const float *gx, PackRef W_int, PackRef Wo2t, const float *o_prev, PackRef Wo1t,
+                    float *gh, float *gy, float *gymax, hipStream_t s) {
+    ChainArgs a = {};
+    a.N = N; a.in = gx; a.o_prev = o_prev;
+    a.w[0] = W_int; a.w[1] = Wo2t; a.w[2] = Wo1t;
+    a.gh = gh; a.gy = gy; a.gmax = gymax;
+    return launch_chain<P_BX_BO>(F, a, s);
 }
 
 }  // namespace sn

@@ -320,23 +320,25 @@ sn_status forces_rows(int N, const int32_t *row_ptr, const int32_t *col, const i
                       hipStream_t s);
 
 // atomwise.hip
-sn_status embed(int N, int F, int T, const int32_t *types, const float *emb, float *h, int *status,
-                hipStream_t s);
 sn_status replica_sum(int B, const int32_t *replica_ptr, const float *eps, float *energy, hipStream_t s);
 
 // mlp.hip (fused atom-wise layers; see the kernel comments there).  The
 // weights come from the weight pack (slots written by mlp_pack).
 sn_status mlp_pack(const sn_model &m, char *pack, hipStream_t s);
-// xmax (optional): per-atom max_f |x|
-sn_status mlp_x(int N, int F, const float *h, PackRef W_in, float *x, float *xmax, hipStream_t s);
-sn_status mlp_out(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
-                  float *o, float *h, hipStream_t s);
-sn_status mlp_readout(int N, int F, const float *h, PackRef R1, const float *c1, PackRef R1t, const float *R2,
-                      const float *c2, float *eps, float *gh, hipStream_t s);
-// gymax (optional): per-atom max_f |g_y|
-sn_status mlp_bwd_out(int N, int F, const float *gh, PackRef Wo2t, const float *o, PackRef Wo1t, float *gy,
-                      float *gymax, hipStream_t s);
-sn_status mlp_bwd_x(int N, int F, const float *gx, PackRef W_int, float *gh, hipStream_t s);
+// The chains of layers between CFConvs.  xmax / gymax: per-atom row maxima.
+// h = Emb[type]; x = h W_in (first interaction)
+sn_status mlp_embed_x(int N, int F, int T, const int32_t *types, const float *emb, PackRef W_in, float *h, float *x,
+                      float *xmax, int *status, hipStream_t s);
+// o = y Wo1 + bo1; h += ssp(o) Wo2 + bo2; x = h W_in (of the next interaction)
+sn_status mlp_out_x(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
+                    PackRef W_in, float *o, float *h, float *x, float *xmax, hipStream_t s);
+// the last interaction's OUT, the readout (eps, g_h) and the first backward block (g_y)
+sn_status mlp_tail(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
+                   const float *h, PackRef R1, const float *c1, PackRef R1t, const float *R2, const float *c2,
+                   PackRef Wo2t, PackRef Wo1t, float *eps, float *gh, float *gy, float *gymax, hipStream_t s);
+// g_h += g_x W_in^T (interaction t); the backward block of t - 1 (g_y)
+sn_status mlp_bx_bo(int N, int F, const float *gx, PackRef W_int, PackRef Wo2t, const float *o_prev, PackRef Wo1t,
+                    float *gh, float *gy, float *gymax, hipStream_t s);
 
 // verlet (api.hip)
 
