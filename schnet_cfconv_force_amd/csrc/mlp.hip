@@ -29,9 +29,10 @@ namespace sn {
 
 namespace {
 
-// 8 wavefronts of 16 atoms per block: a 17k-atom system fits in one pass
-// of the CUs, and two buffers of F x F weights fit in LDS
-constexpr int kMlpWaves = 8;
+// 5 wavefronts of 16 atoms per block (one block per CU: two buffers of
+// F x F weights take 128 KB of LDS): a 17k-atom system spreads over 216
+// CUs in one pass; 8 wavefronts (135 CUs) were 8 % slower per launch
+constexpr int kMlpWaves = 5;
 constexpr int kMlpThreads = 64 * kMlpWaves;
 
 template <int F>
