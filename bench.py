@@ -56,15 +56,17 @@ def cfconv_bytes(E: int, N: int, F: int):
     return E * (3 * F + 12) + 2 * N * F * 4
 
 
-KERNEL_SOURCES = ("filter.hip", "graph.hip", "atomwise.hip", "mlp.hip", "neighbors.hip", "api.hip", "sn_internal.h",
-                  "split_mfma.h")
+def kernel_sources() -> list:
+    """The HIP sources and headers of the library (every .hip and .h under csrc/)."""
+    d = os.path.join(ROOT, "schnet_cfconv_force_amd", "csrc")
+    return sorted(n for n in os.listdir(d) if n.endswith((".hip", ".h")))
 
 
 def source_hash() -> str:
     """sha256 of the HIP sources: hardware counters are only valid for this code."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in kernel_sources():
         with open(os.path.join(ROOT, "schnet_cfconv_force_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libsn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["neighbors.hip", "graph.hip", "atomwise.hip", "mlp.hip", "filter.hip", "api.hip"]
+SOURCES = ["neighbors.hip", "graph.hip", "mlp.hip", "filter.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -108,26 +108,15 @@ sn_status clear_status(void *ws, hipStream_t s) {
     return launch_status();
 }
 
-// Velocity Verlet around a force evaluation.  close: the step's closing
-// half kick v += dt/2 c F / m, the step counted in kStepsDone and its edge
-// count written to edge_slot (if set).  open: the next step's opening half
-// kick with the same forces, then the drift r += dt v.  Both in one launch
-// give the same bits as one after the other.  Nothing moves once an error is
+// A step's opening half kick v += dt/2 c F / m and drift r += dt v (the
+// closing kick runs in the force assembly).  Nothing moves once an error is
 // flagged.
-__global__ void verlet_kernel(int N, float *pos, float *vel, const float *forces, const float *inv_mass,
-                              float half_dt_c, float dt, int close, int open, int *status, int *edge_slot) {
+__global__ void open_step_kernel(int N, float *pos, float *vel, const float *forces, const float *inv_mass,
+                                 float half_dt_c, float dt, const int *status) {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (close && edge_slot && idx == 0) *edge_slot = status[kEdgeTotal];
-    if (*status != 0) return;
-    if (close && idx == 0) status[kStepsDone] += 1;
-    if (idx >= 3 * N) return;
-    const float a = forces[idx], im = inv_mass[idx / 3];
-    float v = vel[idx];
-    if (close) v = v + half_dt_c * a * im;
-    if (open) {
-        v = v + half_dt_c * a * im;
-        pos[idx] += dt * v;
-    }
+    if (idx >= 3 * N || *status != 0) return;
+    const float v = vel[idx] + half_dt_c * forces[idx] * inv_mass[idx / 3];
+    pos[idx] += dt * v;
     vel[idx] = v;
 }
 
@@ -236,16 +225,19 @@ sn_status stream_wait(hipEvent_t e, hipStream_t from, hipStream_t to) {
 // the rows unfilled).  packed: the weight pack in the workspace is current
 // (written by filter_pack and mlp_pack since the weights last changed).
 // pairs_ready: the neighbour build has written the pair arrays and count.
+// vf: the integrator's part applied with the forces (MD steps).
 sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const float *pos, const int32_t *row_ptr,
                              const int32_t *col, const int32_t *rev, int64_t E, float *energy, float *forces,
                              char *ws, hipStream_t s, bool device_edges = false, bool packed = false,
-                             bool pairs_ready = false) {
+                             bool pairs_ready = false, const VerletFuse *vf = nullptr) {
     const int N = sys.n_atoms, B = sys.n_replicas, F = m.n_features, I = m.n_interactions;
     const int64_t P = E / 2;
     int *status = reinterpret_cast<int *>(ws);
     const EfLayout L = ef_layout(m, sys, E, kWsBase);
     float *eps = reinterpret_cast<float *>(ws + L.eps);
-    if (N == 0) return replica_sum(B, sys.replica_ptr, eps, energy, s);
+    if (N == 0)
+        return forces_rows(0, B, sys.replica_ptr, eps, energy, row_ptr, col, nullptr, nullptr, nullptr, forces, status,
+                           nullptr, vf, s);
 
     int64_t off[9 * 16 + 6];
     sn_param_offsets(m.n_types, I, F, m.n_rbf, off, (int32_t)(sizeof(off) / sizeof(off[0])));
@@ -320,7 +312,6 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
                 SN_TRY(mlp_tail(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), h, pr(0), c1, pr(1),
                                 R2, c2, pk(t, PK_BOW1), pk(t, PK_BOW2), eps, gh, gy_t(t), gmax_t(t), s));
         }
-        SN_TRY(replica_sum(B, sys.replica_ptr, eps, energy, s));
         // backward through the interactions in reverse (g_y of t is ready); the
         // filter backward of interaction t runs beside the CFConv and layers
         // that lead to t - 1
@@ -342,7 +333,8 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     const sn_status js = stream_wait(ev[2 + 2 * I], s2, s);
     SN_TRY(st);
     SN_TRY(js);
-    return forces_rows(N, row_ptr, col, edge_pair, pgeo, S, forces, status, guard, s);
+    return forces_rows(N, B, sys.replica_ptr, eps, energy, row_ptr, col, edge_pair, pgeo, S, forces, status, guard,
+                       vf, s);
 }
 
 }  // namespace
@@ -508,26 +500,29 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
     pairs.cutoff = model->cutoff;
     pairs.mask = reinterpret_cast<uint64_t *>(w + L.mask);
     pairs.rep = reinterpret_cast<int32_t *>(w + L.rep);
-    const unsigned vblocks = (3 * N + 255) / 256 + 1;   // one more: the step counter at N = 0
-    auto verlet = [&](int close, int open, int32_t step) -> sn_status {
+    auto open_step = [&]() -> sn_status {
+        if (N == 0) return SN_OK;
         ProfScope ps(K_VERLET, s);
-        verlet_kernel<<<vblocks, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, close, open, status,
-                                              edge_log && close ? edge_log + step : nullptr);
+        open_step_kernel<<<(3 * N + 255) / 256, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, status);
         return launch_status();
     };
-    // the first step's opening kick and drift; each later one runs with the
-    // previous step's closing kick (unless the kinetic energy is logged between)
-    if (n_steps > 0) SN_TRY(verlet(0, 1, 0));
+    // the first step's opening kick and drift; each later one runs in the
+    // previous step's force assembly (unless the kinetic energy is logged between)
+    if (n_steps > 0) SN_TRY(open_step());
     for (int32_t step = 0; step < n_steps; ++step) {
         int64_t E_unused = 0;
         bool pairs_done = false;
+        // the build marks the step as begun without error (the steps completed)
         SN_TRY(nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, &E_unused, w, s, false, max_rep,
-                        &pairs, &pairs_done));
+                        &pairs, &pairs_done, step));
         float *eout = epot_log ? epot_log + (int64_t)step * B : eps_scratch;
-        SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, capacity, eout, forces, w, s, true,
-                                  pack_once, pairs_done));
+        // the force assembly closes this step and opens the next (unless the
+        // kinetic energy is logged between the two)
         const int open_next = step + 1 < n_steps;
-        SN_TRY(verlet(1, open_next && !ekin_log, step));
+        const VerletFuse vf{pos, vel, inv_mass, half, dt, 1, open_next && !ekin_log,
+                            edge_log ? edge_log + step : nullptr};
+        SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, capacity, eout, forces, w, s, true,
+                                  pack_once, pairs_done, &vf));
         if (ekin_log) {
             {
                 ProfScope ps(K_KINETIC, s);
@@ -535,14 +530,14 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
                                                  ekin_log + (int64_t)step * B);
                 SN_TRY(launch_status());
             }
-            if (open_next) SN_TRY(verlet(0, 1, step + 1));
+            if (open_next) SN_TRY(open_step());
         }
     }
     int host[kStepsDone + 1] = {};
     SN_HIP(hipMemcpyAsync(host, status, sizeof(host), hipMemcpyDeviceToHost, s));
     SN_HIP(hipStreamSynchronize(s));
     *n_edges = host[kEdgeTotal];
-    if (n_steps_done) *n_steps_done = host[kStepsDone];
+    if (n_steps_done) *n_steps_done = host[kStatusWord] == 0 ? n_steps : host[kStepsDone];
     SN_TRY(clear_status(ws, s));
     return host[kStatusWord];
 }

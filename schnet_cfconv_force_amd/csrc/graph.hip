@@ -164,34 +164,87 @@ __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const i
     if (grp == 0) *reinterpret_cast<float4 *>(out + (int64_t)row * F + 4 * sub) = acc;
 }
 
-// F_i = sum_{e in row i} S[p(e)] * u_e, 16 lanes per row
-__global__ __launch_bounds__(256) void forces_kernel(int N, const int32_t *row_ptr, const int32_t *col,
-                                                     const int32_t *edge_pair, const float4 *pgeo, const float *S,
-                                                     float *forces, int *status, const int *guard) {
-    const int sub = threadIdx.x % 16;
-    const int i = (blockIdx.x * 256 + threadIdx.x) / 16;
-    if (i >= N || (guard && *guard)) return;
-    const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
-    float fx = 0.f, fy = 0.f, fz = 0.f;
-    for (int e = e0 + sub; e < e1; e += 16) {
-        const int p = edge_pair[e];
-        const float4 g = pgeo[p];
-        const float s = (col[e] > i) ? S[p] : -S[p];
-        fx += s * g.x;
-        fy += s * g.y;
-        fz += s * g.z;
+struct ForcesArgs {
+    int N, row_blocks;
+    const int32_t *row_ptr, *col, *edge_pair;
+    const float4 *pgeo;
+    const float *S;
+    float *forces;
+    const int32_t *rptr;
+    const float *eps;
+    float *energy;
+    VerletFuse vf;   // vf.vel null: no integrator part
+    int *status;
+    const int *guard;
+};
+
+__device__ inline int load_status(const int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Blocks [0, row_blocks): F_i = sum_{e in row i} S[p(e)] u_e, 16 lanes per
+// row, then the Verlet part for atom i.  Blocks past them: the energy of one
+// replica each (fixed-order tree, deterministic).
+__global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
+    __shared__ double red[256];
+    __shared__ int s_go;
+    if ((int)blockIdx.x >= a.row_blocks) {
+        const int b = blockIdx.x - a.row_blocks;
+        double s = 0.0;
+        for (int i = a.rptr[b] + threadIdx.x; i < a.rptr[b + 1]; i += 256) s += (double)a.eps[i];
+        red[threadIdx.x] = s;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) a.energy[b] = (float)red[0];
+    } else {
+        if (threadIdx.x == 0) s_go = a.vf.vel && load_status(a.status) == 0;
+        __syncthreads();
+        const int sub = threadIdx.x % 16;
+        const int i = (blockIdx.x * 256 + threadIdx.x) / 16;
+        if (i < a.N && !(a.guard && *a.guard)) {
+            const int e0 = a.row_ptr[i], e1 = a.row_ptr[i + 1];
+            float fx = 0.f, fy = 0.f, fz = 0.f;
+            for (int e = e0 + sub; e < e1; e += 16) {
+                const int p = a.edge_pair[e];
+                const float4 g = a.pgeo[p];
+                const float s = (a.col[e] > i) ? a.S[p] : -a.S[p];
+                fx += s * g.x;
+                fy += s * g.y;
+                fz += s * g.z;
+            }
+            for (int o = 8; o > 0; o >>= 1) {
+                fx += __shfl_xor(fx, o, 16);
+                fy += __shfl_xor(fy, o, 16);
+                fz += __shfl_xor(fz, o, 16);
+            }
+            if (sub == 0) {
+                a.forces[3 * i] = fx;
+                a.forces[3 * i + 1] = fy;
+                a.forces[3 * i + 2] = fz;
+                const bool finite = isfinite(fx) && isfinite(fy) && isfinite(fz);
+                if (!finite) flag_status(a.status, SN_ERR_NONFINITE);
+                if (s_go && finite) {
+                    const float im = a.vf.inv_mass[i];
+                    const float f3[3] = {fx, fy, fz};
+#pragma unroll
+                    for (int c = 0; c < 3; ++c) {
+                        float v = a.vf.vel[3 * i + c];
+                        if (a.vf.close) v = v + a.vf.half * f3[c] * im;
+                        if (a.vf.open) {
+                            v = v + a.vf.half * f3[c] * im;
+                            a.vf.pos[3 * i + c] += a.vf.dt * v;
+                        }
+                        a.vf.vel[3 * i + c] = v;
+                    }
+                }
+            }
+        }
     }
-    for (int o = 8; o > 0; o >>= 1) {
-        fx += __shfl_xor(fx, o, 16);
-        fy += __shfl_xor(fy, o, 16);
-        fz += __shfl_xor(fz, o, 16);
-    }
-    if (sub == 0) {
-        forces[3 * i] = fx;
-        forces[3 * i + 1] = fy;
-        forces[3 * i + 2] = fz;
-        if (!(isfinite(fx) && isfinite(fy) && isfinite(fz))) flag_status(status, SN_ERR_NONFINITE);
-    }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && a.vf.close && a.vf.edge_slot)
+        *a.vf.edge_slot = a.status[kEdgeTotal];
 }
 
 }  // namespace
@@ -244,11 +297,20 @@ sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const
     return launch_status();
 }
 
-sn_status forces_rows(int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
-                      const float4 *pgeo, const float *S, float *forces, int *status, const int *guard,
+sn_status forces_rows(int N, int B, const int32_t *replica_ptr, const float *eps, float *energy,
+                      const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair, const float4 *pgeo,
+                      const float *S, float *forces, int *status, const int *guard, const VerletFuse *vf,
                       hipStream_t s) {
     ProfScope ps(K_FORCES, s);
-    forces_kernel<<<(N + 15) / 16, 256, 0, s>>>(N, row_ptr, col, edge_pair, pgeo, S, forces, status, guard);
+    ForcesArgs a;
+    a.N = N;
+    a.row_blocks = (N + 15) / 16;
+    a.row_ptr = row_ptr; a.col = col; a.edge_pair = edge_pair; a.pgeo = pgeo; a.S = S; a.forces = forces;
+    a.rptr = replica_ptr; a.eps = eps; a.energy = energy;
+    a.vf = vf ? *vf : VerletFuse{};
+    a.status = status;
+    a.guard = guard;
+    forces_kernel<<<a.row_blocks + B, 256, 0, s>>>(a);
     return launch_status();
 }
 

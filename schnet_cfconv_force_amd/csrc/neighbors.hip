@@ -126,7 +126,7 @@ __device__ inline bool block_bbox(const float *pos, int s, int e, float (*red)[N
 // entry) and the builder's status slots.
 __global__ __launch_bounds__(256) void grid_kernel(const float *pos, const int32_t *rptr, PredParams pp,
                                                    float cell_edge, CellGrid *grid, int *rep_of, int *cell_cnt,
-                                                   int *cell_fill, int64_t n_cells, int *status) {
+                                                   int *cell_fill, int64_t n_cells, int step_mark, int *status) {
     __shared__ float red[6][4];
     const int b = blockIdx.x;
     const int s = rptr[b], e = rptr[b + 1];
@@ -141,6 +141,7 @@ __global__ __launch_bounds__(256) void grid_kernel(const float *pos, const int32
     if (b == 0 && threadIdx.x == 0) {
         status[kMaxRow] = 0;
         status[kEdgeTotal] = 0;
+        if (step_mark >= 0 && *status == 0) status[kStepsDone] = step_mark;
     }
     for (int i = s + threadIdx.x; i < e; i += 256) rep_of[i] = b;
     float lo[3], hi[3];
@@ -449,6 +450,7 @@ struct TileArgs {
     int64_t capacity;
     int flag;                    // flag SN_ERR_ROW / SN_ERR_CAPACITY in the status word
     NbPairOut pr;                // pr.edge_pair null: no pair arrays
+    int step_mark;               // >= 0: to status slot kStepsDone unless an error is flagged
     int *status;
 };
 
@@ -475,6 +477,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_count_kernel(TileArgs a) {
     if (threadIdx.x == 0) {
         s_sum = 0;
         s_max = 0;
+        if (blockIdx.x == 0 && a.step_mark >= 0 && *a.status == 0) a.status[kStepsDone] = a.step_mark;
     }
     if (tile_positions(a.pos, s, n, sp)) {       // the fill pass sees the flag and writes nothing
         if (threadIdx.x == 0) flag_status(a.status, SN_ERR_NONFINITE);
@@ -688,7 +691,7 @@ static int *pinned_counters() {
 
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
                    int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync,
-                   int max_rep, const NbPairOut *pairs, bool *pairs_done) {
+                   int max_rep, const NbPairOut *pairs, bool *pairs_done, int step_mark) {
     if (pairs_done) *pairs_done = false;
     const int N = sys.n_atoms, B = sys.n_replicas;
     int *status = reinterpret_cast<int *>(ws);
@@ -740,6 +743,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         a.capacity = capacity;
         a.flag = sync ? 0 : 1;
         a.pr = pairs ? *pairs : NbPairOut{};
+        a.step_mark = step_mark;
         a.status = status;
         {
             ProfScope ps(K_NB_COUNT, s);
@@ -768,7 +772,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
     {
         ProfScope ps(K_NB_GRID, s);
         grid_kernel<<<B, 256, 0, s>>>(pos, sys.replica_ptr, pp, cell_edge, grid, rep_of, cell_cnt, cell_fill,
-                                      L.n_cells, status);
+                                      L.n_cells, step_mark, status);
         SN_TRY(launch_status());
     }
     {

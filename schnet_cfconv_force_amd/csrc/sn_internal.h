@@ -18,7 +18,11 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // Device status words at the head of the workspace: the first error code
 // (0 = none), the longest row and the edge total of the last neighbour
 // build, the pair count of the last pair setup, and the MD steps completed.
-enum StatusSlot { kStatusWord = 0, kMaxRow = 1, kEdgeTotal = 2, kPairTotal = 3, kStepsDone = 4, kStatusSlots = 64 };
+enum StatusSlot {
+    kStatusWord = 0, kMaxRow = 1, kEdgeTotal = 2, kPairTotal = 3,
+    kStepsDone = 4,    // MD: index of the last step that began with no error flagged
+    kStatusSlots = 64
+};
 
 #define SN_TRY(expr)                               \
     do {                                           \
@@ -262,12 +266,15 @@ constexpr int kTileMaxSplit = 16;       // blocks per replica in that build
 // checks the capacity and row lengths on the device and flags errors; every
 // kernel that reads the CSR afterwards returns at once when the status word
 // is set (the rows may then be unfilled).  max_rep: the largest replica's atom count
-// (-1: unknown); when it is at most kRepMaxAtoms the replica-local build
+// (-1: unknown); when it is at most kRepMaxAtoms the tile build
 // runs, and with `pairs` set it also writes the pair arrays and the pair
 // count (status slot kPairTotal; 0 after an error) and sets *pairs_done.
+// step_mark >= 0: the first kernel writes it to status slot kStepsDone if no
+// error is flagged by then (MD steps).
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
                    int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync = true,
-                   int max_rep = -1, const NbPairOut *pairs = nullptr, bool *pairs_done = nullptr);
+                   int max_rep = -1, const NbPairOut *pairs = nullptr, bool *pairs_done = nullptr,
+                   int step_mark = -1);
 // Check run by the scan's last block once the total is known: the pair
 // count is E / 2 (E >= 0), or row_ptr[N] / 2 (E < 0), and must equal the
 // total (the number of upper edges).  status[kPairTotal] receives it, or 0
@@ -315,12 +322,26 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
 sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
                  const float *pfc, const uint32_t *phi24, const float *in, float *out, const int *guard,
                  hipStream_t s);
-sn_status forces_rows(int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
-                      const float4 *pgeo, const float *S, float *forces, int *status, const int *guard,
+// The integrator's part of an MD step that the force assembly applies as it
+// writes each atom's force: close = the step's closing half kick
+// v += half F / m (and its edge count to edge_slot if set); open = the next
+// step's opening half kick with the same force and the drift r += dt v.
+// Atoms do not move once an error is flagged.
+struct VerletFuse {
+    float *pos, *vel;
+    const float *inv_mass;
+    float half, dt;
+    int close, open;
+    int *edge_slot;
+};
+// F_i = sum_{e in row i} S_p(e) u_e, one launch that also sums the atom
+// energies eps into energy[b] per replica and, with vf, applies its Verlet
+// part.
+sn_status forces_rows(int N, int B, const int32_t *replica_ptr, const float *eps, float *energy,
+                      const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair, const float4 *pgeo,
+                      const float *S, float *forces, int *status, const int *guard, const VerletFuse *vf,
                       hipStream_t s);
 
-// atomwise.hip
-sn_status replica_sum(int B, const int32_t *replica_ptr, const float *eps, float *energy, hipStream_t s);
 
 // mlp.hip (fused atom-wise layers; see the kernel comments there).  The
 // weights come from the weight pack (slots written by mlp_pack).
