@@ -93,6 +93,7 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     L.pack = take(pack_bytes((int)I));
     L.rep = take(8 * kTileMaxSplit * B);   // the tile neighbour build's per-block counts
     L.mask = take(8 * (kRepMaxAtoms / 64) * N);   // and its row masks
+    L.h0 = take(4 * N * F);                // the embedding rows (kept across MD steps)
     L.total = o;
     return L;
 }
@@ -226,10 +227,12 @@ sn_status stream_wait(hipEvent_t e, hipStream_t from, hipStream_t to) {
 // (written by filter_pack and mlp_pack since the weights last changed).
 // pairs_ready: the neighbour build has written the pair arrays and count.
 // vf: the integrator's part applied with the forces (MD steps).
+// embedded: h0, x_0 and its row maxima are current (the types do not change
+// during an MD call).
 sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const float *pos, const int32_t *row_ptr,
                              const int32_t *col, const int32_t *rev, int64_t E, float *energy, float *forces,
                              char *ws, hipStream_t s, bool device_edges = false, bool packed = false,
-                             bool pairs_ready = false, const VerletFuse *vf = nullptr) {
+                             bool pairs_ready = false, const VerletFuse *vf = nullptr, bool embedded = false) {
     const int N = sys.n_atoms, B = sys.n_replicas, F = m.n_features, I = m.n_interactions;
     const int64_t P = E / 2;
     int *status = reinterpret_cast<int *>(ws);
@@ -253,7 +256,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     const float4 *pgeo = reinterpret_cast<const float4 *>(ws + L.pgeo);
     const float *pfc = F32(L.pfc);
     const float *pdfc = F32(L.pdfc);
-    float *h = F32(L.h), *y = F32(L.y), *gh = F32(L.gh);
+    float *h = F32(L.h), *y = F32(L.y), *gh = F32(L.gh), *h0 = F32(L.h0);
     float *S = F32(L.S);
     const int64_t NF = (int64_t)N * F;
     auto phi_t = [&](int t) { return reinterpret_cast<uint32_t *>(ws + L.phi) + P * fp24_words(F) * t; };
@@ -292,7 +295,9 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
         SN_TRY(stream_wait(ev[0], s, s2));
         SN_TRY(filter_forward(m, 0, pgeo, P, phi_t(0), pack, p_dev, guard, s2));
         if (s2 != s && hipEventRecord(ev[1], s2) != hipSuccess) return SN_ERR_HIP;
-        SN_TRY(mlp_embed_x(N, F, m.n_types, sys.types, prm + off[0], pk(0, PK_XW), h, x_t(0), xmax_t(0), status, s));
+        if (!embedded)
+            SN_TRY(mlp_embed_x(N, F, m.n_types, sys.types, prm + off[0], pk(0, PK_XW), h0, x_t(0), xmax_t(0), status,
+                               s));
         for (int t = 0; t < I; ++t) {
             if (s2 != s && hipStreamWaitEvent(s, ev[1 + t], 0) != hipSuccess) return SN_ERR_HIP;
             SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, guard, s));
@@ -307,9 +312,10 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
             }
             if (t + 1 < I)
                 SN_TRY(mlp_out_x(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), pk(t + 1, PK_XW),
-                                 o_t(t), h, x_t(t + 1), xmax_t(t + 1), s));
+                                 o_t(t), t == 0 ? h0 : h, h, x_t(t + 1), xmax_t(t + 1), s));
             else   // the last interaction, the readout and the first backward block
-                SN_TRY(mlp_tail(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), h, pr(0), c1, pr(1),
+                SN_TRY(mlp_tail(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), t == 0 ? h0 : h,
+                                pr(0), c1, pr(1),
                                 R2, c2, pk(t, PK_BOW1), pk(t, PK_BOW2), eps, gh, gy_t(t), gmax_t(t), s));
         }
         // backward through the interactions in reverse (g_y of t is ready); the
@@ -484,10 +490,23 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
     float *eps_scratch = reinterpret_cast<float *>(w + L.eps) + N;
     // the weights do not change during the call: one weight pack serves every
     // step, unless the neighbour build's scratch reaches into it
-    const bool pack_once = nb_layout(*sys, kWsBase).total <= L.pack;
+    const size_t nb_end = nb_layout(*sys, kWsBase).total;
+    const bool pack_once = nb_end <= L.pack;
     if (pack_once) {
         SN_TRY(filter_pack(*model, w + L.pack, s));
         SN_TRY(mlp_pack(*model, w + L.pack, s));
+    }
+    // nor do the types: the embedding rows and the first interaction's x are
+    // computed once (where no neighbour scratch overlaps them)
+    const bool embed_once = pack_once && nb_end <= L.x && N > 0;
+    if (embed_once) {
+        int64_t off[9 * 16 + 6];
+        sn_param_offsets(model->n_types, model->n_interactions, model->n_features, model->n_rbf, off,
+                         (int32_t)(sizeof(off) / sizeof(off[0])));
+        SN_TRY(mlp_embed_x(N, model->n_features, model->n_types, sys->types, model->params + off[0],
+                           pack_ref(w + L.pack, model->n_interactions, pack_slot(0, PK_XW)),
+                           reinterpret_cast<float *>(w + L.h0), reinterpret_cast<float *>(w + L.x),
+                           reinterpret_cast<float *>(w + L.xmax), status, s));
     }
     // small replicas: the neighbour build also writes the pair arrays
     const int max_rep = N > 0 && n_steps > 0 ? max_replica_atoms(*sys, s) : -1;
@@ -522,7 +541,7 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
         const VerletFuse vf{pos, vel, inv_mass, half, dt, 1, open_next && !ekin_log,
                             edge_log ? edge_log + step : nullptr};
         SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, capacity, eout, forces, w, s, true,
-                                  pack_once, pairs_done, &vf));
+                                  pack_once, pairs_done, &vf, embed_once));
         if (ekin_log) {
             {
                 ProfScope ps(K_KINETIC, s);

@@ -197,7 +197,8 @@ struct ChainArgs {
     const float *c1, *R2, *c2;   // readout
     float *o;                    // OUT_X: o (stored)
     const float *o_prev;         // BX_BO: o of interaction t - 1
-    float *h;                    // EMBED_X: written; OUT_X: updated; TAIL: read
+    const float *h_in;           // OUT_X, TAIL: h before this interaction's update
+    float *h;                    // EMBED_X, OUT_X: h written
     float *x, *xmax;             // x_{t+1} and its row maxima
     float *eps;                  // TAIL
     float *gh;                   // TAIL: written; BX_BO: updated
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
         if (active) {
             float d[M][4];
             layer<M, M>(z, s_bh, s_bl, sw1, lane, d);
-            load_rows<M>(a.h, F, w, h);
+            load_rows<M>(a.h_in, F, w, h);
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
         if (active) {
             float d[M][4];
             layer<M, M>(z, s_bh, s_bl, sw1, lane, d);
-            load_rows<M>(a.h, F, w, h);
+            load_rows<M>(a.h_in, F, w, h);
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -501,11 +502,11 @@ sn_status mlp_embed_x(int N, int F, int T, const int32_t *types, const float *em
 }
 
 sn_status mlp_out_x(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
-                    PackRef W_in, float *o, float *h, float *x, float *xmax, hipStream_t s) {
+                    PackRef W_in, float *o, const float *h_in, float *h, float *x, float *xmax, hipStream_t s) {
     ChainArgs a = {};
     a.N = N; a.in = y; a.bo1 = bo1; a.bo2 = bo2;
     a.w[0] = Wo1; a.w[1] = Wo2; a.w[2] = W_in;
-    a.o = o; a.h = h; a.x = x; a.xmax = xmax;
+    a.o = o; a.h_in = h_in; a.h = h; a.x = x; a.xmax = xmax;
     return launch_chain<P_OUT_X>(F, a, s);
 }
 
@@ -515,7 +516,7 @@ sn_status mlp_tail(int N, int F, const float *y, PackRef Wo1, const float *bo1, 
     ChainArgs a = {};
     a.N = N; a.in = y; a.bo1 = bo1; a.bo2 = bo2; a.c1 = c1; a.R2 = R2; a.c2 = c2;
     a.w[0] = Wo1; a.w[1] = Wo2; a.w[2] = R1; a.w[3] = R1t; a.w[4] = Wo2t; a.w[5] = Wo1t;
-    a.h = const_cast<float *>(h); a.eps = eps; a.gh = gh; a.gy = gy; a.gmax = gymax;
+    a.h_in = h; a.eps = eps; a.gh = gh; a.gy = gy; a.gmax = gymax;
     return launch_chain<P_TAIL>(F, a, s);
 }
 

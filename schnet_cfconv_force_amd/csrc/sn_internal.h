@@ -138,7 +138,7 @@ struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
 
 struct EfLayout {            // energy/force scratch (offsets from ws base)
     size_t up_first, up_cnt, up_ptr, edge_pair, pair_ij, pgeo, pfc, pdfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, pack,
-        rep, mask, total;
+        rep, mask, h0, total;
 };
 
 // Weight pack: every weight matrix of the model pre-split into fp16 hi / lo
@@ -350,9 +350,9 @@ sn_status mlp_pack(const sn_model &m, char *pack, hipStream_t s);
 // h = Emb[type]; x = h W_in (first interaction)
 sn_status mlp_embed_x(int N, int F, int T, const int32_t *types, const float *emb, PackRef W_in, float *h, float *x,
                       float *xmax, int *status, hipStream_t s);
-// o = y Wo1 + bo1; h += ssp(o) Wo2 + bo2; x = h W_in (of the next interaction)
+// o = y Wo1 + bo1; h = h_in + ssp(o) Wo2 + bo2; x = h W_in (of the next interaction)
 sn_status mlp_out_x(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
-                    PackRef W_in, float *o, float *h, float *x, float *xmax, hipStream_t s);
+                    PackRef W_in, float *o, const float *h_in, float *h, float *x, float *xmax, hipStream_t s);
 // the last interaction's OUT, the readout (eps, g_h) and the first backward block (g_y)
 sn_status mlp_tail(int N, int F, const float *y, PackRef Wo1, const float *bo1, PackRef Wo2, const float *bo2,
                    const float *h, PackRef R1, const float *c1, PackRef R1t, const float *R2, const float *c2,
