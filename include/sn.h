@@ -170,12 +170,7 @@ sn_status sn_build_csr_neighbors(const sn_system *sys, const float *pos /* [N][3
  * Outputs: energy[B] (one per replica) and forces[N][3] = -dE/dr.
  * Atomic-free and deterministic: repeated calls give identical bits.
  * Does not synchronise; a non-finite force sets the device status read by
- * sn_read_status().  The filter-network kernels run on a library-owned
- * auxiliary stream of the device (default priority), forked from and
- * joined back into `stream` with events, so the call is ordered on `stream`
- * like a single kernel and may be captured into a graph.  With per-kernel
- * timing enabled (sn_profile_enable) or SN_SERIAL=1 in the environment,
- * everything runs on `stream` alone. */
+ * sn_read_status().  Every kernel runs on `stream`, in order. */
 sn_status sn_energy_forces(const sn_model *model, const sn_system *sys, const float *pos,
                            const int32_t *row_ptr, const int32_t *col_idx, const int32_t *rev_idx,
                            int64_t n_edges, float *energy /* [B] */, float *forces /* [N][3] */,
