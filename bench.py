@@ -51,9 +51,9 @@ def filter_flops_per_pair(F: int, K: int):
 
 def cfconv_bytes(E: int, N: int, F: int):
     """Algorithmic HBM bytes of one CFConv launch: per directed edge the filter
-    row (3F: 24-bit values), col, pair index and envelope (12 B); per atom one
-    input row read and one output row written."""
-    return E * (3 * F + 12) + 2 * N * F * 4
+    row (3F: 24-bit values, the envelope already applied), col and pair index
+    (8 B); per atom one input row read and one output row written."""
+    return E * (3 * F + 8) + 2 * N * F * 4
 
 
 def kernel_sources() -> list:

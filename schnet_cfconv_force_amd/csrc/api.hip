@@ -78,7 +78,7 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     L.pair_ij = take(8 * P);
     L.pgeo = take(16 * P);
     L.pfc = take(4 * P);
-    L.pdfc = take(4 * P);
+    L.plfc = take(4 * P);
     L.phi = take(4 * I * P * fp24_words((int)F));   // 24-bit filter rows
     L.x = take(4 * I * N * F);
     L.o = take(4 * I * N * F);
@@ -210,7 +210,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     const int2 *pair_ij = reinterpret_cast<const int2 *>(ws + L.pair_ij);
     const float4 *pgeo = reinterpret_cast<const float4 *>(ws + L.pgeo);
     const float *pfc = F32(L.pfc);
-    const float *pdfc = F32(L.pdfc);
+    const float *plfc = F32(L.plfc);
     float *h = F32(L.h), *y = F32(L.y), *gh = F32(L.gh), *h0 = F32(L.h0);
     float *S = F32(L.S);
     const int64_t NF = (int64_t)N * F;
@@ -238,11 +238,11 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     }
     if (!pairs_ready)
         SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, device_edges ? -1 : E, m.cutoff, ws, L, status, guard, s));
-    SN_TRY(filter_forward(m, 0, pgeo, P, phi_t(0), pack, p_dev, guard, s));
+    SN_TRY(filter_forward(m, 0, pgeo, pfc, P, phi_t(0), pack, p_dev, guard, s));
     if (!embedded)
         SN_TRY(mlp_embed_x(N, F, m.n_types, sys.types, prm + off[0], pk(0, PK_XW), h0, x_t(0), xmax_t(0), status, s));
     for (int t = 0; t < I; ++t) {
-        SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), x_t(t), y, guard, s));
+        SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, phi_t(t), x_t(t), y, guard, s));
         if (t + 1 < I) {
             SN_TRY(mlp_out_x(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), pk(t + 1, PK_XW),
                              o_t(t), t == 0 ? h0 : h, h, x_t(t + 1), xmax_t(t + 1), s));
@@ -250,7 +250,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
             // phi_t: one interaction's rows (24-bit, about 200 MB for 64
             // replicas) then stay in the Infinity Cache from their write to
             // their read
-            SN_TRY(filter_forward(m, t + 1, pgeo, P, phi_t(t + 1), pack, p_dev, guard, s));
+            SN_TRY(filter_forward(m, t + 1, pgeo, pfc, P, phi_t(t + 1), pack, p_dev, guard, s));
         } else {   // the last interaction, the readout and the first backward block
             SN_TRY(mlp_tail(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), t == 0 ? h0 : h, pr(0),
                             c1, pr(1), R2, c2, pk(t, PK_BOW1), pk(t, PK_BOW2), eps, gh, gy_t(t), gmax_t(t), s));
@@ -260,10 +260,10 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     // backward CFConv of t follows the filter backward that has just streamed
     // the same filter rows
     for (int t = I - 1; t >= 0; --t) {
-        SN_TRY(filter_backward(m, t, pgeo, pfc, pdfc, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
+        SN_TRY(filter_backward(m, t, pgeo, pfc, plfc, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
                                t != I - 1, pack, p_dev, guard, s));
         if (t > 0) {   // dE/dh below the first block is not needed for forces
-            SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, pfc, phi_t(t), gy_t(t), y, guard, s));
+            SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, phi_t(t), gy_t(t), y, guard, s));
             SN_TRY(mlp_bx_bo(N, F, y, pk(t, PK_BXW), pk(t - 1, PK_BOW1), o_t(t - 1), pk(t - 1, PK_BOW2), gh,
                              gy_t(t - 1), gmax_t(t - 1), s));
         }
@@ -444,7 +444,7 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
     pairs.pair_ij = reinterpret_cast<int2 *>(w + L.pair_ij);
     pairs.pgeo = reinterpret_cast<float4 *>(w + L.pgeo);
     pairs.pfc = reinterpret_cast<float *>(w + L.pfc);
-    pairs.pdfc = reinterpret_cast<float *>(w + L.pdfc);
+    pairs.plfc = reinterpret_cast<float *>(w + L.plfc);
     pairs.cutoff = model->cutoff;
     pairs.mask = reinterpret_cast<uint64_t *>(w + L.mask);
     pairs.rep = reinterpret_cast<int32_t *>(w + L.rep);

@@ -67,7 +67,8 @@ struct FilterArgs {
     uint32_t *phi24;             // forward output [P][3F/4] (the 24-bit row format)
     // backward
     const int2 *pair_ij;
-    const float *fc, *dfc;       // [P]: envelope fc(d_p) and its derivative fc'(d_p)
+    const float *fc, *lfc;       // [P]: envelope fc(d_p) and fc'(d_p) / fc(d_p); the forward
+                                 // multiplies the stored rows by fc
     const float *x, *gy;         // [N][F]
     const uint32_t *phi24_in;    // [P][3F/4] (the 24-bit row format)
     float *S;                    // [P]
@@ -266,12 +267,17 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     // the distance of the wavefront's next tile is loaded one tile ahead, so
     // that its latency (and the wait for the earlier tile's stores, which the
     // same counter tracks) is not paid at the start of every tile
+    // (with the envelope factor of the stored rows, when there is one)
     auto load_d = [&](int64_t t) {
         const int64_t q = t * 16 + (threadIdx.x % 16);
         return (t < tile_end && q < P) ? a.dsrc[q * a.dstride + a.doff] : 0.0f;
     };
-    float d_next = load_d(tile);
-    asm volatile("" : "+v"(d_next));
+    auto load_fc = [&](int64_t t) {
+        const int64_t q = t * 16 + (threadIdx.x % 16);
+        return (a.fc && t < tile_end && q < P) ? a.fc[q] : 1.0f;
+    };
+    float d_next = load_d(tile), fc_next = load_fc(tile);
+    asm volatile("" : "+v"(d_next), "+v"(fc_next));
     for (; tile < tile_end; tile += stride) {
         // keep the weight-fragment LDS reads inside the loop: hoisted out of
         // it they would need hundreds of registers
@@ -280,8 +286,9 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
         asm volatile("" : "+v"(lane));
         const int slot = lane / 16;
         const int64_t p = tile * 16 + lane % 16;
-        const float d = d_next;
+        const float d = d_next, fcp = fc_next;
         d_next = load_d(tile + stride);
+        fc_next = load_fc(tile + stride);
         half8 rh[2], rl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -332,11 +339,12 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
                                  &zh[t], &zl[t], acc);
             // the next distance has arrived long before; taking it here keeps
             // the loop's first wait from also waiting for these stores
-            asm volatile("" : "+v"(d_next));
+            asm volatile("" : "+v"(d_next), "+v"(fc_next));
             if (p < P) {
+                const float ws = os * fcp;
 #pragma unroll
                 for (int g = 0; g < MG; ++g) {
-                    const floatx4 v = acc[g][0] * os;
+                    const floatx4 v = acc[g][0] * ws;
                     if (a.phi24) {
                         const Packed4 w = pack_fp24(v[0], v[1], v[2], v[3]);
                         *reinterpret_cast<uint3 *>(a.phi24 + p * fp24_words(F) + 3 * (4 * (m0 + g) + slot)) =
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         const float d = live ? a.dsrc[p * a.dstride + a.doff] : 0.0f;
         const int2 ij = live ? a.pair_ij[p] : make_int2(0, 0);
         const float fc = live ? a.fc[p] : 0.0f;
-        const float dfc = live ? a.dfc[p] : 0.0f;
+        const float lfc = live ? a.lfc[p] : 0.0f;
         // G = g_y_i x_j + g_y_j x_i on the features 32 t + 8 slot + j, times
         // 2^(13 - e1) with |G| < 2^e1 from the per-atom row maxima, split into
         // the B operands of all k-steps
@@ -493,7 +501,8 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
             asm volatile("" : "+v"(sk)::"memory");
         }
         // S_p = fc sum_k g_rbf_k rbf_k' + g_fc fc'(d), summed over the four k-slot lanes
-        float sp = fmaf(fc * srb, ldexpf(sk, e1 + es), gfc * dfc);
+        // (gfc = <G, fc phi> from the stored rows, so gfc fc'/fc = <G, phi> fc')
+        float sp = fmaf(fc * srb, ldexpf(sk, e1 + es), gfc * lfc);
         sp += __shfl_xor(sp, 16, 64);
         sp += __shfl_xor(sp, 32, 64);
         if (live && slot == 0) a.S[p] = a.accumulate ? a.S[p] + sp : sp;
@@ -655,7 +664,7 @@ sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s) {
     return launch_status();
 }
 
-sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, uint32_t *phi24,
+sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, int64_t P, uint32_t *phi24,
                          const char *pack, const int *p_dev, const int *guard, hipStream_t s) {
     FilterArgs a = make_args(m, t);
     attach_pack(a, m, t, pack, PK_FA2);
@@ -666,6 +675,7 @@ sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P
     a.P_dev = p_dev;
     a.guard = guard;
     a.phi24 = phi24;
+    a.fc = pfc;
     return fwd_dispatch(a, m.n_features, s);
 }
 
@@ -679,7 +689,7 @@ sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t
     return fwd_dispatch(a, m.n_features, s);
 }
 
-sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
+sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *plfc,
                           const int2 *pair_ij, int64_t P, int N, const uint32_t *phi24, const float *x, const float *gy,
                           const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
                           const int *p_dev, const int *guard, hipStream_t s) {
@@ -695,7 +705,7 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
     a.P_dev = p_dev;
     a.guard = guard;
     a.fc = pfc;
-    a.dfc = pdfc;
+    a.lfc = plfc;
     a.x = x;
     a.gy = gy;
     a.phi24_in = phi24;

@@ -49,7 +49,7 @@ struct PairArgs {
     int32_t *edge_pair;
     int2 *pair_ij;
     float4 *pgeo;
-    float *pfc, *pdfc;
+    float *pfc, *plfc;
     int periodic;
     float L[3], invL[3];
     float cutoff;
@@ -83,11 +83,11 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
             a.edge_pair[e] = p;
             a.pair_ij[p] = make_int2(i, j);
             float4 g;
-            float fc, dfc;
-            pair_geometry(a.pos + 3 * i, a.pos + 3 * j, a.periodic, a.L, a.invL, a.cutoff, g, fc, dfc);
+            float fc, lfc;
+            pair_geometry(a.pos + 3 * i, a.pos + 3 * j, a.periodic, a.L, a.invL, a.cutoff, g, fc, lfc);
             a.pgeo[p] = g;
             a.pfc[p] = fc;
-            a.pdfc[p] = dfc;
+            a.plfc[p] = lfc;
         } else {
             // the reverse edge (j, i) is an upper edge of row j
             const int r = a.rev[e];
@@ -103,14 +103,14 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
     }
 }
 
-// y_i = sum_{e in row i} pfc[p] * phi[p] (.) in[col(e)], phi in the 24-bit
-// row format (three words per four features).  One wavefront per
+// y_i = sum_{e in row i} W[p] (.) in[col(e)], W = fc phi in the 24-bit row
+// format (three words per four features).  One wavefront per
 // row: F/4 lanes cover the features (one float4 each) and the 64/(F/4) lane
 // groups take interleaved edges of the same row, so every wavefront streams
 // one row with several edges in flight and no lanes wait on a longer row.
 template <int F>
 __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const int32_t *row_ptr,
-                                                     const int32_t *col, const int32_t *edge_pair, const float *pfc,
+                                                     const int32_t *col, const int32_t *edge_pair,
                                                      const uint32_t *phi24, const float *in, float *out,
                                                      const int *guard) {
     constexpr int LPR = F / 4;            // lanes per feature row
@@ -127,11 +127,9 @@ __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const i
         // 64 edges' indices loaded once, coalesced, then broadcast
         const int k = eb + lane;
         int cj = 0, cp = 0;
-        float cw = 0.0f;
         if (k < e1) {
             cj = col[k];
             cp = edge_pair[k];
-            cw = pfc[cp];
         }
         const int n = min(64, e1 - eb);
         const int rounds = (n + G - 1) / G;     // uniform over the wavefront
@@ -141,15 +139,14 @@ __global__ __launch_bounds__(256) void cfconv_kernel(int N, int nblocks, const i
             const int src = t < n ? t : n - 1;  // shuffle sources are always live lanes
             const int j = __shfl(cj, src, 64);
             const int p = __shfl(cp, src, 64);
-            const float w = __shfl(cw, src, 64);
             if (t < n) {
                 const uint3 fw = *reinterpret_cast<const uint3 *>(phi24 + (int64_t)p * fp24_words(F) + 3 * sub);
                 const float4 f = unpack_fp24(fw.x, fw.y, fw.z);
                 const float4 x = *reinterpret_cast<const float4 *>(in + (int64_t)j * F + 4 * sub);
-                acc.x += w * f.x * x.x;
-                acc.y += w * f.y * x.y;
-                acc.z += w * f.z * x.z;
-                acc.w += w * f.w * x.w;
+                acc.x = fmaf(f.x, x.x, acc.x);
+                acc.y = fmaf(f.y, x.y, acc.y);
+                acc.z = fmaf(f.z, x.z, acc.z);
+                acc.w = fmaf(f.w, x.w, acc.w);
             }
         }
     }
@@ -268,7 +265,7 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
     a.pair_ij = reinterpret_cast<int2 *>(ws + L.pair_ij);
     a.pgeo = reinterpret_cast<float4 *>(ws + L.pgeo);
     a.pfc = reinterpret_cast<float *>(ws + L.pfc);
-    a.pdfc = reinterpret_cast<float *>(ws + L.pdfc);
+    a.plfc = reinterpret_cast<float *>(ws + L.plfc);
     a.periodic = sys.periodic ? 1 : 0;
     for (int c = 0; c < 3; ++c) {
         a.L[c] = sys.periodic ? sys.box[c] : 1.0f;
@@ -283,15 +280,14 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
 }
 
 sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
-                 const float *pfc, const uint32_t *phi24, const float *in, float *out, const int *guard,
-                 hipStream_t s) {
+                 const uint32_t *phi24, const float *in, float *out, const int *guard, hipStream_t s) {
     ProfScope ps(K_CFCONV, s);
     const int nb = (N + 3) / 4;          // four rows (wavefronts) per block
     const int grid = xcd_grid(nb);
     switch (F) {
-        case 32: cfconv_kernel<32><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out, guard); break;
-        case 64: cfconv_kernel<64><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out, guard); break;
-        case 128: cfconv_kernel<128><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, pfc, phi24, in, out, guard); break;
+        case 32: cfconv_kernel<32><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, phi24, in, out, guard); break;
+        case 64: cfconv_kernel<64><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, phi24, in, out, guard); break;
+        case 128: cfconv_kernel<128><<<grid, 256, 0, s>>>(N, nb, row_ptr, col, edge_pair, phi24, in, out, guard); break;
         default: return SN_ERR_INVALID;
     }
     return launch_status();

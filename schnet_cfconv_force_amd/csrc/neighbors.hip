@@ -617,11 +617,11 @@ __global__ __launch_bounds__(kTileThreads, 8) void tile_fill_kernel(TileArgs a) 
                 a.pr.edge_pair[ed] = (int)p;
                 a.pr.pair_ij[p] = make_int2(i, s + c);
                 float4 g;
-                float fc, dfc;
-                pair_geometry(sp + 3 * r, sp + 3 * c, a.pp.periodic, a.pp.L, a.pp.invL, a.pr.cutoff, g, fc, dfc);
+                float fc, lfc;
+                pair_geometry(sp + 3 * r, sp + 3 * c, a.pp.periodic, a.pp.L, a.pp.invL, a.pr.cutoff, g, fc, lfc);
                 a.pr.pgeo[p] = g;
                 a.pr.pfc[p] = fc;
-                a.pr.pdfc[p] = dfc;
+                a.pr.plfc[p] = lfc;
             } else {
                 a.pr.edge_pair[ed] = sym ? (int)(pbase + s_upp[c] + (kc - s_upf[c])) : 0;
             }

@@ -137,7 +137,7 @@ struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
 };
 
 struct EfLayout {            // energy/force scratch (offsets from ws base)
-    size_t up_first, up_cnt, up_ptr, edge_pair, pair_ij, pgeo, pfc, pdfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, pack,
+    size_t up_first, up_cnt, up_ptr, edge_pair, pair_ij, pgeo, pfc, plfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, pack,
         rep, mask, h0, total;
 };
 
@@ -211,11 +211,13 @@ __host__ __device__ inline void sincos_quadrant(float th, float &sn, float &cs) 
 
 // Geometry of the pair (i, j) at positions ri, rj (three floats each): unit
 // vector from i to j and distance in pgeo, the cosine envelope
-// (cos(pi d / rc) + 1) / 2 in fc and its derivative in dfc (0 at and beyond
-// rc).  Every fused multiply-add is written out, so the bits do not depend
-// on a file's contraction setting.
+// fc = (cos(pi d / rc) + 1) / 2 and lfc = fc'(d) / fc(d), the derivative of
+// ln fc (both 0 at and beyond rc; the filter rows are stored multiplied by
+// fc, so the backward pass needs fc' only in this ratio).  Every fused
+// multiply-add is written out, so the bits do not depend on a file's
+// contraction setting.
 __device__ inline void pair_geometry(const float *ri, const float *rj, int periodic, const float (&L)[3],
-                                     const float (&invL)[3], float cutoff, float4 &pgeo, float &fc, float &dfc) {
+                                     const float (&invL)[3], float cutoff, float4 &pgeo, float &fc, float &lfc) {
     float dx = rj[0] - ri[0], dy = rj[1] - ri[1], dz = rj[2] - ri[2];
     if (periodic) {
         dx = fmaf(-L[0], rintf(dx * invL[0]), dx);
@@ -226,16 +228,17 @@ __device__ inline void pair_geometry(const float *ri, const float *rj, int perio
     const float inv = 1.0f / d;
     pgeo = make_float4(dx * inv, dy * inv, dz * inv, d);
     fc = 0.0f;
-    dfc = 0.0f;
+    lfc = 0.0f;
     if (d < cutoff) {
-        // written as cos^2(pi d / (2 rc)): no cancellation near rc; the
-        // derivative -(pi / (2 rc)) sin(pi d / rc) = -(pi / rc) sin cos of the half angle
+        // written as cos^2(pi d / (2 rc)): no cancellation near rc; its
+        // derivative -(pi / (2 rc)) sin(pi d / rc) = -(pi / rc) sin cos of the
+        // half angle, so fc' / fc = -(pi / rc) sin / cos (cos > 0 for d < rc)
         constexpr float kPi = 3.14159265358979323846f;
         const float th = (0.5f * kPi) * d / cutoff;
         float sn, c;
         sincos_quadrant(th, sn, c);
         fc = c * c;
-        dfc = -(kPi / cutoff) * sn * c;
+        lfc = -(kPi / cutoff) * sn / c;
     }
 }
 
@@ -249,7 +252,7 @@ struct NbPairOut {
     int32_t *edge_pair;
     int2 *pair_ij;
     float4 *pgeo;
-    float *pfc, *pdfc;
+    float *pfc, *plfc;
     float cutoff;
     uint64_t *mask;
     int32_t *rep;
@@ -299,12 +302,13 @@ sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s);
 // phi24: the filter rows [P][3F/4] in the 24-bit row format (see pack_fp24).
 // P: the pair capacity (launch size); p_dev (may be null): the device pair
 // count; guard (may be null): no pairs are processed while *guard is set.
-sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, int64_t P, uint32_t *phi24,
+// The rows are stored multiplied by the envelope pfc[p] (the CFConv's weight W_p).
+sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, int64_t P, uint32_t *phi24,
                          const char *pack, const int *p_dev, const int *guard, hipStream_t s);
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
 // xmax / gmax: per-atom max_f |x[i][f]| and max_f |g_y[i][f]| of interaction t
-// pfc / pdfc: per-pair envelope fc(d) and its derivative fc'(d)
-sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *pdfc,
+// pfc / plfc: per-pair envelope fc(d) and fc'(d) / fc(d); phi24: the rows W = fc phi
+sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *plfc,
                           const int2 *pair_ij, int64_t P, int N, const uint32_t *phi24, const float *x, const float *gy,
                           const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
                           const int *p_dev, const int *guard, hipStream_t s);
@@ -318,10 +322,9 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
                       const int32_t *rev, int64_t E, float cutoff, char *ws, const EfLayout &L, int *status,
                       const int *guard, hipStream_t s);
-// phi24: the filter rows in the 24-bit row format
+// phi24: the filter rows W = fc phi in the 24-bit row format
 sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
-                 const float *pfc, const uint32_t *phi24, const float *in, float *out, const int *guard,
-                 hipStream_t s);
+                 const uint32_t *phi24, const float *in, float *out, const int *guard, hipStream_t s);
 // The integrator's part of an MD step that the force assembly applies as it
 // writes each atom's force: close = the step's closing half kick
 // v += half F / m (and its edge count to edge_slot if set); open = the next
