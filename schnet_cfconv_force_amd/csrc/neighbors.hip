@@ -442,7 +442,8 @@ constexpr int kTileWords = kRepMaxAtoms / 64;
 struct TileArgs {
     const float *pos;
     const int32_t *rptr;
-    int B, N, R;                 // R blocks per replica
+    int B, N;
+    int Rc, R;                   // blocks per replica: count pass, fill pass
     PredParams pp;
     uint64_t *mask;              // [N][kTileWords] row masks
     int32_t *rep;                // [2 B R]: edge count, then longest row, per block
@@ -471,7 +472,7 @@ __device__ inline bool tile_positions(const float *pos, int s, int n, float *sp)
 __global__ __launch_bounds__(kTileThreads) void tile_count_kernel(TileArgs a) {
     __shared__ float sp[3 * kRepMaxAtoms];
     __shared__ int s_sum, s_max;
-    const int b = blockIdx.x / a.R, part = blockIdx.x % a.R;
+    const int b = blockIdx.x / a.Rc, part = blockIdx.x % a.Rc;
     const int s = a.rptr[b], e = a.rptr[b + 1], n = e - s;
     const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
     if (threadIdx.x == 0) {
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_count_kernel(TileArgs a) {
         return;
     }
     const int W = (n + kWave - 1) / kWave;
-    const int per = (n + a.R - 1) / a.R, q0 = part * per, q1 = min(n, q0 + per);
+    const int per = (n + a.Rc - 1) / a.Rc, q0 = part * per, q1 = min(n, q0 + per);
     int sum = 0, mx = 0;
     for (int q = q0 + wv; q < q1; q += kTileWaves) {
         const float xi = sp[3 * q], yi = sp[3 * q + 1], zi = sp[3 * q + 2];
@@ -511,7 +512,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_count_kernel(TileArgs a) {
     __syncthreads();
     if (threadIdx.x == 0) {
         a.rep[blockIdx.x] = s_sum;
-        a.rep[a.B * a.R + blockIdx.x] = s_max;
+        a.rep[a.B * a.Rc + blockIdx.x] = s_max;
     }
 }
 
@@ -535,18 +536,26 @@ __global__ __launch_bounds__(kTileThreads, 8) void tile_fill_kernel(TileArgs a) 
     }
     __syncthreads();
     {
-        const int first = b * a.R;                // this replica's first block: "before" = earlier replicas
+        const int first = b * a.Rc;               // this replica's first count block: "before" = earlier replicas
         unsigned long long before = 0, total = 0;
         int mx = 0;
-        for (int r = threadIdx.x; r < a.B * a.R; r += kTileThreads) {
+        for (int r = threadIdx.x; r < a.B * a.Rc; r += kTileThreads) {
             const unsigned long long v = (unsigned)a.rep[r];
             total += v;
             if (r < first) before += v;
-            mx = max(mx, a.rep[a.B * a.R + r]);
+            mx = max(mx, a.rep[a.B * a.Rc + r]);
         }
-        if (total) atomicAdd(&s_total, total);
-        if (before) atomicAdd(&s_before, before);
-        if (mx) atomicMax(&s_max, mx);
+        // wavefront sums first: one LDS atomic per wavefront and value
+        for (int o = 32; o > 0; o >>= 1) {
+            total += __shfl_xor(total, o, kWave);
+            before += __shfl_xor(before, o, kWave);
+            mx = max(mx, __shfl_xor(mx, o, kWave));
+        }
+        if (lane == 0) {
+            if (total) atomicAdd(&s_total, total);
+            if (before) atomicAdd(&s_before, before);
+            if (mx) atomicMax(&s_max, mx);
+        }
     }
     __syncthreads();
     if (s_st != 0) return;                        // uniform: nothing is written after an error
@@ -732,7 +741,9 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         a.rptr = sys.replica_ptr;
         a.B = B;
         a.N = N;
-        // blocks per replica: about two per CU over the launch
+        // blocks per replica: about one per CU for the count pass and two for
+        // the fill pass (measured best on 64 replicas)
+        a.Rc = std::min(kTileMaxSplit, std::max(1, (256 + B - 1) / B));
         a.R = std::min(kTileMaxSplit, std::max(1, (512 + B - 1) / B));
         a.pp = pp;
         a.mask = pairs ? pairs->mask : reinterpret_cast<uint64_t *>(ws + L.mask);
@@ -747,7 +758,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         a.status = status;
         {
             ProfScope ps(K_NB_COUNT, s);
-            tile_count_kernel<<<B * a.R, kTileThreads, 0, s>>>(a);
+            tile_count_kernel<<<B * a.Rc, kTileThreads, 0, s>>>(a);
             SN_TRY(launch_status());
         }
         {
