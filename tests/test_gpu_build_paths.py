@@ -122,3 +122,52 @@ def test_verlet_on_both_paths_matches_oracle(sn, sizes):
     assert force_errors(forces.cpu().numpy(), f_ref, rp).max() < 1e-3
     ep = epot.cpu().numpy()
     assert np.abs(ep - ep_ref).max() <= 1e-4 * np.abs(ep_ref).max()
+
+
+@pytest.mark.parametrize("F,I,log_ekin", [(32, 1, False), (64, 1, True), (64, 2, False), (128, 2, True)])
+def test_verlet_model_shapes_match_oracle(sn, F, I, log_ekin):
+    """MD on the tile path for other feature widths and interaction counts: with one interaction
+    the last chain reads the embedding rows kept across steps; logging the kinetic energy splits
+    the opening kick from the force assembly."""
+    import torch
+    say(f"[md shapes] F={F} I={I} ekin={log_ekin}")
+    pos, rp = _system([150, 170], 22.0, 40 + F + I)
+    params, hyper = _model(F=F, K=12, I=I, T=4, rc=7.0, seed=F + I)
+    types = np.random.default_rng(F).integers(0, 4, len(pos)).astype(np.int32)
+    inv_mass = np.full(len(pos), 1.0 / 110.0, np.float32)
+    vel = synth.maxwell_boltzmann(len(pos), rp, 110.0, 300.0, 3).astype(np.float32)
+    model = sn.Model(params, hyper)
+    system = sn.System(rp, types)
+    cap = 200 * len(pos)
+    ws = sn.workspace(model, system, cap)
+    p, v, im = dev(pos), dev(vel), dev(inv_mass)
+    row_ptr, col, rev, E = sn.build_csr_neighbors(system, p, 7.0, cap, ws)
+    _, forces = sn.energy_forces(model, system, p, row_ptr, col, rev, E, ws)
+    n, B = 4, len(rp) - 1
+    epot = torch.zeros((n, B), dtype=torch.float32, device="cuda")
+    ekin = torch.zeros((n, B), dtype=torch.float32, device="cuda") if log_ekin else None
+    sn.verlet_step(model, system, p, v, forces, im, 2.0, synth.FORCE_TO_ACCEL, n, 7.0, cap, ws, epot, ekin)
+    torch.cuda.synchronize()
+    r_ref, v_ref, f_ref, ep_ref, ek_ref = O.verlet(params, hyper, types, pos, vel, inv_mass, rp, 2.0,
+                                                   synth.FORCE_TO_ACCEL, n, 7.0)
+    assert np.abs(p.cpu().numpy() - r_ref).max() < 1e-4
+    assert np.abs(v.cpu().numpy() - v_ref).max() < 1e-4 * np.abs(v_ref).max()
+    assert force_errors(forces.cpu().numpy(), f_ref, rp).max() < 1e-3
+    assert np.abs(epot.cpu().numpy() - ep_ref).max() <= 1e-4 * np.abs(ep_ref).max()
+    if log_ekin:
+        assert np.abs(ekin.cpu().numpy() - ek_ref).max() <= 1e-4 * np.abs(ek_ref).max()
+
+
+def test_verlet_empty_system_counts_steps(sn):
+    """No atoms: the steps still complete and every energy is zero."""
+    import torch
+    params, hyper = _model()
+    model = sn.Model(params, hyper)
+    system = sn.System(np.array([0, 0], np.int32), np.zeros(0, np.int32))
+    ws = sn.workspace(model, system, 64)
+    z = torch.zeros((0, 3), dtype=torch.float32, device="cuda")
+    epot = torch.full((3, 1), 7.0, dtype=torch.float32, device="cuda")
+    rp, _, _, ne = sn.verlet_step(model, system, z, z.clone(), z.clone(), torch.zeros(0, device="cuda"), 2.0,
+                                  synth.FORCE_TO_ACCEL, 3, 7.0, 64, ws, epot)
+    torch.cuda.synchronize()
+    assert ne == 0 and np.all(epot.cpu().numpy() == 0.0)
