@@ -153,15 +153,18 @@ __device__ inline void basis8_d(const Basis &b, float u0, float (&rb)[8], float 
     }
 }
 
-// Stage A1 for the first GEMM: s_a1[(m*KS + ks)*64 + l] holds, for output
+// Stage A1 for the first GEMM: s_a1[(m*kKS + ks)*64 + l] holds, for output
 // feature f = 16m + l%16, the weights A1[k][f], k = 32 ks + 8(l/16) + j
-// (zero for k >= K, so basis values beyond K never contribute).  Returns
-// the scale exponent; *s_max must hold 0 on entry.
+// (zero for k >= K, so basis values beyond K never contribute; with K <= 32
+// the kernels skip the second k-step).  The fixed stride of kKS steps makes
+// every fragment offset a compile-time constant.  Returns the scale
+// exponent; *s_max must hold 0 on entry.
+constexpr int kKS = 2;   // 32-wide k-steps of the first layer (K <= 64)
 template <int F, int NTHR>
-__device__ inline int stage_a1(const FilterArgs &a, half8 *s_hi, half8 *s_lo, int KS, unsigned *s_max) {
+__device__ inline int stage_a1(const FilterArgs &a, half8 *s_hi, half8 *s_lo, unsigned *s_max) {
     constexpr int MT = F / 16;
-    return stage_split<MT * 2 * 64, NTHR>(s_hi, s_lo, MT * KS * 64, s_max, [&](int idx, float (&v)[8]) {
-        const int m = idx / (KS * 64), ks = (idx / 64) % KS, l = idx % 64;
+    return stage_split<MT * kKS * 64, NTHR>(s_hi, s_lo, MT * kKS * 64, s_max, [&](int idx, float (&v)[8]) {
+        const int m = idx / (kKS * 64), ks = (idx / 64) % kKS, l = idx % 64;
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = w1<F>(a, 32 * ks + 8 * (l / 16) + j, 16 * m + l % 16);
     });
@@ -231,14 +234,14 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;                      // 32-wide k steps of the F x F GEMM
     constexpr int MG = MT < kFwdMG ? MT : kFwdMG;   // output tiles per group
-    __shared__ half8 s_a1h[MT * 2 * 64], s_a1l[MT * 2 * 64];
+    __shared__ half8 s_a1h[MT * kKS * 64], s_a1l[MT * kKS * 64];
     __shared__ half8 s_a2h[MT * T2 * 64], s_a2l[MT * T2 * 64];   // [m][t][l]: ln2 A2[chain_k(t, l/16, j)][16 m + l%16]
     __shared__ float s_b1[F], s_b2[F];
     __shared__ unsigned s_max[3];
     const int KS = (a.K + 31) / 32;
     int sa1, sa2, sz;
     if (a.pa1h) {
-        copy_frags<MT * 2 * 64, kFwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * KS * 64);
+        copy_frags<MT * kKS * 64, kFwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * kKS * 64);
         copy_frags<MT * T2 * 64, kFwdThreads>(s_a2h, s_a2l, a.pa2h, a.pa2l, MT * T2 * 64);
         sa1 = a.psc1[0];
         sz = a.psc1[1];
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
         if (threadIdx.x < 3) s_max[threadIdx.x] = 0u;
         __syncthreads();
         first_layer_bound<F>(a, &s_max[2]);
-        sa1 = stage_a1<F, kFwdThreads>(a, s_a1h, s_a1l, KS, &s_max[0]);
+        sa1 = stage_a1<F, kFwdThreads>(a, s_a1h, s_a1l, &s_max[0]);
         sa2 = stage_split<MT * T2 * 64, kFwdThreads>(s_a2h, s_a2l, MT * T2 * 64, &s_max[1],
                                                      [&](int idx, float (&v)[8]) { a2_fwd_frag<F>(a, idx, v); });
         sz = split_scale(__uint_as_float(s_max[2]) * kLog2e + 1.0f);
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 if (ks < KS)
-                    mma_split<MG, 1>(s_a1h + (m0 * KS + ks) * 64 + lane, s_a1l + (m0 * KS + ks) * 64 + lane, KS * 64,
+                    mma_split<MG, 1>(s_a1h + (m0 * kKS + ks) * 64 + lane, s_a1l + (m0 * kKS + ks) * 64 + lane, kKS * 64,
                                      &rh[ks], &rl[ks], acc);
 #pragma unroll
             for (int g = 0; g < MG; ++g)
@@ -364,21 +367,21 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;
     constexpr int MG = MT < kBwdMG ? MT : kBwdMG;
-    __shared__ half8 s_a1h[MT * 2 * 64], s_a1l[MT * 2 * 64];      // [m][ks][l] as in the forward pass
+    __shared__ half8 s_a1h[MT * kKS * 64], s_a1l[MT * kKS * 64];      // [m][ks][l] as in the forward pass
     __shared__ half8 s_a2bh[MT * T2 * 64], s_a2bl[MT * T2 * 64];  // [m][t][l]: A2[16 m + l%16][32 t + 8(l/16) + j]
     __shared__ float s_b1[F];
     __shared__ unsigned s_max[2];
     const int KS = (a.K + 31) / 32;
     int sa1, sa2;
     if (a.pa1h) {
-        copy_frags<MT * 2 * 64, kBwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * KS * 64);
+        copy_frags<MT * kKS * 64, kBwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * kKS * 64);
         copy_frags<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, a.pa2h, a.pa2l, MT * T2 * 64);
         sa1 = a.psc1[0];
         sa2 = a.psc2[0];
     } else {
         if (threadIdx.x < 2) s_max[threadIdx.x] = 0u;
         __syncthreads();
-        sa1 = stage_a1<F, kBwdThreads>(a, s_a1h, s_a1l, KS, &s_max[0]);
+        sa1 = stage_a1<F, kBwdThreads>(a, s_a1h, s_a1l, &s_max[0]);
         sa2 = stage_split<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, MT * T2 * 64, &s_max[1],
                                                      [&](int idx, float (&v)[8]) { a2_bwd_frag<F>(a, idx, v); });
     }
@@ -488,7 +491,7 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 if (ks < KS)
-                    mma_split2<MG>(s_a1h + (m0 * KS + ks) * 64 + lane, s_a1l + (m0 * KS + ks) * 64 + lane, KS * 64,
+                    mma_split2<MG>(s_a1h + (m0 * kKS + ks) * 64 + lane, s_a1l + (m0 * kKS + ks) * 64 + lane, kKS * 64,
                                    rh[ks], rl[ks], am, qh[ks], ql[ks], tm);
 #pragma unroll
             for (int m = 0; m < MG; ++m)
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(kFwdThreads) void filter_pack_kernel(FilterPackArgs
     int sc0 = 0, sc1 = 0;
     if (kind == PK_FA1) {
         first_layer_bound<F>(a, &s_max[1]);
-        sc0 = stage_a1<F, kFwdThreads>(a, hi, lo, (a.K + 31) / 32, &s_max[0]);   // its barrier completes s_max[1]
+        sc0 = stage_a1<F, kFwdThreads>(a, hi, lo, &s_max[0]);   // its barrier completes s_max[1]
         sc1 = split_scale(__uint_as_float(s_max[1]) * kLog2e + 1.0f);
     } else if (kind == PK_FA2) {
         sc0 = stage_split<MT * T2 * 64, kFwdThreads>(hi, lo, MT * T2 * 64, &s_max[0],
