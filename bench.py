@@ -162,7 +162,8 @@ def summarize_util(csv_path: str, workload: str, command: str, n_simd: int = 102
     for r in csv.DictReader(open(csv_path)):
         vals[_short_kernel(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
     rows = []
-    for k in ("filter_bwd_kernel", "filter_fwd_kernel", "cfconv_kernel", "mlp_kernel", "rows_kernel"):
+    for k in ("filter_bwd_kernel", "filter_fwd_kernel", "cfconv_kernel", "chain_kernel", "tile_count_kernel",
+              "tile_fill_kernel", "forces_kernel"):
         if k not in vals:
             continue
         m = {c: sum(v) / len(v) for c, v in vals[k].items()}

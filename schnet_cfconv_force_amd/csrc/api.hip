@@ -23,8 +23,8 @@ std::mutex g_prof_mu;
 std::vector<ProfRecord> g_prof_open;   // started, not yet stopped (stack per class)
 std::vector<ProfRecord> g_prof_done;
 const char *kClassNames[K_NUM_CLASSES] = {
-    "nb_grid", "nb_bin", "nb_scan", "nb_count", "nb_fill", "nb_rev", "pairs", "embed", "mlp",
-    "filter_fwd", "cfconv", "readout", "energy", "filter_bwd", "forces", "verlet", "kinetic", "pack"};
+    "nb_grid", "nb_bin", "nb_scan", "nb_count", "nb_fill", "nb_rev", "pairs", "mlp",
+    "filter_fwd", "cfconv", "filter_bwd", "forces", "verlet", "kinetic", "pack"};
 }  // namespace
 
 std::vector<hipEvent_t> g_event_pool;     // reused events (creating events is slow)

@@ -109,8 +109,8 @@ __device__ inline int xcd_block(int n) {
 
 enum KernelClass {
     K_NB_GRID = 0, K_NB_BIN, K_NB_SCAN, K_NB_COUNT, K_NB_FILL, K_NB_REV,
-    K_PAIRS, K_EMBED, K_MLP, K_FILTER_FWD, K_CFCONV, K_READOUT, K_ENERGY,
-    K_FILTER_BWD, K_FORCES, K_VERLET, K_KINETIC, K_PACK, K_NUM_CLASSES
+    K_PAIRS, K_MLP, K_FILTER_FWD, K_CFCONV, K_FILTER_BWD, K_FORCES, K_VERLET, K_KINETIC, K_PACK,
+    K_NUM_CLASSES
 };
 
 void prof_begin(int cls, hipStream_t s);
