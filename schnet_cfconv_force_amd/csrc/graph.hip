@@ -192,6 +192,8 @@ __global__ __launch_bounds__(64 * kCfWaves) void cfconv_kernel(int N, const int3
         }
 }
 
+constexpr int kFrLanes = 16;   // lanes per row of the force assembly (32 was faster for forces alone, slower with the MD kicks)
+
 struct ForcesArgs {
     int N, row_blocks;
     const int32_t *row_ptr, *col, *edge_pair;
@@ -210,8 +212,8 @@ __device__ inline int load_status(const int *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Blocks [0, row_blocks): F_i = sum_{e in row i} S[p(e)] u_e, 16 lanes per
-// row, then the Verlet part for atom i.  Blocks past them: the energy of one
+// Blocks [0, row_blocks): F_i = sum_{e in row i} S[p(e)] u_e, kFrLanes lanes
+// per row, then the Verlet part for atom i.  Blocks past them: the energy of one
 // replica each (fixed-order tree, deterministic).
 __global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
     __shared__ double red[256];
@@ -230,12 +232,12 @@ __global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
     } else {
         if (threadIdx.x == 0) s_go = a.vf.vel && load_status(a.status) == 0;
         __syncthreads();
-        const int sub = threadIdx.x % 16;
-        const int i = (blockIdx.x * 256 + threadIdx.x) / 16;
+        const int sub = threadIdx.x % kFrLanes;
+        const int i = (blockIdx.x * 256 + threadIdx.x) / kFrLanes;
         if (i < a.N && !(a.guard && *a.guard)) {
             const int e0 = a.row_ptr[i], e1 = a.row_ptr[i + 1];
             float fx = 0.f, fy = 0.f, fz = 0.f;
-            for (int e = e0 + sub; e < e1; e += 16) {
+            for (int e = e0 + sub; e < e1; e += kFrLanes) {
                 const int p = a.edge_pair[e];
                 const float4 g = a.pgeo[p];
                 const float s = (a.col[e] > i) ? a.S[p] : -a.S[p];
@@ -243,10 +245,10 @@ __global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
                 fy += s * g.y;
                 fz += s * g.z;
             }
-            for (int o = 8; o > 0; o >>= 1) {
-                fx += __shfl_xor(fx, o, 16);
-                fy += __shfl_xor(fy, o, 16);
-                fz += __shfl_xor(fz, o, 16);
+            for (int o = kFrLanes / 2; o > 0; o >>= 1) {
+                fx += __shfl_xor(fx, o, kFrLanes);
+                fy += __shfl_xor(fy, o, kFrLanes);
+                fz += __shfl_xor(fz, o, kFrLanes);
             }
             if (sub == 0) {
                 a.forces[3 * i] = fx;
@@ -331,7 +333,7 @@ sn_status forces_rows(int N, int B, const int32_t *replica_ptr, const float *eps
     ProfScope ps(K_FORCES, s);
     ForcesArgs a;
     a.N = N;
-    a.row_blocks = (N + 15) / 16;
+    a.row_blocks = (N + 256 / kFrLanes - 1) / (256 / kFrLanes);
     a.row_ptr = row_ptr; a.col = col; a.edge_pair = edge_pair; a.pgeo = pgeo; a.S = S; a.forces = forces;
     a.rptr = replica_ptr; a.eps = eps; a.energy = energy;
     a.vf = vf ? *vf : VerletFuse{};
