@@ -256,14 +256,15 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
                             c1, pr(1), R2, c2, pk(t, PK_BOW1), pk(t, PK_BOW2), eps, gh, gy_t(t), gmax_t(t), s));
         }
     }
-    // backward through the interactions in reverse (g_y of t is ready); the
-    // backward CFConv of t follows the filter backward that has just streamed
-    // the same filter rows
+    // backward through the interactions in reverse (g_y of t is ready).  The
+    // input-gradient CFConv (not needed below the first block) goes first,
+    // while more of the filter rows it reads are still in the Infinity Cache;
+    // the filter backward does not read them.
     for (int t = I - 1; t >= 0; --t) {
-        SN_TRY(filter_backward(m, t, pgeo, pfc, plfc, pair_ij, P, N, phi_t(t), x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
+        if (t > 0) SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, phi_t(t), gy_t(t), y, guard, s));
+        SN_TRY(filter_backward(m, t, pgeo, pfc, plfc, pair_ij, P, N, x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
                                t != I - 1, pack, p_dev, guard, s));
-        if (t > 0) {   // dE/dh below the first block is not needed for forces
-            SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, phi_t(t), gy_t(t), y, guard, s));
+        if (t > 0) {
             SN_TRY(mlp_bx_bo(N, F, y, pk(t, PK_BXW), pk(t - 1, PK_BOW1), o_t(t - 1), pk(t - 1, PK_BOW2), gh,
                              gy_t(t - 1), gmax_t(t - 1), s));
         }

@@ -9,6 +9,10 @@
 // gradient of E with respect to the shared filter row):
 //   g_fc = <G, phi>,  g_phi = fc G,  g_a = (g_phi A2^T) (.) sigmoid(a),
 //   g_rbf = g_a A1^T,  S_p += sum_k g_rbf_k rbf_k'(d) + g_fc fc'(d).
+// The backward does not read the stored rows back: with z = softplus(a),
+// phi = z A2 + b2', b2' = b2 - ln 2 (column sums of A2), so
+// g_fc = <A2 G, z> + <G, b2'> comes from the recomputed first layer and the
+// product g_z = A2 G that the pass forms anyway.
 //
 // Precision.  The products use the split form of split_mfma.h: an operand
 // scaled by a power of two to below 2^14 is held as fp16 hi and lo halves,
@@ -70,7 +74,7 @@ struct FilterArgs {
     const float *fc, *lfc;       // [P]: envelope fc(d_p) and fc'(d_p) / fc(d_p); the forward
                                  // multiplies the stored rows by fc
     const float *x, *gy;         // [N][F]
-    const uint32_t *phi24_in;    // [P][3F/4] (the 24-bit row format)
+    const float *b2f;            // [F]: b2' = b2 - ln 2 (column sums of A2), from the weight pack
     float *S;                    // [P]
     const float *xmax, *gmax;    // [N]: max_f |x_i[f]|, max_f |g_y_i[f]|
     int accumulate;
@@ -370,22 +374,16 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     __shared__ half8 s_a1h[MT * kKS * 64], s_a1l[MT * kKS * 64];      // [m][ks][l] as in the forward pass
     __shared__ half8 s_a2bh[MT * T2 * 64], s_a2bl[MT * T2 * 64];  // [m][t][l]: A2[16 m + l%16][32 t + 8(l/16) + j]
     __shared__ float s_b1[F];
-    __shared__ unsigned s_max[2];
+    __shared__ float4 s_b2f[F / 4];
     const int KS = (a.K + 31) / 32;
-    int sa1, sa2;
-    if (a.pa1h) {
-        copy_frags<MT * kKS * 64, kBwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * kKS * 64);
-        copy_frags<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, a.pa2h, a.pa2l, MT * T2 * 64);
-        sa1 = a.psc1[0];
-        sa2 = a.psc2[0];
-    } else {
-        if (threadIdx.x < 2) s_max[threadIdx.x] = 0u;
-        __syncthreads();
-        sa1 = stage_a1<F, kBwdThreads>(a, s_a1h, s_a1l, &s_max[0]);
-        sa2 = stage_split<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, MT * T2 * 64, &s_max[1],
-                                                     [&](int idx, float (&v)[8]) { a2_bwd_frag<F>(a, idx, v); });
+    // the weights come from the pack (which also holds the folded bias)
+    copy_frags<MT * kKS * 64, kBwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * kKS * 64);
+    copy_frags<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, a.pa2h, a.pa2l, MT * T2 * 64);
+    const int sa1 = a.psc1[0], sa2 = a.psc2[0];
+    for (int f = threadIdx.x; f < F; f += blockDim.x) {
+        s_b1[f] = ldexpf(a.b1[f], sa1);
+        reinterpret_cast<float *>(s_b2f)[f] = a.b2f[f];
     }
-    for (int f = threadIdx.x; f < F; f += blockDim.x) s_b1[f] = ldexpf(a.b1[f], sa1);
     __syncthreads();
     const Basis bs = make_basis(a);
     const float cs = ldexpf(-kLog2e, -sa1);              // recomputed accumulator -> -a log2(e)
@@ -418,11 +416,10 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
             e1 = (bound > 0.0f && bound < INFINITY) ? ilogbf(bound) + 1 : 0;
         }
         const float fs = ldexpf(1.0f, (kSplitTop - 1) - e1);
-        float gfc = 0.0f;
+        float gfc = 0.0f;   // <G, b2'> here; <A2 G, z> below
         half8 gh[T2], gl[T2];
         {
             const int64_t bi = (int64_t)ij.x * F + 8 * slot, bj = (int64_t)ij.y * F + 8 * slot;
-            const int64_t bp = (live ? p : 0) * fp24_words(F) + 6 * slot;   // features 8 slot ..
 #pragma unroll
             for (int t = 0; t < T2; ++t) {
                 asm volatile("" ::: "memory");   // at most one step's gathers in flight
@@ -434,11 +431,10 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
                     const float4 gyj = *reinterpret_cast<const float4 *>(a.gy + bj + o);
                     const float4 xi = *reinterpret_cast<const float4 *>(a.x + bi + o);
                     const float4 xj = *reinterpret_cast<const float4 *>(a.x + bj + o);
-                    const uint3 pw = *reinterpret_cast<const uint3 *>(a.phi24_in + bp + 3 * (o / 4));
-                    const float4 ph = unpack_fp24(pw.x, pw.y, pw.z);
+                    const float4 bf = s_b2f[(o + 8 * slot) / 4];
                     const float g0 = gyi.x * xj.x + gyj.x * xi.x, g1 = gyi.y * xj.y + gyj.y * xi.y;
                     const float g2 = gyi.z * xj.z + gyj.z * xi.z, g3 = gyi.w * xj.w + gyj.w * xi.w;
-                    gfc += g0 * ph.x + g1 * ph.y + g2 * ph.z + g3 * ph.w;
+                    gfc += g0 * bf.x + g1 * bf.y + g2 * bf.z + g3 * bf.w;
                     v[4 * q + 0] = fs * g0; v[4 * q + 1] = fs * g1;
                     v[4 * q + 2] = fs * g2; v[4 * q + 3] = fs * g3;
                 }
@@ -469,7 +465,7 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
         // scaled), then sum_g g_z sigmoid(a) a' -- which is sum_k g_rbf_k
         // rbf_k' up to the envelope and the scales, the RBF part of dE/dd,
         // without forming g_rbf
-        float sk = 0.0f;
+        float sk = 0.0f, zg = 0.0f;
 #pragma unroll
         for (int m0 = 0; m0 < MT; m0 += MG) {
             floatx4 gz[MG][1];
@@ -497,15 +493,22 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
             for (int m = 0; m < MG; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(am[m][r] * cs));
+                    // with y = -a log2(e): sigmoid(a) = 1 / u and softplus(a) log2(e)
+                    // = log2(u) - y, u = 1 + 2^y (the exponent capped at 64, where
+                    // softplus is below 2^-64 and taken as 0)
+                    const float y = am[m][r] * cs;
+                    const float u = 1.0f + __builtin_amdgcn_exp2f(fminf(y, 64.0f));
+                    const float sg = __builtin_amdgcn_rcpf(u);
                     sk = fmaf(gz[m][0][r] * sg, tm[m][r], sk);
+                    zg = fmaf(fmaxf(__builtin_amdgcn_logf(u) - y, 0.0f), gz[m][0][r], zg);
                 }
             // the group is finished before the next group's fragments are read
-            asm volatile("" : "+v"(sk)::"memory");
+            asm volatile("" : "+v"(sk), "+v"(zg)::"memory");
         }
-        // S_p = fc sum_k g_rbf_k rbf_k' + g_fc fc'(d), summed over the four k-slot lanes
-        // (gfc = <G, fc phi> from the stored rows, so gfc fc'/fc = <G, phi> fc')
-        float sp = fmaf(fc * srb, ldexpf(sk, e1 + es), gfc * lfc);
+        // S_p = fc sum_k g_rbf_k rbf_k' + g_fc fc'(d), summed over the four k-slot lanes;
+        // g_fc = <G, phi> = <G, b2'> + ln 2 <A2 G, softplus(a) log2(e)>, and fc' = fc lfc
+        gfc = fmaf(kLn2, ldexpf(zg, e1 + es + sa1), gfc);
+        float sp = fc * fmaf(srb, ldexpf(sk, e1 + es), gfc * lfc);
         sp += __shfl_xor(sp, 16, 64);
         sp += __shfl_xor(sp, 32, 64);
         if (live && slot == 0) a.S[p] = a.accumulate ? a.S[p] + sp : sp;
@@ -517,7 +520,7 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
 // matrix), each staging one matrix exactly as the kernels above would, but
 // into the pack.
 struct FilterWeights {
-    const float *A1, *A2, *b1;
+    const float *A1, *A2, *b1, *b2;
     const int16_t *qA1, *qA2;
     const float *sA1, *sA2;
 };
@@ -557,6 +560,20 @@ __global__ __launch_bounds__(kFwdThreads) void filter_pack_kernel(FilterPackArgs
     } else {
         sc0 = stage_split<MT * T2 * 64, kFwdThreads>(hi, lo, MT * T2 * 64, &s_max[0],
                                                      [&](int idx, float (&v)[8]) { a2_bwd_frag<F>(a, idx, v); });
+        // the backward's folded bias b2' = b2 - ln 2 sum_g A2[g][.]: each of
+        // NP thread groups sums F / NP rows, then the parts are added in order
+        constexpr int NP = kFwdThreads / F;
+        __shared__ float s_part[kFwdThreads];
+        const int f = threadIdx.x % F, part = threadIdx.x / F;
+        float c = 0.0f;
+        for (int g = part * (F / NP); g < (part + 1) * (F / NP); ++g) c += w2<F>(a, g, f);
+        s_part[threadIdx.x] = c;
+        __syncthreads();
+        if (threadIdx.x < F) {
+            float sum = 0.0f;
+            for (int q = 0; q < NP; ++q) sum += s_part[q * F + f];
+            const_cast<float *>(pack_vec(pa.pack, pa.I, t))[f] = fmaf(-kLn2, sum, pa.w[t].b2[f]);
+        }
     }
     if (threadIdx.x == 0) {
         int *sc = const_cast<int *>(r.sc);
@@ -655,7 +672,7 @@ sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s) {
     pa.K = m.n_rbf;
     for (int t = 0; t < I; ++t) {
         const FilterArgs a = make_args(m, t);
-        pa.w[t] = FilterWeights{a.A1, a.A2, a.b1, a.qA1, a.qA2, a.sA1, a.sA2};
+        pa.w[t] = FilterWeights{a.A1, a.A2, a.b1, a.b2, a.qA1, a.qA2, a.sA1, a.sA2};
     }
     ProfScope ps(K_PACK, s);
     switch (m.n_features) {
@@ -693,13 +710,15 @@ sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t
 }
 
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *plfc,
-                          const int2 *pair_ij, int64_t P, int N, const uint32_t *phi24, const float *x, const float *gy,
-                          const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
-                          const int *p_dev, const int *guard, hipStream_t s) {
+                          const int2 *pair_ij, int64_t P, int N, const float *x, const float *gy, const float *xmax,
+                          const float *gmax, float *S, int accumulate, const char *pack, const int *p_dev,
+                          const int *guard, hipStream_t s) {
     if (P <= 0) return SN_OK;
+    if (!pack) return SN_ERR_INVALID;
     (void)N;
     FilterArgs a = make_args(m, t);
     attach_pack(a, m, t, pack, PK_FA2B);
+    a.b2f = pack_vec(pack, m.n_interactions, t);
     a.dsrc = reinterpret_cast<const float *>(pgeo);
     a.dstride = 4;
     a.doff = 3;
@@ -711,7 +730,6 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
     a.lfc = plfc;
     a.x = x;
     a.gy = gy;
-    a.phi24_in = phi24;
     a.S = S;
     a.xmax = xmax;
     a.gmax = gmax;

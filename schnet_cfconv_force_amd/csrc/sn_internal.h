@@ -124,7 +124,7 @@ struct ProfScope {
 
 // --------------------------------------------------------------- workspace
 
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace: [0, 256) status words, then the scratch of the neighbour
 // builder or of the energy/force pipeline (they are never live at the same
@@ -147,7 +147,8 @@ struct EfLayout {            // energy/force scratch (offsets from ws base)
 // straight copy.  One slot per matrix: hi [kPackSlotFrags] then lo
 // [kPackSlotFrags] 16-byte fragments; after all slots, two ints per slot
 // (the power-of-two scale of the split, and one more scale where a kernel
-// needs it).
+// needs it); then, per interaction, kPackVecFloats floats of per-feature
+// constants (the filter backward's folded second-layer bias).
 enum PackKind {
     PK_FA1 = 0,   // filter first layer (both passes)
     PK_FA2,       // filter second layer, forward (chained order, times ln 2)
@@ -162,10 +163,17 @@ enum PackKind {
 };
 constexpr int kPackSlotFrags = 2048;
 constexpr size_t kPackSlotBytes = 2 * size_t(kPackSlotFrags) * 16;
+constexpr int kPackVecFloats = 128;   // the largest feature count
 __host__ __device__ inline int pack_slot(int t, int kind) { return t * PK_PER_T + kind; }
 __host__ __device__ inline int pack_readout_slot(int I, int k) { return I * PK_PER_T + k; }   // k = 0: R1, 1: R1 transposed (chained)
 __host__ __device__ inline int pack_slots(int I) { return I * PK_PER_T + 2; }
-inline size_t pack_bytes(int I) { return pack_slots(I) * kPackSlotBytes + align256(8 * size_t(pack_slots(I))); }
+__host__ __device__ inline size_t pack_vec_offset(int I) {
+    return pack_slots(I) * kPackSlotBytes + align256(8 * size_t(pack_slots(I)));
+}
+inline size_t pack_bytes(int I) { return pack_vec_offset(I) + align256(4 * size_t(kPackVecFloats) * I); }
+__host__ __device__ inline const float *pack_vec(const char *pack, int I, int t) {
+    return reinterpret_cast<const float *>(pack + pack_vec_offset(I)) + kPackVecFloats * t;
+}
 struct PackRef {             // device pointers of one slot
     const void *hi, *lo;
     const int *sc;
@@ -307,11 +315,13 @@ sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, const flo
                          const char *pack, const int *p_dev, const int *guard, hipStream_t s);
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
 // xmax / gmax: per-atom max_f |x[i][f]| and max_f |g_y[i][f]| of interaction t
-// pfc / plfc: per-pair envelope fc(d) and fc'(d) / fc(d); phi24: the rows W = fc phi
+// pfc / plfc: per-pair envelope fc(d) and fc'(d) / fc(d).  The stored rows are
+// not read (the pass recomputes what it needs of them).  pack: the weight pack
+// (required).
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *plfc,
-                          const int2 *pair_ij, int64_t P, int N, const uint32_t *phi24, const float *x, const float *gy,
-                          const float *xmax, const float *gmax, float *S, int accumulate, const char *pack,
-                          const int *p_dev, const int *guard, hipStream_t s);
+                          const int2 *pair_ij, int64_t P, int N, const float *x, const float *gy, const float *xmax,
+                          const float *gmax, float *S, int accumulate, const char *pack, const int *p_dev,
+                          const int *guard, hipStream_t s);
 
 // graph.hip
 // E: the edge count, or -1 to take it from row_ptr[N] on the device.  Writes
