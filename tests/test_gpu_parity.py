@@ -298,6 +298,23 @@ def test_energy_forces_other_model_shapes(sn, F, K, I, T):
     _compare(E, Fo, E_ref, F_ref, eps_abs, rp, f"F={F} K={K}")
 
 
+def test_energy_forces_with_saturated_first_layer(sn):
+    """Half of the first layer's features pushed to a ~ -60, where the sigmoid and softplus are
+    below 1e-26 (the backward filter caps its exponent there, below a = -44): energies and forces
+    still match the oracle."""
+    say("[saturated first layer] tiny_chain, b1 - 60 on even features")
+    base = synth.make_config("tiny_chain")
+    F = base["hyper"]["n_features"]
+    shift = np.where(np.arange(F) % 2 == 0, -60.0, 0.0)
+    blocks = [dict(blk, b1=(blk["b1"] + shift).astype(np.float32)) for blk in base["params"]["interactions"]]
+    cfg = dict(base, params=dict(base["params"], interactions=blocks))
+    L = Loaded(sn, cfg)
+    E, Fo = L.eval(sn)
+    E_ref, F_ref, eps_abs, _ = oracle_full(cfg)
+    assert np.all(np.isfinite(E)) and np.all(np.isfinite(Fo))
+    _compare(E, Fo, E_ref, F_ref, eps_abs, cfg["replica_ptr"], "saturated first layer")
+
+
 def test_graph_without_edges_and_single_atom_replicas(sn):
     """No pair within the cutoff: forces are exactly zero and the energy is the readout of the
     atom-wise layers alone; replicas of one atom and of zero atoms are allowed."""
