@@ -494,13 +494,13 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     // with y = -a log2(e): sigmoid(a) = 1 / u and softplus(a) log2(e)
-                    // = log2(u) - y, u = 1 + 2^y (the exponent capped at 64, where
-                    // softplus is below 2^-64 and taken as 0)
-                    const float y = am[m][r] * cs;
-                    const float u = 1.0f + __builtin_amdgcn_exp2f(fminf(y, 64.0f));
+                    // = log2(u) - y, u = 1 + 2^y.  y is capped at 64: beyond it both
+                    // are below 2^-64 (the cap leaves 2^-64 and 0)
+                    const float y = fminf(am[m][r] * cs, 64.0f);
+                    const float u = 1.0f + __builtin_amdgcn_exp2f(y);
                     const float sg = __builtin_amdgcn_rcpf(u);
                     sk = fmaf(gz[m][0][r] * sg, tm[m][r], sk);
-                    zg = fmaf(fmaxf(__builtin_amdgcn_logf(u) - y, 0.0f), gz[m][0][r], zg);
+                    zg = fmaf(__builtin_amdgcn_logf(u) - y, gz[m][0][r], zg);
                 }
             // the group is finished before the next group's fragments are read
             asm volatile("" : "+v"(sk), "+v"(zg)::"memory");
