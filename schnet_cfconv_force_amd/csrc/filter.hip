@@ -4,7 +4,7 @@
 //
 // Per pair p with distance d_p (one row shared by both directed edges):
 //   a   = rbf(d) A1 + b1            rbf_k = exp(-gamma (d - mu_k)^2), K <= 64
-//   phi = ssp(a) A2 + b2            (the envelope fc(d) is applied by the CFConv)
+//   phi = ssp(a) A2 + b2            (stored times the envelope: W = fc(d) phi, the CFConv's weight)
 // and, in the backward pass, with G_p = g_y_i (.) x_j + g_y_j (.) x_i (the
 // gradient of E with respect to the shared filter row):
 //   g_fc = <G, phi>,  g_phi = fc G,  g_a = (g_phi A2^T) (.) sigmoid(a),
