@@ -225,6 +225,64 @@ def test_forces_match_central_differences_periodic():
     assert np.max(np.abs(f - fd)) <= 1e-6 * np.max(np.abs(f))
 
 
+def _periodic_cell(n=10, L=9.0, seed=31):
+    """n particles in a cubic periodic cell of side L (min distance 1.5 A), 2 types."""
+    params, hyper = _tiny_model(F=8, K=6, I=2, T=2, rc=4.0, seed=13)
+    pos = synth.box_rsa(n, L, 1.5, synth.seed64(seed))
+    types = np.random.default_rng(seed).integers(0, 2, n).astype(np.int32)
+    return params, hyper, pos, types, np.array([L, L, L], np.float32)
+
+
+def test_periodic_energy_and_forces_equal_explicit_replication():
+    """The periodic branch (minimum image) against an open-boundary system built by hand.
+
+    In an I-interaction model the energy of atom i depends on the atoms within I rc of it,
+    and the force on i on the atom energies within I rc of i, whose own inputs reach
+    another I rc: with a shell of 2 L >= 2 I rc (L = 9, rc = 4, I = 2) around the central
+    cell, the 5 x 5 x 5 replication gives the central atoms their full periodic environment.
+    Their atom energies and forces must then equal the periodic system's; the sum of the
+    central atom energies is the periodic energy.  Removing the minimum image from the
+    oracle's pair geometry breaks this (the cross-boundary pairs would fall beyond rc).
+    """
+    params, hyper, pos, types, box = _periodic_cell()
+    L = float(box[0])
+    n = len(pos)
+    rp1 = np.array([0, n], np.int32)
+    csr_p = O.neighbors_bruteforce(pos.astype(np.float32), rp1, hyper["cutoff"], box)
+    Ep, Fp, inter_p = O.energy_forces(params, hyper, types, pos, rp1, csr_p, box, return_intermediates=True)
+    shifts = np.array([(a, b, c) for a in range(-2, 3) for b in range(-2, 3) for c in range(-2, 3)], np.float64)
+    centre = int(np.flatnonzero((shifts == 0).all(axis=1))[0])
+    big = (pos[None, :, :] + L * shifts[:, None, :]).reshape(-1, 3)
+    big_types = np.tile(types, len(shifts))
+    rpb = np.array([0, len(big)], np.int32)
+    csr_o = O.neighbors_bruteforce(big.astype(np.float32), rpb, hyper["cutoff"])
+    # every image pair the periodic list holds appears in the open one (no ties at rc)
+    assert len(csr_p[1]) > 2 * n
+    _, Fo, inter_o = O.energy_forces(params, hyper, big_types, big, rpb, csr_o, return_intermediates=True)
+    sl = slice(centre * n, (centre + 1) * n)
+    eps_o, eps_p = inter_o["eps"][sl], inter_p["eps"]
+    assert np.max(np.abs(eps_o - eps_p)) <= 1e-12 * np.max(np.abs(eps_p))
+    assert abs(eps_o.sum() - Ep[0]) <= 1e-12 * np.abs(eps_p).sum()
+    assert np.max(np.abs(Fo[sl] - Fp)) <= 1e-12 * np.max(np.abs(Fp))
+    assert np.max(np.abs(Fp)) > 1e-3                      # the cell does interact
+
+
+def test_periodic_lattice_translation_invariance():
+    """Shifting every atom by one vector and wrapping into [0, L) leaves the periodic energy and
+    forces unchanged (the wrap moves atoms across the boundary, so pairs change images)."""
+    params, hyper, pos, types, box = _periodic_cell(seed=47)
+    L = float(box[0])
+    rp1 = np.array([0, len(pos)], np.int32)
+    E0, F0 = _ef(params, hyper, types, pos, rp1, box)
+    rng = np.random.default_rng(8)
+    for _ in range(3):
+        moved = np.mod(pos + rng.uniform(0.0, L, 3), L)
+        assert np.any(np.abs(moved - pos - (moved - pos).mean(axis=0)) > 1.0)   # some atoms wrapped
+        E1, F1 = _ef(params, hyper, types, moved, rp1, box)
+        assert abs(E1[0] - E0[0]) <= 1e-12 * abs(E0[0])
+        assert np.max(np.abs(F1 - F0)) <= 1e-11 * np.max(np.abs(F0))
+
+
 def test_net_force_and_torque_vanish():
     c = synth.make_config("batched_replicas", n_replicas=3)
     pos = c["pos"].astype(np.float64)
