@@ -176,18 +176,48 @@ sn_status sn_energy_forces(const sn_model *model, const sn_system *sys, const fl
                            int64_t n_edges, float *energy /* [B] */, float *forces /* [N][3] */,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* Flags of sn_verlet_step. */
+#define SN_MD_GRAPH 1u  /* record one rebuild interval of steps as a HIP graph and replay it */
+
 /* Velocity Verlet over all replicas ("Achievement" item 1, FlashSchNet
- * summary page: aggregate MD throughput of parallel replicas).
+ * summary page: aggregate MD throughput of parallel replicas; the neighbour
+ * skin and the replay of each rebuild interval as one graph follow the
+ * abstract of "Ab Initio Accuracy Beyond the Cutoff ..." (Tessera), which
+ * keeps the list topology across updates with a conservative skin).
  * Per step, with a = force_to_accel * F * inv_mass:
- *     v += dt/2 a;  r += dt v;  rebuild the neighbour list at r_list;
+ *     v += dt/2 a;  r += dt v;  (re)build the neighbour list at r_list;
  *     F = F(r);  v += dt/2 a
  * On entry `forces` must hold F(r) for the entry positions (call
  * sn_energy_forces once before the first step); on return it holds F at the
  * final positions.  pos, vel, forces [N][3] are updated in place;
- * inv_mass[N].  row_ptr/col_idx/rev_idx (capacity as above) receive the
- * last neighbour list and *n_edges its size (host).  epot_log and ekin_log,
- * if not NULL, receive per step and replica the potential energy and
- * 0.5 sum m v^2 / force_to_accel ([n_steps][B], device); edge_log, if not
+ * inv_mass[N].
+ *
+ * Neighbour list.  rebuild_every = 1 rebuilds it at r_list every step (exact
+ * for r_list >= cutoff).  Any other value keeps a list built at r_list =
+ * cutoff + skin across steps: it is rebuilt at the call's first step, every
+ * rebuild_every steps (0: never on a schedule), and at the step after any
+ * atom has drifted more than skin/2 from where it was at the last build
+ * (checked on the device during the drift; no host synchronisation).  Every
+ * pair within the cutoff is then always in the list (two atoms close in by
+ * at most skin), and the kept pairs get their geometry from the current
+ * positions each step; pairs beyond the cutoff have a zero envelope and
+ * contribute exactly nothing, so results equal those of a per-step rebuild
+ * up to summation order.  With skin <= 0 any motion triggers a rebuild.
+ * The list is still built in full when it is rebuilt; skin pairs cost filter
+ * work (about ((cutoff + skin)/cutoff)^3 - 1 more pairs).
+ *
+ * flags: 0 or SN_MD_GRAPH.  With SN_MD_GRAPH the launches of one rebuild
+ * interval (rebuild_every steps when it is above 1, else 10 steps; at most
+ * n_steps) are recorded once, on a private stream, as a HIP graph that is
+ * replayed on `stream`; the steps left over run as ordinary launches.  The
+ * results are bit-identical to the same call without the flag.
+ *
+ * row_ptr/col_idx/rev_idx (capacity as above) receive the last neighbour
+ * list built (at r_list) and *n_edges its size (host).  epot_log and
+ * ekin_log, if not NULL, receive per step and replica the potential energy
+ * and 0.5 sum m v^2 / force_to_accel ([n_steps][B] doubles, device; both are
+ * sums over the replica's atoms taken in fp64, so that the drift of their
+ * sum is resolved below fp32 rounding); edge_log, if not
  * NULL, the edge count of each step's neighbour list ([n_steps], device).
  * The steps run without host synchronisation: the edge and pair counts stay
  * on the device, the capacity and row-length checks run there, and the
@@ -196,12 +226,14 @@ sn_status sn_energy_forces(const sn_model *model, const sn_system *sys, const fl
  * the kernels that read a neighbour list do nothing; the call returns that
  * error, with *n_steps_done (host, may be NULL) = the steps completed before
  * it; pos, vel, forces and the neighbour-list outputs then hold the state of
- * the failing step, not a valid one. */
+ * the failing step, not a valid one.  SN_ERR_INVALID also for
+ * rebuild_every < 0 or an unknown flag; SN_ERR_HIP if recording or
+ * replaying the graph fails. */
 sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos, float *vel, float *forces,
                          const float *inv_mass, float dt, float force_to_accel, int32_t n_steps,
-                         float r_list, int32_t *row_ptr, int32_t *col_idx, int32_t *rev_idx,
-                         int64_t capacity, int64_t *n_edges, float *epot_log, float *ekin_log,
-                         int32_t *edge_log, int32_t *n_steps_done, void *ws, size_t ws_bytes, void *stream);
+                         int32_t rebuild_every, float r_list, int32_t *row_ptr, int32_t *col_idx, int32_t *rev_idx,
+                         int64_t capacity, int64_t *n_edges, double *epot_log, double *ekin_log, int32_t *edge_log,
+                         int32_t *n_steps_done, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /* Filter network alone ("How", flash radial basis and the filter network,
  * FlashSchNet summary page): phi[p][F] = ssp(rbf(d_p) A1 + b1) A2 + b2 of

@@ -24,6 +24,7 @@ SN_ERR_NONFINITE = -5
 SN_ERR_WORKSPACE = -6
 SN_ERR_ROW = -7
 SN_MAX_ROW = 2048
+SN_MD_GRAPH = 1
 
 EXPORTED = (
     "sn_param_count", "sn_param_offsets", "sn_quantize_filter_weights", "sn_workspace_bytes",
@@ -76,8 +77,8 @@ def lib() -> ctypes.CDLL:
         "sn_version": (i32, []),
         "sn_build_csr_neighbors": (i32, [PS, vp, f32, vp, vp, vp, i64, P64, vp, sz, vp]),
         "sn_energy_forces": (i32, [PM, PS, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]),
-        "sn_verlet_step": (i32, [PM, PS, vp, vp, vp, vp, f32, f32, i32, f32, vp, vp, vp, i64, P64, vp, vp, vp,
-                                 ctypes.POINTER(ctypes.c_int32), vp, sz, vp]),
+        "sn_verlet_step": (i32, [PM, PS, vp, vp, vp, vp, f32, f32, i32, i32, f32, vp, vp, vp, i64, P64, vp, vp, vp,
+                                 ctypes.POINTER(ctypes.c_int32), ctypes.c_uint32, vp, sz, vp]),
         "sn_filter_forward": (i32, [PM, i32, vp, i64, vp, vp]),
         "sn_read_status": (i32, [vp, vp]),
         "sn_profile_enable": (None, [i32]),
@@ -258,9 +259,12 @@ def energy_forces(model: Model, system: System, pos, row_ptr, col, rev, n_edges:
 
 def verlet_step(model: Model, system: System, pos, vel, forces, inv_mass, dt: float, force_to_accel: float,
                 n_steps: int, r_list: float, capacity: int, ws, epot_log=None, ekin_log=None, csr=None,
-                stream=None, edge_log=None):
+                stream=None, edge_log=None, rebuild_every: int = 1, graph: bool = False):
     """sn_verlet_step; pos, vel, forces are updated in place.  Returns (row_ptr, col, rev, n_edges).
-    edge_log (optional int32 device tensor [n_steps]) receives each step's edge count."""
+    epot_log, ekin_log (optional float64 device tensors [n_steps, B]) receive each step's replica energies,
+    edge_log (optional int32 device tensor [n_steps]) each step's edge count.
+    rebuild_every != 1 keeps a list built at r_list = cutoff + skin across steps (rebuilt on schedule
+    and when an atom drifts beyond skin/2); graph=True replays one rebuild interval as a HIP graph."""
     torch = _torch()
     dev = pos.device
     if csr is None:
@@ -269,13 +273,20 @@ def verlet_step(model: Model, system: System, pos, vel, forces, inv_mass, dt: fl
         rev = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
     else:
         row_ptr, col, rev = csr
+    # the logs are written by the device: wrong types or sizes would be written out of bounds
+    for name, t, dt_ in (("epot_log", epot_log, torch.float64), ("ekin_log", ekin_log, torch.float64),
+                         ("edge_log", edge_log, torch.int32)):
+        need = n_steps * (system.n_replicas if name != "edge_log" else 1)
+        if t is not None and (t.dtype != dt_ or t.numel() < need or not t.is_contiguous() or t.device != dev):
+            raise ValueError(f"{name} must be a contiguous {dt_} tensor on {dev} with at least {need} values")
     ne = ctypes.c_int64(0)
     done = ctypes.c_int32(0)
     st = lib().sn_verlet_step(ctypes.byref(model.c), ctypes.byref(system.c), pos.data_ptr(), vel.data_ptr(),
                               forces.data_ptr(), inv_mass.data_ptr(), float(dt), float(force_to_accel),
-                              int(n_steps), float(r_list), row_ptr.data_ptr(), col.data_ptr(), rev.data_ptr(),
-                              int(capacity), ctypes.byref(ne), _ptr(epot_log), _ptr(ekin_log), _ptr(edge_log),
-                              ctypes.byref(done), ws.data_ptr(), ws.numel(), _stream(stream))
+                              int(n_steps), int(rebuild_every), float(r_list), row_ptr.data_ptr(), col.data_ptr(),
+                              rev.data_ptr(), int(capacity), ctypes.byref(ne), _ptr(epot_log), _ptr(ekin_log),
+                              _ptr(edge_log), ctypes.byref(done), SN_MD_GRAPH if graph else 0, ws.data_ptr(),
+                              ws.numel(), _stream(stream))
     if st != SN_OK:
         err = SnError(st, "sn_verlet_step")
         err.steps_done = done.value

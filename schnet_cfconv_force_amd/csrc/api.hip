@@ -1,6 +1,7 @@
 // C-ABI entry points of libsn.so: argument checks, workspace carving, the
 // energy/force pipeline, the velocity-Verlet driver and per-kernel timing.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -12,22 +13,27 @@
 namespace sn {
 
 // --------------------------------------------------------------- timing
+//
+// The per-kernel timer is the library's only process-wide state: a switch
+// and the lists of recorded events, all behind one mutex (the switch is an
+// atomic).  It is a measuring aid, off unless sn_profile_enable() turns it
+// on; launches recorded into a HIP graph are never timed.
 
 namespace {
 struct ProfRecord {
     int cls;
     hipEvent_t start, stop;
 };
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
+thread_local bool t_capturing = false;   // this thread is recording a HIP graph
 std::mutex g_prof_mu;
 std::vector<ProfRecord> g_prof_open;   // started, not yet stopped (stack per class)
 std::vector<ProfRecord> g_prof_done;
+std::vector<hipEvent_t> g_event_pool;  // reused events (creating events is slow)
 const char *kClassNames[K_NUM_CLASSES] = {
     "nb_grid", "nb_bin", "nb_scan", "nb_count", "nb_fill", "nb_rev", "pairs", "mlp",
     "filter_fwd", "cfconv", "filter_bwd", "forces", "verlet", "kinetic", "pack"};
 }  // namespace
-
-std::vector<hipEvent_t> g_event_pool;     // reused events (creating events is slow)
 
 static hipEvent_t pooled_event() {
     if (!g_event_pool.empty()) {
@@ -41,7 +47,7 @@ static hipEvent_t pooled_event() {
 }
 
 void prof_begin(int cls, hipStream_t s) {
-    if (!g_prof_on) return;
+    if (!g_prof_on.load(std::memory_order_relaxed) || t_capturing) return;
     std::lock_guard<std::mutex> g(g_prof_mu);
     ProfRecord r{cls, pooled_event(), pooled_event()};
     if (!r.start || !r.stop) return;
@@ -50,7 +56,7 @@ void prof_begin(int cls, hipStream_t s) {
 }
 
 void prof_end(int cls, hipStream_t s) {
-    if (!g_prof_on) return;
+    if (!g_prof_on.load(std::memory_order_relaxed) || t_capturing) return;
     std::lock_guard<std::mutex> g(g_prof_mu);
     for (size_t k = g_prof_open.size(); k-- > 0;) {
         if (g_prof_open[k].cls == cls) {
@@ -94,6 +100,7 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     L.rep = take(8 * kTileMaxSplit * B);   // the tile neighbour build's per-block counts
     L.mask = take(8 * (kRepMaxAtoms / 64) * N);   // and its row masks
     L.h0 = take(4 * N * F);                // the embedding rows (kept across MD steps)
+    L.ref_pos = take(12 * N);              // positions at the last neighbour build (skin)
     L.total = o;
     return L;
 }
@@ -111,20 +118,55 @@ sn_status clear_status(void *ws, hipStream_t s) {
 
 // A step's opening half kick v += dt/2 c F / m and drift r += dt v (the
 // closing kick runs in the force assembly).  Nothing moves once an error is
-// flagged.
+// flagged.  Device-driven steps (n_total >= 0): only when the current step
+// (status slot kMdStep minus one) is not the call's last; with ref_pos set,
+// an atom that ends more than sqrt(half_skin2) from it sets kDisplaced.
 __global__ void open_step_kernel(int N, float *pos, float *vel, const float *forces, const float *inv_mass,
-                                 float half_dt_c, float dt, const int *status) {
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= 3 * N || *status != 0) return;
-    const float v = vel[idx] + half_dt_c * forces[idx] * inv_mass[idx / 3];
-    pos[idx] += dt * v;
-    vel[idx] = v;
+                                 float half_dt_c, float dt, int *status, int n_total, const float *ref_pos,
+                                 float half_skin2) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N || status[kStatusWord] != 0) return;
+    if (n_total >= 0 && status[kMdStep] >= n_total) return;
+    float r2 = 0.0f;
+    for (int c = 0; c < 3; ++c) {
+        // explicit fused multiply-adds, as in the force assembly's kicks
+        const float v = fmaf(half_dt_c * forces[3 * i + c], inv_mass[i], vel[3 * i + c]);
+        const float r = fmaf(dt, v, pos[3 * i + c]);
+        pos[3 * i + c] = r;
+        vel[3 * i + c] = v;
+        if (ref_pos) {
+            const float dr = r - ref_pos[3 * i + c];
+            r2 = fmaf(dr, dr, r2);
+        }
+    }
+    if (ref_pos && !(r2 <= half_skin2))
+        __hip_atomic_store(status + kDisplaced, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The first launch of a device-driven MD step (one thread): advances the
+// step counter, records the step as begun while no error is flagged, and
+// decides whether the step rebuilds the neighbour list: at the call's first
+// step, when an atom left half the skin during the last drift, and every
+// rebuild_every steps (0: only on displacement).
+__global__ void md_begin_kernel(int *status, int rebuild_every) {
+    if (threadIdx.x != 0) return;
+    const int step = status[kMdStep];
+    status[kMdStep] = step + 1;
+    if (status[kStatusWord] == 0) status[kStepsDone] = step;
+    const bool build = step == 0 || status[kDisplaced] != 0 ||
+                       (rebuild_every > 0 && step - status[kLastBuild] >= rebuild_every);
+    status[kBuildFlag] = build ? 1 : 0;
+    status[kDisplaced] = 0;
+    if (build) status[kLastBuild] = step;
+}
+
+// out[b] = sum over replica b of m v^2 / (2 c), in fp64; step_status (may be
+// null): device-driven steps, out[(status[kMdStep] - 1) B + b]
 __global__ __launch_bounds__(256) void kinetic_kernel(const int32_t *rptr, const float *vel, const float *inv_mass,
-                                                      float inv_2c, float *out) {
+                                                      double inv_2c, double *out, const int *step_status) {
     __shared__ double red[256];
     const int b = blockIdx.x;
+    if (step_status) out += (int64_t)(step_status[kMdStep] - 1) * gridDim.x;
     double s = 0.0;
     for (int i = rptr[b] + threadIdx.x; i < rptr[b + 1]; i += 256) {
         double v2 = (double)vel[3 * i] * vel[3 * i] + (double)vel[3 * i + 1] * vel[3 * i + 1] +
@@ -137,7 +179,7 @@ __global__ __launch_bounds__(256) void kinetic_kernel(const int32_t *rptr, const
         if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
-    if (threadIdx.x == 0) out[b] = (float)(red[0] * inv_2c);
+    if (threadIdx.x == 0) out[b] = red[0] * inv_2c;
 }
 
 sn_status check_system(const sn_system *sys) {
@@ -184,10 +226,16 @@ size_t bytes_needed(const sn_model *m, const sn_system *s, int64_t E) {
 // vf: the integrator's part applied with the forces (MD steps).
 // embedded: h0, x_0 and its row maxima are current (the types do not change
 // during an MD call).
+// build_flag (may be null): the pair setup runs only when *build_flag is set
+// (device-driven MD steps; on the others the pair arrays are kept and their
+// geometry refreshed).  elog (may be null): the replica energies in fp64,
+// at elog[step B + b] with elog_by_step (device-driven steps).  energy may be
+// null when elog is set.
 sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const float *pos, const int32_t *row_ptr,
                              const int32_t *col, const int32_t *rev, int64_t E, float *energy, float *forces,
                              char *ws, hipStream_t s, bool device_edges = false, bool packed = false,
-                             bool pairs_ready = false, const VerletFuse *vf = nullptr, bool embedded = false) {
+                             bool pairs_ready = false, const VerletFuse *vf = nullptr, bool embedded = false,
+                             const int *build_flag = nullptr, double *elog = nullptr, int elog_by_step = 0) {
     const int N = sys.n_atoms, B = sys.n_replicas, F = m.n_features, I = m.n_interactions;
     const int64_t P = E / 2;
     int *status = reinterpret_cast<int *>(ws);
@@ -195,7 +243,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     float *eps = reinterpret_cast<float *>(ws + L.eps);
     if (N == 0)
         return forces_rows(0, B, sys.replica_ptr, eps, energy, row_ptr, col, nullptr, nullptr, nullptr, forces, status,
-                           nullptr, vf, s);
+                           nullptr, vf, s, elog, elog_by_step);
 
     int64_t off[9 * 16 + 6];
     sn_param_offsets(m.n_types, I, F, m.n_rbf, off, (int32_t)(sizeof(off) / sizeof(off[0])));
@@ -237,7 +285,8 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
         SN_TRY(mlp_pack(m, pack, s));
     }
     if (!pairs_ready)
-        SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, device_edges ? -1 : E, m.cutoff, ws, L, status, guard, s));
+        SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, device_edges ? -1 : E, m.cutoff, ws, L, status, guard, s,
+                           build_flag));
     SN_TRY(filter_forward(m, 0, pgeo, pfc, P, phi_t(0), pack, p_dev, guard, s));
     if (!embedded)
         SN_TRY(mlp_embed_x(N, F, m.n_types, sys.types, prm + off[0], pk(0, PK_XW), h0, x_t(0), xmax_t(0), status, s));
@@ -270,8 +319,27 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
         }
     }
     return forces_rows(N, B, sys.replica_ptr, eps, energy, row_ptr, col, edge_pair, pgeo, S, forces, status, guard,
-                       vf, s);
+                       vf, s, elog, elog_by_step);
 }
+
+// Ends a stream capture that an error interrupted and frees what it made.
+struct CaptureGuard {
+    hipStream_t cs = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    bool open = false;
+    ~CaptureGuard() {
+        t_capturing = false;
+        if (open) {
+            hipGraph_t g = nullptr;
+            (void)hipStreamEndCapture(cs, &g);
+            if (g) (void)hipGraphDestroy(g);
+        }
+        if (exec) (void)hipGraphExecDestroy(exec);
+        if (graph) (void)hipGraphDestroy(graph);
+        if (cs) (void)hipStreamDestroy(cs);
+    }
+};
 
 }  // namespace
 }  // namespace sn
@@ -280,7 +348,7 @@ using namespace sn;
 
 extern "C" {
 
-int32_t sn_version(void) { return 1; }
+int32_t sn_version(void) { return 2; }
 
 const char *sn_status_string(sn_status st) {
     switch (st) {
@@ -393,15 +461,15 @@ sn_status sn_energy_forces(const sn_model *model, const sn_system *sys, const fl
 }
 
 sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos, float *vel, float *forces,
-                         const float *inv_mass, float dt, float force_to_accel, int32_t n_steps, float r_list,
-                         int32_t *row_ptr, int32_t *col_idx, int32_t *rev_idx, int64_t capacity, int64_t *n_edges,
-                         float *epot_log, float *ekin_log, int32_t *edge_log, int32_t *n_steps_done, void *ws,
-                         size_t ws_bytes, void *stream) {
+                         const float *inv_mass, float dt, float force_to_accel, int32_t n_steps,
+                         int32_t rebuild_every, float r_list, int32_t *row_ptr, int32_t *col_idx, int32_t *rev_idx,
+                         int64_t capacity, int64_t *n_edges, double *epot_log, double *ekin_log, int32_t *edge_log,
+                         int32_t *n_steps_done, uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
     if (n_steps_done) *n_steps_done = 0;
     SN_TRY(check_system(sys));
     SN_TRY(check_model(model));
-    if (n_steps < 0 || !n_edges || !row_ptr || !(r_list > 0.0f) || !std::isfinite(dt) ||
-        !std::isfinite(force_to_accel))
+    if (n_steps < 0 || rebuild_every < 0 || (flags & ~uint32_t(SN_MD_GRAPH)) != 0 || !n_edges || !row_ptr ||
+        !(r_list > 0.0f) || !std::isfinite(r_list) || !std::isfinite(dt) || !std::isfinite(force_to_accel))
         return SN_ERR_INVALID;
     const int N = sys->n_atoms, B = sys->n_replicas;
     if (N > 0 && (!pos || !vel || !forces || !inv_mass || !col_idx || !rev_idx)) return SN_ERR_INVALID;
@@ -411,13 +479,22 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
     SN_TRY(clear_status(ws, s));
     int *status = reinterpret_cast<int *>(w);
     const float half = 0.5f * dt * force_to_accel;
+    // Steps are either host-driven (the list rebuilt every step, each step's
+    // log slots passed as arguments) or device-driven: a neighbour skin
+    // (rebuild_every != 1) or graph replay needs every step's launches to be
+    // identical, so the step index, the rebuild decision and the log slots
+    // then live in the status words (md_begin_kernel).
+    const bool skin = rebuild_every != 1;
+    const bool device_steps = skin || (flags & SN_MD_GRAPH);
+    const float half_skin = 0.5f * (r_list - model->cutoff);
+    const float half_skin2 = half_skin > 0.0f ? half_skin * half_skin : 0.0f;
     // no host synchronisation inside the loop: the neighbour build and the
     // pipeline take the edge and pair counts on the device, errors are
     // flagged in the status word (after which nothing moves and the kernels
     // that read the neighbour list do nothing), and the counters are read
     // once at the end
     const EfLayout L = ef_layout(*model, *sys, capacity, kWsBase);
-    float *eps_scratch = reinterpret_cast<float *>(w + L.eps) + N;
+    float *ref_pos = skin ? reinterpret_cast<float *>(w + L.ref_pos) : nullptr;
     // the weights do not change during the call: one weight pack serves every
     // step, unless the neighbour build's scratch reaches into it
     const size_t nb_end = nb_layout(*sys, kWsBase).total;
@@ -449,38 +526,89 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
     pairs.cutoff = model->cutoff;
     pairs.mask = reinterpret_cast<uint64_t *>(w + L.mask);
     pairs.rep = reinterpret_cast<int32_t *>(w + L.rep);
-    auto open_step = [&]() -> sn_status {
+    // the opening half kick and drift: host-driven steps pass n_total = -1
+    // (always), device-driven ones let the kernel skip it after the last step
+    auto open_step = [&](hipStream_t st, int n_total, const float *ref) -> sn_status {
         if (N == 0) return SN_OK;
-        ProfScope ps(K_VERLET, s);
-        open_step_kernel<<<(3 * N + 255) / 256, 256, 0, s>>>(N, pos, vel, forces, inv_mass, half, dt, status);
+        ProfScope ps(K_VERLET, st);
+        open_step_kernel<<<(N + 255) / 256, 256, 0, st>>>(N, pos, vel, forces, inv_mass, half, dt, status, n_total,
+                                                          ref, half_skin2);
         return launch_status();
+    };
+    // one step; `step` is only used by host-driven steps
+    const int *build_flag = device_steps ? status + kBuildFlag : nullptr;
+    auto one_step = [&](hipStream_t st, int32_t step) -> sn_status {
+        if (device_steps) {
+            ProfScope ps(K_VERLET, st);
+            md_begin_kernel<<<1, 64, 0, st>>>(status, rebuild_every);
+            SN_TRY(launch_status());
+        }
+        int64_t E_unused = 0;
+        bool pairs_done = false;
+        // host-driven: the build marks the step as begun without error (the steps completed)
+        SN_TRY(nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, &E_unused, w, st, false, max_rep,
+                        &pairs, &pairs_done, device_steps ? -1 : step, build_flag));
+        if (skin) SN_TRY(pairs_refresh(*sys, pos, model->cutoff, w, L, status, capacity / 2, st));
+        double *elog = epot_log ? (device_steps ? epot_log : epot_log + (int64_t)step * B) : nullptr;
+        // the force assembly closes this step and opens the next (unless the
+        // kinetic energy is logged between the two)
+        VerletFuse vf{};
+        vf.pos = pos;
+        vf.vel = vel;
+        vf.inv_mass = inv_mass;
+        vf.half = half;
+        vf.dt = dt;
+        vf.close = 1;
+        vf.ref_pos = ref_pos;
+        vf.half_skin2 = half_skin2;
+        if (device_steps) {
+            vf.open = !ekin_log;
+            vf.n_total = n_steps;
+            vf.edge_log = edge_log;
+        } else {
+            vf.open = step + 1 < n_steps && !ekin_log;
+            vf.n_total = -1;
+            vf.edge_slot = edge_log ? edge_log + step : nullptr;
+        }
+        SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, capacity, nullptr, forces, w, st,
+                                  true, pack_once, pairs_done, &vf, embed_once, build_flag, elog,
+                                  device_steps ? 1 : 0));
+        if (ekin_log) {
+            {
+                ProfScope ps(K_KINETIC, st);
+                kinetic_kernel<<<B, 256, 0, st>>>(sys->replica_ptr, vel, inv_mass, 0.5 / (double)force_to_accel,
+                                                  device_steps ? ekin_log : ekin_log + (int64_t)step * B,
+                                                  device_steps ? status : nullptr);
+                SN_TRY(launch_status());
+            }
+            if (device_steps) SN_TRY(open_step(st, n_steps, ref_pos));
+            else if (step + 1 < n_steps) SN_TRY(open_step(st, -1, nullptr));
+        }
+        return SN_OK;
     };
     // the first step's opening kick and drift; each later one runs in the
     // previous step's force assembly (unless the kinetic energy is logged between)
-    if (n_steps > 0) SN_TRY(open_step());
-    for (int32_t step = 0; step < n_steps; ++step) {
-        int64_t E_unused = 0;
-        bool pairs_done = false;
-        // the build marks the step as begun without error (the steps completed)
-        SN_TRY(nb_build(*sys, pos, r_list, row_ptr, col_idx, rev_idx, capacity, &E_unused, w, s, false, max_rep,
-                        &pairs, &pairs_done, step));
-        float *eout = epot_log ? epot_log + (int64_t)step * B : eps_scratch;
-        // the force assembly closes this step and opens the next (unless the
-        // kinetic energy is logged between the two)
-        const int open_next = step + 1 < n_steps;
-        const VerletFuse vf{pos, vel, inv_mass, half, dt, 1, open_next && !ekin_log,
-                            edge_log ? edge_log + step : nullptr};
-        SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, capacity, eout, forces, w, s, true,
-                                  pack_once, pairs_done, &vf, embed_once));
-        if (ekin_log) {
-            {
-                ProfScope ps(K_KINETIC, s);
-                kinetic_kernel<<<B, 256, 0, s>>>(sys->replica_ptr, vel, inv_mass, 0.5f / force_to_accel,
-                                                 ekin_log + (int64_t)step * B);
-                SN_TRY(launch_status());
-            }
-            if (open_next) SN_TRY(open_step());
-        }
+    if (n_steps > 0) SN_TRY(open_step(s, -1, nullptr));
+    int32_t done = 0;
+    if ((flags & SN_MD_GRAPH) && n_steps > 0) {
+        // one rebuild interval recorded as a HIP graph (on a private stream;
+        // nothing runs while recording) and replayed on the caller's stream
+        const int32_t G = std::max(1, std::min(n_steps, rebuild_every > 1 ? rebuild_every : 10));
+        CaptureGuard cg;
+        SN_HIP(hipStreamCreateWithFlags(&cg.cs, hipStreamNonBlocking));
+        SN_HIP(hipStreamBeginCapture(cg.cs, hipStreamCaptureModeThreadLocal));
+        cg.open = true;
+        t_capturing = true;
+        for (int32_t g = 0; g < G; ++g) SN_TRY(one_step(cg.cs, -1));
+        t_capturing = false;
+        cg.open = false;
+        SN_HIP(hipStreamEndCapture(cg.cs, &cg.graph));
+        SN_HIP(hipGraphInstantiate(&cg.exec, cg.graph, nullptr, nullptr, 0));
+        for (; done + G <= n_steps; done += G) SN_HIP(hipGraphLaunch(cg.exec, s));
+        for (; done < n_steps; ++done) SN_TRY(one_step(s, done));
+        SN_HIP(hipStreamSynchronize(s));
+    } else {
+        for (; done < n_steps; ++done) SN_TRY(one_step(s, done));
     }
     int host[kStepsDone + 1] = {};
     SN_HIP(hipMemcpyAsync(host, status, sizeof(host), hipMemcpyDeviceToHost, s));
@@ -509,7 +637,7 @@ sn_status sn_read_status(void *ws, void *stream) {
     return v;
 }
 
-void sn_profile_enable(int32_t on) { g_prof_on = on != 0; }
+void sn_profile_enable(int32_t on) { g_prof_on.store(on != 0); }
 
 int32_t sn_profile_classes(void) { return K_NUM_CLASSES; }
 

@@ -582,16 +582,16 @@ __global__ __launch_bounds__(kFwdThreads) void filter_pack_kernel(FilterPackArgs
     }
 }
 
+// Compute units of the current device (read once per process; the
+// initialisation of a function-local static is thread-safe).
 int num_cus() {
-    static int n = 0;
-    if (n == 0) {
+    static const int n = [] {
         int dev = 0, v = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            n = 256;
-    }
+            return v;
+        return 256;
+    }();
     return n;
 }
 

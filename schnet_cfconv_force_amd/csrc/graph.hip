@@ -25,9 +25,9 @@ namespace {
 
 // thread per row: first upper edge and number of upper edges
 __global__ void pair_count_kernel(int N, const int32_t *row_ptr, const int32_t *col, int32_t *up_first,
-                                  int32_t *up_cnt, const int *guard) {
+                                  int32_t *up_cnt, const int *guard, const int *run_flag) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= N) return;
+    if (i >= N || (run_flag && *run_flag == 0)) return;
     if (guard && *guard) {               // the pair count is then 0: nothing reads these
         up_cnt[i] = 0;
         return;
@@ -56,13 +56,14 @@ struct PairArgs {
     int64_t E;
     int *status;
     const int *guard;
+    const int *run_flag;
 };
 
 // one wavefront per row: pair index of every edge; geometry of upper edges
 __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
     const int lane = threadIdx.x % 64;
     const int i = blockIdx.x * 4 + threadIdx.x / 64;
-    if (i >= a.N || (a.guard && *a.guard)) return;
+    if (i >= a.N || (a.guard && *a.guard) || (a.run_flag && *a.run_flag == 0)) return;
     const int64_t P = a.status[kPairTotal];   // written by the pair count check
     const int e0 = a.row_ptr[i], e1 = a.row_ptr[i + 1];
     const int uf = a.up_first[i], up = a.up_ptr[i];
@@ -101,6 +102,40 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(PairArgs a) {
             a.edge_pair[e] = p;
         }
     }
+}
+
+struct RefreshArgs {
+    const float *pos;
+    float *ref_pos;
+    int N;
+    const int2 *pair_ij;
+    float4 *pgeo;
+    float *pfc, *plfc;
+    int periodic;
+    float L[3], invL[3];
+    float cutoff;
+    const int *status;
+};
+
+// Neighbour skin: on a step that rebuilt the list, record the positions it
+// was built from; on the others, the pairs of the kept list get their
+// geometry from the current positions (pairs now beyond the cutoff get a
+// zero envelope and contribute nothing).
+__global__ __launch_bounds__(256) void pair_refresh_kernel(RefreshArgs a) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (a.status[kStatusWord] != 0) return;   // the list may be unfilled after an error
+    if (a.status[kBuildFlag] != 0) {
+        if (idx < 3 * (int64_t)a.N) a.ref_pos[idx] = a.pos[idx];
+        return;
+    }
+    if (idx >= a.status[kPairTotal]) return;
+    const int2 ij = a.pair_ij[idx];
+    float4 g;
+    float fc, lfc;
+    pair_geometry(a.pos + 3 * ij.x, a.pos + 3 * ij.y, a.periodic, a.L, a.invL, a.cutoff, g, fc, lfc);
+    a.pgeo[idx] = g;
+    a.pfc[idx] = fc;
+    a.plfc[idx] = lfc;
 }
 
 // y_i = sum_{e in row i} W[p] (.) in[col(e)], W = fc phi in the 24-bit row
@@ -202,7 +237,9 @@ struct ForcesArgs {
     float *forces;
     const int32_t *rptr;
     const float *eps;
-    float *energy;
+    float *energy;        // (may be null) energy[b]
+    double *elog;         // (may be null) MD log: elog[b], or elog[step B + b] with elog_by_step
+    int elog_by_step;     // step = status[kMdStep] - 1 (device-driven steps)
     VerletFuse vf;   // vf.vel null: no integrator part
     int *status;
     const int *guard;
@@ -217,7 +254,10 @@ __device__ inline int load_status(const int *p) {
 // replica each (fixed-order tree, deterministic).
 __global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
     __shared__ double red[256];
-    __shared__ int s_go;
+    __shared__ int s_go, s_open;
+    // device-driven steps: this step's index (the words are written only by
+    // the step's first launch, so every block reads the same value)
+    const int step = a.vf.n_total >= 0 || a.elog_by_step ? a.status[kMdStep] - 1 : 0;
     if ((int)blockIdx.x >= a.row_blocks) {
         const int b = blockIdx.x - a.row_blocks;
         double s = 0.0;
@@ -228,9 +268,15 @@ __global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
             if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
             __syncthreads();
         }
-        if (threadIdx.x == 0) a.energy[b] = (float)red[0];
+        if (threadIdx.x == 0) {
+            if (a.energy) a.energy[b] = (float)red[0];
+            if (a.elog) a.elog[(a.elog_by_step ? (int64_t)step * (gridDim.x - a.row_blocks) : 0) + b] = red[0];
+        }
     } else {
-        if (threadIdx.x == 0) s_go = a.vf.vel && load_status(a.status) == 0;
+        if (threadIdx.x == 0) {
+            s_go = a.vf.vel && load_status(a.status) == 0;
+            s_open = a.vf.open && (a.vf.n_total < 0 || step + 1 < a.vf.n_total);
+        }
         __syncthreads();
         const int sub = threadIdx.x % kFrLanes;
         const int i = (blockIdx.x * 256 + threadIdx.x) / kFrLanes;
@@ -259,37 +305,54 @@ __global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
                 if (s_go && finite) {
                     const float im = a.vf.inv_mass[i];
                     const float f3[3] = {fx, fy, fz};
+                    float r2 = 0.0f;
 #pragma unroll
                     for (int c = 0; c < 3; ++c) {
+                        // the kicks and the drift as explicit fused multiply-adds,
+                        // as in open_step_kernel: the same bits whichever launch
+                        // applies them
+                        const float hf = a.vf.half * f3[c];
                         float v = a.vf.vel[3 * i + c];
-                        if (a.vf.close) v = v + a.vf.half * f3[c] * im;
-                        if (a.vf.open) {
-                            v = v + a.vf.half * f3[c] * im;
-                            a.vf.pos[3 * i + c] += a.vf.dt * v;
+                        if (a.vf.close) v = fmaf(hf, im, v);
+                        if (s_open) {
+                            v = fmaf(hf, im, v);
+                            const float r = fmaf(a.vf.dt, v, a.vf.pos[3 * i + c]);
+                            a.vf.pos[3 * i + c] = r;
+                            if (a.vf.ref_pos) {
+                                const float dr = r - a.vf.ref_pos[3 * i + c];
+                                r2 = fmaf(dr, dr, r2);
+                            }
                         }
                         a.vf.vel[3 * i + c] = v;
                     }
+                    // beyond half the skin from where the list was built: the
+                    // next step rebuilds (every writer stores the same value)
+                    if (a.vf.ref_pos && !(r2 <= a.vf.half_skin2))
+                        __hip_atomic_store(a.status + kDisplaced, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0 && a.vf.close && a.vf.edge_slot)
-        *a.vf.edge_slot = a.status[kEdgeTotal];
+    if (blockIdx.x == 0 && threadIdx.x == 0 && a.vf.close) {
+        if (a.vf.edge_slot) *a.vf.edge_slot = a.status[kEdgeTotal];
+        if (a.vf.edge_log) a.vf.edge_log[step] = a.status[kEdgeTotal];
+    }
 }
 
 }  // namespace
 
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
                       const int32_t *rev, int64_t E, float cutoff, char *ws, const EfLayout &L, int *status,
-                      const int *guard, hipStream_t s) {
+                      const int *guard, hipStream_t s, const int *run_flag) {
     const int N = sys.n_atoms;
     ProfScope ps(K_PAIRS, s);
     int32_t *up_first = reinterpret_cast<int32_t *>(ws + L.up_first);
     int32_t *up_cnt = reinterpret_cast<int32_t *>(ws + L.up_cnt);
     int32_t *up_ptr = reinterpret_cast<int32_t *>(ws + L.up_ptr);
-    pair_count_kernel<<<(N + 255) / 256, 256, 0, s>>>(N, row_ptr, col, up_first, up_cnt, guard);
+    pair_count_kernel<<<(N + 255) / 256, 256, 0, s>>>(N, row_ptr, col, up_first, up_cnt, guard, run_flag);
     SN_TRY(launch_status());
-    SN_TRY(scan_exclusive(up_cnt, up_ptr, N, nullptr, nullptr, s, PairCountCheck{status, row_ptr, N, E, guard != nullptr}));
+    SN_TRY(scan_exclusive(up_cnt, up_ptr, N, nullptr, nullptr, s, PairCountCheck{status, row_ptr, N, E, guard != nullptr},
+                          run_flag));
     PairArgs a;
     a.N = N;
     a.row_ptr = row_ptr; a.col = col; a.rev = rev; a.up_first = up_first; a.up_ptr = up_ptr;
@@ -308,7 +371,32 @@ sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row
     a.E = E;
     a.status = status;
     a.guard = guard;
+    a.run_flag = run_flag;
     pair_fill_kernel<<<(N + 3) / 4, 256, 0, s>>>(a);
+    return launch_status();
+}
+
+sn_status pairs_refresh(const sn_system &sys, const float *pos, float cutoff, char *ws, const EfLayout &L,
+                        int *status, int64_t P_cap, hipStream_t s) {
+    ProfScope ps(K_PAIRS, s);
+    RefreshArgs a;
+    a.pos = pos;
+    a.ref_pos = reinterpret_cast<float *>(ws + L.ref_pos);
+    a.N = sys.n_atoms;
+    a.pair_ij = reinterpret_cast<const int2 *>(ws + L.pair_ij);
+    a.pgeo = reinterpret_cast<float4 *>(ws + L.pgeo);
+    a.pfc = reinterpret_cast<float *>(ws + L.pfc);
+    a.plfc = reinterpret_cast<float *>(ws + L.plfc);
+    a.periodic = sys.periodic ? 1 : 0;
+    for (int c = 0; c < 3; ++c) {
+        a.L[c] = sys.periodic ? sys.box[c] : 1.0f;
+        a.invL[c] = (float)(1.0 / (double)a.L[c]);
+    }
+    a.cutoff = cutoff;
+    a.status = status;
+    const int64_t n = std::max<int64_t>(P_cap, 3 * (int64_t)sys.n_atoms);
+    if (n <= 0) return SN_OK;
+    pair_refresh_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
     return launch_status();
 }
 
@@ -329,14 +417,17 @@ sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const
 sn_status forces_rows(int N, int B, const int32_t *replica_ptr, const float *eps, float *energy,
                       const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair, const float4 *pgeo,
                       const float *S, float *forces, int *status, const int *guard, const VerletFuse *vf,
-                      hipStream_t s) {
+                      hipStream_t s, double *elog, int elog_by_step) {
     ProfScope ps(K_FORCES, s);
     ForcesArgs a;
     a.N = N;
     a.row_blocks = (N + 256 / kFrLanes - 1) / (256 / kFrLanes);
     a.row_ptr = row_ptr; a.col = col; a.edge_pair = edge_pair; a.pgeo = pgeo; a.S = S; a.forces = forces;
     a.rptr = replica_ptr; a.eps = eps; a.energy = energy;
+    a.elog = elog;
+    a.elog_by_step = elog_by_step;
     a.vf = vf ? *vf : VerletFuse{};
+    if (!vf) a.vf.n_total = -1;
     a.status = status;
     a.guard = guard;
     forces_kernel<<<a.row_blocks + B, 256, 0, s>>>(a);

@@ -41,6 +41,10 @@ struct PredParams {
     int periodic;
 };
 
+// Device-driven MD steps rebuild the list only some of the time: every
+// kernel of the build then returns at once unless the step's flag is set.
+__device__ inline bool skipped(const int *run_flag) { return run_flag && *run_flag == 0; }
+
 __global__ void fill_int_kernel(int *p, int v, int64_t n) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = v;
@@ -126,8 +130,10 @@ __device__ inline bool block_bbox(const float *pos, int s, int e, float (*red)[N
 // entry) and the builder's status slots.
 __global__ __launch_bounds__(256) void grid_kernel(const float *pos, const int32_t *rptr, PredParams pp,
                                                    float cell_edge, CellGrid *grid, int *rep_of, int *cell_cnt,
-                                                   int *cell_fill, int64_t n_cells, int step_mark, int *status) {
+                                                   int *cell_fill, int64_t n_cells, int step_mark, int *status,
+                                                   const int *run_flag) {
     __shared__ float red[6][4];
+    if (skipped(run_flag)) return;
     const int b = blockIdx.x;
     const int s = rptr[b], e = rptr[b + 1];
     for (int64_t c = 8 * (int64_t)s + 64 * b + threadIdx.x; c < 8 * (int64_t)e + 64 * (b + 1); c += blockDim.x) {
@@ -164,9 +170,9 @@ __device__ inline int cell_coord(float x, int c, const CellGrid &g, const PredPa
 }
 
 __global__ void bin_kernel(const float *pos, int n_atoms, const CellGrid *grid, const int *rep_of, PredParams pp,
-                           int *cell_of, int *cell_cnt) {
+                           int *cell_of, int *cell_cnt, const int *run_flag) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n_atoms) return;
+    if (i >= n_atoms || skipped(run_flag)) return;
     const CellGrid g = grid[rep_of[i]];
     int c0 = cell_coord(pos[3 * i + 0], 0, g, pp);
     int c1 = cell_coord(pos[3 * i + 1], 1, g, pp);
@@ -177,9 +183,9 @@ __global__ void bin_kernel(const float *pos, int n_atoms, const CellGrid *grid, 
 }
 
 __global__ void place_kernel(const float *pos, int n_atoms, const int *cell_of, const int *cell_start,
-                             int *cell_fill, float4 *spos) {
+                             int *cell_fill, float4 *spos, const int *run_flag) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n_atoms) return;
+    if (i >= n_atoms || skipped(run_flag)) return;
     int cell = cell_of[i];
     int slot = atomicAdd(&cell_fill[cell], 1);
     spos[cell_start[cell] + slot] = make_float4(pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], __int_as_float(i));
@@ -213,14 +219,14 @@ __global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos
                                                                const int *rep_of, const int *cell_start,
                                                                const float4 *spos, PredParams pp, int *cnt,
                                                                const int32_t *row_ptr, int32_t *col, int64_t capacity,
-                                                               int *status) {
+                                                               int *status, const int *run_flag) {
     __shared__ int s_start[kNbWaves][28];
     __shared__ int s_pre[kNbWaves][28];
     __shared__ int s_buf[FILL ? kNbWaves : 1][FILL ? SN_MAX_ROW : 1];
     const int wv = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int i = blockIdx.x * kNbWaves + wv;
-    if (i >= n_atoms) return;                       // whole wavefront exits together
+    if (i >= n_atoms || skipped(run_flag)) return;   // whole wavefront exits together
     const CellGrid g = grid[rep_of[i]];
     const float xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
     const int ci[3] = {cell_coord(xi, 0, g, pp), cell_coord(yi, 1, g, pp), cell_coord(zi, 2, g, pp)};
@@ -305,10 +311,11 @@ __global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos
 
 // One wavefront per row: rev[e] = index of (j, i) in row j.
 __global__ __launch_bounds__(256) void rev_kernel(int n_atoms, const int32_t *row_ptr, const int32_t *col,
-                                                  int32_t *rev, int *status) {
+                                                  int32_t *rev, int *status, const int *run_flag) {
     const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int i = blockIdx.x * 4 + wv;
-    if (i >= n_atoms || *status != 0) return;   // after an error the rows may not be filled
+    // after an error the rows may not be filled
+    if (i >= n_atoms || *status != 0 || skipped(run_flag)) return;
     const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
     for (int e = e0 + lane; e < e1; e += kWave) {
         const int j = col[e];
@@ -380,8 +387,9 @@ __device__ inline void load4(const int32_t *in, int n, int64_t b, int v[4]) {
 // out must not overlap; in must be 16-byte aligned.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t *in, int32_t *out, int n,
                                                             int32_t *total_slot, int32_t *max_slot,
-                                                            PairCountCheck chk) {
+                                                            PairCountCheck chk, const int *run_flag) {
     __shared__ int s_w[kScanThreads / 64];
+    if (skipped(run_flag)) return;
     const int64_t t0 = (int64_t)blockIdx.x * kScanTile;   // a multiple of 4 * kScanThreads
     const bool last = blockIdx.x == gridDim.x - 1;
     int pre = 0, mx = 0;
@@ -453,6 +461,7 @@ struct TileArgs {
     NbPairOut pr;                // pr.edge_pair null: no pair arrays
     int step_mark;               // >= 0: to status slot kStepsDone unless an error is flagged
     int *status;
+    const int *run_flag;         // (may be null) nothing is done unless *run_flag is non-zero
 };
 
 __device__ inline uint64_t below_mask(int bit) { return (1ull << bit) - 1ull; }
@@ -472,6 +481,7 @@ __device__ inline bool tile_positions(const float *pos, int s, int n, float *sp)
 __global__ __launch_bounds__(kTileThreads) void tile_count_kernel(TileArgs a) {
     __shared__ float sp[3 * kRepMaxAtoms];
     __shared__ int s_sum, s_max;
+    if (skipped(a.run_flag)) return;
     const int b = blockIdx.x / a.Rc, part = blockIdx.x % a.Rc;
     const int s = a.rptr[b], e = a.rptr[b + 1], n = e - s;
     const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
@@ -524,6 +534,7 @@ __global__ __launch_bounds__(kTileThreads, 8) void tile_fill_kernel(TileArgs a) 
     __shared__ int s_sw[kTileWaves];
     __shared__ unsigned long long s_before, s_total;
     __shared__ int s_max, s_st;
+    if (skipped(a.run_flag)) return;
     const int b = blockIdx.x / a.R, part = blockIdx.x % a.R;
     const int s = a.rptr[b], e = a.rptr[b + 1], n = e - s;
     const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
@@ -641,11 +652,11 @@ __global__ __launch_bounds__(kTileThreads, 8) void tile_fill_kernel(TileArgs a) 
 }  // namespace
 
 sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
-                         hipStream_t s, PairCountCheck chk) {
+                         hipStream_t s, PairCountCheck chk, const int *run_flag) {
     ProfScope ps(K_NB_SCAN, s);
     if (n < 0 || in == out) return SN_ERR_INVALID;
     const int ntiles = n > 0 ? (n + kScanTile - 1) / kScanTile : 1;
-    scan_kernel<<<ntiles, kScanThreads, 0, s>>>(in, out, n, total_slot, max_slot, chk);
+    scan_kernel<<<ntiles, kScanThreads, 0, s>>>(in, out, n, total_slot, max_slot, chk, run_flag);
     return launch_status();
 }
 
@@ -689,18 +700,19 @@ int max_replica_atoms(const sn_system &sys, hipStream_t s) {
     return m;
 }
 
-// Host-pinned landing slot for the counters read back once per build.
-static int *pinned_counters() {
-    static int *p = nullptr;
-    if (!p) {
-        if (hipHostMalloc((void **)&p, 256, hipHostMallocDefault) != hipSuccess) p = nullptr;
-    }
-    return p;
+// The build's counters (status, longest row, edge total), read back into
+// host memory of the caller's thread: a copy into pageable memory, then the
+// stream is synchronised (no library-wide host buffer, so calls on other
+// streams or threads cannot overwrite each other's counters).
+static sn_status read_counters(const int *status, int (&host)[4], hipStream_t s) {
+    SN_HIP(hipMemcpyAsync(host, status, sizeof(host), hipMemcpyDeviceToHost, s));
+    SN_HIP(hipStreamSynchronize(s));
+    return SN_OK;
 }
 
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
                    int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync,
-                   int max_rep, const NbPairOut *pairs, bool *pairs_done, int step_mark) {
+                   int max_rep, const NbPairOut *pairs, bool *pairs_done, int step_mark, const int *run_flag) {
     if (pairs_done) *pairs_done = false;
     const int N = sys.n_atoms, B = sys.n_replicas;
     int *status = reinterpret_cast<int *>(ws);
@@ -756,6 +768,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         a.pr = pairs ? *pairs : NbPairOut{};
         a.step_mark = step_mark;
         a.status = status;
+        a.run_flag = run_flag;
         {
             ProfScope ps(K_NB_COUNT, s);
             tile_count_kernel<<<B * a.Rc, kTileThreads, 0, s>>>(a);
@@ -768,10 +781,8 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         }
         if (pairs_done) *pairs_done = pairs != nullptr;
         if (sync) {
-            int *host = pinned_counters();
-            if (!host) return SN_ERR_HIP;
-            SN_HIP(hipMemcpyAsync(host, status, 4 * 4, hipMemcpyDeviceToHost, s));
-            SN_HIP(hipStreamSynchronize(s));
+            int host[4];
+            SN_TRY(read_counters(status, host, s));
             const int st = host[kStatusWord], max_row = host[kMaxRow];
             *n_edges = host[kEdgeTotal];
             if (st != 0) return st;
@@ -783,33 +794,32 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
     {
         ProfScope ps(K_NB_GRID, s);
         grid_kernel<<<B, 256, 0, s>>>(pos, sys.replica_ptr, pp, cell_edge, grid, rep_of, cell_cnt, cell_fill,
-                                      L.n_cells, step_mark, status);
+                                      L.n_cells, step_mark, status, run_flag);
         SN_TRY(launch_status());
     }
     {
         ProfScope ps(K_NB_BIN, s);
-        bin_kernel<<<(N + 255) / 256, 256, 0, s>>>(pos, N, grid, rep_of, pp, cell_of, cell_cnt);
+        bin_kernel<<<(N + 255) / 256, 256, 0, s>>>(pos, N, grid, rep_of, pp, cell_of, cell_cnt, run_flag);
         SN_TRY(launch_status());
     }
-    SN_TRY(scan_exclusive(cell_cnt, cell_start, (int)L.n_cells, nullptr, nullptr, s));
+    SN_TRY(scan_exclusive(cell_cnt, cell_start, (int)L.n_cells, nullptr, nullptr, s, PairCountCheck{}, run_flag));
     {
         ProfScope ps(K_NB_BIN, s);
-        place_kernel<<<(N + 255) / 256, 256, 0, s>>>(pos, N, cell_of, cell_start, cell_fill, spos);
+        place_kernel<<<(N + 255) / 256, 256, 0, s>>>(pos, N, cell_of, cell_start, cell_fill, spos, run_flag);
         SN_TRY(launch_status());
     }
     const int blocks = (N + kNbWaves - 1) / kNbWaves;
     {
         ProfScope ps(K_NB_COUNT, s);
         rows_kernel<false><<<blocks, kWave * kNbWaves, 0, s>>>(pos, N, grid, rep_of, cell_start, spos, pp,
-                                                               row_cnt, nullptr, nullptr, capacity, status);
+                                                               row_cnt, nullptr, nullptr, capacity, status, run_flag);
         SN_TRY(launch_status());
     }
-    SN_TRY(scan_exclusive(row_cnt, row_ptr, N, status + kEdgeTotal, status + kMaxRow, s));
+    SN_TRY(scan_exclusive(row_cnt, row_ptr, N, status + kEdgeTotal, status + kMaxRow, s, PairCountCheck{},
+                          run_flag));
     if (sync) {
-        int *host = pinned_counters();
-        if (!host) return SN_ERR_HIP;
-        SN_HIP(hipMemcpyAsync(host, status, 4 * 4, hipMemcpyDeviceToHost, s));
-        SN_HIP(hipStreamSynchronize(s));
+        int host[4];
+        SN_TRY(read_counters(status, host, s));
         const int st = host[kStatusWord], max_row = host[kMaxRow];
         const int64_t E = host[kEdgeTotal];
         *n_edges = E;
@@ -820,12 +830,12 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
     {
         ProfScope ps(K_NB_FILL, s);
         rows_kernel<true><<<blocks, kWave * kNbWaves, 0, s>>>(pos, N, grid, rep_of, cell_start, spos, pp, nullptr,
-                                                              row_ptr, col, capacity, status);
+                                                              row_ptr, col, capacity, status, run_flag);
         SN_TRY(launch_status());
     }
     {
         ProfScope ps(K_NB_REV, s);
-        rev_kernel<<<(N + 3) / 4, 256, 0, s>>>(N, row_ptr, col, rev, status);
+        rev_kernel<<<(N + 3) / 4, 256, 0, s>>>(N, row_ptr, col, rev, status, run_flag);
         SN_TRY(launch_status());
     }
     return SN_OK;

@@ -14,13 +14,19 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // --------------------------------------------------------------- status
 
-// Device status word slots (int32, in the first 256 bytes of the workspace).
-// Device status words at the head of the workspace: the first error code
-// (0 = none), the longest row and the edge total of the last neighbour
-// build, the pair count of the last pair setup, and the MD steps completed.
+// Device status words at the head of the workspace (int32, the first 256
+// bytes): the first error code (0 = none), the longest row and the edge
+// total of the last neighbour build, the pair count of the last pair setup,
+// the MD steps completed, and the state of device-driven MD steps.
 enum StatusSlot {
     kStatusWord = 0, kMaxRow = 1, kEdgeTotal = 2, kPairTotal = 3,
     kStepsDone = 4,    // MD: index of the last step that began with no error flagged
+    // device-driven MD steps (a rebuild interval or a replayed graph): the
+    // launches of every step are identical and these words carry what varies
+    kMdStep = 5,       // steps begun in this call (the current step's index + 1)
+    kBuildFlag = 6,    // 1: the current step rebuilds the neighbour list
+    kDisplaced = 7,    // set when an atom drifted beyond half the skin since the last build
+    kLastBuild = 8,    // index of the step that last rebuilt the list
     kStatusSlots = 64
 };
 
@@ -138,7 +144,7 @@ struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
 
 struct EfLayout {            // energy/force scratch (offsets from ws base)
     size_t up_first, up_cnt, up_ptr, edge_pair, pair_ij, pgeo, pfc, plfc, phi, x, o, gy, h, y, gh, eps, S, xmax, gmax, pack,
-        rep, mask, h0, total;
+        rep, mask, h0, ref_pos, total;
 };
 
 // Weight pack: every weight matrix of the model pre-split into fp16 hi / lo
@@ -281,11 +287,13 @@ constexpr int kTileMaxSplit = 16;       // blocks per replica in that build
 // runs, and with `pairs` set it also writes the pair arrays and the pair
 // count (status slot kPairTotal; 0 after an error) and sets *pairs_done.
 // step_mark >= 0: the first kernel writes it to status slot kStepsDone if no
-// error is flagged by then (MD steps).
+// error is flagged by then (MD steps).  run_flag (may be null): every kernel
+// of the build returns at once unless *run_flag is non-zero (device-driven MD
+// steps that rebuild only some of the time).
 sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t *row_ptr, int32_t *col,
                    int32_t *rev, int64_t capacity, int64_t *n_edges, char *ws, hipStream_t s, bool sync = true,
                    int max_rep = -1, const NbPairOut *pairs = nullptr, bool *pairs_done = nullptr,
-                   int step_mark = -1);
+                   int step_mark = -1, const int *run_flag = nullptr);
 // Check run by the scan's last block once the total is known: the pair
 // count is E / 2 (E >= 0), or row_ptr[N] / 2 (E < 0), and must equal the
 // total (the number of upper edges).  status[kPairTotal] receives it, or 0
@@ -300,8 +308,9 @@ struct PairCountCheck {
 };
 // Exclusive prefix sum (one launch); out[n] = total; optional device slots
 // receive the total and the maximum input.  in and out must not overlap.
+// run_flag (may be null): nothing happens unless *run_flag is non-zero.
 sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
-                         hipStream_t s, PairCountCheck chk = PairCountCheck{});
+                         hipStream_t s, PairCountCheck chk = PairCountCheck{}, const int *run_flag = nullptr);
 
 // filter.hip
 // Writes the filter slots of the weight pack (all interactions).
@@ -329,9 +338,18 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
 // guard (here and below; may be null): the kernels return at once while
 // *guard is non-zero, for a CSR that a flagged neighbour build may have left
 // unfilled (the pair count is then 0).
+// run_flag (may be null): the kernels return at once unless *run_flag is
+// non-zero (the list was rebuilt in this device-driven MD step).
 sn_status pairs_setup(const sn_system &sys, const float *pos, const int32_t *row_ptr, const int32_t *col,
                       const int32_t *rev, int64_t E, float cutoff, char *ws, const EfLayout &L, int *status,
-                      const int *guard, hipStream_t s);
+                      const int *guard, hipStream_t s, const int *run_flag = nullptr);
+// Neighbour skin, on the steps of a device-driven MD call: when the step
+// rebuilt the list (status slot kBuildFlag set) the positions are recorded
+// in ref_pos [N][3]; otherwise the geometry of every pair of the kept list
+// (pair_ij, status slot kPairTotal pairs) is recomputed from the positions.
+// P_cap: the pair capacity (launch size).
+sn_status pairs_refresh(const sn_system &sys, const float *pos, float cutoff, char *ws, const EfLayout &L,
+                        int *status, int64_t P_cap, hipStream_t s);
 // phi24: the filter rows W = fc phi in the 24-bit row format
 sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair,
                  const uint32_t *phi24, const float *in, float *out, const int *guard, hipStream_t s);
@@ -340,20 +358,31 @@ sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const
 // v += half F / m (and its edge count to edge_slot if set); open = the next
 // step's opening half kick with the same force and the drift r += dt v.
 // Atoms do not move once an error is flagged.
+// Device-driven steps (n_total >= 0): the step index is status slot kMdStep
+// minus one; the opening part runs only when step + 1 < n_total, the edge
+// count goes to edge_log[step] (if set); with ref_pos set, an atom that the
+// drift leaves more than sqrt(half_skin2) from ref_pos sets status slot
+// kDisplaced.
 struct VerletFuse {
     float *pos, *vel;
     const float *inv_mass;
     float half, dt;
     int close, open;
     int *edge_slot;
+    int n_total;
+    int *edge_log;
+    const float *ref_pos;
+    float half_skin2;
 };
 // F_i = sum_{e in row i} S_p(e) u_e, one launch that also sums the atom
-// energies eps into energy[b] per replica and, with vf, applies its Verlet
-// part.
+// energies eps per replica (in fp64) into energy[b] (fp32, if energy is set)
+// and elog[b] (fp64, if elog is set; elog[step B + b] when elog_by_step is
+// set: device-driven steps, step = status[kMdStep] - 1) and, with vf,
+// applies its Verlet part.
 sn_status forces_rows(int N, int B, const int32_t *replica_ptr, const float *eps, float *energy,
                       const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair, const float4 *pgeo,
                       const float *S, float *forces, int *status, const int *guard, const VerletFuse *vf,
-                      hipStream_t s);
+                      hipStream_t s, double *elog = nullptr, int elog_by_step = 0);
 
 
 // mlp.hip (fused atom-wise layers; see the kernel comments there).  The

@@ -50,3 +50,19 @@ def oracle_full(cfg, params=None):
     rp = cfg["replica_ptr"]
     eps_abs = np.array([np.abs(inter["eps"][rp[b]:rp[b + 1]]).sum() for b in range(len(rp) - 1)])
     return E, F, eps_abs, csr
+
+
+def md_evaluation_errors(cfg_params, hyper, types, replica_ptr, box, pos_gpu, forces_gpu, epot_gpu):
+    """Energy and force errors of an MD state against the oracle evaluated at the GPU's own positions.
+
+    The GPU carries positions in fp32 and the oracle's trajectory in fp64, so their trajectories part
+    by rounding; evaluating the oracle at the GPU's positions separates the energy/force evaluation,
+    which must meet the contract tolerances, from that divergence.  Returns the per-replica energy
+    errors and the per-component force errors (both relative, as energy_errors / force_errors)."""
+    pos = np.asarray(pos_gpu, np.float32)
+    csr = O.neighbors_bruteforce(pos, replica_ptr, hyper["cutoff"], box)
+    E, F, inter = O.energy_forces(cfg_params, hyper, types, pos.astype(np.float64), replica_ptr, csr, box,
+                                  return_intermediates=True)
+    rp = replica_ptr
+    eps_abs = np.array([np.abs(inter["eps"][rp[b]:rp[b + 1]]).sum() for b in range(len(rp) - 1)])
+    return energy_errors(epot_gpu, E, eps_abs), force_errors(forces_gpu, F, rp)

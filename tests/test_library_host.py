@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(sn.EXPORTED)
-    assert lib.sn_version() == 1
+    assert lib.sn_version() == 2
 
 
 def test_status_strings():
@@ -108,3 +108,32 @@ def test_workspace_bytes_grow_with_edges():
     # the stored filter rows alone need I * (E/2) * F * 3 bytes (24-bit values)
     assert b - a >= 3 * (50000 - 500) * 128 * 3
     assert sn.lib().sn_workspace_bytes(None, ctypes.byref(sysc), 0) > 0
+
+
+def test_verlet_rejects_bad_schedule_and_flags_before_any_gpu_work():
+    """sn_verlet_step validates rebuild_every (>= 0) and flags (0 or SN_MD_GRAPH) on the host: with
+    either out of range it returns SN_ERR_INVALID before touching a pointer (the ones passed here are
+    dummies that a GPU call would fault on)."""
+    sn = _sn()
+    import ctypes
+    cfg = synth.make_config("tiny_chain")
+    h = cfg["hyper"]
+    m = sn.binding.SnModel(h["n_types"], h["n_interactions"], h["n_features"], h["n_rbf"], h["cutoff"],
+                           h["rbf_lo"], h["rbf_hi"], h["rbf_gamma"], 0, 16, None, None)
+    sysc = sn.binding.SnSystem(32, 1, 16, 16, 0, (ctypes.c_float * 3)(0, 0, 0))
+    lib = sn.lib()
+    ne = ctypes.c_int64(0)
+    done = ctypes.c_int32(7)
+    dummy = 16
+
+    def call(n_steps, rebuild_every, flags, r_list=11.0):
+        return lib.sn_verlet_step(ctypes.byref(m), ctypes.byref(sysc), dummy, dummy, dummy, dummy, 2.0,
+                                  synth.FORCE_TO_ACCEL, n_steps, rebuild_every, r_list, dummy, dummy, dummy, 1000,
+                                  ctypes.byref(ne), None, None, None, ctypes.byref(done), flags, dummy, 1 << 30,
+                                  None)
+    assert call(10, -1, 0) == sn.SN_ERR_INVALID
+    assert done.value == 0                       # written before any check
+    assert call(10, 5, 2) == sn.SN_ERR_INVALID   # unknown flag bit
+    assert call(10, 5, sn.SN_MD_GRAPH | 4) == sn.SN_ERR_INVALID
+    assert call(-1, 1, 0) == sn.SN_ERR_INVALID
+    assert call(10, 1, 0, r_list=float("nan")) == sn.SN_ERR_INVALID
