@@ -242,6 +242,27 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
 sn_status sn_filter_forward(const sn_model *model, int32_t interaction, const float *d, int64_t n,
                             float *phi, void *stream);
 
+/* Energy and forces without allocation, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The same computation as
+ * sn_energy_forces (same kernels, same bits), with its scratch in a static
+ * device array of SN_STATIC_SCRATCH_BYTES that the library holds on every GPU
+ * it runs on until the process ends.  It allocates nothing, calls no
+ * allocating routine and does not synchronise.
+ * Limits and errors: SN_ERR_WORKSPACE when sn_workspace_bytes(model, sys,
+ * n_edges) exceeds SN_STATIC_SCRATCH_BYTES (checked on the host, before any
+ * GPU work); otherwise as sn_energy_forces.  `stream` must belong to the
+ * current device.  status_out (device int32, may be NULL) receives, in
+ * stream order, the call's device status (SN_OK, or for example
+ * SN_ERR_NONFINITE).  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams or host threads) race and give
+ * undefined results; calls ordered on one stream are safe. */
+#define SN_STATIC_SCRATCH_BYTES (64u << 20)
+sn_status sn_energy_forces_static(const sn_model *model, const sn_system *sys, const float *pos,
+                                  const int32_t *row_ptr, const int32_t *col_idx, const int32_t *rev_idx,
+                                  int64_t n_edges, float *energy /* [B] */, float *forces /* [N][3] */,
+                                  int32_t *status_out, void *stream);
+
 /* Synchronise `stream`, return the device status word of workspace `ws`
  * (SN_OK or the first error a kernel flagged) and clear it. */
 sn_status sn_read_status(void *ws, void *stream);

@@ -30,8 +30,9 @@ EXPORTED = (
     "sn_param_count", "sn_param_offsets", "sn_quantize_filter_weights", "sn_workspace_bytes",
     "sn_status_string", "sn_version", "sn_build_csr_neighbors", "sn_energy_forces", "sn_verlet_step",
     "sn_filter_forward", "sn_read_status", "sn_profile_enable", "sn_profile_classes", "sn_profile_name",
-    "sn_profile_collect",
+    "sn_profile_collect", "sn_energy_forces_static",
 )
+SN_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class SnSystem(ctypes.Structure):
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
         "sn_version": (i32, []),
         "sn_build_csr_neighbors": (i32, [PS, vp, f32, vp, vp, vp, i64, P64, vp, sz, vp]),
         "sn_energy_forces": (i32, [PM, PS, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]),
+        "sn_energy_forces_static": (i32, [PM, PS, vp, vp, vp, vp, i64, vp, vp, vp, vp]),
         "sn_verlet_step": (i32, [PM, PS, vp, vp, vp, vp, f32, f32, i32, i32, f32, vp, vp, vp, i64, P64, vp, vp, vp,
                                  ctypes.POINTER(ctypes.c_int32), ctypes.c_uint32, vp, sz, vp]),
         "sn_filter_forward": (i32, [PM, i32, vp, i64, vp, vp]),
@@ -254,6 +256,25 @@ def energy_forces(model: Model, system: System, pos, row_ptr, col, rev, n_edges:
                                 col.data_ptr(), rev.data_ptr(), int(n_edges), energy.data_ptr(), forces.data_ptr(),
                                 ws.data_ptr(), ws.numel(), _stream(stream))
     _check(st, "sn_energy_forces")
+    return energy, forces
+
+
+def energy_forces_static(model: Model, system: System, pos, row_ptr, col, rev, n_edges: int, energy=None,
+                         forces=None, status=None, stream=None):
+    """sn_energy_forces_static (no workspace, nothing allocated by the library) -> (energy[B], forces[N,3]).
+    status (optional int32 device tensor [1]) receives the call's device status in stream order."""
+    torch = _torch()
+    dev = pos.device
+    if energy is None:
+        energy = torch.empty(system.n_replicas, dtype=torch.float32, device=dev)
+    if forces is None:
+        forces = torch.empty((system.n_atoms, 3), dtype=torch.float32, device=dev)
+    if status is not None and (status.dtype != torch.int32 or status.numel() < 1 or status.device != dev):
+        raise ValueError("status must be an int32 tensor on the device with at least one value")
+    st = lib().sn_energy_forces_static(ctypes.byref(model.c), ctypes.byref(system.c), pos.data_ptr(),
+                                       row_ptr.data_ptr(), col.data_ptr(), rev.data_ptr(), int(n_edges),
+                                       energy.data_ptr(), forces.data_ptr(), _ptr(status), _stream(stream))
+    _check(st, "sn_energy_forces_static")
     return energy, forces
 
 

@@ -344,6 +344,49 @@ struct CaptureGuard {
 }  // namespace
 }  // namespace sn
 
+// --------------------------------------------------------------- no-allocation variant
+//
+// sn_energy_forces_static runs the energy/force pipeline with its scratch in
+// `scratch`, a file-scope device array of a fixed size, instead of a
+// caller's workspace, for callers that cannot allocate.  In host code the
+// array's name only stands in for the symbol: its device address (one per
+// GPU, each GPU holding its own copy from module load until the process
+// ends) is looked up with hipGetSymbolAddress on the first call on each
+// device, with that device current, and kept in a per-device table; only
+// that address is ever passed to kernels.
+namespace sn {
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;   // 64 MiB per GPU
+constexpr int kStaticScratchDevices = 64;
+}  // namespace sn
+
+static __device__ __align__(256) char scratch[sn::kStaticScratchBytes];
+
+namespace sn {
+namespace {
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[kStaticScratchDevices] = {};
+
+// The device address of `scratch` on the current device (looked up once per device).
+sn_status static_scratch(char **out) {
+    int dev = -1;
+    SN_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kStaticScratchDevices) return SN_ERR_INVALID;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SN_ERR_HIP;
+        g_scratch_ptr[dev] = static_cast<char *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return SN_OK;
+}
+
+__global__ void copy_status_kernel(const int *status, int32_t *out) {
+    if (threadIdx.x == 0) *out = status[kStatusWord];
+}
+}  // namespace
+}  // namespace sn
+
 using namespace sn;
 
 extern "C" {
@@ -635,6 +678,28 @@ sn_status sn_read_status(void *ws, void *stream) {
     SN_HIP(hipStreamSynchronize(s));
     SN_TRY(clear_status(ws, s));
     return v;
+}
+
+sn_status sn_energy_forces_static(const sn_model *model, const sn_system *sys, const float *pos,
+                                  const int32_t *row_ptr, const int32_t *col_idx, const int32_t *rev_idx,
+                                  int64_t n_edges, float *energy, float *forces, int32_t *status_out,
+                                  void *stream) {
+    SN_TRY(check_system(sys));
+    SN_TRY(check_model(model));
+    if (n_edges < 0 || (n_edges & 1) || n_edges > INT32_MAX || !energy) return SN_ERR_INVALID;
+    if (sys->n_atoms > 0 && (!pos || !row_ptr || !forces)) return SN_ERR_INVALID;
+    if (n_edges > 0 && (!col_idx || !rev_idx)) return SN_ERR_INVALID;
+    if (bytes_needed(model, sys, n_edges) > kStaticScratchBytes) return SN_ERR_WORKSPACE;
+    char *ws = nullptr;
+    SN_TRY(static_scratch(&ws));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    SN_TRY(clear_status(ws, s));   // a kernel: the array keeps the previous call's contents
+    SN_TRY(energy_forces_impl(*model, *sys, pos, row_ptr, col_idx, rev_idx, n_edges, energy, forces, ws, s));
+    if (status_out) {
+        copy_status_kernel<<<1, 64, 0, s>>>(reinterpret_cast<const int *>(ws), status_out);
+        SN_TRY(launch_status());
+    }
+    return SN_OK;
 }
 
 void sn_profile_enable(int32_t on) { g_prof_on.store(on != 0); }
