@@ -6,6 +6,11 @@ evaluation (radial basis, filter network, CFConv, readout, analytic
 backward, forces) and the second half kick.  Inputs are seeded synthetic CG
 chains resident in HBM before timing starts.
 
+The headline line is the 64 x 269-bead workload's MD rate; the same JSON line
+carries, under "configs", the other workloads (evaluations and neighbour
+builds with their kernel rooflines, MD under several neighbour-list
+schedules) and the int16 filter weights' rate and drift.
+
 Prints one JSON line.  Usage:
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched_replicas]
 """
@@ -41,19 +46,20 @@ WORKLOAD_TEXT = {
 
 
 def filter_flops_per_pair(F: int, K: int):
-    """Algorithmic FLOPs of one pair (both directed edges) in one interaction.
+    """Algorithmic FLOPs of one filter evaluation (one unordered pair, shared by its two directed
+    edges) in one interaction:
+        forward : rbf @ A1 (2KF) + ssp(a) @ A2 (2F^2)
+        backward: g_phi @ A2^T (2F^2) + g_a @ A1^T (2FK)
+    Recomputed products and padding are not counted."""
+    return 2 * K * F + 2 * F * F, 2 * F * F + 2 * F * K
 
-    forward : rbf @ A1 (2KF) + ssp(a) @ A2 (2F^2)
-    backward: recomputed rbf @ A1 (2KF) + g_phi @ A2^T (2F^2) + g_a @ A1^T (2FK)
-    """
-    return 2 * K * F + 2 * F * F, 4 * K * F + 2 * F * F
 
-
-def cfconv_bytes(E: int, N: int, F: int):
-    """Algorithmic HBM bytes of one CFConv launch: per directed edge the filter
-    row (3F: 24-bit values, the envelope already applied), col and pair index
-    (8 B); per atom one input row read and one output row written."""
-    return E * (3 * F + 8) + 2 * N * F * 4
+def cfconv_algorithmic_bytes(E: int, F: int):
+    """Algorithmic HBM bytes of one CFConv launch: per directed edge its filter row (4F bytes in
+    fp32) and its column index (4 bytes).  The gathered input rows are served by the caches; the
+    kernel itself stores each row once per pair in 24 bits and reads it from both of its edges, so
+    the counters measure what it really moves."""
+    return E * (4 * F + 4)
 
 
 def kernel_sources() -> list:
@@ -279,7 +285,209 @@ def cpu_baseline(cfg, seconds: float):
     return {"value": evals_per_s, "unit": "evals/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} single-replica oracle evaluations (brute-force neighbour list + fp64 energy "
                       f"and forces) of replicas {idx}, {dt:.1f} s, scaled to all {B} replicas",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "host_cpu_count": os.cpu_count(), "blas_threads": int(threads),
+            "threads_note": "NumPy fp64; its BLAS calls (the matrix products) use blas_threads threads, "
+                            "the rest of the oracle one"}
+
+
+# ---------------------------------------------------------------------------
+# measured runs
+
+
+class Workload:
+    """One seeded workload on the device: model, system, positions, velocities, initial forces."""
+
+    def __init__(self, sn, torch, name: str, fmt: int = 0):
+        import numpy as np
+        import synth
+        self.sn, self.torch, self.name = sn, torch, name
+        cfg = synth.make_config(name)
+        self.cfg = cfg
+        h = cfg["hyper"]
+        self.N, self.B = len(cfg["pos"]), len(cfg["replica_ptr"]) - 1
+        self.F, self.K, self.I = h["n_features"], h["n_rbf"], h["n_interactions"]
+        self.cutoff = h["cutoff"]
+        if "vel" not in cfg:
+            cfg["vel"] = synth.maxwell_boltzmann(self.N, cfg["replica_ptr"], 110.0, 300.0, 2)
+            cfg["inv_mass"] = np.full(self.N, 1.0 / 110.0, np.float32)
+        self.model = sn.Model(cfg["params"], h, filter_format=fmt)
+        self.system = sn.System(cfg["replica_ptr"], cfg["types"], cfg["box"])
+        self.capacity = self.N * 200
+        self.ws = sn.workspace(self.model, self.system, self.capacity)
+        self.row_ptr = torch.empty(self.N + 1, dtype=torch.int32, device="cuda")
+        self.col = torch.empty(self.capacity, dtype=torch.int32, device="cuda")
+        self.rev = torch.empty(self.capacity, dtype=torch.int32, device="cuda")
+        self.reset()
+
+    def reset(self):
+        torch, sn, cfg = self.torch, self.sn, self.cfg
+        self.pos = torch.from_numpy(cfg["pos"]).cuda()
+        self.vel = torch.from_numpy(cfg["vel"]).cuda()
+        self.inv_mass = torch.from_numpy(cfg["inv_mass"]).cuda()
+        rp, col, rev, E = sn.build_csr_neighbors(self.system, self.pos, self.cutoff, self.capacity, self.ws)
+        self.E = E
+        self.row_ptr.copy_(rp)
+        self.col[:E].copy_(col)
+        self.rev[:E].copy_(rev)
+        _, self.forces = sn.energy_forces(self.model, self.system, self.pos, self.row_ptr, self.col, self.rev, E,
+                                          self.ws)
+        torch.cuda.synchronize()
+
+    def md(self, n, skin=0.0, rebuild_every=1, graph=False, epot=None, ekin=None):
+        """n MD steps in one call; returns each step's edge count."""
+        import synth
+        if n <= 0:
+            return []
+        elog = self.torch.zeros(n, dtype=self.torch.int32, device="cuda")
+        self.sn.verlet_step(self.model, self.system, self.pos, self.vel, self.forces, self.inv_mass, 2.0,
+                            synth.FORCE_TO_ACCEL, n, self.cutoff + skin, self.capacity, self.ws, epot, ekin,
+                            csr=(self.row_ptr, self.col, self.rev), edge_log=elog, rebuild_every=rebuild_every,
+                            graph=graph)
+        return [int(e) for e in elog.cpu().tolist()]
+
+    def eval(self):
+        self.sn.energy_forces(self.model, self.system, self.pos, self.row_ptr, self.col, self.rev, self.E, self.ws,
+                              forces=self.forces)
+
+    def build(self):
+        return self.sn.build_csr_neighbors(self.system, self.pos, self.cutoff, self.capacity, self.ws)
+
+    def time_md(self, steps, warmup, **kw):
+        """Wall-clock seconds per MD step (one call of `steps` steps, no timing events inside)."""
+        self.reset()
+        self.md(warmup, **kw)
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        edges = self.md(steps, **kw)
+        self.torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps, edges
+
+    def profile(self, fn, n):
+        """Per kernel class: (total ms, launches) from HIP events around every launch of n calls."""
+        sn = self.sn
+        sn.profile_enable(True)
+        sn.profile_collect()
+        for _ in range(n):
+            fn()
+        self.torch.cuda.synchronize()
+        prof = sn.profile_collect()
+        sn.profile_enable(False)
+        return prof
+
+
+def kernel_rooflines(prof, P, E, F, K, traffic=None, flops_pairs=None):
+    """Roofline entries of the filter kernels (matrix cores, fp16 peak) and the CFConv (HBM).
+
+    prof: per class (total ms, launches) over launches that each processed P pairs / E directed
+    edges (flops_pairs overrides the pair count summed over all launches of a class).
+    traffic: counter bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled), or None."""
+    fwd_pp, bwd_pp = filter_flops_per_pair(F, K)
+    out = {}
+    for name, per_pair, kern in (("filter_bwd", bwd_pp, "filter_bwd_kernel"), ("filter_fwd", fwd_pp,
+                                                                                "filter_fwd_kernel")):
+        if name not in prof:
+            continue
+        ms, n = prof[name]
+        pairs = flops_pairs[name] if flops_pairs else P * n
+        flops = per_pair * pairs
+        achieved = flops / (ms * 1e-3) / 1e12
+        out[name] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_MFMA_TFLOPS, 4),
+                     "traffic": traffic.get(kern) if traffic else None,
+                     "avg_launch_us": round(1e3 * ms / n, 2), "flops_per_launch": int(flops / n),
+                     "flops_basis": "fp32 algorithmic FLOPs of one filter evaluation per unordered pair "
+                                    f"({per_pair} per pair; recompute and padding not counted)",
+                     "mfma_dtype": "f16 (each fp32 product as three fp16 products)",
+                     "frac_of_split_peak": round(achieved / PEAK_SPLIT_F16_TFLOPS, 4),
+                     "split_peak_TFLOPs": round(PEAK_SPLIT_F16_TFLOPS, 1)}
+    if "cfconv" in prof:
+        ms, n = prof["cfconv"]
+        us = 1e3 * ms / n
+        alg = cfconv_algorithmic_bytes(E, F)
+        r = {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s", "avg_launch_us": round(us, 2),
+             "algorithmic_bytes_per_launch": int(alg),
+             "algorithmic_GBs": round(alg / (us * 1e-6) / 1e9, 1),
+             "algorithmic_basis": "4F + 4 bytes per directed edge (an fp32 filter row and a column index)"}
+        t = traffic.get("cfconv_kernel") if traffic else None
+        if t:
+            achieved = t / (us * 1e-6) / 1e9
+            r.update({"achieved": round(achieved, 1), "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": t,
+                      "achieved_basis": "hardware counters (FETCH_SIZE + WRITE_SIZE, scaled) / launch time"})
+        else:
+            r.update({"achieved": None, "frac": None, "traffic": None,
+                      "achieved_basis": "no counter profile for the current kernels"})
+        out["cfconv"] = r
+    return out
+
+
+def kernels_table(prof, steps):
+    return {k: {"ms_per_step": v[0] / steps, "launches_per_step": v[1] / steps, "avg_us": 1e3 * v[0] / max(v[1], 1)}
+            for k, v in prof.items()}
+
+
+def measure_eval_config(sn, torch, name, n_rep=20):
+    """Fixed-CSR evaluations, the neighbour build, one evaluation with its rebuild, and the kernel
+    rooflines of one workload."""
+    import numpy as np
+    W = Workload(sn, torch, name)
+    for _ in range(3):
+        W.eval()
+    torch.cuda.synchronize()
+    assert sn.read_status(W.ws) == sn.SN_OK
+    ev = event_times(W.eval, n_rep)
+    nb = event_times(W.build, n_rep)
+    both = event_times(lambda: (W.build(), W.eval()), n_rep)
+    prof = W.profile(W.eval, 5)
+    med = float(np.median(ev))
+    res = {"workload": WORKLOAD_TEXT[name], "n_atoms": W.N, "n_replicas": W.B, "n_edges": W.E,
+           "eval_ms": {"median": round(med, 4), "min": round(float(np.min(ev)), 4), "n": n_rep},
+           "evals_per_s": round(1e3 / med, 2), "edges_per_s": round(W.E * 1e3 / med, 1),
+           "neighbour_build_ms": {"median": round(float(np.median(nb)), 4), "min": round(float(np.min(nb)), 4)},
+           "rebuild_plus_eval_ms": round(float(np.median(both)), 4),
+           "roofline_kernels": kernel_rooflines(prof, W.E // 2, W.E, W.F, W.K),
+           "kernels": kernels_table(prof, 5)}
+    return W, res
+
+
+def md_variants(W, steps, warmup, variants):
+    """MD steps/s and aggregate ns/day of a workload under several neighbour-list schedules."""
+    out = {}
+    for label, kw in variants:
+        sec, edges = W.time_md(steps, warmup, **kw)
+        out[label] = {"steps_per_s": round(1.0 / sec, 2), "ms_per_step": round(sec * 1e3, 4),
+                      "ns_per_day": round(W.B / sec * 2.0 * 1e-6 * 86400.0, 1), "edges_mean": round(
+                          sum(edges) / len(edges), 1), "schedule": kw}
+    return out
+
+
+def int16_drift(sn, torch, steps=100):
+    """Drift of the int16 filter weights from the fp32 weights on the 64 x 269 workload: one
+    evaluation at the same neighbour list (relative energy change, RMS force change over RMS force)
+    and the difference of the total-energy traces over `steps` MD steps (fp64 logs)."""
+    import numpy as np
+    runs = {}
+    for fmt in (0, 1):
+        W = Workload(sn, torch, "batched_replicas", fmt=fmt)
+        e, f = sn.energy_forces(W.model, W.system, W.pos, W.row_ptr, W.col, W.rev, W.E, W.ws)
+        e = e.cpu().numpy().astype(np.float64)
+        f = f.cpu().numpy().astype(np.float64)
+        ep = torch.zeros((steps, W.B), dtype=torch.float64, device="cuda")
+        ek = torch.zeros((steps, W.B), dtype=torch.float64, device="cuda")
+        W.md(steps, epot=ep, ekin=ek)
+        tot = (ep + ek).cpu().numpy()
+        runs[fmt] = (e, f, tot, ek.cpu().numpy())
+        sec, _ = W.time_md(20, 3)
+        runs[fmt] += (sec,)
+    e0, f0, t0, k0, s0 = runs[0]
+    e1, f1, t1, _, s1 = runs[1]
+    return {"rel_dE_max": float(np.abs(e1 - e0).max() / np.abs(e0).max()),
+            "rms_dF_over_rms_F": float(np.sqrt(((f1 - f0) ** 2).mean() / (f0 ** 2).mean())),
+            "etot_trace_max_abs_diff_kcal_mol": float(np.abs(t1 - t0).max()),
+            "etot_trace_diff_over_mean_ekin": float(np.abs(t1 - t0).max() / k0.mean()),
+            "etot_drift_fp32_kcal_mol": float(np.abs(t0 - t0[0]).max()),
+            "etot_drift_int16_kcal_mol": float(np.abs(t1 - t1[0]).max()),
+            "md_steps": steps,
+            "md_steps_per_s_fp32": round(1.0 / s0, 2), "md_steps_per_s_int16": round(1.0 / s1, 2)}
 
 
 def main():
@@ -289,8 +497,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batched_replicas", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--filter-format", type=int, default=0, choices=[0, 1])
+    ap.add_argument("--graph", action="store_true", help="replay the MD steps as a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="only the headline workload")
     ap.add_argument("--no-measure-peaks", dest="measure_peaks", action="store_false",
                     help="skip the device-copy and fp16-GEMM rate measurements (fractions of measured rates)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -323,7 +533,9 @@ def main():
     import torch
 
     import schnet_cfconv_force_amd as sn
-    import synth
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     if args.copy_probe_mb > 0:
         src = torch.ones(args.copy_probe_mb << 18, dtype=torch.float32, device="cuda")
@@ -332,108 +544,57 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    cfg = synth.make_config(args.workload)
-    h = cfg["hyper"]
-    N, B = len(cfg["pos"]), len(cfg["replica_ptr"]) - 1
-    F, K, I = h["n_features"], h["n_rbf"], h["n_interactions"]
-    dt_fs = cfg.get("dt_fs", 2.0)
-    if "vel" not in cfg:
-        cfg["vel"] = synth.maxwell_boltzmann(N, cfg["replica_ptr"], 110.0, 300.0, 2)
-        cfg["inv_mass"] = np.full(N, 1.0 / 110.0, np.float32)
-
-    model = sn.Model(cfg["params"], h, filter_format=args.filter_format)
-    system = sn.System(cfg["replica_ptr"], cfg["types"], cfg["box"])
-    pos = torch.from_numpy(cfg["pos"]).cuda()
-    vel = torch.from_numpy(cfg["vel"]).cuda()
-    inv_mass = torch.from_numpy(cfg["inv_mass"]).cuda()
-    capacity = N * 160
-    ws = sn.workspace(model, system, capacity)
-    row_ptr = torch.empty(N + 1, dtype=torch.int32, device="cuda")
-    col = torch.empty(capacity, dtype=torch.int32, device="cuda")
-    rev = torch.empty(capacity, dtype=torch.int32, device="cuda")
-    rp_, col_, rev_, E0 = sn.build_csr_neighbors(system, pos, h["cutoff"], capacity, ws)
-    _, forces = sn.energy_forces(model, system, pos, rp_, col_, rev_, E0, ws)
-    csr = (row_ptr, col, rev)
-
-    def md(n):
-        # one call runs all n steps (the library synchronises once, at its end)
-        if n <= 0:
-            return []
-        elog = torch.zeros(n, dtype=torch.int32, device="cuda")
-        sn.verlet_step(model, system, pos, vel, forces, inv_mass, dt_fs, synth.FORCE_TO_ACCEL, n,
-                       h["cutoff"], capacity, ws, csr=csr, edge_log=elog)
-        return [int(e) for e in elog.cpu().tolist()]
-
-    md(args.warmup)
+    # ---------------------------------------------------------------- headline
+    log(f"headline: {args.workload} MD, {args.steps} steps")
+    W = Workload(sn, torch, args.workload, fmt=args.filter_format)
+    N, B, F, K, I = W.N, W.B, W.F, W.K, W.I
+    W.md(args.warmup, graph=args.graph)
     torch.cuda.synchronize()
     # uninstrumented pass (no timing events in the stream)
     t0 = time.perf_counter()
-    md(args.steps)
+    edges = W.md(args.steps, graph=args.graph)
     torch.cuda.synchronize()
     sec_plain = (time.perf_counter() - t0) / args.steps
-    # instrumented pass: HIP events around every kernel on the launch stream
+    # instrumented pass: HIP events around every kernel on the launch stream (the graph is not used
+    # here: launches recorded into a graph are not timed individually)
     sn.profile_enable(True)
     sn.profile_collect()
     t0 = time.perf_counter()
-    edges = md(args.steps)
+    edges_p = W.md(args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     prof = sn.profile_collect()
     sn.profile_enable(False)
-    assert sn.read_status(ws) == sn.SN_OK
-
+    assert sn.read_status(W.ws) == sn.SN_OK
     sec_events = (t1 - t0) / args.steps
-    sec = sec_plain
-    evals_per_s = 1.0 / sec
+    evals_per_s = 1.0 / sec_plain
     E_mean = float(np.mean(edges))
-    P_total = sum(e // 2 for e in edges)
-    ns_per_day = B * evals_per_s * dt_fs * 1e-6 * 86400.0
+    P_total = sum(e // 2 for e in edges_p)
+    ns_per_day = B * evals_per_s * 2.0 * 1e-6 * 86400.0
 
     # fixed-CSR energy+force evaluations (the same kernels without rebuild / integration)
-    E_last = edges[-1]
+    # the last step (of the instrumented pass) rebuilt the list at the final positions, into W's
+    # list buffers
+    E_last = edges_p[-1]
+    W.E = E_last
     for _ in range(3):
-        sn.energy_forces(model, system, pos, row_ptr, col, rev, E_last, ws, forces=forces)
+        W.eval()
     torch.cuda.synchronize()
     n_fixed = max(20, args.steps)
     t2 = time.perf_counter()
     for _ in range(n_fixed):
-        sn.energy_forces(model, system, pos, row_ptr, col, rev, E_last, ws, forces=forces)
+        W.eval()
     torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    fixed_evals_per_s = n_fixed / (t3 - t2)
-    eval_ms = event_times(lambda: sn.energy_forces(model, system, pos, row_ptr, col, rev, E_last, ws,
-                                                   forces=forces), n_fixed)
-    # the neighbour build alone (cell list + CSR), same positions
-    nb_ms = event_times(lambda: sn.build_csr_neighbors(system, pos, h["cutoff"], capacity, ws), n_fixed)
+    fixed_evals_per_s = n_fixed / (time.perf_counter() - t2)
+    eval_ms = event_times(W.eval, n_fixed)
+    assert sn.read_status(W.ws) == sn.SN_OK
+    nb_ms = event_times(W.build, n_fixed)
     peaks = measured_peaks(torch) if args.measure_peaks else None
 
-    fwd_pp, bwd_pp = filter_flops_per_pair(F, K)
-    kernels = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps,
-                   "avg_us": 1e3 * v[0] / max(v[1], 1)} for k, v in prof.items()}
-    dominant = max(prof.items(), key=lambda kv: kv[1][0])[0]
-    rl = {}
-    for name, per_pair in (("filter_bwd", bwd_pp), ("filter_fwd", fwd_pp)):
-        if name in prof:
-            ms, n = prof[name]
-            flops = per_pair * P_total * I          # summed over every launch of the timed region
-            achieved = flops / (ms * 1e-3) / 1e12
-            rl[name] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_SPLIT_F16_TFLOPS, 1),
-                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_SPLIT_F16_TFLOPS, 4), "traffic": None,
-                        "mfma_dtype": "f16 split (3 products per fp32 product)",
-                        "avg_launch_us": round(1e3 * ms / n, 2),
-                        "flops_per_launch": int(per_pair * P_total * I / n)}
-    if "cfconv" in prof:
-        ms, n = prof["cfconv"]
-        byts = cfconv_bytes(int(E_mean), N, F) * n
-        achieved = byts / (ms * 1e-3) / 1e9
-        rl["cfconv"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                        "avg_launch_us": round(1e3 * ms / n, 2), "bytes_per_launch": int(byts / n)}
     traffic = load_traffic(args.workload)
-    if traffic:
-        kname = {"filter_bwd": "filter_bwd_kernel", "filter_fwd": "filter_fwd_kernel", "cfconv": "cfconv_kernel"}
-        for name, r in rl.items():
-            r["traffic"] = traffic.get(kname[name])
+    pairs_per_class = {k: P_total * I for k in ("filter_fwd", "filter_bwd")}
+    rl = kernel_rooflines(prof, None, int(E_mean), F, K, traffic, flops_pairs=pairs_per_class)
+    dominant = max(prof.items(), key=lambda kv: kv[1][0])[0]
     main_rl = rl.get(dominant) or rl.get("filter_bwd")
 
     out = {
@@ -443,16 +604,17 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(sec * 1e3, 4),
+        "ms_per_step": round(sec_plain * 1e3, 4),
         "ms_per_step_with_kernel_events": round(sec_events * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if args.filter_format == 0 else "f32 (int16 filter weights)",
+        "dtype": "fp32 (fp32-accurate split-fp16 MFMA products, filter rows stored in 24 bits)"
+                 + (", int16 filter weights" if args.filter_format else ""),
         "data": "synthetic (seeded CG chains / particle box, random-init weights)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload, "n_atoms": N,
                    "n_replicas": B, "n_edges_mean": round(E_mean, 1), "n_interactions": I, "n_features": F,
-                   "n_rbf": K, "dt_fs": dt_fs, "parallelism": "single GPU"},
+                   "n_rbf": K, "dt_fs": 2.0, "graph_replay": bool(args.graph), "parallelism": "single GPU"},
         "edges_per_s": round(E_mean * evals_per_s, 1),
         "ns_per_day": round(ns_per_day, 1),
         "evals_per_s_fixed_csr": round(fixed_evals_per_s, 2),
@@ -462,19 +624,53 @@ def main():
         "neighbour_build_ms": {"median": round(float(np.median(nb_ms)), 4), "min": round(float(np.min(nb_ms)), 4),
                                "n": len(nb_ms)},
         "peak_device_memory_bytes": int(torch.cuda.max_memory_allocated()),
-        "workspace_bytes": int(ws.numel()),
+        "workspace_bytes": int(W.ws.numel()),
         "roofline": main_rl,
         "roofline_kernels": rl,
         "dominant_kernel": dominant,
-        "kernels": kernels,
+        "kernels": kernels_table(prof, args.steps),
         "context": {"pages_ns_per_day": 1000, "pages_hardware": "1x NVIDIA RTX PRO 6000, 64 x 269-bead 1ENH"},
     }
     if peaks:
         out["measured_peaks"] = peaks
         for r in rl.values():
-            ref = peaks["hbm_copy_GBs"] if r["unit"] == "GB/s" else peaks["split_f16_mfma_TFLOPs_via_gemm"]
+            if r.get("achieved") is None:
+                continue
+            ref = peaks["hbm_copy_GBs"] if r["unit"] == "GB/s" else peaks["f16_gemm_TFLOPs"]
             r["frac_vs_measured"] = round(r["achieved"] / ref, 4)
+    del W
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- the other workloads
+    if not args.no_configs:
+        configs = {}
+        md_kw = [("rebuild_every_step", {}), ("rebuild_every_step_graph", {"graph": True}),
+                 ("skin_0.5A_graph", {"skin": 0.5, "rebuild_every": 0, "graph": True}),
+                 ("skin_1A_graph", {"skin": 1.0, "rebuild_every": 0, "graph": True})]
+        for name in ("tiny_chain", "single_protein", "larger_cg", "dense_box"):
+            log(f"config {name}")
+            Wc, res = measure_eval_config(sn, torch, name)
+            if name in ("tiny_chain", "single_protein"):
+                res["md"] = md_variants(Wc, 200, 20, md_kw)
+            else:
+                res["md"] = md_variants(Wc, 10, 3, md_kw[:2])
+            configs[name] = res
+            del Wc
+            torch.cuda.empty_cache()
+        log("config batched_replicas neighbour-list schedules")
+        Wb = Workload(sn, torch, "batched_replicas")
+        configs["batched_replicas"] = {"workload": WORKLOAD_TEXT["batched_replicas"],
+                                       "md": md_variants(Wb, 20, 3, md_kw)}
+        del Wb
+        torch.cuda.empty_cache()
+        log("config batched_replicas with int16 filter weights")
+        configs["batched_replicas_int16"] = {
+            "workload": WORKLOAD_TEXT["batched_replicas"] + "; per-output-channel int16 filter weights",
+            **int16_drift(sn, torch)}
+        out["configs"] = configs
     if not args.no_cpu_baseline:
+        log("cpu baseline")
+        cfg = __import__("synth").make_config(args.workload)
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(out))
 
