@@ -38,8 +38,9 @@ WORKLOAD_TEXT = {
                         "F=128, 50 Gaussians; velocity Verlet 2 fs, neighbour list rebuilt every step",
     "larger_cg": "16 replicas x 1000-bead compact CG chain, rc 12 A, 5 interactions, F=128, 50 Gaussians; "
                  "velocity Verlet 2 fs, rebuild every step",
-    "dense_box": "15,668 particles, periodic box at 0.1/A^3, rc 6 A, 3 interactions, F=128, 32 Gaussians; "
-                 "velocity Verlet 2 fs, rebuild every step",
+    "dense_box": "15,668 particles, periodic box at 0.1/A^3, rc 6 A, 3 interactions, F=128, 32 Gaussians, "
+                 "particles numbered along a Morton curve of 6 A cells; velocity Verlet 2 fs, rebuild every step",
+    "dense_box_random_order": "the same periodic box with its particles in random-sequential-addition order",
     "single_protein": "1 x 269-bead CG chain, rc 12 A, 3 interactions, F=128, 50 Gaussians",
     "tiny_chain": "1 x 32-bead CG chain, rc 10 A, 2 interactions, F=32, 16 Gaussians",
 }
@@ -647,12 +648,12 @@ def main():
         md_kw = [("rebuild_every_step", {}), ("rebuild_every_step_graph", {"graph": True}),
                  ("skin_0.5A_graph", {"skin": 0.5, "rebuild_every": 0, "graph": True}),
                  ("skin_1A_graph", {"skin": 1.0, "rebuild_every": 0, "graph": True})]
-        for name in ("tiny_chain", "single_protein", "larger_cg", "dense_box"):
+        for name in ("tiny_chain", "single_protein", "larger_cg", "dense_box", "dense_box_random_order"):
             log(f"config {name}")
             Wc, res = measure_eval_config(sn, torch, name)
             if name in ("tiny_chain", "single_protein"):
                 res["md"] = md_variants(Wc, 200, 20, md_kw)
-            else:
+            elif name != "dense_box_random_order":
                 res["md"] = md_variants(Wc, 10, 3, md_kw[:2])
             configs[name] = res
             del Wc

@@ -88,6 +88,20 @@ def box_rsa(n: int, L: float, dmin: float, seed: int) -> np.ndarray:
     return pos
 
 
+def morton_order(pos: np.ndarray, L: float, cell: float) -> np.ndarray:
+    """Permutation that numbers particles of a periodic box along a Morton (Z-order) curve of
+    cells of edge >= `cell`, ties in their existing order: the spatial numbering MD engines keep
+    their atoms in, so that neighbours have nearby indices.  Random sequential addition numbers
+    the particles in the random order they were placed."""
+    m = max(1, int(np.floor(L / cell)))
+    c = np.clip(np.floor(np.mod(pos, L) * (m / L)).astype(np.int64), 0, m - 1)
+    code = np.zeros(len(pos), np.int64)
+    for bit in range(int(np.ceil(np.log2(m))) + 1):
+        for axis in range(3):
+            code |= ((c[:, axis] >> bit) & 1) << (3 * bit + axis)
+    return np.argsort(code, kind="stable")
+
+
 def radius_of_gyration(pos: np.ndarray) -> float:
     c = pos - pos.mean(axis=0)
     return float(np.sqrt((c * c).sum(axis=1).mean()))
@@ -159,6 +173,8 @@ def maxwell_boltzmann(n_atoms: int, replica_ptr: np.ndarray, mass: float, temper
 # ---------------------------------------------------------------------------
 
 CONFIG_NAMES = ("tiny_chain", "single_protein", "batched_replicas", "larger_cg", "dense_box")
+# the periodic box with its particles in the order random sequential addition placed them
+EXTRA_CONFIG_NAMES = ("dense_box_random_order",)
 
 
 def _compact_protein_chain(n: int, seed: int, r_conf: float, rg_target: float, moves: int):
@@ -232,11 +248,13 @@ def make_config(name: str, n_replicas: int | None = None) -> dict:
         trng = np.random.default_rng([3, 1])
         per_chain_types = [trng.integers(0, T, 1000) for _ in range(16)][:len(chains)]
         params = init_params(T, I, F, K, [3, 2])
-    elif name == "dense_box":
+    elif name in ("dense_box", "dense_box_random_order"):
         T, I, F, K, rc, lo, hi = 4, 3, 128, 32, 6.0, 0.0, 6.0
         n = 15668
         L = (n / 0.1) ** (1.0 / 3.0)
         p = box_rsa(n, L, 1.0, seed64(4))
+        if name == "dense_box":
+            p = p[morton_order(p, L, rc)]
         chains = ((p, float("nan")),)
         per_chain_types = [np.random.default_rng([4, 1]).integers(0, T, n)]
         params = init_params(T, I, F, K, [4, 2])
