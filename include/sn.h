@@ -237,10 +237,13 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
 
 /* Filter network alone ("How", flash radial basis and the filter network,
  * FlashSchNet summary page): phi[p][F] = ssp(rbf(d_p) A1 + b1) A2 + b2 of
- * interaction `interaction` for n distances d[p] (no envelope).  The same
- * kernel sn_energy_forces uses; exposed for testing and benchmarking. */
+ * interaction `interaction` for n distances d[p] (no envelope), in fp32.
+ * It writes the filter part of the weight pack into ws (a workspace as for
+ * the calls above; it needs at least 256 bytes plus the weight pack) and
+ * runs the same kernel and weight pack as sn_energy_forces, which stores
+ * fc phi in the 24-bit row format instead.  For testing and benchmarking. */
 sn_status sn_filter_forward(const sn_model *model, int32_t interaction, const float *d, int64_t n,
-                            float *phi, void *stream);
+                            float *phi, void *ws, size_t ws_bytes, void *stream);
 
 /* Energy and forces without allocation, for callers that cannot allocate
  * device memory or pass a workspace (code under HIP graph capture, tight

@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
         "sn_energy_forces_static": (i32, [PM, PS, vp, vp, vp, vp, i64, vp, vp, vp, vp]),
         "sn_verlet_step": (i32, [PM, PS, vp, vp, vp, vp, f32, f32, i32, i32, f32, vp, vp, vp, i64, P64, vp, vp, vp,
                                  ctypes.POINTER(ctypes.c_int32), ctypes.c_uint32, vp, sz, vp]),
-        "sn_filter_forward": (i32, [PM, i32, vp, i64, vp, vp]),
+        "sn_filter_forward": (i32, [PM, i32, vp, i64, vp, vp, sz, vp]),
         "sn_read_status": (i32, [vp, vp]),
         "sn_profile_enable": (None, [i32]),
         "sn_profile_classes": (i32, []),
@@ -316,14 +316,14 @@ def verlet_step(model: Model, system: System, pos, vel, forces, inv_mass, dt: fl
     return row_ptr, col[:ne.value], rev[:ne.value], ne.value
 
 
-def filter_forward(model: Model, interaction: int, d, phi=None, stream=None):
-    """sn_filter_forward: phi[n, F] = ssp(rbf(d) A1 + b1) A2 + b2 (no envelope)."""
+def filter_forward(model: Model, interaction: int, d, ws, phi=None, stream=None):
+    """sn_filter_forward: phi[n, F] = ssp(rbf(d) A1 + b1) A2 + b2 (no envelope); ws: a workspace."""
     torch = _torch()
     n = d.numel()
     if phi is None:
         phi = torch.empty((n, model.hyper["n_features"]), dtype=torch.float32, device=d.device)
     _check(lib().sn_filter_forward(ctypes.byref(model.c), int(interaction), d.data_ptr(), n, phi.data_ptr(),
-                                   _stream(stream)), "sn_filter_forward")
+                                   ws.data_ptr(), ws.numel(), _stream(stream)), "sn_filter_forward")
     return phi
 
 

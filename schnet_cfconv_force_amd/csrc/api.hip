@@ -663,11 +663,15 @@ sn_status sn_verlet_step(const sn_model *model, const sn_system *sys, float *pos
 }
 
 sn_status sn_filter_forward(const sn_model *model, int32_t interaction, const float *d, int64_t n, float *phi,
-                            void *stream) {
+                            void *ws, size_t ws_bytes, void *stream) {
     SN_TRY(check_model(model));
     if (interaction < 0 || interaction >= model->n_interactions || n < 0 || (n > 0 && (!d || !phi)))
         return SN_ERR_INVALID;
-    return filter_forward_plain(*model, interaction, d, n, phi, reinterpret_cast<hipStream_t>(stream));
+    SN_TRY(check_ws(ws, ws_bytes, kWsBase + pack_bytes(model->n_interactions)));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char *pack = reinterpret_cast<char *>(ws) + kWsBase;
+    SN_TRY(filter_pack(*model, pack, s));
+    return filter_forward_plain(*model, interaction, d, n, phi, pack, s);
 }
 
 sn_status sn_read_status(void *ws, void *stream) {

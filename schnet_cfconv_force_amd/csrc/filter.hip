@@ -38,9 +38,9 @@
 // 16-byte reads per lane feeds three matrix instructions.  The radial basis
 // is generated in registers from d (no E x K tensor exists anywhere).
 //
-// Work distribution: persistent blocks (one per CU, weights staged once into
-// LDS, int16 codes dequantised while staging); each wavefront loops over
-// 16-pair tiles of an XCD-contiguous range.
+// Work distribution: persistent blocks (one per CU, weights copied once into
+// LDS from the weight pack, where int16 codes were dequantised); each
+// wavefront loops over 16-pair tiles of an XCD-contiguous range.
 #include "split_mfma.h"
 
 namespace sn {
@@ -78,8 +78,8 @@ struct FilterArgs {
     float *S;                    // [P]
     const float *xmax, *gmax;    // [N]: max_f |x_i[f]|, max_f |g_y_i[f]|
     int accumulate;
-    // weight pack (or null): the first layer, the pass's second layer, and
-    // their scales (first layer: {sa1, sz}; second layer: {sa2, -})
+    // weight pack: the first layer, the pass's second layer, and their
+    // scales (first layer: {sa1, sz}; second layer: {sa2, -})
     const half8 *pa1h, *pa1l, *pa2h, *pa2l;
     const int *psc1, *psc2;
 };
@@ -241,24 +241,11 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     __shared__ half8 s_a1h[MT * kKS * 64], s_a1l[MT * kKS * 64];
     __shared__ half8 s_a2h[MT * T2 * 64], s_a2l[MT * T2 * 64];   // [m][t][l]: ln2 A2[chain_k(t, l/16, j)][16 m + l%16]
     __shared__ float s_b1[F], s_b2[F];
-    __shared__ unsigned s_max[3];
     const int KS = (a.K + 31) / 32;
-    int sa1, sa2, sz;
-    if (a.pa1h) {
-        copy_frags<MT * kKS * 64, kFwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * kKS * 64);
-        copy_frags<MT * T2 * 64, kFwdThreads>(s_a2h, s_a2l, a.pa2h, a.pa2l, MT * T2 * 64);
-        sa1 = a.psc1[0];
-        sz = a.psc1[1];
-        sa2 = a.psc2[0];
-    } else {
-        if (threadIdx.x < 3) s_max[threadIdx.x] = 0u;
-        __syncthreads();
-        first_layer_bound<F>(a, &s_max[2]);
-        sa1 = stage_a1<F, kFwdThreads>(a, s_a1h, s_a1l, &s_max[0]);
-        sa2 = stage_split<MT * T2 * 64, kFwdThreads>(s_a2h, s_a2l, MT * T2 * 64, &s_max[1],
-                                                     [&](int idx, float (&v)[8]) { a2_fwd_frag<F>(a, idx, v); });
-        sz = split_scale(__uint_as_float(s_max[2]) * kLog2e + 1.0f);
-    }
+    // the weights come from the pack
+    copy_frags<MT * kKS * 64, kFwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * kKS * 64);
+    copy_frags<MT * T2 * 64, kFwdThreads>(s_a2h, s_a2l, a.pa2h, a.pa2l, MT * T2 * 64);
+    const int sa1 = a.psc1[0], sz = a.psc1[1], sa2 = a.psc2[0];
     for (int f = threadIdx.x; f < F; f += blockDim.x) {
         s_b1[f] = ldexpf(a.b1[f], sa1);
         s_b2[f] = ldexpf(a.b2[f], sz + sa2);
@@ -686,6 +673,7 @@ sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s) {
 
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, int64_t P, uint32_t *phi24,
                          const char *pack, const int *p_dev, const int *guard, hipStream_t s) {
+    if (!pack) return SN_ERR_INVALID;
     FilterArgs a = make_args(m, t);
     attach_pack(a, m, t, pack, PK_FA2);
     a.dsrc = reinterpret_cast<const float *>(pgeo);
@@ -699,8 +687,11 @@ sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, const flo
     return fwd_dispatch(a, m.n_features, s);
 }
 
-sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s) {
+sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, const char *pack,
+                               hipStream_t s) {
+    if (!pack) return SN_ERR_INVALID;
     FilterArgs a = make_args(m, t);
+    attach_pack(a, m, t, pack, PK_FA2);
     a.dsrc = d;
     a.dstride = 1;
     a.doff = 0;

@@ -315,14 +315,16 @@ sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_
 // filter.hip
 // Writes the filter slots of the weight pack (all interactions).
 sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s);
-// pack: the weight pack written by filter_pack, or null (the kernels then stage from the weights).
+// pack: the weight pack written by filter_pack (required).
 // phi24: the filter rows [P][3F/4] in the 24-bit row format (see pack_fp24).
 // P: the pair capacity (launch size); p_dev (may be null): the device pair
 // count; guard (may be null): no pairs are processed while *guard is set.
 // The rows are stored multiplied by the envelope pfc[p] (the CFConv's weight W_p).
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, int64_t P, uint32_t *phi24,
                          const char *pack, const int *p_dev, const int *guard, hipStream_t s);
-sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, hipStream_t s);
+// phi [P][F] in fp32 without the envelope, for n = P distances d (the same kernel).
+sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, const char *pack,
+                               hipStream_t s);
 // xmax / gmax: per-atom max_f |x[i][f]| and max_f |g_y[i][f]| of interaction t
 // pfc / plfc: per-pair envelope fc(d) and fc'(d) / fc(d).  The stored rows are
 // not read (the pass recomputes what it needs of them).  pack: the weight pack

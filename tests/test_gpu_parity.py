@@ -67,12 +67,14 @@ def test_filter_forward_matches_oracle(sn, name, fmt):
     cfg = synth.make_config(name)
     h = cfg["hyper"]
     model = sn.Model(cfg["params"], h, filter_format=fmt)
+    system = sn.System(cfg["replica_ptr"], cfg["types"], cfg["box"])
+    ws = sn.workspace(model, system, 64)
     rng = np.random.default_rng(5)
     d = np.concatenate([np.linspace(0.05, h["cutoff"] * 1.1, 997), rng.uniform(0, h["cutoff"], 1003)])
     d = d.astype(np.float32)       # 2000 values: several tiles plus a ragged one
     params = O.dequantized_params(cfg["params"]) if fmt == 1 else cfg["params"]
     for t in range(h["n_interactions"]):
-        phi = sn.filter_forward(model, t, dev(d)).cpu().numpy().astype(np.float64)
+        phi = sn.filter_forward(model, t, dev(d), ws).cpu().numpy().astype(np.float64)
         blk = {k: np.asarray(v, np.float64) for k, v in params["interactions"][t].items()}
         e, _ = O.gaussian_rbf(d, h["n_rbf"], h["rbf_lo"], h["rbf_hi"], h["rbf_gamma"])
         ref = O.ssp(e @ blk["A1"] + blk["b1"]) @ blk["A2"] + blk["b2"]
