@@ -48,6 +48,11 @@ namespace sn {
 namespace {
 
 constexpr int kFwdThreads = 1024;   // 4 wavefronts per SIMD
+// Systems with fewer 16-pair tiles than 16 per compute unit run the filter
+// kernels in blocks of one wavefront per SIMD instead, so that their tiles
+// spread over up to four times as many compute units (one block per CU
+// either way: the staged weights take most of the LDS).
+constexpr int kSmallThreads = 256;
 constexpr int kFwdMG = 4;           // forward output tiles per product group
 constexpr int kBwdThreads = 1024;   // 4 wavefronts per SIMD
 constexpr int kBwdMG = 1;           // backward output tiles per group (register budget of 4 wavefronts)
@@ -232,8 +237,8 @@ __device__ inline void mma_split2(const half8 *whi, const half8 *wlo, int stride
     }
 }
 
-template <int F>
-__global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
+template <int F, int NTHR>
+__global__ __launch_bounds__(NTHR) void filter_fwd_kernel(FilterArgs a) {
     const int64_t P = (a.guard && *a.guard) ? 0 : a.P_dev ? (int64_t)*a.P_dev : a.P;
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;                      // 32-wide k steps of the F x F GEMM
@@ -243,8 +248,8 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     __shared__ float s_b1[F], s_b2[F];
     const int KS = (a.K + 31) / 32;
     // the weights come from the pack
-    copy_frags<MT * kKS * 64, kFwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * kKS * 64);
-    copy_frags<MT * T2 * 64, kFwdThreads>(s_a2h, s_a2l, a.pa2h, a.pa2l, MT * T2 * 64);
+    copy_frags<MT * kKS * 64, NTHR>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * kKS * 64);
+    copy_frags<MT * T2 * 64, NTHR>(s_a2h, s_a2l, a.pa2h, a.pa2l, MT * T2 * 64);
     const int sa1 = a.psc1[0], sz = a.psc1[1], sa2 = a.psc2[0];
     for (int f = threadIdx.x; f < F; f += blockDim.x) {
         s_b1[f] = ldexpf(a.b1[f], sa1);
@@ -352,8 +357,8 @@ __global__ __launch_bounds__(kFwdThreads) void filter_fwd_kernel(FilterArgs a) {
     }
 }
 
-template <int F>
-__global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
+template <int F, int NTHR>
+__global__ __launch_bounds__(NTHR) void filter_bwd_kernel(FilterArgs a) {
     const int64_t P = (a.guard && *a.guard) ? 0 : a.P_dev ? (int64_t)*a.P_dev : a.P;
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;
@@ -364,8 +369,8 @@ __global__ __launch_bounds__(kBwdThreads) void filter_bwd_kernel(FilterArgs a) {
     __shared__ float4 s_b2f[F / 4];
     const int KS = (a.K + 31) / 32;
     // the weights come from the pack (which also holds the folded bias)
-    copy_frags<MT * kKS * 64, kBwdThreads>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * kKS * 64);
-    copy_frags<MT * T2 * 64, kBwdThreads>(s_a2bh, s_a2bl, a.pa2h, a.pa2l, MT * T2 * 64);
+    copy_frags<MT * kKS * 64, NTHR>(s_a1h, s_a1l, a.pa1h, a.pa1l, MT * kKS * 64);
+    copy_frags<MT * T2 * 64, NTHR>(s_a2bh, s_a2bl, a.pa2h, a.pa2l, MT * T2 * 64);
     const int sa1 = a.psc1[0], sa2 = a.psc2[0];
     for (int f = threadIdx.x; f < F; f += blockDim.x) {
         s_b1[f] = ldexpf(a.b1[f], sa1);
@@ -610,18 +615,30 @@ FilterArgs make_args(const sn_model &m, int t) {
 template <int F>
 sn_status launch_fwd(const FilterArgs &a, hipStream_t s) {
     const int64_t tiles = (a.P + 15) / 16;
+    if (tiles < (int64_t)num_cus() * (kFwdThreads / 64)) {
+        const int waves = kSmallThreads / 64;
+        const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
+        filter_fwd_kernel<F, kSmallThreads><<<grid, kSmallThreads, 0, s>>>(a);
+        return launch_status();
+    }
     const int waves = kFwdThreads / 64;
     const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
-    filter_fwd_kernel<F><<<grid, kFwdThreads, 0, s>>>(a);
+    filter_fwd_kernel<F, kFwdThreads><<<grid, kFwdThreads, 0, s>>>(a);
     return launch_status();
 }
 
 template <int F>
 sn_status launch_bwd(const FilterArgs &a, hipStream_t s) {
     const int64_t tiles = (a.P + 15) / 16;
+    if (tiles < (int64_t)num_cus() * (kBwdThreads / 64)) {
+        const int waves = kSmallThreads / 64;
+        const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
+        filter_bwd_kernel<F, kSmallThreads><<<grid, kSmallThreads, 0, s>>>(a);
+        return launch_status();
+    }
     const int waves = kBwdThreads / 64;
     const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
-    filter_bwd_kernel<F><<<grid, kBwdThreads, 0, s>>>(a);
+    filter_bwd_kernel<F, kBwdThreads><<<grid, kBwdThreads, 0, s>>>(a);
     return launch_status();
 }
 
