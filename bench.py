@@ -206,6 +206,47 @@ def summarize_util(csv_path: str, workload: str, command: str, n_simd: int = 102
     ])
 
 
+def summarize_stats(csv_path: str, workload: str, command: str) -> str:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run (its kernel_stats.csv), one row per
+    kernel: calls, average / min / max duration in microseconds and share of GPU time."""
+    import csv
+    rows = []
+    for r in csv.DictReader(open(csv_path)):
+        name = r.get("Name") or r.get("KernelName") or ""
+        calls = int(float(r.get("Calls", 0)))
+        avg = float(r.get("AverageNs", 0.0)) / 1e3
+        mn = float(r.get("MinNs", 0.0)) / 1e3
+        mx = float(r.get("MaxNs", 0.0)) / 1e3
+        pct = float(r.get("Percentage", 0.0))
+        if name.startswith("Cijk_"):
+            label = "vendor fp16 GEMM (the device-rate probe)"
+        elif "copyBuffer" in name:
+            label = "runtime copy kernel (probes and host transfers)"
+        else:
+            label = _short_kernel(name) + (name[name.find("<"):name.find(">") + 1] if "<" in name else "")
+        rows.append((pct, f"| {label} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.2f} % |"))
+    rows.sort(key=lambda t: -t[0])
+    return "\n".join([
+        f"# rocprofv3 kernel statistics, {workload}",
+        "",
+        "Command (repository root, MI355X):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "The run covers the device-rate probes, the initial neighbour build and evaluation, the warm-up,",
+        "uninstrumented and event-timed MD steps, and the fixed-list evaluations and neighbour builds that",
+        "bench.py times after them; every library kernel runs on one stream, so each duration is that",
+        "kernel alone.  Durations in microseconds, from the kernel_stats.csv that the command writes.",
+        "",
+        "| kernel | calls | average us | min us | max us | share of GPU time |",
+        "|---|---|---|---|---|---|",
+        *[r for _, r in rows],
+        "",
+    ])
+
+
 def load_traffic(workload: str):
     import json as _json
     path = traffic_file(workload)
@@ -516,7 +557,15 @@ def main():
     ap.add_argument("--pmc-command", default="", help="command line recorded in the traffic summary")
     ap.add_argument("--summarize-util", metavar="CSV",
                     help="write the MFMA/VALU/LDS counter summary of one rocprofv3 --pmc run to profiles/ and exit")
+    ap.add_argument("--summarize-stats", metavar="CSV",
+                    help="write the summary of a rocprofv3 --kernel-trace --stats run to profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_stats:
+        md = summarize_stats(args.summarize_stats, args.workload, args.pmc_command)
+        with open(os.path.join(ROOT, "profiles", f"kernel_stats_{args.workload}.md"), "w") as f:
+            f.write(md)
+        print(md)
+        return
     if args.summarize_util:
         md = summarize_util(args.summarize_util, args.workload, args.pmc_command)
         with open(os.path.join(ROOT, "profiles", f"mfma_lds_{args.workload}.md"), "w") as f:
