@@ -574,19 +574,6 @@ __global__ __launch_bounds__(kFwdThreads) void filter_pack_kernel(FilterPackArgs
     }
 }
 
-// Compute units of the current device (read once per process; the
-// initialisation of a function-local static is thread-safe).
-int num_cus() {
-    static const int n = [] {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            return v;
-        return 256;
-    }();
-    return n;
-}
-
 FilterArgs make_args(const sn_model &m, int t) {
     const int F = m.n_features, K = m.n_rbf, I = m.n_interactions, T = m.n_types;
     int64_t off[9 * 16 + 6];
@@ -666,6 +653,20 @@ void attach_pack(FilterArgs &a, const sn_model &m, int t, const char *pack, int 
 }
 
 }  // namespace
+
+// Compute units of the current device (read once per process; the
+// initialisation of a function-local static is thread-safe).
+int num_cus() {
+    static const int n = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            return v;
+        return 256;
+    }();
+    return n;
+}
+
 
 sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s) {
     const int I = m.n_interactions;

@@ -29,31 +29,6 @@ namespace sn {
 
 namespace {
 
-// 5 wavefronts of 16 atoms per block (one block per CU: two buffers of
-// F x F weights take 128 KB of LDS): a 17k-atom system spreads over 216
-// CUs in one pass; 8 wavefronts (135 CUs) were 8 % slower per launch
-constexpr int kMlpWaves = 5;
-constexpr int kMlpThreads = 64 * kMlpWaves;
-
-template <int F>
-struct Dims {
-    static constexpr int M = F / 16;                 // 16-feature tiles of a row
-    static constexpr int MR = F / 32;                // tiles of the readout's hidden layer (F / 2)
-    static constexpr int T = (F + 31) / 32;          // 32-wide k steps over F inputs
-    static constexpr int TR = (F / 2 + 31) / 32;     // ... over F / 2 inputs
-    static constexpr int LAYER = M * T * 64;         // fragments of an F x F layer
-    static constexpr int R1F = MR * T * 64;          // readout first layer (F -> F / 2)
-    static constexpr int R2F = M * TR * 64;          // readout second layer (F / 2 -> F)
-    static constexpr int BUF = LAYER > R1F + R2F ? LAYER : R1F + R2F;
-    static constexpr int IT = (BUF + kMlpThreads - 1) / kMlpThreads;   // fragments per thread
-};
-
-// the atom's largest magnitude over its four k-slot lanes
-__device__ inline float atom_max(float amax) {
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    return fmaxf(amax, __shfl_xor(amax, 32, 64));
-}
-
 // Weights of fragment idx of a layer ([m][t][l], T k steps) in the
 // accumulator-chained order: value j = weight(row 16 m + l%16, column
 // 32 t + 16 (j / 4) + 4 (l / 16) + j % 4); 0 beyond kdim.  W is [kdim][mdim]
@@ -79,108 +54,273 @@ __device__ inline void layer_frag(const float *W, int kdim, int mdim, int idx, f
     }
 }
 
-// One wavefront's 16 atoms.
-struct Wave {
-    int lane, slot, atom;
-    bool live;
+// Blocks of eight wavefronts (two per SIMD) take NA tiles of 16 atoms
+// (NA = 1..5, from the system size, so that small systems still spread over
+// many compute units).  In every layer the output tiles of 16 features are
+// split over the wavefronts (over four groups, the other factor of two over
+// the atom tiles; over all eight when the block has one atom tile): a
+// wavefront loads only its own weight fragments, from the pack straight
+// into registers, and applies each to all of its atom tiles.  A layer's
+// output becomes the next layer's B operands through LDS: each wavefront
+// publishes per-atom partial maxima, takes every atom's scale from all of
+// them, and writes its part of the split operands; the next layer reads each
+// atom tile's operands.  Barriers synchronise LDS only, so weight loads for
+// the next layer and row stores stay in flight across them.
+constexpr int kMlpWaves = 8;
+constexpr int kMlpThreads = 64 * kMlpWaves;
+constexpr int kMlpMaxTiles = 5;
+
+template <int F>
+struct Dims {
+    static constexpr int M = F / 16;                 // 16-feature tiles of a row
+    static constexpr int MR = F / 32;                // tiles of the readout's hidden layer (F / 2)
+    static constexpr int T = (F + 31) / 32;          // 32-wide k steps over F inputs
+    static constexpr int TR = (F / 2 + 31) / 32;     // ... over F / 2 inputs
 };
 
-template <int M>
-__device__ inline void load_rows(const float *src, int F, const Wave &w, float (&v)[M][4]) {
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (w.live) q = *reinterpret_cast<const float4 *>(src + (int64_t)w.atom * F + 16 * m + 4 * w.slot);
-        v[m][0] = q.x; v[m][1] = q.y; v[m][2] = q.z; v[m][3] = q.w;
-    }
-}
-
-template <int M>
-__device__ inline void store_rows(float *dst, int F, const Wave &w, const float (&v)[M][4]) {
-    if (!w.live) return;
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-        *reinterpret_cast<float4 *>(dst + (int64_t)w.atom * F + 16 * m + 4 * w.slot) =
-            make_float4(v[m][0], v[m][1], v[m][2], v[m][3]);
-}
-
-// per-atom max_f |v| (every lane of the atom gets it)
-template <int M>
-__device__ inline float row_absmax(const float (&v)[M][4]) {
-    float mx = 0.0f;
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(v[m][r]));
-    return atom_max(mx);
-}
-
-// out = in W for 16 atoms: MI input tiles, MO output tiles; W as fragments
-// [m][t][l] in LDS (hi at wh, lo at wl) with split scale sw.
-template <int MI, int MO>
-__device__ inline void layer(const float (&in)[MI][4], const half8 *wh, const half8 *wl, int sw, int lane,
-                             float (&out)[MO][4]) {
-    constexpr int T = (16 * MI + 31) / 32;
-    constexpr int MG = MO < 4 ? MO : 4;
-    const int sx = split_scale(row_absmax(in));
-    half8 bh[T], bl[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int m = 2 * t + (j >> 2);
-            v[j] = m < MI ? ldexpf(in[m < MI ? m : 0][j & 3], sx) : 0.0f;
-        }
-        split8(v, bh[t], bl[t]);
-    }
-#pragma unroll
-    for (int m0 = 0; m0 < MO; m0 += MG) {
-        floatx4 acc[MG][1];
-#pragma unroll
-        for (int m = 0; m < MG; ++m) acc[m][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-            mma_split<MG, 1>(wh + (m0 * T + t) * 64 + lane, wl + (m0 * T + t) * 64 + lane, T * 64, &bh[t], &bl[t],
-                             acc);
-#pragma unroll
-        for (int m = 0; m < MG; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) out[m0 + m][r] = ldexpf(acc[m][0][r], -(sw + sx));
-    }
-}
-
-// A weight slot's fragments on their way from the pack to an LDS buffer:
-// loaded into registers before a layer runs, stored after the barrier that
-// frees the buffer.
-template <int F>
-struct Prefetch {
-    half8 h[Dims<F>::IT], l[Dims<F>::IT];
+// A layer with MO output tiles: WM wavefront groups along the features, WA
+// along the atom tiles.  Wavefront w owns the output tiles NI (w % WM) + i,
+// i < NI, of the atom tiles w / WM + WA k, k < NK.
+template <int MO, int NA>
+struct Units {
+    static constexpr int WMAX = NA == 1 ? kMlpWaves : kMlpWaves / 2;
+    static constexpr int WM = MO < WMAX ? MO : WMAX;
+    static constexpr int WA = kMlpWaves / WM;
+    static constexpr int NI = MO / WM;
+    static constexpr int NK = (NA + WA - 1) / WA;
+    static_assert(MO % WM == 0 && kMlpWaves % WM == 0, "output tiles: a power of two");
 };
 
-// (fragments 0..nf-1 of slot r go to buffer positions at..at+nf-1)
-template <int F>
-__device__ inline void prefetch_load(Prefetch<F> &p, const PackRef &r, int nf, int at = 0) {
+// The wavefront's view of its block.
+struct Blk {
+    int lane, slot, w;   // lane, its k-slot (lane / 16), wavefront
+    int tile0, nt;       // the block's first atom tile, and its number of tiles
+    int N;
+    __device__ int atom(int a) const { return (tile0 + a) * 16 + lane % 16; }
+};
+
+template <int MO, int NA>
+__device__ inline int unit_m(const Blk &b, int i) { return Units<MO, NA>::NI * (b.w % Units<MO, NA>::WM) + i; }
+template <int MO, int NA>
+__device__ inline int unit_a(const Blk &b, int k) { return b.w / Units<MO, NA>::WM + Units<MO, NA>::WA * k; }
+
+// value v[i][k][r]: output tile unit_m(i), atom lane % 16 of tile unit_a(k),
+// feature 16 unit_m(i) + 4 slot + r
+template <int MO, int NA>
+using Vals = float[Units<MO, NA>::NI][Units<MO, NA>::NK][4];
+template <int MO, int NA>
+using Accs = floatx4[Units<MO, NA>::NI][Units<MO, NA>::NK];
+
+template <int F, int NA>
+struct ChainSmem {
+    half8 bh[2][NA * Dims<F>::T * 64];   // split B operands [buffer][(tile T + t) 64 + lane]
+    half8 bl[2][NA * Dims<F>::T * 64];
+    float pmax[NA * 16][kMlpWaves];      // per-atom partial maxima of the wavefront groups
+    float psum[NA * 16][kMlpWaves];      // per-atom partial readout sums
+    int sx[NA * 16];                     // per-atom split exponents of the published operands
+};
+
+// LDS-only block barrier: pending LDS operations complete first; global
+// loads and stores stay in flight.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// the atom's largest magnitude over its four k-slot lanes
+__device__ inline float atom_max(float amax) {
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    return fmaxf(amax, __shfl_xor(amax, 32, 64));
+}
+
+template <int F, int MO, int NA>
+__device__ inline void load_vals(const float *src, const Blk &b, Vals<MO, NA> &v) {
+    using U = Units<MO, NA>;
 #pragma unroll
-    for (int it = 0; it < Dims<F>::IT; ++it) {
-        const int idx = (int)threadIdx.x + it * kMlpThreads - at;
-        if (idx >= 0 && idx < nf) {
-            p.h[it] = static_cast<const half8 *>(r.hi)[idx];
-            p.l[it] = static_cast<const half8 *>(r.lo)[idx];
+    for (int k = 0; k < U::NK; ++k) {
+        const int at = unit_a<MO, NA>(b, k);
+        const bool live = at < b.nt && b.atom(at) < b.N;
+#pragma unroll
+        for (int i = 0; i < U::NI; ++i) {
+            float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (live)
+                q = *reinterpret_cast<const float4 *>(src + (int64_t)b.atom(at) * F + 16 * unit_m<MO, NA>(b, i) +
+                                                      4 * b.slot);
+            v[i][k][0] = q.x; v[i][k][1] = q.y; v[i][k][2] = q.z; v[i][k][3] = q.w;
         }
     }
 }
 
-template <int F>
-__device__ inline void prefetch_store(const Prefetch<F> &p, half8 *dh, half8 *dl, int nf) {
+template <int F, int MO, int NA>
+__device__ inline void store_vals(float *dst, const Blk &b, const Vals<MO, NA> &v) {
+    using U = Units<MO, NA>;
 #pragma unroll
-    for (int it = 0; it < Dims<F>::IT; ++it) {
-        const int idx = (int)threadIdx.x + it * kMlpThreads;
-        if (idx < nf) {
-            dh[idx] = p.h[it];
-            dl[idx] = p.l[it];
+    for (int k = 0; k < U::NK; ++k) {
+        const int at = unit_a<MO, NA>(b, k);
+        if (at < b.nt && b.atom(at) < b.N)
+#pragma unroll
+            for (int i = 0; i < U::NI; ++i)
+                *reinterpret_cast<float4 *>(dst + (int64_t)b.atom(at) * F + 16 * unit_m<MO, NA>(b, i) + 4 * b.slot) =
+                    make_float4(v[i][k][0], v[i][k][1], v[i][k][2], v[i][k][3]);
+    }
+}
+
+// Per-atom partial maxima of |v| into pmax (lanes of k-slot 0 write).
+template <int F, int MO, int NA>
+__device__ inline void partial_max(ChainSmem<F, NA> &sm, const Blk &b, const Vals<MO, NA> &v) {
+    using U = Units<MO, NA>;
+#pragma unroll
+    for (int k = 0; k < U::NK; ++k) {
+        const int at = unit_a<MO, NA>(b, k);
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < U::NI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(v[i][k][r]));
+        mx = atom_max(mx);
+        if (at < b.nt && b.slot == 0) sm.pmax[at * 16 + b.lane][b.w % U::WM] = mx;
+    }
+}
+
+// Publish v (a layer's output, MO tiles) as the next layer's B operands in
+// buffer buf, each atom scaled by 2^sx from its largest magnitude over all
+// MO tiles (sx goes to sm.sx for the next layer's unscaling).  A k-step with
+// only one 16-feature tile gets zeros in its other half.  Holds two block
+// barriers; sm.sx is written between them, after every wavefront has
+// unscaled with the previous exponents.
+template <int F, int MO, int NA>
+__device__ inline void publish(ChainSmem<F, NA> &sm, int buf, const Blk &b, const Vals<MO, NA> &v) {
+    using U = Units<MO, NA>;
+    constexpr int T = Dims<F>::T;
+    partial_max<F, MO, NA>(sm, b, v);
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < U::NK; ++k) {
+        const int at = unit_a<MO, NA>(b, k);
+        if (at >= b.nt) continue;
+        float mx = 0.0f;
+#pragma unroll
+        for (int g = 0; g < U::WM; ++g) mx = fmaxf(mx, sm.pmax[at * 16 + b.lane % 16][g]);
+        const int s = split_scale(mx);
+        if (b.w % U::WM == 0 && b.slot == 0) sm.sx[at * 16 + b.lane] = s;
+        if (U::NI % 2 == 0) {
+#pragma unroll
+            for (int i = 0; i < U::NI; i += 2) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = ldexpf(v[i + j / 4][k][j % 4], s);
+                half8 hi, lo;
+                split8(x, hi, lo);
+                const int idx = (at * T + unit_m<MO, NA>(b, i) / 2) * 64 + b.lane;
+                sm.bh[buf][idx] = hi;
+                sm.bl[buf][idx] = lo;
+            }
+        } else {
+            const int m = unit_m<MO, NA>(b, 0);
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = ldexpf(v[0][k][j], s);
+            half4 hi, lo;
+            split4(x, hi, lo);
+            const int idx = (at * T + m / 2) * 64 + b.lane;
+            reinterpret_cast<half4 *>(&sm.bh[buf][idx])[m % 2] = hi;
+            reinterpret_cast<half4 *>(&sm.bl[buf][idx])[m % 2] = lo;
+            if (MO % 2 == 1 && m == MO - 1) {
+                const half4 z = {0, 0, 0, 0};
+                reinterpret_cast<half4 *>(&sm.bh[buf][idx])[1] = z;
+                reinterpret_cast<half4 *>(&sm.bl[buf][idx])[1] = z;
+            }
         }
     }
+    lds_barrier();
+}
+
+// The wavefront's weight fragments of a layer (MO output tiles, TIN k
+// steps; [m][t][l] in the pack).
+template <int MO, int TIN, int NA>
+struct AFrag {
+    half8 h[Units<MO, NA>::NI][TIN], l[Units<MO, NA>::NI][TIN];
+};
+
+template <int MO, int TIN, int NA>
+__device__ inline void load_a(const PackRef &W, const Blk &b, AFrag<MO, TIN, NA> &A) {
+    const half8 *wh = static_cast<const half8 *>(W.hi), *wl = static_cast<const half8 *>(W.lo);
+#pragma unroll
+    for (int i = 0; i < Units<MO, NA>::NI; ++i)
+#pragma unroll
+        for (int t = 0; t < TIN; ++t) {
+            const int idx = (unit_m<MO, NA>(b, i) * TIN + t) * 64 + b.lane;
+            A.h[i][t] = wh[idx];
+            A.l[i][t] = wl[idx];
+        }
+}
+
+// acc = B W for the wavefront's units, B from buffer buf; per accumulator
+// the products run hi.hi, hi.lo, lo.hi per k step, in k order.  Tiles past
+// the block's last are computed too (their columns are never used).
+template <int F, int MO, int TIN, int NA>
+__device__ inline void layer_mma(const ChainSmem<F, NA> &sm, int buf, const Blk &b, const AFrag<MO, TIN, NA> &A,
+                                 Accs<MO, NA> &acc) {
+    using U = Units<MO, NA>;
+    constexpr int T = Dims<F>::T;
+#pragma unroll
+    for (int i = 0; i < U::NI; ++i)
+#pragma unroll
+        for (int k = 0; k < U::NK; ++k) acc[i][k] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < TIN; ++t) {
+        half8 bh[U::NK], bl[U::NK];
+#pragma unroll
+        for (int k = 0; k < U::NK; ++k) {
+            const int at = min(unit_a<MO, NA>(b, k), NA - 1);
+            bh[k] = sm.bh[buf][(at * T + t) * 64 + b.lane];
+            bl[k] = sm.bl[buf][(at * T + t) * 64 + b.lane];
+        }
+#pragma unroll
+        for (int i = 0; i < U::NI; ++i)
+#pragma unroll
+            for (int k = 0; k < U::NK; ++k)
+                acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.h[i][t], bh[k], acc[i][k], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < U::NI; ++i)
+#pragma unroll
+            for (int k = 0; k < U::NK; ++k)
+                acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.h[i][t], bl[k], acc[i][k], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < U::NI; ++i)
+#pragma unroll
+            for (int k = 0; k < U::NK; ++k)
+                acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.l[i][t], bh[k], acc[i][k], 0, 0, 0);
+    }
+}
+
+// out = acc 2^-(sw + sx) (the layer's unscaled output; sx of the layer's
+// input, from sm.sx)
+template <int F, int MO, int NA>
+__device__ inline void unscale(const ChainSmem<F, NA> &sm, const Accs<MO, NA> &acc, int sw, const Blk &b,
+                               Vals<MO, NA> &out) {
+    using U = Units<MO, NA>;
+#pragma unroll
+    for (int k = 0; k < U::NK; ++k) {
+        const int at = min(unit_a<MO, NA>(b, k), NA - 1);
+        const int e = -(sw + sm.sx[at * 16 + b.lane % 16]);
+#pragma unroll
+        for (int i = 0; i < U::NI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[i][k][r] = ldexpf(acc[i][k][r], e);
+    }
+}
+
+// dst[atom] = max_f |v[atom][f]| (after a block barrier)
+template <int F, int MO, int NA>
+__device__ inline void store_row_max(ChainSmem<F, NA> &sm, const Blk &b, const Vals<MO, NA> &v, float *dst) {
+    partial_max<F, MO, NA>(sm, b, v);
+    lds_barrier();
+    if (b.w == 0 && b.lane < 16)
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int g = 0; g < Units<MO, NA>::WM; ++g) mx = fmaxf(mx, sm.pmax[a * 16 + b.lane][g]);
+            if (a < b.nt && b.atom(a) < b.N) dst[b.atom(a)] = mx;
+        }
 }
 
 enum Prog { P_EMBED_X = 0, P_OUT_X, P_TAIL, P_BX_BO };
@@ -205,202 +345,231 @@ struct ChainArgs {
     float *gy, *gmax;            // TAIL, BX_BO: g_y and its row maxima
 };
 
-template <int F, int PROG>
+template <int F, int PROG, int NA>
 __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
     using D = Dims<F>;
-    constexpr int M = D::M, MR = D::MR;
-    __shared__ half8 s_ah[D::BUF], s_al[D::BUF], s_bh[D::BUF], s_bl[D::BUF];
-    Wave w;
-    w.lane = threadIdx.x % 64;
-    w.slot = w.lane / 16;
-    const int base = (blockIdx.x * kMlpWaves + threadIdx.x / 64) * 16;
-    w.atom = base + w.lane % 16;
-    w.live = w.atom < a.N;
-    const bool active = base < a.N;   // the wavefront has atoms (all waves join the barriers)
-    const int lane = w.lane;
-    Prefetch<F> pf;
+    constexpr int M = D::M, MR = D::MR, T = D::T, TR = D::TR;
+    using U = Units<M, NA>;
+    __shared__ ChainSmem<F, NA> sm;
+    Blk b;
+    b.lane = threadIdx.x % 64;
+    b.slot = b.lane / 16;
+    b.w = threadIdx.x / 64;
+    b.tile0 = blockIdx.x * NA;
+    b.nt = min(NA, (a.N + 15) / 16 - b.tile0);
+    b.N = a.N;
+    Accs<M, NA> acc;
 
     if (PROG == P_EMBED_X) {
-        copy_frags<D::BUF, kMlpThreads>(s_ah, s_al, static_cast<const half8 *>(a.w[0].hi),
-                                        static_cast<const half8 *>(a.w[0].lo), D::LAYER);
-        const int sw0 = a.w[0].sc[0];
-        float h[M][4];
-        if (active) {
-            int z = w.live ? a.types[w.atom] : 0;
+        AFrag<M, T, NA> A0;
+        load_a<M, T, NA>(a.w[0], b, A0);
+        Vals<M, NA> h;
+#pragma unroll
+        for (int k = 0; k < U::NK; ++k) {
+            const int at = unit_a<M, NA>(b, k);
+            const bool live = at < b.nt && b.atom(at) < b.N;
+            int z = live ? a.types[b.atom(at)] : 0;
             if (z < 0 || z >= a.n_types) {
-                if (w.slot == 0) flag_status(a.status, SN_ERR_INVALID);
+                flag_status(a.status, SN_ERR_INVALID);
                 z = 0;
             }
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const float4 q = *reinterpret_cast<const float4 *>(a.emb + (int64_t)z * F + 16 * m + 4 * w.slot);
-                h[m][0] = q.x; h[m][1] = q.y; h[m][2] = q.z; h[m][3] = q.w;
+            for (int i = 0; i < U::NI; ++i) {
+                const float4 q = *reinterpret_cast<const float4 *>(a.emb + (int64_t)z * F + 16 * unit_m<M, NA>(b, i) +
+                                                                   4 * b.slot);
+                h[i][k][0] = q.x; h[i][k][1] = q.y; h[i][k][2] = q.z; h[i][k][3] = q.w;
             }
-            store_rows<M>(a.h, F, w, h);
         }
-        __syncthreads();
-        if (!active) return;
-        float x[M][4];
-        layer<M, M>(h, s_ah, s_al, sw0, lane, x);
-        store_rows<M>(a.x, F, w, x);
-        const float mx = row_absmax(x);
-        if (w.live && w.slot == 0) a.xmax[w.atom] = mx;
+        store_vals<F, M, NA>(a.h, b, h);
+        publish<F, M, NA>(sm, 0, b, h);
+        layer_mma<F, M, T, NA>(sm, 0, b, A0, acc);
+        Vals<M, NA> x;
+        unscale<F, M, NA>(sm, acc, a.w[0].sc[0], b, x);
+        store_vals<F, M, NA>(a.x, b, x);
+        store_row_max<F, M, NA>(sm, b, x, a.xmax);
         return;
     }
 
-    // the first two layers' weights; the first layer's input
-    copy_frags<D::BUF, kMlpThreads>(s_ah, s_al, static_cast<const half8 *>(a.w[0].hi),
-                                    static_cast<const half8 *>(a.w[0].lo), D::LAYER);
-    copy_frags<D::BUF, kMlpThreads>(s_bh, s_bl, static_cast<const half8 *>(a.w[1].hi),
-                                    static_cast<const half8 *>(a.w[1].lo), D::LAYER);
-    const int sw0 = a.w[0].sc[0], sw1 = a.w[1].sc[0];
-    float in[M][4];
-    if (active) load_rows<M>(a.in, F, w, in);
-    __syncthreads();
-
     if (PROG == P_OUT_X) {
-        prefetch_load<F>(pf, a.w[2], D::LAYER);
-        const int sw2 = a.w[2].sc[0];
-        float o[M][4], z[M][4];
-        if (active) {
-            layer<M, M>(in, s_ah, s_al, sw0, lane, o);
+        // layers: Wo1, Wo2, W_in of the next interaction
+        AFrag<M, T, NA> A;
+        load_a<M, T, NA>(a.w[0], b, A);
+        Vals<M, NA> v, hin;   // every row load is issued up front
+        load_vals<F, M, NA>(a.in, b, v);
+        load_vals<F, M, NA>(a.h_in, b, hin);
+        publish<F, M, NA>(sm, 0, b, v);
+        layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
+        load_a<M, T, NA>(a.w[1], b, A);
+        {
+            Vals<M, NA> o;
+            unscale<F, M, NA>(sm, acc, a.w[0].sc[0], b, o);
 #pragma unroll
-            for (int m = 0; m < M; ++m)
+            for (int i = 0; i < U::NI; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    o[m][r] += a.bo1[16 * m + 4 * w.slot + r];
-                    z[m][r] = ssp(o[m][r]);
-                }
-            store_rows<M>(a.o, F, w, o);
+                for (int k = 0; k < U::NK; ++k)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        o[i][k][r] += a.bo1[16 * unit_m<M, NA>(b, i) + 4 * b.slot + r];
+                        v[i][k][r] = ssp(o[i][k][r]);
+                    }
+            store_vals<F, M, NA>(a.o, b, o);
         }
-        __syncthreads();                                  // buffer A is free
-        prefetch_store<F>(pf, s_ah, s_al, D::LAYER);
-        float h[M][4];
-        if (active) {
-            float d[M][4];
-            layer<M, M>(z, s_bh, s_bl, sw1, lane, d);
-            load_rows<M>(a.h_in, F, w, h);
+        publish<F, M, NA>(sm, 1, b, v);
+        layer_mma<F, M, T, NA>(sm, 1, b, A, acc);
+        load_a<M, T, NA>(a.w[2], b, A);
+        {
+            Vals<M, NA> d;
+            unscale<F, M, NA>(sm, acc, a.w[1].sc[0], b, d);
 #pragma unroll
-            for (int m = 0; m < M; ++m)
+            for (int i = 0; i < U::NI; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) h[m][r] = h[m][r] + d[m][r] + a.bo2[16 * m + 4 * w.slot + r];
-            store_rows<M>(a.h, F, w, h);
+                for (int k = 0; k < U::NK; ++k)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[i][k][r] = hin[i][k][r] + d[i][k][r] + a.bo2[16 * unit_m<M, NA>(b, i) + 4 * b.slot + r];
+            store_vals<F, M, NA>(a.h, b, v);
         }
-        __syncthreads();                                  // W_in is in buffer A
-        if (!active) return;
-        float x[M][4];
-        layer<M, M>(h, s_ah, s_al, sw2, lane, x);
-        store_rows<M>(a.x, F, w, x);
-        const float mx = row_absmax(x);
-        if (w.live && w.slot == 0) a.xmax[w.atom] = mx;
+        publish<F, M, NA>(sm, 0, b, v);
+        layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
+        unscale<F, M, NA>(sm, acc, a.w[2].sc[0], b, v);
+        store_vals<F, M, NA>(a.x, b, v);
+        store_row_max<F, M, NA>(sm, b, v, a.xmax);
         return;
     }
 
     if (PROG == P_TAIL) {
-        // layers: Wo1 (A), Wo2 (B), R1 and R1^T (A), Wo2^T (B), Wo1^T (A)
-        prefetch_load<F>(pf, a.w[2], D::R1F);
-        prefetch_load<F>(pf, a.w[3], D::R2F, D::R1F);
-        const int sw2 = a.w[2].sc[0], sw3 = a.w[3].sc[0], sw4 = a.w[4].sc[0], sw5 = a.w[5].sc[0];
-        float o[M][4], z[M][4];
-        if (active) {
-            layer<M, M>(in, s_ah, s_al, sw0, lane, o);
+        // layers: Wo1, Wo2, R1, R1^T, Wo2^T, Wo1^T
+        using UR = Units<MR, NA>;
+        AFrag<M, T, NA> A;
+        load_a<M, T, NA>(a.w[0], b, A);
+        Vals<M, NA> v, o, hin;   // every row load is issued up front
+        load_vals<F, M, NA>(a.in, b, v);
+        load_vals<F, M, NA>(a.h_in, b, hin);
+        publish<F, M, NA>(sm, 0, b, v);
+        layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
+        load_a<M, T, NA>(a.w[1], b, A);
+        unscale<F, M, NA>(sm, acc, a.w[0].sc[0], b, o);
 #pragma unroll
-            for (int m = 0; m < M; ++m)
+        for (int i = 0; i < U::NI; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    o[m][r] += a.bo1[16 * m + 4 * w.slot + r];
-                    z[m][r] = ssp(o[m][r]);
-                }
-        }
-        __syncthreads();                                  // buffer A is free
-        prefetch_store<F>(pf, s_ah, s_al, D::R1F + D::R2F);
-        float h[M][4];
-        if (active) {
-            float d[M][4];
-            layer<M, M>(z, s_bh, s_bl, sw1, lane, d);
-            load_rows<M>(a.h_in, F, w, h);
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) h[m][r] = h[m][r] + d[m][r] + a.bo2[16 * m + 4 * w.slot + r];
-        }
-        prefetch_load<F>(pf, a.w[4], D::LAYER);
-        __syncthreads();                                  // R1, R1^T in A; buffer B is free
-        prefetch_store<F>(pf, s_bh, s_bl, D::LAYER);
-        float gh[M][4];
-        if (active) {
-            float q[MR][4], zq[MR][4];
-            layer<M, MR>(h, s_ah, s_al, sw2, lane, q);
-            float eps_part = 0.0f;
-#pragma unroll
-            for (int m = 0; m < MR; ++m)
+            for (int k = 0; k < U::NK; ++k)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int n0 = 16 * m + 4 * w.slot + r;
-                    const float qq = q[m][r] + a.c1[n0];
-                    eps_part += ssp(qq) * a.R2[n0];
-                    zq[m][r] = sigm(qq) * a.R2[n0];
+                    o[i][k][r] += a.bo1[16 * unit_m<M, NA>(b, i) + 4 * b.slot + r];
+                    v[i][k][r] = ssp(o[i][k][r]);
                 }
-            eps_part += __shfl_xor(eps_part, 16, 64);
-            eps_part += __shfl_xor(eps_part, 32, 64);
-            if (w.live && w.slot == 0) a.eps[w.atom] = eps_part + a.c2[0];
-            layer<MR, M>(zq, s_ah + D::R1F, s_al + D::R1F, sw3, lane, gh);
-            store_rows<M>(a.gh, F, w, gh);
-        }
-        prefetch_load<F>(pf, a.w[5], D::LAYER);
-        __syncthreads();                                  // Wo2^T in B; buffer A is free
-        prefetch_store<F>(pf, s_ah, s_al, D::LAYER);
-        float go[M][4];
-        if (active) {
-            layer<M, M>(gh, s_bh, s_bl, sw4, lane, go);
+        publish<F, M, NA>(sm, 1, b, v);
+        layer_mma<F, M, T, NA>(sm, 1, b, A, acc);
+        AFrag<MR, T, NA> AR;
+        load_a<MR, T, NA>(a.w[2], b, AR);
+        {
+            Vals<M, NA> d;
+            unscale<F, M, NA>(sm, acc, a.w[1].sc[0], b, d);
 #pragma unroll
-            for (int m = 0; m < M; ++m)
+            for (int i = 0; i < U::NI; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) go[m][r] *= sigm(o[m][r]);
+                for (int k = 0; k < U::NK; ++k)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[i][k][r] = hin[i][k][r] + d[i][k][r] + a.bo2[16 * unit_m<M, NA>(b, i) + 4 * b.slot + r];
         }
-        __syncthreads();                                  // Wo1^T in A
-        if (!active) return;
-        float gy[M][4];
-        layer<M, M>(go, s_ah, s_al, sw5, lane, gy);
-        store_rows<M>(a.gy, F, w, gy);
-        const float mx = row_absmax(gy);
-        if (w.live && w.slot == 0) a.gmax[w.atom] = mx;
+        publish<F, M, NA>(sm, 0, b, v);
+        {
+            // readout: q = h R1 + c1; eps = ssp(q) . R2 + c2; its gradient
+            // sigmoid(q) (.) R2 goes on through R1^T
+            Accs<MR, NA> accr;
+            layer_mma<F, MR, T, NA>(sm, 0, b, AR, accr);
+            AFrag<M, TR, NA> AT;
+            load_a<M, TR, NA>(a.w[3], b, AT);
+            Vals<MR, NA> q;
+            unscale<F, MR, NA>(sm, accr, a.w[2].sc[0], b, q);
+#pragma unroll
+            for (int k = 0; k < UR::NK; ++k) {
+                const int at = unit_a<MR, NA>(b, k);
+                float e = 0.0f;
+#pragma unroll
+                for (int i = 0; i < UR::NI; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int n0 = 16 * unit_m<MR, NA>(b, i) + 4 * b.slot + r;
+                        const float qq = q[i][k][r] + a.c1[n0];
+                        e += ssp(qq) * a.R2[n0];
+                        q[i][k][r] = sigm(qq) * a.R2[n0];
+                    }
+                e += __shfl_xor(e, 16, 64);
+                e += __shfl_xor(e, 32, 64);
+                if (at < b.nt && b.slot == 0) sm.psum[at * 16 + b.lane][b.w % UR::WM] = e;
+            }
+            publish<F, MR, NA>(sm, 1, b, q);   // its barriers also order the partial sums
+            if (b.w == 0 && b.lane < 16)
+#pragma unroll
+                for (int at = 0; at < NA; ++at) {
+                    float e = sm.psum[at * 16 + b.lane][0];
+#pragma unroll
+                    for (int g = 1; g < UR::WM; ++g) e += sm.psum[at * 16 + b.lane][g];
+                    if (at < b.nt && b.atom(at) < b.N) a.eps[b.atom(at)] = e + a.c2[0];
+                }
+            layer_mma<F, M, TR, NA>(sm, 1, b, AT, acc);
+        }
+        load_a<M, T, NA>(a.w[4], b, A);
+        unscale<F, M, NA>(sm, acc, a.w[3].sc[0], b, v);
+        store_vals<F, M, NA>(a.gh, b, v);
+        publish<F, M, NA>(sm, 0, b, v);
+        layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
+        load_a<M, T, NA>(a.w[5], b, A);
+        unscale<F, M, NA>(sm, acc, a.w[4].sc[0], b, v);
+#pragma unroll
+        for (int i = 0; i < U::NI; ++i)
+#pragma unroll
+            for (int k = 0; k < U::NK; ++k)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[i][k][r] *= sigm(o[i][k][r]);
+        publish<F, M, NA>(sm, 1, b, v);
+        layer_mma<F, M, T, NA>(sm, 1, b, A, acc);
+        unscale<F, M, NA>(sm, acc, a.w[5].sc[0], b, v);
+        store_vals<F, M, NA>(a.gy, b, v);
+        store_row_max<F, M, NA>(sm, b, v, a.gmax);
         return;
     }
 
-    // P_BX_BO: layers W_in^T (A), Wo2^T (B), Wo1^T (A)
-    prefetch_load<F>(pf, a.w[2], D::LAYER);
-    const int sw2 = a.w[2].sc[0];
-    float gh[M][4];
-    if (active) {
-        float d[M][4];
-        layer<M, M>(in, s_ah, s_al, sw0, lane, d);
-        load_rows<M>(a.gh, F, w, gh);
+    // P_BX_BO: layers W_in^T, Wo2^T, Wo1^T
+    AFrag<M, T, NA> A;
+    load_a<M, T, NA>(a.w[0], b, A);
+    Vals<M, NA> v, gh, op;   // every row load is issued up front
+    load_vals<F, M, NA>(a.in, b, v);
+    load_vals<F, M, NA>(a.gh, b, gh);
+    load_vals<F, M, NA>(a.o_prev, b, op);
+    publish<F, M, NA>(sm, 0, b, v);
+    layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
+    load_a<M, T, NA>(a.w[1], b, A);
+    {
+        Vals<M, NA> d;
+        unscale<F, M, NA>(sm, acc, a.w[0].sc[0], b, d);
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+        for (int i = 0; i < U::NI; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) gh[m][r] += d[m][r];
-        store_rows<M>(a.gh, F, w, gh);
+            for (int k = 0; k < U::NK; ++k)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[i][k][r] = gh[i][k][r] + d[i][k][r];
+        store_vals<F, M, NA>(a.gh, b, v);
     }
-    __syncthreads();                                      // buffer A is free
-    prefetch_store<F>(pf, s_ah, s_al, D::LAYER);
-    float go[M][4];
-    if (active) {
-        float op[M][4];
-        layer<M, M>(gh, s_bh, s_bl, sw1, lane, go);
-        load_rows<M>(a.o_prev, F, w, op);
+    publish<F, M, NA>(sm, 1, b, v);
+    layer_mma<F, M, T, NA>(sm, 1, b, A, acc);
+    load_a<M, T, NA>(a.w[2], b, A);
+    {
+        unscale<F, M, NA>(sm, acc, a.w[1].sc[0], b, v);
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+        for (int i = 0; i < U::NI; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) go[m][r] *= sigm(op[m][r]);
+            for (int k = 0; k < U::NK; ++k)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[i][k][r] *= sigm(op[i][k][r]);
     }
-    __syncthreads();                                      // Wo1^T in A
-    if (!active) return;
-    float gy[M][4];
-    layer<M, M>(go, s_ah, s_al, sw2, lane, gy);
-    store_rows<M>(a.gy, F, w, gy);
-    const float mx = row_absmax(gy);
-    if (w.live && w.slot == 0) a.gmax[w.atom] = mx;
+    publish<F, M, NA>(sm, 0, b, v);
+    layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
+    unscale<F, M, NA>(sm, acc, a.w[2].sc[0], b, v);
+    store_vals<F, M, NA>(a.gy, b, v);
+    store_row_max<F, M, NA>(sm, b, v, a.gmax);
 }
 
 // Pre-split one matrix into a weight-pack slot (as a block's staging would
@@ -449,17 +618,30 @@ __global__ __launch_bounds__(kMlpThreads) void mlp_pack_kernel(MlpPackArgs pa) {
     if (threadIdx.x == 0) const_cast<int *>(r.sc)[0] = sc;
 }
 
+template <int PROG, int NA>
+void launch_na(int F, int grid, const ChainArgs &a, hipStream_t s) {
+    switch (F) {
+        case 32: chain_kernel<32, PROG, NA><<<grid, kMlpThreads, 0, s>>>(a); break;
+        case 64: chain_kernel<64, PROG, NA><<<grid, kMlpThreads, 0, s>>>(a); break;
+        default: chain_kernel<128, PROG, NA><<<grid, kMlpThreads, 0, s>>>(a); break;
+    }
+}
+
+// Atom tiles per block: as few as fill the compute units once.
 template <int PROG>
 sn_status launch_chain(int F, const ChainArgs &a, hipStream_t s) {
     if (a.N <= 0) return SN_OK;
+    if (F != 32 && F != 64 && F != 128) return SN_ERR_INVALID;
     ProfScope ps(K_MLP, s);
-    const int atoms_per_block = 16 * kMlpWaves;
-    const int grid = (a.N + atoms_per_block - 1) / atoms_per_block;
-    switch (F) {
-        case 32: chain_kernel<32, PROG><<<grid, kMlpThreads, 0, s>>>(a); break;
-        case 64: chain_kernel<64, PROG><<<grid, kMlpThreads, 0, s>>>(a); break;
-        case 128: chain_kernel<128, PROG><<<grid, kMlpThreads, 0, s>>>(a); break;
-        default: return SN_ERR_INVALID;
+    const int tiles = (a.N + 15) / 16, cus = num_cus();
+    const int na = std::min(kMlpMaxTiles, std::max(1, (tiles + cus - 1) / cus));
+    const int grid = (tiles + na - 1) / na;
+    switch (na) {
+        case 1: launch_na<PROG, 1>(F, grid, a, s); break;
+        case 2: launch_na<PROG, 2>(F, grid, a, s); break;
+        case 3: launch_na<PROG, 3>(F, grid, a, s); break;
+        case 4: launch_na<PROG, 4>(F, grid, a, s); break;
+        default: launch_na<PROG, 5>(F, grid, a, s); break;
     }
     return launch_status();
 }

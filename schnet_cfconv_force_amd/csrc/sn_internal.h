@@ -387,6 +387,9 @@ sn_status forces_rows(int N, int B, const int32_t *replica_ptr, const float *eps
                       hipStream_t s, double *elog = nullptr, int elog_by_step = 0);
 
 
+// Compute units of the current device (filter.hip; read once per process).
+int num_cus();
+
 // mlp.hip (fused atom-wise layers; see the kernel comments there).  The
 // weights come from the weight pack (slots written by mlp_pack).
 sn_status mlp_pack(const sn_model &m, char *pack, hipStream_t s);

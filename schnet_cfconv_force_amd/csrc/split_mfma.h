@@ -54,6 +54,28 @@ __device__ inline void split8(const float (&v)[8], half8 &hi, half8 &lo) {
     lo = l;
 }
 
+// The same for four values (half of one B operand).
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+__device__ inline void split4(const float (&v)[4], half4 &hi, half4 &lo) {
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        x[j] = v[j];
+        asm("" : "+v"(x[j]));
+    }
+    half4 h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = (_Float16)x[j];
+    asm("" : "+v"(h));
+    float m1 = -1.0f;
+    asm("" : "+s"(m1));
+    half4 l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l[j] = (_Float16)fmaf((float)h[j], m1, x[j]);
+    hi = h;
+    lo = l;
+}
+
 // Power-of-two exponent s with amax 2^s in [2^(kSplitTop-1), 2^kSplitTop)
 // (0 for a zero or non-finite maximum).
 __device__ inline int split_scale(float amax) {
