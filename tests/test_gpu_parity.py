@@ -274,6 +274,27 @@ def test_energy_forces_other_model_shapes(sn, F, K, I, T):
     _compare(E, Fo, E_ref, F_ref, eps_abs, rp, f"F={F} K={K}")
 
 
+@pytest.mark.parametrize("F,K,I,T,n_rep", [(32, 16, 2, 4, 56), (64, 33, 2, 4, 100), (64, 16, 1, 3, 60),
+                                           (128, 50, 2, 5, 150), (32, 16, 2, 4, 190)])
+def test_energy_forces_atomwise_block_sizes(sn, F, K, I, T, n_rep):
+    """Systems of 5,040 to 17,100 atoms, so that the atom-wise layers run with every number of
+    16-atom tiles per block (one to five, chosen from the tile count and 256 compute units), each
+    with a ragged last block, for every feature width; every replica against the oracle."""
+    say(f"[atom-wise block sizes] F={F} K={K} I={I} T={T} replicas={n_rep}")
+    pos, rp = _random_system(n_rep, 90, 18.0, 2000 + F + n_rep)
+    rc = 7.0
+    cfg = {"pos": pos, "replica_ptr": rp, "box": None,
+           "types": np.random.default_rng(F + n_rep).integers(0, T, len(pos)).astype(np.int32),
+           "params": synth.init_params(T, I, F, K, [F, K, I, n_rep]),
+           "hyper": {"n_types": T, "n_interactions": I, "n_features": F, "n_rbf": K, "cutoff": rc,
+                     **synth.rbf_hyper(K, 0.0, rc)}}
+    L = Loaded(sn, cfg)
+    E, Fo = L.eval(sn)
+    E_ref, F_ref, eps_abs, csr = oracle_full(cfg)
+    assert len(csr[1]) > 8 * len(pos)
+    _compare(E, Fo, E_ref, F_ref, eps_abs, rp, f"F={F} replicas={n_rep}")
+
+
 def test_energy_forces_with_saturated_first_layer(sn):
     """Half of the first layer's features pushed to a ~ -60, where the sigmoid and softplus are
     below 1e-26 (the backward filter caps its exponent there, below a = -44): energies and forces
