@@ -339,7 +339,7 @@ def cpu_baseline(cfg, seconds: float):
 class Workload:
     """One seeded workload on the device: model, system, positions, velocities, initial forces."""
 
-    def __init__(self, sn, torch, name: str, fmt: int = 0):
+    def __init__(self, sn, torch, name: str, fmt: int = 0, math: int = 0):
         import numpy as np
         import synth
         self.sn, self.torch, self.name = sn, torch, name
@@ -352,7 +352,7 @@ class Workload:
         if "vel" not in cfg:
             cfg["vel"] = synth.maxwell_boltzmann(self.N, cfg["replica_ptr"], 110.0, 300.0, 2)
             cfg["inv_mass"] = np.full(self.N, 1.0 / 110.0, np.float32)
-        self.model = sn.Model(cfg["params"], h, filter_format=fmt)
+        self.model = sn.Model(cfg["params"], h, filter_format=fmt, filter_math=math)
         self.system = sn.System(cfg["replica_ptr"], cfg["types"], cfg["box"])
         self.capacity = self.N * 200
         self.ws = sn.workspace(self.model, self.system, self.capacity)
@@ -502,14 +502,17 @@ def md_variants(W, steps, warmup, variants):
     return out
 
 
-def int16_drift(sn, torch, steps=100):
-    """Drift of the int16 filter weights from the fp32 weights on the 64 x 269 workload: one
-    evaluation at the same neighbour list (relative energy change, RMS force change over RMS force)
-    and the difference of the total-energy traces over `steps` MD steps (fp64 logs)."""
+def mode_drift(sn, torch, mode: str, steps=100):
+    """Drift of an alternative filter mode from the default (fp32 weights, fp32-accurate products) on
+    the 64 x 269 workload: mode "int16" (per-output-channel int16 filter weights) or "fp16_math" (one
+    fp16 product per filter-network product).  One evaluation at the same neighbour list (relative
+    energy change, RMS force change over RMS force), the difference of the total-energy traces over
+    `steps` MD steps (fp64 logs), and both MD rates (timed alternately, best of two)."""
     import numpy as np
+    kw = {"int16": {"fmt": 1}, "fp16_math": {"math": 1}}[mode]
     runs, work = {}, {}
-    for fmt in (0, 1):
-        W = Workload(sn, torch, "batched_replicas", fmt=fmt)
+    for alt in (0, 1):
+        W = Workload(sn, torch, "batched_replicas", **(kw if alt else {}))
         e, f = sn.energy_forces(W.model, W.system, W.pos, W.row_ptr, W.col, W.rev, W.E, W.ws)
         e = e.cpu().numpy().astype(np.float64)
         f = f.cpu().numpy().astype(np.float64)
@@ -517,24 +520,25 @@ def int16_drift(sn, torch, steps=100):
         ek = torch.zeros((steps, W.B), dtype=torch.float64, device="cuda")
         W.md(steps, epot=ep, ekin=ek)
         tot = (ep + ek).cpu().numpy()
-        runs[fmt] = (e, f, tot, ek.cpu().numpy())
-        work[fmt] = W
-    # the two rates timed alternately, twice each (best of two)
+        runs[alt] = (e, f, tot, ek.cpu().numpy())
+        work[alt] = W
     sec = {0: float("inf"), 1: float("inf")}
     for _ in range(2):
-        for fmt in (0, 1):
-            sec[fmt] = min(sec[fmt], work[fmt].time_md(20, 3)[0])
+        for alt in (0, 1):
+            sec[alt] = min(sec[alt], work[alt].time_md(20, 3)[0])
     e0, f0, t0, k0 = runs[0]
     e1, f1, t1, _ = runs[1]
-    s0, s1 = sec[0], sec[1]
-    return {"rel_dE_max": float(np.abs(e1 - e0).max() / np.abs(e0).max()),
+    W1 = work[1]
+    prof = W1.profile(lambda: W1.md(1), 10)
+    return {"kernels": {k: v for k, v in kernels_table(prof, 10).items() if k.startswith("filter")},
+            "rel_dE_max": float(np.abs(e1 - e0).max() / np.abs(e0).max()),
             "rms_dF_over_rms_F": float(np.sqrt(((f1 - f0) ** 2).mean() / (f0 ** 2).mean())),
             "etot_trace_max_abs_diff_kcal_mol": float(np.abs(t1 - t0).max()),
             "etot_trace_diff_over_mean_ekin": float(np.abs(t1 - t0).max() / k0.mean()),
             "etot_drift_fp32_kcal_mol": float(np.abs(t0 - t0[0]).max()),
-            "etot_drift_int16_kcal_mol": float(np.abs(t1 - t1[0]).max()),
+            f"etot_drift_{mode}_kcal_mol": float(np.abs(t1 - t1[0]).max()),
             "md_steps": steps,
-            "md_steps_per_s_fp32": round(1.0 / s0, 2), "md_steps_per_s_int16": round(1.0 / s1, 2)}
+            "md_steps_per_s_fp32": round(1.0 / sec[0], 2), f"md_steps_per_s_{mode}": round(1.0 / sec[1], 2)}
 
 
 def main():
@@ -723,7 +727,12 @@ def main():
         log("config batched_replicas with int16 filter weights")
         configs["batched_replicas_int16"] = {
             "workload": WORKLOAD_TEXT["batched_replicas"] + "; per-output-channel int16 filter weights",
-            **int16_drift(sn, torch)}
+            **mode_drift(sn, torch, "int16")}
+        log("config batched_replicas with one fp16 product per filter product")
+        configs["batched_replicas_fp16_filter_math"] = {
+            "workload": WORKLOAD_TEXT["batched_replicas"] + "; filter network with one fp16 product per fp32 "
+                        "product (reduced precision, not the headline arithmetic)",
+            **mode_drift(sn, torch, "fp16_math")}
         out["configs"] = configs
     if not args.no_cpu_baseline:
         log("cpu baseline")

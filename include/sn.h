@@ -86,6 +86,15 @@ typedef struct sn_system {
  * qweights holds, per interaction, qA1[K][F] then qA2[F][F]; qscales holds,
  * per interaction, sA1[F] then sA2[F]; the weight used is float(q) * s
  * (an fp32 multiply).  The fp32 A1/A2 slots of `params` are then ignored.
+ * filter_math selects the arithmetic of the filter network's two matrix
+ * products (and of their recomputation in the force pass): 0 (the default)
+ * forms each fp32 product from three fp16 matrix-core products (hi.hi +
+ * hi.lo + lo.hi of each operand split into two fp16 halves), which matches
+ * an fp32 evaluation; 1 uses one fp16 product of the rounded operands with
+ * fp32 accumulation, the reduced-precision tensor-core arithmetic that the
+ * FlashSchNet summary page measures its filter network in ("How", the
+ * TF32/MFU bullet), about three times cheaper in matrix instructions and
+ * roughly 10-bit accurate per product.  Everything else is unchanged.
  * Supported shapes: n_features in {32, 64, 128}, 2 <= n_rbf <= 64,
  * n_interactions in [1, 16]. */
 typedef struct sn_model {
@@ -100,6 +109,7 @@ typedef struct sn_model {
     const float *params;      /* device, packed fp32 (see above), 16-byte aligned */
     const int16_t *qweights;  /* device, int16 codes (filter_format 1), else NULL */
     const float *qscales;     /* device, fp32 scales (filter_format 1), else NULL */
+    int32_t filter_math;      /* 0 = fp32-accurate split products, 1 = one fp16 product */
 } sn_model;
 
 /* ---------------------------------------------------------------- host helpers */

@@ -46,7 +46,8 @@ class SnModel(ctypes.Structure):
                 ("n_features", ctypes.c_int32), ("n_rbf", ctypes.c_int32),
                 ("cutoff", ctypes.c_float), ("rbf_lo", ctypes.c_float), ("rbf_hi", ctypes.c_float),
                 ("rbf_gamma", ctypes.c_float), ("filter_format", ctypes.c_int32),
-                ("params", ctypes.c_void_p), ("qweights", ctypes.c_void_p), ("qscales", ctypes.c_void_p)]
+                ("params", ctypes.c_void_p), ("qweights", ctypes.c_void_p), ("qscales", ctypes.c_void_p),
+                ("filter_math", ctypes.c_int32)]
 
 
 class SnError(RuntimeError):
@@ -165,10 +166,11 @@ def _stream(stream=None) -> int:
 class Model:
     """Device copy of the packed weights plus the hyper-parameters (sn_model)."""
 
-    def __init__(self, params: dict, hyper: dict, filter_format: int = 0, device="cuda"):
+    def __init__(self, params: dict, hyper: dict, filter_format: int = 0, filter_math: int = 0, device="cuda"):
         torch = _torch()
         self.hyper = dict(hyper)
         self.filter_format = int(filter_format)
+        self.filter_math = int(filter_math)
         packed = pack_params(params, hyper)
         self.params = torch.from_numpy(packed).to(device)
         self.qweights = self.qscales = None
@@ -179,7 +181,7 @@ class Model:
         h = self.hyper
         self.c = SnModel(h["n_types"], h["n_interactions"], h["n_features"], h["n_rbf"], h["cutoff"],
                          h["rbf_lo"], h["rbf_hi"], h["rbf_gamma"], self.filter_format, _ptr(self.params),
-                         _ptr(self.qweights), _ptr(self.qscales))
+                         _ptr(self.qweights), _ptr(self.qscales), self.filter_math)
 
 
 class System:

@@ -201,6 +201,7 @@ sn_status check_model(const sn_model *m) {
         return SN_ERR_INVALID;
     if (m->filter_format != 0 && m->filter_format != 1) return SN_ERR_INVALID;
     if (m->filter_format == 1 && (!m->qweights || !m->qscales)) return SN_ERR_INVALID;
+    if (m->filter_math != 0 && m->filter_math != 1) return SN_ERR_INVALID;
     return SN_OK;
 }
 

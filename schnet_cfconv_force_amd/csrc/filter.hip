@@ -237,7 +237,24 @@ __device__ inline void mma_split2(const half8 *whi, const half8 *wlo, int stride
     }
 }
 
-template <int F, int NTHR>
+// The same with one fp16 product per pair of operands.
+template <int MG>
+__device__ inline void mma_one2(const half8 *whi, int stride, const half8 &bh0, floatx4 *acc0, const half8 &bh1,
+                                floatx4 *acc1) {
+    half8 ah[MG];
+#pragma unroll
+    for (int m = 0; m < MG; ++m) ah[m] = whi[m * stride];
+#pragma unroll
+    for (int m = 0; m < MG; ++m) {
+        acc0[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bh0, acc0[m], 0, 0, 0);
+        acc1[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bh1, acc1[m], 0, 0, 0);
+    }
+}
+
+// ONE selects the arithmetic of the products: 0 = three fp16 products per
+// fp32 product (split operands), 1 = one fp16 product of the rounded
+// operands (the scales and everything else are the same).
+template <int F, int NTHR, int ONE>
 __global__ __launch_bounds__(NTHR) void filter_fwd_kernel(FilterArgs a) {
     const int64_t P = (a.guard && *a.guard) ? 0 : a.P_dev ? (int64_t)*a.P_dev : a.P;
     constexpr int MT = F / 16;
@@ -293,7 +310,10 @@ __global__ __launch_bounds__(NTHR) void filter_fwd_kernel(FilterArgs a) {
         for (int ks = 0; ks < 2; ++ks) {
             float v[8];
             basis8(bs, basis_u0(bs, d, 32 * ks + 8 * slot), v);
-            split8(v, rh[ks], rl[ks]);
+            if (ONE)
+                rh[ks] = to_half8(v);
+            else
+                split8(v, rh[ks], rl[ks]);
         }
         // z 2^sz = (ssp(rbf A1 + b1) / ln 2) 2^sz on features 16 m + 4 slot + r,
         // in groups of MG tiles; ssp(a) / ln 2 = max(y, 0) + log2(1 + 2^-|y|) - 1
@@ -306,9 +326,13 @@ __global__ __launch_bounds__(NTHR) void filter_fwd_kernel(FilterArgs a) {
             for (int g = 0; g < MG; ++g) acc[g][0] = *reinterpret_cast<const floatx4 *>(s_b1 + 16 * (m0 + g) + 4 * slot);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                if (ks < KS)
-                    mma_split<MG, 1>(s_a1h + (m0 * kKS + ks) * 64 + lane, s_a1l + (m0 * kKS + ks) * 64 + lane, kKS * 64,
-                                     &rh[ks], &rl[ks], acc);
+                if (ks < KS) {
+                    if (ONE)
+                        mma_one<MG, 1>(s_a1h + (m0 * kKS + ks) * 64 + lane, kKS * 64, &rh[ks], acc);
+                    else
+                        mma_split<MG, 1>(s_a1h + (m0 * kKS + ks) * 64 + lane, s_a1l + (m0 * kKS + ks) * 64 + lane,
+                                         kKS * 64, &rh[ks], &rl[ks], acc);
+                }
 #pragma unroll
             for (int g = 0; g < MG; ++g)
 #pragma unroll
@@ -325,7 +349,10 @@ __global__ __launch_bounds__(NTHR) void filter_fwd_kernel(FilterArgs a) {
             float v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = z[2 * t + (j >> 2)][j & 3];
-            split8(v, zh[t], zl[t]);
+            if (ONE)
+                zh[t] = to_half8(v);
+            else
+                split8(v, zh[t], zl[t]);
         }
 #pragma unroll
         for (int m0 = 0; m0 < MT; m0 += MG) {
@@ -333,9 +360,13 @@ __global__ __launch_bounds__(NTHR) void filter_fwd_kernel(FilterArgs a) {
 #pragma unroll
             for (int g = 0; g < MG; ++g) acc[g][0] = *reinterpret_cast<const floatx4 *>(s_b2 + 16 * (m0 + g) + 4 * slot);
 #pragma unroll
-            for (int t = 0; t < T2; ++t)
-                mma_split<MG, 1>(s_a2h + (m0 * T2 + t) * 64 + lane, s_a2l + (m0 * T2 + t) * 64 + lane, T2 * 64,
-                                 &zh[t], &zl[t], acc);
+            for (int t = 0; t < T2; ++t) {
+                if (ONE)
+                    mma_one<MG, 1>(s_a2h + (m0 * T2 + t) * 64 + lane, T2 * 64, &zh[t], acc);
+                else
+                    mma_split<MG, 1>(s_a2h + (m0 * T2 + t) * 64 + lane, s_a2l + (m0 * T2 + t) * 64 + lane, T2 * 64,
+                                     &zh[t], &zl[t], acc);
+            }
             // the next distance has arrived long before; taking it here keeps
             // the loop's first wait from also waiting for these stores
             asm volatile("" : "+v"(d_next), "+v"(fc_next));
@@ -357,7 +388,7 @@ __global__ __launch_bounds__(NTHR) void filter_fwd_kernel(FilterArgs a) {
     }
 }
 
-template <int F, int NTHR>
+template <int F, int NTHR, int ONE>
 __global__ __launch_bounds__(NTHR) void filter_bwd_kernel(FilterArgs a) {
     const int64_t P = (a.guard && *a.guard) ? 0 : a.P_dev ? (int64_t)*a.P_dev : a.P;
     constexpr int MT = F / 16;
@@ -430,7 +461,10 @@ __global__ __launch_bounds__(NTHR) void filter_bwd_kernel(FilterArgs a) {
                     v[4 * q + 0] = fs * g0; v[4 * q + 1] = fs * g1;
                     v[4 * q + 2] = fs * g2; v[4 * q + 3] = fs * g3;
                 }
-                split8(v, gh[t], gl[t]);
+                if (ONE)
+                    gh[t] = to_half8(v);
+                else
+                    split8(v, gh[t], gl[t]);
                 // the step is consumed before the next step's gathers issue
                 asm volatile("" : "+v"(gh[t]), "+v"(gl[t]), "+v"(gfc));
             }
@@ -448,8 +482,13 @@ __global__ __launch_bounds__(NTHR) void filter_bwd_kernel(FilterArgs a) {
             for (int ks = 0; ks < 2; ++ks) {
                 float rb[8], du[8];
                 basis8_d(bs, basis_u0(bs, dr, 32 * ks + 8 * slot), rb, du);
-                split8(rb, rh[ks], rl[ks]);
-                split8(du, qh[ks], ql[ks]);
+                if (ONE) {
+                    rh[ks] = to_half8(rb);
+                    qh[ks] = to_half8(du);
+                } else {
+                    split8(rb, rh[ks], rl[ks]);
+                    split8(du, qh[ks], ql[ks]);
+                }
             }
         }
         // per group of MG output tiles (features 16 m ..): g_z = A2 G, the
@@ -464,9 +503,13 @@ __global__ __launch_bounds__(NTHR) void filter_bwd_kernel(FilterArgs a) {
 #pragma unroll
             for (int m = 0; m < MG; ++m) gz[m][0] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < T2; ++t)
-                mma_split<MG, 1>(s_a2bh + (m0 * T2 + t) * 64 + lane, s_a2bl + (m0 * T2 + t) * 64 + lane, T2 * 64,
-                                 &gh[t], &gl[t], gz);
+            for (int t = 0; t < T2; ++t) {
+                if (ONE)
+                    mma_one<MG, 1>(s_a2bh + (m0 * T2 + t) * 64 + lane, T2 * 64, &gh[t], gz);
+                else
+                    mma_split<MG, 1>(s_a2bh + (m0 * T2 + t) * 64 + lane, s_a2bl + (m0 * T2 + t) * 64 + lane,
+                                     T2 * 64, &gh[t], &gl[t], gz);
+            }
             // g_z is complete before the recompute's operands are read
 #pragma unroll
             for (int m = 0; m < MG; ++m) asm volatile("" : "+v"(gz[m][0])::"memory");
@@ -478,9 +521,13 @@ __global__ __launch_bounds__(NTHR) void filter_bwd_kernel(FilterArgs a) {
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                if (ks < KS)
-                    mma_split2<MG>(s_a1h + (m0 * kKS + ks) * 64 + lane, s_a1l + (m0 * kKS + ks) * 64 + lane, kKS * 64,
-                                   rh[ks], rl[ks], am, qh[ks], ql[ks], tm);
+                if (ks < KS) {
+                    if (ONE)
+                        mma_one2<MG>(s_a1h + (m0 * kKS + ks) * 64 + lane, kKS * 64, rh[ks], am, qh[ks], tm);
+                    else
+                        mma_split2<MG>(s_a1h + (m0 * kKS + ks) * 64 + lane, s_a1l + (m0 * kKS + ks) * 64 + lane,
+                                       kKS * 64, rh[ks], rl[ks], am, qh[ks], ql[ks], tm);
+                }
 #pragma unroll
             for (int m = 0; m < MG; ++m)
 #pragma unroll
@@ -599,43 +646,43 @@ FilterArgs make_args(const sn_model &m, int t) {
     return a;
 }
 
-template <int F>
+template <int F, int ONE>
 sn_status launch_fwd(const FilterArgs &a, hipStream_t s) {
     const int64_t tiles = (a.P + 15) / 16;
     if (tiles < (int64_t)num_cus() * (kFwdThreads / 64)) {
         const int waves = kSmallThreads / 64;
         const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
-        filter_fwd_kernel<F, kSmallThreads><<<grid, kSmallThreads, 0, s>>>(a);
+        filter_fwd_kernel<F, kSmallThreads, ONE><<<grid, kSmallThreads, 0, s>>>(a);
         return launch_status();
     }
     const int waves = kFwdThreads / 64;
     const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
-    filter_fwd_kernel<F, kFwdThreads><<<grid, kFwdThreads, 0, s>>>(a);
+    filter_fwd_kernel<F, kFwdThreads, ONE><<<grid, kFwdThreads, 0, s>>>(a);
     return launch_status();
 }
 
-template <int F>
+template <int F, int ONE>
 sn_status launch_bwd(const FilterArgs &a, hipStream_t s) {
     const int64_t tiles = (a.P + 15) / 16;
     if (tiles < (int64_t)num_cus() * (kBwdThreads / 64)) {
         const int waves = kSmallThreads / 64;
         const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
-        filter_bwd_kernel<F, kSmallThreads><<<grid, kSmallThreads, 0, s>>>(a);
+        filter_bwd_kernel<F, kSmallThreads, ONE><<<grid, kSmallThreads, 0, s>>>(a);
         return launch_status();
     }
     const int waves = kBwdThreads / 64;
     const int grid = xcd_grid((int)std::min<int64_t>(num_cus(), (tiles + waves - 1) / waves));
-    filter_bwd_kernel<F, kBwdThreads><<<grid, kBwdThreads, 0, s>>>(a);
+    filter_bwd_kernel<F, kBwdThreads, ONE><<<grid, kBwdThreads, 0, s>>>(a);
     return launch_status();
 }
 
-sn_status fwd_dispatch(const FilterArgs &a, int F, hipStream_t s) {
+sn_status fwd_dispatch(const FilterArgs &a, int F, int one, hipStream_t s) {
     if (a.P <= 0) return SN_OK;
     ProfScope ps(K_FILTER_FWD, s);
     switch (F) {
-        case 32: return launch_fwd<32>(a, s);
-        case 64: return launch_fwd<64>(a, s);
-        case 128: return launch_fwd<128>(a, s);
+        case 32: return one ? launch_fwd<32, 1>(a, s) : launch_fwd<32, 0>(a, s);
+        case 64: return one ? launch_fwd<64, 1>(a, s) : launch_fwd<64, 0>(a, s);
+        case 128: return one ? launch_fwd<128, 1>(a, s) : launch_fwd<128, 0>(a, s);
         default: return SN_ERR_INVALID;
     }
 }
@@ -702,7 +749,7 @@ sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, const flo
     a.guard = guard;
     a.phi24 = phi24;
     a.fc = pfc;
-    return fwd_dispatch(a, m.n_features, s);
+    return fwd_dispatch(a, m.n_features, m.filter_math, s);
 }
 
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, const char *pack,
@@ -715,7 +762,7 @@ sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t
     a.doff = 0;
     a.P = P;
     a.phi = phi;
-    return fwd_dispatch(a, m.n_features, s);
+    return fwd_dispatch(a, m.n_features, m.filter_math, s);
 }
 
 sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, const float *plfc,
@@ -745,9 +792,9 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
     a.accumulate = accumulate;
     ProfScope ps(K_FILTER_BWD, s);
     switch (m.n_features) {
-        case 32: return launch_bwd<32>(a, s);
-        case 64: return launch_bwd<64>(a, s);
-        case 128: return launch_bwd<128>(a, s);
+        case 32: return m.filter_math ? launch_bwd<32, 1>(a, s) : launch_bwd<32, 0>(a, s);
+        case 64: return m.filter_math ? launch_bwd<64, 1>(a, s) : launch_bwd<64, 0>(a, s);
+        case 128: return m.filter_math ? launch_bwd<128, 1>(a, s) : launch_bwd<128, 0>(a, s);
         default: return SN_ERR_INVALID;
     }
 }

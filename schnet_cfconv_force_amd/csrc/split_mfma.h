@@ -76,6 +76,14 @@ __device__ inline void split4(const float (&v)[4], half4 &hi, half4 &lo) {
     lo = l;
 }
 
+// One fp16 operand (no low half), for products taken in plain fp16.
+__device__ inline half8 to_half8(const float (&v)[8]) {
+    half8 h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = (_Float16)v[j];
+    return h;
+}
+
 // Power-of-two exponent s with amax 2^s in [2^(kSplitTop-1), 2^kSplitTop)
 // (0 for a zero or non-finite maximum).
 __device__ inline int split_scale(float amax) {
@@ -173,6 +181,19 @@ __device__ inline void mma_split(const half8 *whi, const half8 *wlo, int stride,
     for (int m = 0; m < MG; ++m)
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[m], bh[n], acc[m][n], 0, 0, 0);
+}
+
+// acc[m][n] += A_m B_n with one fp16 product per pair of operands (the hi
+// halves only): fp32 accumulation of fp16-rounded operands.
+template <int MG, int NT>
+__device__ inline void mma_one(const half8 *whi, int stride, const half8 *bh, floatx4 (*acc)[NT]) {
+    half8 ah[MG];
+#pragma unroll
+    for (int m = 0; m < MG; ++m) ah[m] = whi[m * stride];
+#pragma unroll
+    for (int m = 0; m < MG; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bh[n], acc[m][n], 0, 0, 0);
 }
 
 }  // namespace sn

@@ -137,3 +137,8 @@ def test_verlet_rejects_bad_schedule_and_flags_before_any_gpu_work():
     assert call(10, 5, sn.SN_MD_GRAPH | 4) == sn.SN_ERR_INVALID
     assert call(-1, 1, 0) == sn.SN_ERR_INVALID
     assert call(10, 1, 0, r_list=float("nan")) == sn.SN_ERR_INVALID
+    # the filter arithmetic is 0 (fp32-accurate) or 1 (one fp16 product); others are refused
+    m.filter_math = 2
+    assert call(10, 1, 0) == sn.SN_ERR_INVALID
+    m.filter_math = -1
+    assert call(10, 1, 0) == sn.SN_ERR_INVALID
