@@ -392,7 +392,7 @@ using namespace sn;
 
 extern "C" {
 
-int32_t sn_version(void) { return 2; }
+int32_t sn_version(void) { return 3; }
 
 const char *sn_status_string(sn_status st) {
     switch (st) {

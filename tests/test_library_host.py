@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(sn.EXPORTED)
-    assert lib.sn_version() == 2
+    assert lib.sn_version() == 3
 
 
 def test_status_strings():
