@@ -1,14 +1,14 @@
 // Atom-wise layers of the interaction blocks and the readout, fused per
-// wavefront of 16 atoms and run on the matrix cores.
+// chain of layers and run on the matrix cores.
 //
 // Computed transposed (output features are the M dimension, atoms the N
 // dimension of v_mfma_f32_16x16x32_f16), with operands in the split-fp16
 // form of split_mfma.h.  Every layer's weights sit in the weight pack in
-// the accumulator-chained order, so a layer's input is always held the way
-// an accumulator leaves it (lane = atom l%16, features 16 m + 4 (l/16) + r):
-// rows load with one float4 per tile, and a layer's output feeds the next
-// layer as its B operand without leaving the registers.  Each atom's
-// operands are scaled by a power of two from the atom's own maximum.
+// the accumulator-chained order, so a layer's output, as an accumulator
+// leaves it (lane = atom l%16, features 16 m + 4 (l/16) + r), is already
+// laid out as the next layer's B operand; rows load with one float4 per
+// tile.  Each atom's operands are scaled by a power of two from the atom's
+// own maximum.
 //
 // One launch runs a chain of layers between two CFConvs:
 //   EMBED_X   h = Emb[type];  x_0 = h W_in
@@ -20,9 +20,8 @@
 //   BX_BO     g_h += g_x W_in^T (interaction t), then for t - 1:
 //             g_o = (g_h Wo2^T) (.) sigmoid(o), g_y = g_o Wo1^T
 // x and g_y also get their per-atom row maxima (the filter backward's
-// scales).  A block stages its chain's weights in two LDS buffers: while one
-// layer runs, the next layer's fragments are already loaded into registers
-// and go to the freed buffer after a block barrier.
+// scales).  How a block divides a layer among its wavefronts and passes
+// operands between layers is described at kMlpWaves below.
 #include "split_mfma.h"
 
 namespace sn {
