@@ -486,7 +486,7 @@ def measure_eval_config(sn, torch, name, n_rep=20):
            "evals_per_s": round(1e3 / med, 2), "edges_per_s": round(W.E * 1e3 / med, 1),
            "neighbour_build_ms": {"median": round(float(np.median(nb)), 4), "min": round(float(np.min(nb)), 4)},
            "rebuild_plus_eval_ms": round(float(np.median(both)), 4),
-           "roofline_kernels": kernel_rooflines(prof, W.E // 2, W.E, W.F, W.K),
+           "roofline_kernels": kernel_rooflines(prof, W.E // 2, W.E, W.F, W.K, load_traffic(name)),
            "kernels": kernels_table(prof, 5)}
     return W, res
 

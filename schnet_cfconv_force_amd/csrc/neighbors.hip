@@ -124,36 +124,76 @@ __device__ inline bool block_bbox(const float *pos, int s, int e, float (*red)[N
     return bad;
 }
 
-// One block per replica: atom -> replica map, bounding box, cell grid.  It
-// also clears the replica's slice of the cell counters (cells [8 s + 64 b,
+// The cell grid in two launches, so that a large replica is spread over
+// many compute units.  grid_part_kernel: R blocks per replica, block (b,
+// part) takes a 1/R slice of replica b's atoms (atom -> replica map and a
+// partial bounding box with its non-finite flag, written to part[8 (b R +
+// part) ..]) and of its cells (the counters are cleared: cells [8 s + 64 b,
 // 8 e + 64 (b + 1)) belong to replica b; the last block clears the final
-// entry) and the builder's status slots.
-__global__ __launch_bounds__(256) void grid_kernel(const float *pos, const int32_t *rptr, PredParams pp,
-                                                   float cell_edge, CellGrid *grid, int *rep_of, int *cell_cnt,
-                                                   int *cell_fill, int64_t n_cells, int step_mark, int *status,
-                                                   const int *run_flag) {
+// entry); block 0 also resets the builder's status slots.  grid_make_kernel
+// (one wavefront per replica) combines the R partial boxes into the
+// replica's grid (min / max: the result does not depend on the order).
+__global__ __launch_bounds__(256) void grid_part_kernel(const float *pos, const int32_t *rptr, int R, float *part,
+                                                        int *rep_of, int *cell_cnt, int *cell_fill, int64_t n_cells,
+                                                        int step_mark, int *status, const int *run_flag) {
     __shared__ float red[6][4];
     if (skipped(run_flag)) return;
-    const int b = blockIdx.x;
+    const int b = blockIdx.x / R, k = blockIdx.x % R;
     const int s = rptr[b], e = rptr[b + 1];
-    for (int64_t c = 8 * (int64_t)s + 64 * b + threadIdx.x; c < 8 * (int64_t)e + 64 * (b + 1); c += blockDim.x) {
+    const int64_t c0 = 8 * (int64_t)s + 64 * b, c1 = 8 * (int64_t)e + 64 * (b + 1);
+    const int64_t cper = (c1 - c0 + R - 1) / R;
+    const int64_t cs = c0 + k * cper, ce = min(c1, cs + cper);
+    for (int64_t c = cs + threadIdx.x; c < ce; c += blockDim.x) {
         cell_cnt[c] = 0;
         cell_fill[c] = 0;
     }
-    if (b == gridDim.x - 1 && threadIdx.x == 0) {
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
         cell_cnt[n_cells] = 0;
         cell_fill[n_cells] = 0;
     }
-    if (b == 0 && threadIdx.x == 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         status[kMaxRow] = 0;
         status[kEdgeTotal] = 0;
         if (step_mark >= 0 && *status == 0) status[kStepsDone] = step_mark;
     }
-    for (int i = s + threadIdx.x; i < e; i += 256) rep_of[i] = b;
+    const int aper = (e - s + R - 1) / R;
+    const int as = min(e, s + k * aper), ae = min(e, as + aper);
+    for (int i = as + threadIdx.x; i < ae; i += 256) rep_of[i] = b;
     float lo[3], hi[3];
-    const bool bad = block_bbox<256>(pos, s, e, red, lo, hi);
+    const bool bad = block_bbox<256>(pos, as, ae, red, lo, hi);
     if (threadIdx.x != 0) return;
+    float *o = part + 8 * (int64_t)blockIdx.x;
+    for (int c = 0; c < 3; ++c) {
+        o[c] = lo[c];
+        o[3 + c] = hi[c];
+    }
+    o[6] = bad ? 1.0f : 0.0f;
+}
+
+__global__ __launch_bounds__(64) void grid_make_kernel(const int32_t *rptr, int R, const float *part, PredParams pp,
+                                                       float cell_edge, CellGrid *grid, int *status,
+                                                       const int *run_flag) {
+    if (skipped(run_flag)) return;
+    const int b = blockIdx.x, lane = threadIdx.x;
+    float lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
+    bool bad = false;
+    for (int k = lane; k < R; k += 64) {
+        const float *o = part + 8 * ((int64_t)b * R + k);
+        for (int c = 0; c < 3; ++c) {
+            lo[c] = fminf(lo[c], o[c]);
+            hi[c] = fmaxf(hi[c], o[3 + c]);
+        }
+        bad |= o[6] != 0.0f;
+    }
+    for (int c = 0; c < 3; ++c)
+        for (int o = 32; o > 0; o >>= 1) {
+            lo[c] = fminf(lo[c], __shfl_xor(lo[c], o, 64));
+            hi[c] = fmaxf(hi[c], __shfl_xor(hi[c], o, 64));
+        }
+    bad = __any(bad);
+    if (lane != 0) return;
     if (bad) flag_status(status, SN_ERR_NONFINITE);
+    const int s = rptr[b], e = rptr[b + 1];
     grid[b] = make_grid(lo, hi, bad, e - s, pp, cell_edge, 8 * s + 64 * b);
 }
 
@@ -212,14 +252,18 @@ __device__ inline bool within(float xi, float yi, float zi, float4 q, const Pred
     return r2 < pp.rl2;
 }
 
-// One wavefront per atom.  FILL = false: write the row length into cnt[i].
-// FILL = true: write the sorted row into col[row_ptr[i] ...].
+// One wavefront per atom.  FILL = false: write the row length into cnt[i]
+// and, for rows of at most kRowKeep entries, the row's columns in candidate
+// order into keep[i kRowKeep ...].  FILL = true: write the sorted row into
+// col[row_ptr[i] ...], from keep when the row fitted there, else by testing
+// the candidates again.
+constexpr int kRowKeep = 256;
 template <bool FILL>
 __global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos, int n_atoms, const CellGrid *grid,
                                                                const int *rep_of, const int *cell_start,
                                                                const float4 *spos, PredParams pp, int *cnt,
-                                                               const int32_t *row_ptr, int32_t *col, int64_t capacity,
-                                                               int *status, const int *run_flag) {
+                                                               int32_t *keep, const int32_t *row_ptr, int32_t *col,
+                                                               int64_t capacity, int *status, const int *run_flag) {
     __shared__ int s_start[kNbWaves][28];
     __shared__ int s_pre[kNbWaves][28];
     __shared__ int s_buf[FILL ? kNbWaves : 1][FILL ? SN_MAX_ROW : 1];
@@ -227,6 +271,22 @@ __global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos
     const int lane = threadIdx.x % kWave;
     const int i = blockIdx.x * kNbWaves + wv;
     if (i >= n_atoms || skipped(run_flag)) return;   // whole wavefront exits together
+    if (FILL) {
+        // a row kept by the count pass: its columns, unsorted, into LDS
+        const int r0 = row_ptr[i];
+        const int n = row_ptr[i + 1] - r0;
+        if (n <= kRowKeep && (int64_t)row_ptr[n_atoms] <= capacity) {
+            for (int k = lane; k < n; k += kWave) s_buf[FILL ? wv : 0][FILL ? k : 0] = keep[(int64_t)i * kRowKeep + k];
+            wave_sync();
+            for (int k = lane; k < n; k += kWave) {
+                const int v = s_buf[FILL ? wv : 0][FILL ? k : 0];
+                int rank = 0;
+                for (int m = 0; m < n; ++m) rank += (s_buf[FILL ? wv : 0][FILL ? m : 0] < v);
+                col[r0 + rank] = v;
+            }
+            return;
+        }
+    }
     const CellGrid g = grid[rep_of[i]];
     const float xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
     const int ci[3] = {cell_coord(xi, 0, g, pp), cell_coord(yi, 1, g, pp), cell_coord(zi, 2, g, pp)};
@@ -281,9 +341,11 @@ __global__ __launch_bounds__(kWave * kNbWaves) void rows_kernel(const float *pos
             pass = (j != i) && within(xi, yi, zi, q, pp);
         }
         uint64_t mask = __ballot(pass);
+        const int off = base + __popcll(mask & ((1ull << lane) - 1ull));
         if (FILL) {
-            int off = base + __popcll(mask & ((1ull << lane) - 1ull));
             if (pass && off < SN_MAX_ROW) s_buf[FILL ? wv : 0][FILL ? off : 0] = j;
+        } else if (pass && off < kRowKeep) {
+            keep[(int64_t)i * kRowKeep + off] = j;
         }
         base += __popcll(mask);
     }
@@ -666,12 +728,16 @@ static sn_status fill_int(int *p, int v, int64_t n, hipStream_t s) {
     return launch_status();
 }
 
+// Blocks per replica of the cell-grid set-up: about 256 in all.
+static int grid_parts(int B) { return B >= 256 ? 1 : (256 + B - 1) / B; }
+
 NbLayout nb_layout(const sn_system &sys, size_t base) {
     NbLayout L;
     const int64_t N = sys.n_atoms, B = sys.n_replicas;
     L.n_cells = 8 * N + 64 * B;
     size_t o = base;
     L.grid = o;       o = align256(o + sizeof(CellGrid) * B);
+    L.gpart = o;      o = align256(o + 4 * 8 * (int64_t)B * grid_parts((int)B));
     L.rep_of = o;     o = align256(o + 4 * N);
     L.cell_of = o;    o = align256(o + 4 * N);
     L.cell_cnt = o;   o = align256(o + 4 * (L.n_cells + 1));
@@ -679,6 +745,7 @@ NbLayout nb_layout(const sn_system &sys, size_t base) {
     L.cell_fill = o;  o = align256(o + 4 * (L.n_cells + 1));
     L.spos = o;       o = align256(o + 16 * N);
     L.row_cnt = o;    o = align256(o + 4 * N);
+    L.keep = o;       o = align256(o + 4 * (int64_t)kRowKeep * N);
     L.rep = o;        o = align256(o + 8 * kTileMaxSplit * B);
     L.mask = o;       o = align256(o + 8 * kTileWords * N);
     L.total = o;
@@ -793,8 +860,12 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
     }
     {
         ProfScope ps(K_NB_GRID, s);
-        grid_kernel<<<B, 256, 0, s>>>(pos, sys.replica_ptr, pp, cell_edge, grid, rep_of, cell_cnt, cell_fill,
-                                      L.n_cells, step_mark, status, run_flag);
+        const int R = grid_parts(B);
+        float *part = reinterpret_cast<float *>(ws + L.gpart);
+        grid_part_kernel<<<B * R, 256, 0, s>>>(pos, sys.replica_ptr, R, part, rep_of, cell_cnt, cell_fill,
+                                               L.n_cells, step_mark, status, run_flag);
+        SN_TRY(launch_status());
+        grid_make_kernel<<<B, 64, 0, s>>>(sys.replica_ptr, R, part, pp, cell_edge, grid, status, run_flag);
         SN_TRY(launch_status());
     }
     {
@@ -809,10 +880,12 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         SN_TRY(launch_status());
     }
     const int blocks = (N + kNbWaves - 1) / kNbWaves;
+    int32_t *keep = reinterpret_cast<int32_t *>(ws + L.keep);
     {
         ProfScope ps(K_NB_COUNT, s);
         rows_kernel<false><<<blocks, kWave * kNbWaves, 0, s>>>(pos, N, grid, rep_of, cell_start, spos, pp,
-                                                               row_cnt, nullptr, nullptr, capacity, status, run_flag);
+                                                               row_cnt, keep, nullptr, nullptr, capacity, status,
+                                                               run_flag);
         SN_TRY(launch_status());
     }
     SN_TRY(scan_exclusive(row_cnt, row_ptr, N, status + kEdgeTotal, status + kMaxRow, s, PairCountCheck{},
@@ -830,7 +903,7 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
     {
         ProfScope ps(K_NB_FILL, s);
         rows_kernel<true><<<blocks, kWave * kNbWaves, 0, s>>>(pos, N, grid, rep_of, cell_start, spos, pp, nullptr,
-                                                              row_ptr, col, capacity, status, run_flag);
+                                                              keep, row_ptr, col, capacity, status, run_flag);
         SN_TRY(launch_status());
     }
     {

@@ -138,7 +138,7 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_
 constexpr size_t kWsBase = 256;
 
 struct NbLayout {            // neighbour-builder scratch (offsets from ws base)
-    size_t grid, rep_of, cell_of, cell_cnt, cell_start, cell_fill, spos, row_cnt, rep, mask, total;
+    size_t grid, gpart, rep_of, cell_of, cell_cnt, cell_start, cell_fill, spos, row_cnt, keep, rep, mask, total;
     int64_t n_cells;         // capacity of the cell table
 };
 
