@@ -51,6 +51,30 @@ def _model(F=32, K=8, I=1, T=3, rc=7.0, seed=11):
                                                   "cutoff": rc, **synth.rbf_hyper(K, 0.0, rc)}
 
 
+def test_cell_list_rows_longer_and_shorter_than_the_kept_length(sn):
+    """The cell-list fill pass sorts the rows its count pass kept (up to 256 entries) and tests the
+    candidates again for longer ones: a dense replica (rows of ~300-450) and a sparse one (rows of
+    ~40) in one build, CSR bit-identical to the oracle's."""
+    say("[build paths] cell list, rows above and below the kept length")
+    pos = np.concatenate([synth.box_rsa(1500, 24.0, 1.0, synth.seed64(77, 0)),
+                          synth.box_rsa(700, 40.0, 1.0, synth.seed64(77, 1)) + 100.0]).astype(np.float32)
+    rp = np.array([0, 1500, 2200], np.int32)
+    params, hyper = _model(rc=6.5)
+    model = sn.Model(params, hyper)
+    system = sn.System(rp, np.zeros(len(pos), np.int32), None)
+    cap = 600 * len(pos)
+    ws = sn.workspace(model, system, cap)
+    row_ptr, col, rev, E = sn.build_csr_neighbors(system, dev(pos), 9.5, cap, ws)
+    ref = O.neighbors_bruteforce(pos, rp, 9.5, None)
+    lens = np.diff(ref[0])
+    say(f"   E={E}, row lengths {lens.min()}..{lens.max()}, {int((lens > 256).sum())} rows above 256")
+    assert lens.max() > 256 and lens.min() < 256
+    assert E == len(ref[1])
+    assert np.array_equal(row_ptr.cpu().numpy(), ref[0])
+    assert np.array_equal(col.cpu().numpy()[:E], ref[1])
+    assert np.array_equal(rev.cpu().numpy()[:E], ref[2])
+
+
 @pytest.mark.parametrize("sizes,periodic", [
     ([TILE_MAX, TILE_MAX], False),         # mask path at its largest replica
     ([TILE_MAX, TILE_MAX + 1], False),     # one atom more: the cell list
