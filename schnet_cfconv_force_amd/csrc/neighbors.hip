@@ -8,15 +8,17 @@
 // multiply-add, so the list is bit-for-bit reproducible from the positions.
 //
 // Pipeline (all on the caller's stream):
-//   grid    one block per replica: bounding box -> per-replica cell grid
+//   grid    ~256 blocks in all: cleared cell table, partial bounding boxes;
+//           then one wavefront per replica: its cell grid
 //   bin     one thread per atom: cell index, atomic cell histogram
 //   scan    cell histogram -> cell start offsets
 //   place   one thread per atom: atom copied into its cell's slot range
 //   count   one wavefront per atom: candidates of the 27 surrounding cells,
-//           exact predicate, row length
+//           exact predicate (survivors compacted by ballot), row length;
+//           rows of up to kRowKeep entries are kept in the workspace
 //   scan    row lengths -> row_ptr, total read back by the host
-//   fill    one wavefront per atom: same candidates, survivors compacted
-//           into LDS by ballot, then rank-sorted into col_idx
+//   fill    one wavefront per atom: the kept row (or, for a longer row, the
+//           candidates tested again) in LDS, rank-sorted into col_idx
 //   rev     one wavefront per row: binary search of i in row j
 // The order of atoms inside a cell depends on atomic arrival order; the
 // sorted rows do not, so the output is deterministic.
