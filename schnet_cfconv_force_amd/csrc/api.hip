@@ -288,7 +288,16 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     if (!pairs_ready)
         SN_TRY(pairs_setup(sys, pos, row_ptr, col, rev, device_edges ? -1 : E, m.cutoff, ws, L, status, guard, s,
                            build_flag));
-    SN_TRY(filter_forward(m, 0, pgeo, pfc, P, phi_t(0), pack, p_dev, guard, s));
+    // few pairs: every interaction's rows in one launch (they are small, so
+    // the cache argument below does not apply)
+    const bool fused = filter_forward_fused(m, P);
+    if (fused) {
+        uint32_t *rows[16];
+        for (int t = 0; t < I; ++t) rows[t] = phi_t(t);
+        SN_TRY(filter_forward_all(m, pgeo, pfc, P, rows, pack, p_dev, guard, s));
+    } else {
+        SN_TRY(filter_forward(m, 0, pgeo, pfc, P, phi_t(0), pack, p_dev, guard, s));
+    }
     if (!embedded)
         SN_TRY(mlp_embed_x(N, F, m.n_types, sys.types, prm + off[0], pk(0, PK_XW), h0, x_t(0), xmax_t(0), status, s));
     for (int t = 0; t < I; ++t) {
@@ -300,7 +309,7 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
             // phi_t: one interaction's rows (24-bit, about 200 MB for 64
             // replicas) then stay in the Infinity Cache from their write to
             // their read
-            SN_TRY(filter_forward(m, t + 1, pgeo, pfc, P, phi_t(t + 1), pack, p_dev, guard, s));
+            if (!fused) SN_TRY(filter_forward(m, t + 1, pgeo, pfc, P, phi_t(t + 1), pack, p_dev, guard, s));
         } else {   // the last interaction, the readout and the first backward block
             SN_TRY(mlp_tail(N, F, y, pk(t, PK_OW1), blk(t, BO1), pk(t, PK_OW2), blk(t, BO2), t == 0 ? h0 : h, pr(0),
                             c1, pr(1), R2, c2, pk(t, PK_BOW1), pk(t, PK_BOW2), eps, gh, gy_t(t), gmax_t(t), s));

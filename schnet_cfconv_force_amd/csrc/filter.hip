@@ -255,7 +255,7 @@ __device__ inline void mma_one2(const half8 *whi, int stride, const half8 &bh0, 
 // fp32 product (split operands), 1 = one fp16 product of the rounded
 // operands (the scales and everything else are the same).
 template <int F, int NTHR, int ONE>
-__global__ __launch_bounds__(NTHR) void filter_fwd_kernel(FilterArgs a) {
+__device__ inline void filter_fwd_body(const FilterArgs &a) {
     const int64_t P = (a.guard && *a.guard) ? 0 : a.P_dev ? (int64_t)*a.P_dev : a.P;
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;                      // 32-wide k steps of the F x F GEMM
@@ -386,6 +386,22 @@ __global__ __launch_bounds__(NTHR) void filter_fwd_kernel(FilterArgs a) {
             }
         }
     }
+}
+
+template <int F, int NTHR, int ONE>
+__global__ __launch_bounds__(NTHR) void filter_fwd_kernel(FilterArgs a) {
+    filter_fwd_body<F, NTHR, ONE>(a);
+}
+
+// Systems with few pairs: every interaction's forward filter in one launch
+// (blockIdx.y = interaction), which saves I - 1 launch ramps per evaluation.
+constexpr int kFusedMaxI = 8;
+struct FilterArgsSet {
+    FilterArgs a[kFusedMaxI];
+};
+template <int F, int NTHR, int ONE>
+__global__ __launch_bounds__(NTHR) void filter_fwd_all_kernel(FilterArgsSet set) {
+    filter_fwd_body<F, NTHR, ONE>(set.a[blockIdx.y]);
 }
 
 template <int F, int NTHR, int ONE>
@@ -676,6 +692,18 @@ sn_status launch_bwd(const FilterArgs &a, hipStream_t s) {
     return launch_status();
 }
 
+// All interactions at once (systems with few pair tiles): at most num_cus
+// blocks in all, so that one pass over the GPU covers every interaction.
+template <int F, int ONE>
+sn_status launch_fwd_all(const FilterArgsSet &set, int I, int64_t P, hipStream_t s) {
+    const int64_t tiles = (P + 15) / 16;
+    const int waves = kSmallThreads / 64;
+    const int per = std::max(1, num_cus() / I);
+    const int gx = xcd_grid((int)std::min<int64_t>(per, (tiles + waves - 1) / waves));
+    filter_fwd_all_kernel<F, kSmallThreads, ONE><<<dim3(gx, I), kSmallThreads, 0, s>>>(set);
+    return launch_status();
+}
+
 sn_status fwd_dispatch(const FilterArgs &a, int F, int one, hipStream_t s) {
     if (a.P <= 0) return SN_OK;
     ProfScope ps(K_FILTER_FWD, s);
@@ -750,6 +778,38 @@ sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, const flo
     a.phi24 = phi24;
     a.fc = pfc;
     return fwd_dispatch(a, m.n_features, m.filter_math, s);
+}
+
+bool filter_forward_fused(const sn_model &m, int64_t P) {
+    return P > 0 && m.n_interactions <= kFusedMaxI && (P + 15) / 16 < (int64_t)num_cus() * (kFwdThreads / 64);
+}
+
+sn_status filter_forward_all(const sn_model &m, const float4 *pgeo, const float *pfc, int64_t P,
+                             uint32_t *const *phi24, const char *pack, const int *p_dev, const int *guard,
+                             hipStream_t s) {
+    if (!pack || !filter_forward_fused(m, P)) return SN_ERR_INVALID;
+    FilterArgsSet set = {};
+    const int I = m.n_interactions;
+    for (int t = 0; t < I; ++t) {
+        FilterArgs &a = set.a[t];
+        a = make_args(m, t);
+        attach_pack(a, m, t, pack, PK_FA2);
+        a.dsrc = reinterpret_cast<const float *>(pgeo);
+        a.dstride = 4;
+        a.doff = 3;
+        a.P = P;
+        a.P_dev = p_dev;
+        a.guard = guard;
+        a.phi24 = phi24[t];
+        a.fc = pfc;
+    }
+    ProfScope ps(K_FILTER_FWD, s);
+    switch (m.n_features) {
+        case 32: return m.filter_math ? launch_fwd_all<32, 1>(set, I, P, s) : launch_fwd_all<32, 0>(set, I, P, s);
+        case 64: return m.filter_math ? launch_fwd_all<64, 1>(set, I, P, s) : launch_fwd_all<64, 0>(set, I, P, s);
+        case 128: return m.filter_math ? launch_fwd_all<128, 1>(set, I, P, s) : launch_fwd_all<128, 0>(set, I, P, s);
+        default: return SN_ERR_INVALID;
+    }
 }
 
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, const char *pack,

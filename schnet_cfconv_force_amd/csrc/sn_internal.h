@@ -322,6 +322,13 @@ sn_status filter_pack(const sn_model &m, char *pack, hipStream_t s);
 // The rows are stored multiplied by the envelope pfc[p] (the CFConv's weight W_p).
 sn_status filter_forward(const sn_model &m, int t, const float4 *pgeo, const float *pfc, int64_t P, uint32_t *phi24,
                          const char *pack, const int *p_dev, const int *guard, hipStream_t s);
+// Whether a system of P pairs (capacity) runs every interaction's forward
+// filter in one launch (few pair tiles, at most 8 interactions), and that
+// launch: phi24[t] receives interaction t's rows.
+bool filter_forward_fused(const sn_model &m, int64_t P);
+sn_status filter_forward_all(const sn_model &m, const float4 *pgeo, const float *pfc, int64_t P,
+                             uint32_t *const *phi24, const char *pack, const int *p_dev, const int *guard,
+                             hipStream_t s);
 // phi [P][F] in fp32 without the envelope, for n = P distances d (the same kernel).
 sn_status filter_forward_plain(const sn_model &m, int t, const float *d, int64_t P, float *phi, const char *pack,
                                hipStream_t s);
