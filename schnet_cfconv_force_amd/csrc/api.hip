@@ -93,7 +93,7 @@ EfLayout ef_layout(const sn_model &m, const sn_system &sys, int64_t E, size_t ba
     L.y = take(4 * N * F);
     L.gh = take(4 * N * F);
     L.eps = take(4 * N + 4 * B);   // eps[N], then an energy scratch [B]
-    L.S = take(4 * P);
+    L.S = take(4 * P * I);   // one slice per interaction (small systems; otherwise slice 0 accumulates)
     L.xmax = take(4 * I * N);
     L.gmax = take(4 * I * N);
     L.pack = take(pack_bytes((int)I));
@@ -243,8 +243,8 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     const EfLayout L = ef_layout(m, sys, E, kWsBase);
     float *eps = reinterpret_cast<float *>(ws + L.eps);
     if (N == 0)
-        return forces_rows(0, B, sys.replica_ptr, eps, energy, row_ptr, col, nullptr, nullptr, nullptr, forces, status,
-                           nullptr, vf, s, elog, elog_by_step);
+        return forces_rows(0, B, sys.replica_ptr, eps, energy, row_ptr, col, nullptr, nullptr, nullptr, 1, 0, forces,
+                           status, nullptr, vf, s, elog, elog_by_step);
 
     int64_t off[9 * 16 + 6];
     sn_param_offsets(m.n_types, I, F, m.n_rbf, off, (int32_t)(sizeof(off) / sizeof(off[0])));
@@ -319,17 +319,32 @@ sn_status energy_forces_impl(const sn_model &m, const sn_system &sys, const floa
     // input-gradient CFConv (not needed below the first block) goes first,
     // while more of the filter rows it reads are still in the Infinity Cache;
     // the filter backward does not read them.
+    // With few pairs the filter backward of every interaction runs as one
+    // launch after the chain (each g_y_t is kept), each interaction into its
+    // own S slice; the force assembly adds the slices in the order of the
+    // per-interaction accumulation.
     for (int t = I - 1; t >= 0; --t) {
         if (t > 0) SN_TRY(cfconv(F, N, row_ptr, col, edge_pair, phi_t(t), gy_t(t), y, guard, s));
-        SN_TRY(filter_backward(m, t, pgeo, pfc, plfc, pair_ij, P, N, x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
-                               t != I - 1, pack, p_dev, guard, s));
+        if (!fused)
+            SN_TRY(filter_backward(m, t, pgeo, pfc, plfc, pair_ij, P, N, x_t(t), gy_t(t), xmax_t(t), gmax_t(t), S,
+                                   t != I - 1, pack, p_dev, guard, s));
         if (t > 0) {
             SN_TRY(mlp_bx_bo(N, F, y, pk(t, PK_BXW), pk(t - 1, PK_BOW1), o_t(t - 1), pk(t - 1, PK_BOW2), gh,
                              gy_t(t - 1), gmax_t(t - 1), s));
         }
     }
-    return forces_rows(N, B, sys.replica_ptr, eps, energy, row_ptr, col, edge_pair, pgeo, S, forces, status, guard,
-                       vf, s, elog, elog_by_step);
+    if (fused) {
+        const float *xs[16], *gys[16], *xm[16], *gm[16];
+        for (int t = 0; t < I; ++t) {
+            xs[t] = x_t(t);
+            gys[t] = gy_t(t);
+            xm[t] = xmax_t(t);
+            gm[t] = gmax_t(t);
+        }
+        SN_TRY(filter_backward_all(m, pgeo, pfc, plfc, pair_ij, P, xs, gys, xm, gm, S, pack, p_dev, guard, s));
+    }
+    return forces_rows(N, B, sys.replica_ptr, eps, energy, row_ptr, col, edge_pair, pgeo, S, fused ? I : 1, P, forces,
+                       status, guard, vf, s, elog, elog_by_step);
 }
 
 // Ends a stream capture that an error interrupted and frees what it made.

@@ -405,7 +405,7 @@ __global__ __launch_bounds__(NTHR) void filter_fwd_all_kernel(FilterArgsSet set)
 }
 
 template <int F, int NTHR, int ONE>
-__global__ __launch_bounds__(NTHR) void filter_bwd_kernel(FilterArgs a) {
+__device__ inline void filter_bwd_body(const FilterArgs &a) {
     const int64_t P = (a.guard && *a.guard) ? 0 : a.P_dev ? (int64_t)*a.P_dev : a.P;
     constexpr int MT = F / 16;
     constexpr int T2 = MT / 2;
@@ -571,6 +571,19 @@ __global__ __launch_bounds__(NTHR) void filter_bwd_kernel(FilterArgs a) {
 }
 
 
+template <int F, int NTHR, int ONE>
+__global__ __launch_bounds__(NTHR) void filter_bwd_kernel(FilterArgs a) {
+    filter_bwd_body<F, NTHR, ONE>(a);
+}
+
+// Systems with few pairs: every interaction's backward filter in one launch
+// (blockIdx.y = interaction), each writing its own S slice.
+template <int F, int NTHR, int ONE>
+__global__ __launch_bounds__(NTHR) void filter_bwd_all_kernel(FilterArgsSet set) {
+    filter_bwd_body<F, NTHR, ONE>(set.a[blockIdx.y]);
+}
+
+
 // The filter's slots of the weight pack: one block per (interaction,
 // matrix), each staging one matrix exactly as the kernels above would, but
 // into the pack.
@@ -701,6 +714,16 @@ sn_status launch_fwd_all(const FilterArgsSet &set, int I, int64_t P, hipStream_t
     const int per = std::max(1, num_cus() / I);
     const int gx = xcd_grid((int)std::min<int64_t>(per, (tiles + waves - 1) / waves));
     filter_fwd_all_kernel<F, kSmallThreads, ONE><<<dim3(gx, I), kSmallThreads, 0, s>>>(set);
+    return launch_status();
+}
+
+template <int F, int ONE>
+sn_status launch_bwd_all(const FilterArgsSet &set, int I, int64_t P, hipStream_t s) {
+    const int64_t tiles = (P + 15) / 16;
+    const int waves = kSmallThreads / 64;
+    const int per = std::max(1, num_cus() / I);
+    const int gx = xcd_grid((int)std::min<int64_t>(per, (tiles + waves - 1) / waves));
+    filter_bwd_all_kernel<F, kSmallThreads, ONE><<<dim3(gx, I), kSmallThreads, 0, s>>>(set);
     return launch_status();
 }
 
@@ -855,6 +878,45 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
         case 32: return m.filter_math ? launch_bwd<32, 1>(a, s) : launch_bwd<32, 0>(a, s);
         case 64: return m.filter_math ? launch_bwd<64, 1>(a, s) : launch_bwd<64, 0>(a, s);
         case 128: return m.filter_math ? launch_bwd<128, 1>(a, s) : launch_bwd<128, 0>(a, s);
+        default: return SN_ERR_INVALID;
+    }
+}
+
+
+sn_status filter_backward_all(const sn_model &m, const float4 *pgeo, const float *pfc, const float *plfc,
+                              const int2 *pair_ij, int64_t P, const float *const *x, const float *const *gy,
+                              const float *const *xmax, const float *const *gmax, float *S, const char *pack,
+                              const int *p_dev, const int *guard, hipStream_t s) {
+    if (P <= 0) return SN_OK;
+    if (!pack || !filter_forward_fused(m, P)) return SN_ERR_INVALID;
+    FilterArgsSet set = {};
+    const int I = m.n_interactions;
+    for (int t = 0; t < I; ++t) {
+        FilterArgs &a = set.a[t];
+        a = make_args(m, t);
+        attach_pack(a, m, t, pack, PK_FA2B);
+        a.b2f = pack_vec(pack, m.n_interactions, t);
+        a.dsrc = reinterpret_cast<const float *>(pgeo);
+        a.dstride = 4;
+        a.doff = 3;
+        a.P = P;
+        a.pair_ij = pair_ij;
+        a.P_dev = p_dev;
+        a.guard = guard;
+        a.fc = pfc;
+        a.lfc = plfc;
+        a.x = x[t];
+        a.gy = gy[t];
+        a.S = S + P * t;
+        a.xmax = xmax[t];
+        a.gmax = gmax[t];
+        a.accumulate = 0;
+    }
+    ProfScope ps(K_FILTER_BWD, s);
+    switch (m.n_features) {
+        case 32: return m.filter_math ? launch_bwd_all<32, 1>(set, I, P, s) : launch_bwd_all<32, 0>(set, I, P, s);
+        case 64: return m.filter_math ? launch_bwd_all<64, 1>(set, I, P, s) : launch_bwd_all<64, 0>(set, I, P, s);
+        case 128: return m.filter_math ? launch_bwd_all<128, 1>(set, I, P, s) : launch_bwd_all<128, 0>(set, I, P, s);
         default: return SN_ERR_INVALID;
     }
 }

@@ -234,6 +234,8 @@ struct ForcesArgs {
     const int32_t *row_ptr, *col, *edge_pair;
     const float4 *pgeo;
     const float *S;
+    int s_parts;          // S_p = S[(s_parts - 1) s_stride + p] + ... + S[p]
+    int64_t s_stride;
     float *forces;
     const int32_t *rptr;
     const float *eps;
@@ -286,7 +288,9 @@ __global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
             for (int e = e0 + sub; e < e1; e += kFrLanes) {
                 const int p = a.edge_pair[e];
                 const float4 g = a.pgeo[p];
-                const float s = (a.col[e] > i) ? a.S[p] : -a.S[p];
+                float sv = a.S[(a.s_parts - 1) * a.s_stride + p];
+                for (int t = a.s_parts - 2; t >= 0; --t) sv += a.S[t * a.s_stride + p];
+                const float s = (a.col[e] > i) ? sv : -sv;
                 fx += s * g.x;
                 fy += s * g.y;
                 fz += s * g.z;
@@ -416,13 +420,15 @@ sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const
 
 sn_status forces_rows(int N, int B, const int32_t *replica_ptr, const float *eps, float *energy,
                       const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair, const float4 *pgeo,
-                      const float *S, float *forces, int *status, const int *guard, const VerletFuse *vf,
-                      hipStream_t s, double *elog, int elog_by_step) {
+                      const float *S, int s_parts, int64_t s_stride, float *forces, int *status, const int *guard,
+                      const VerletFuse *vf, hipStream_t s, double *elog, int elog_by_step) {
     ProfScope ps(K_FORCES, s);
     ForcesArgs a;
     a.N = N;
     a.row_blocks = (N + 256 / kFrLanes - 1) / (256 / kFrLanes);
     a.row_ptr = row_ptr; a.col = col; a.edge_pair = edge_pair; a.pgeo = pgeo; a.S = S; a.forces = forces;
+    a.s_parts = s_parts;
+    a.s_stride = s_stride;
     a.rptr = replica_ptr; a.eps = eps; a.energy = energy;
     a.elog = elog;
     a.elog_by_step = elog_by_step;

@@ -341,6 +341,14 @@ sn_status filter_backward(const sn_model &m, int t, const float4 *pgeo, const fl
                           const float *gmax, float *S, int accumulate, const char *pack, const int *p_dev,
                           const int *guard, hipStream_t s);
 
+// The backward filter of every interaction in one launch (the systems of
+// filter_forward_fused), interaction t writing S[t P ...]; x, gy, xmax and
+// gmax are per-interaction arrays of pointers.
+sn_status filter_backward_all(const sn_model &m, const float4 *pgeo, const float *pfc, const float *plfc,
+                              const int2 *pair_ij, int64_t P, const float *const *x, const float *const *gy,
+                              const float *const *xmax, const float *const *gmax, float *S, const char *pack,
+                              const int *p_dev, const int *guard, hipStream_t s);
+
 // graph.hip
 // E: the edge count, or -1 to take it from row_ptr[N] on the device.  Writes
 // the pair count to the status slot kPairTotal (0 after a failed check).
@@ -383,15 +391,17 @@ struct VerletFuse {
     const float *ref_pos;
     float half_skin2;
 };
-// F_i = sum_{e in row i} S_p(e) u_e, one launch that also sums the atom
+// F_i = sum_{e in row i} S_p(e) u_e with S_p = S[(s_parts - 1) stride + p] +
+// ... + S[p] (parts added from the last, as the filter backward accumulates
+// them when it runs interaction by interaction), one launch that also sums the atom
 // energies eps per replica (in fp64) into energy[b] (fp32, if energy is set)
 // and elog[b] (fp64, if elog is set; elog[step B + b] when elog_by_step is
 // set: device-driven steps, step = status[kMdStep] - 1) and, with vf,
 // applies its Verlet part.
 sn_status forces_rows(int N, int B, const int32_t *replica_ptr, const float *eps, float *energy,
                       const int32_t *row_ptr, const int32_t *col, const int32_t *edge_pair, const float4 *pgeo,
-                      const float *S, float *forces, int *status, const int *guard, const VerletFuse *vf,
-                      hipStream_t s, double *elog = nullptr, int elog_by_step = 0);
+                      const float *S, int s_parts, int64_t s_stride, float *forces, int *status, const int *guard,
+                      const VerletFuse *vf, hipStream_t s, double *elog = nullptr, int elog_by_step = 0);
 
 
 // Compute units of the current device (filter.hip; read once per process).
