@@ -117,7 +117,17 @@ struct ChainSmem {
     float pmax[NA * 16][kMlpWaves];      // per-atom partial maxima of the wavefront groups
     float psum[NA * 16][kMlpWaves];      // per-atom partial readout sums
     int sx[NA * 16];                     // per-atom split exponents of the published operands
+    float bias[2][F];                    // OUT biases bo1, bo2
+    float rc1[F / 2], rr2[F / 2];        // readout c1, R2
+    float rc2;                           // readout c2
+    int sc[6];                           // split scales of the chain's layers
 };
+
+// A bias's four features 16 m + 4 slot .. + 3 of the lane.
+template <int F, int NA>
+__device__ inline float4 bias4(const ChainSmem<F, NA> &sm, int which, int m, int slot) {
+    return *reinterpret_cast<const float4 *>(&sm.bias[which][16 * m + 4 * slot]);
+}
 
 // LDS-only block barrier: pending LDS operations complete first; global
 // loads and stores stay in flight.
@@ -344,6 +354,27 @@ struct ChainArgs {
     float *gy, *gmax;            // TAIL, BX_BO: g_y and its row maxima
 };
 
+// The chain's small constants (biases, readout vectors, layer scales) into
+// LDS at the start, so that no layer waits on a global load of them; the
+// first publish's barriers make them visible.
+template <int F, int NA>
+__device__ inline void stage_consts(const ChainArgs &a, ChainSmem<F, NA> &sm) {
+    const int f = threadIdx.x;   // F <= 128 < kMlpThreads: one value per thread
+    if (f < F) {
+        if (a.bo1) sm.bias[0][f] = a.bo1[f];
+        if (a.bo2) sm.bias[1][f] = a.bo2[f];
+        if (a.c1 && f < F / 2) {
+            sm.rc1[f] = a.c1[f];
+            sm.rr2[f] = a.R2[f];
+        }
+        if (a.c2 && f == 0) sm.rc2 = a.c2[0];
+    }
+    // one scale per wavefront (the loads of different wavefronts overlap)
+#pragma unroll
+    for (int k = 0; k < 6; ++k)
+        if (threadIdx.x == 64 * k && a.w[k].sc) sm.sc[k] = a.w[k].sc[0];
+}
+
 template <int F, int PROG, int NA>
 __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
     using D = Dims<F>;
@@ -358,6 +389,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
     b.nt = min(NA, (a.N + 15) / 16 - b.tile0);
     b.N = a.N;
     Accs<M, NA> acc;
+    stage_consts<F, NA>(a, sm);
 
     if (PROG == P_EMBED_X) {
         AFrag<M, T, NA> A0;
@@ -383,7 +415,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
         publish<F, M, NA>(sm, 0, b, h);
         layer_mma<F, M, T, NA>(sm, 0, b, A0, acc);
         Vals<M, NA> x;
-        unscale<F, M, NA>(sm, acc, a.w[0].sc[0], b, x);
+        unscale<F, M, NA>(sm, acc, sm.sc[0], b, x);
         store_vals<F, M, NA>(a.x, b, x);
         store_row_max<F, M, NA>(sm, b, x, a.xmax);
         return;
@@ -401,16 +433,17 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
         load_a<M, T, NA>(a.w[1], b, A);
         {
             Vals<M, NA> o;
-            unscale<F, M, NA>(sm, acc, a.w[0].sc[0], b, o);
+            unscale<F, M, NA>(sm, acc, sm.sc[0], b, o);
 #pragma unroll
-            for (int i = 0; i < U::NI; ++i)
+            for (int i = 0; i < U::NI; ++i) {
+                const float4 c = bias4(sm, 0, unit_m<M, NA>(b, i), b.slot);
 #pragma unroll
-                for (int k = 0; k < U::NK; ++k)
+                for (int k = 0; k < U::NK; ++k) {
+                    o[i][k][0] += c.x; o[i][k][1] += c.y; o[i][k][2] += c.z; o[i][k][3] += c.w;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        o[i][k][r] += a.bo1[16 * unit_m<M, NA>(b, i) + 4 * b.slot + r];
-                        v[i][k][r] = ssp(o[i][k][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) v[i][k][r] = ssp(o[i][k][r]);
+                }
+            }
             store_vals<F, M, NA>(a.o, b, o);
         }
         publish<F, M, NA>(sm, 1, b, v);
@@ -418,19 +451,21 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
         load_a<M, T, NA>(a.w[2], b, A);
         {
             Vals<M, NA> d;
-            unscale<F, M, NA>(sm, acc, a.w[1].sc[0], b, d);
+            unscale<F, M, NA>(sm, acc, sm.sc[1], b, d);
 #pragma unroll
-            for (int i = 0; i < U::NI; ++i)
+            for (int i = 0; i < U::NI; ++i) {
+                const float4 c = bias4(sm, 1, unit_m<M, NA>(b, i), b.slot);
+                const float cb[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
                 for (int k = 0; k < U::NK; ++k)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        v[i][k][r] = hin[i][k][r] + d[i][k][r] + a.bo2[16 * unit_m<M, NA>(b, i) + 4 * b.slot + r];
+                    for (int r = 0; r < 4; ++r) v[i][k][r] = hin[i][k][r] + d[i][k][r] + cb[r];
+            }
             store_vals<F, M, NA>(a.h, b, v);
         }
         publish<F, M, NA>(sm, 0, b, v);
         layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
-        unscale<F, M, NA>(sm, acc, a.w[2].sc[0], b, v);
+        unscale<F, M, NA>(sm, acc, sm.sc[2], b, v);
         store_vals<F, M, NA>(a.x, b, v);
         store_row_max<F, M, NA>(sm, b, v, a.xmax);
         return;
@@ -447,30 +482,33 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
         publish<F, M, NA>(sm, 0, b, v);
         layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
         load_a<M, T, NA>(a.w[1], b, A);
-        unscale<F, M, NA>(sm, acc, a.w[0].sc[0], b, o);
+        unscale<F, M, NA>(sm, acc, sm.sc[0], b, o);
 #pragma unroll
-        for (int i = 0; i < U::NI; ++i)
+        for (int i = 0; i < U::NI; ++i) {
+            const float4 c = bias4(sm, 0, unit_m<M, NA>(b, i), b.slot);
 #pragma unroll
-            for (int k = 0; k < U::NK; ++k)
+            for (int k = 0; k < U::NK; ++k) {
+                o[i][k][0] += c.x; o[i][k][1] += c.y; o[i][k][2] += c.z; o[i][k][3] += c.w;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    o[i][k][r] += a.bo1[16 * unit_m<M, NA>(b, i) + 4 * b.slot + r];
-                    v[i][k][r] = ssp(o[i][k][r]);
-                }
+                for (int r = 0; r < 4; ++r) v[i][k][r] = ssp(o[i][k][r]);
+            }
+        }
         publish<F, M, NA>(sm, 1, b, v);
         layer_mma<F, M, T, NA>(sm, 1, b, A, acc);
         AFrag<MR, T, NA> AR;
         load_a<MR, T, NA>(a.w[2], b, AR);
         {
             Vals<M, NA> d;
-            unscale<F, M, NA>(sm, acc, a.w[1].sc[0], b, d);
+            unscale<F, M, NA>(sm, acc, sm.sc[1], b, d);
 #pragma unroll
-            for (int i = 0; i < U::NI; ++i)
+            for (int i = 0; i < U::NI; ++i) {
+                const float4 c = bias4(sm, 1, unit_m<M, NA>(b, i), b.slot);
+                const float cb[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
                 for (int k = 0; k < U::NK; ++k)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        v[i][k][r] = hin[i][k][r] + d[i][k][r] + a.bo2[16 * unit_m<M, NA>(b, i) + 4 * b.slot + r];
+                    for (int r = 0; r < 4; ++r) v[i][k][r] = hin[i][k][r] + d[i][k][r] + cb[r];
+            }
         }
         publish<F, M, NA>(sm, 0, b, v);
         {
@@ -481,7 +519,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
             AFrag<M, TR, NA> AT;
             load_a<M, TR, NA>(a.w[3], b, AT);
             Vals<MR, NA> q;
-            unscale<F, MR, NA>(sm, accr, a.w[2].sc[0], b, q);
+            unscale<F, MR, NA>(sm, accr, sm.sc[2], b, q);
 #pragma unroll
             for (int k = 0; k < UR::NK; ++k) {
                 const int at = unit_a<MR, NA>(b, k);
@@ -491,9 +529,9 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int n0 = 16 * unit_m<MR, NA>(b, i) + 4 * b.slot + r;
-                        const float qq = q[i][k][r] + a.c1[n0];
-                        e += ssp(qq) * a.R2[n0];
-                        q[i][k][r] = sigm(qq) * a.R2[n0];
+                        const float qq = q[i][k][r] + sm.rc1[n0];
+                        e += ssp(qq) * sm.rr2[n0];
+                        q[i][k][r] = sigm(qq) * sm.rr2[n0];
                     }
                 e += __shfl_xor(e, 16, 64);
                 e += __shfl_xor(e, 32, 64);
@@ -506,17 +544,17 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
                     float e = sm.psum[at * 16 + b.lane][0];
 #pragma unroll
                     for (int g = 1; g < UR::WM; ++g) e += sm.psum[at * 16 + b.lane][g];
-                    if (at < b.nt && b.atom(at) < b.N) a.eps[b.atom(at)] = e + a.c2[0];
+                    if (at < b.nt && b.atom(at) < b.N) a.eps[b.atom(at)] = e + sm.rc2;
                 }
             layer_mma<F, M, TR, NA>(sm, 1, b, AT, acc);
         }
         load_a<M, T, NA>(a.w[4], b, A);
-        unscale<F, M, NA>(sm, acc, a.w[3].sc[0], b, v);
+        unscale<F, M, NA>(sm, acc, sm.sc[3], b, v);
         store_vals<F, M, NA>(a.gh, b, v);
         publish<F, M, NA>(sm, 0, b, v);
         layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
         load_a<M, T, NA>(a.w[5], b, A);
-        unscale<F, M, NA>(sm, acc, a.w[4].sc[0], b, v);
+        unscale<F, M, NA>(sm, acc, sm.sc[4], b, v);
 #pragma unroll
         for (int i = 0; i < U::NI; ++i)
 #pragma unroll
@@ -525,7 +563,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
                 for (int r = 0; r < 4; ++r) v[i][k][r] *= sigm(o[i][k][r]);
         publish<F, M, NA>(sm, 1, b, v);
         layer_mma<F, M, T, NA>(sm, 1, b, A, acc);
-        unscale<F, M, NA>(sm, acc, a.w[5].sc[0], b, v);
+        unscale<F, M, NA>(sm, acc, sm.sc[5], b, v);
         store_vals<F, M, NA>(a.gy, b, v);
         store_row_max<F, M, NA>(sm, b, v, a.gmax);
         return;
@@ -543,7 +581,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
     load_a<M, T, NA>(a.w[1], b, A);
     {
         Vals<M, NA> d;
-        unscale<F, M, NA>(sm, acc, a.w[0].sc[0], b, d);
+        unscale<F, M, NA>(sm, acc, sm.sc[0], b, d);
 #pragma unroll
         for (int i = 0; i < U::NI; ++i)
 #pragma unroll
@@ -556,7 +594,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
     layer_mma<F, M, T, NA>(sm, 1, b, A, acc);
     load_a<M, T, NA>(a.w[2], b, A);
     {
-        unscale<F, M, NA>(sm, acc, a.w[1].sc[0], b, v);
+        unscale<F, M, NA>(sm, acc, sm.sc[1], b, v);
 #pragma unroll
         for (int i = 0; i < U::NI; ++i)
 #pragma unroll
@@ -566,7 +604,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
     }
     publish<F, M, NA>(sm, 0, b, v);
     layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
-    unscale<F, M, NA>(sm, acc, a.w[2].sc[0], b, v);
+    unscale<F, M, NA>(sm, acc, sm.sc[2], b, v);
     store_vals<F, M, NA>(a.gy, b, v);
     store_row_max<F, M, NA>(sm, b, v, a.gmax);
 }
