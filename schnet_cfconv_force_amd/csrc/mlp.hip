@@ -354,25 +354,50 @@ struct ChainArgs {
     float *gy, *gmax;            // TAIL, BX_BO: g_y and its row maxima
 };
 
-// The chain's small constants (biases, readout vectors, layer scales) into
-// LDS at the start, so that no layer waits on a global load of them; the
-// first publish's barriers make them visible.
-template <int F, int NA>
-__device__ inline void stage_consts(const ChainArgs &a, ChainSmem<F, NA> &sm) {
-    const int f = threadIdx.x;   // F <= 128 < kMlpThreads: one value per thread
+// The chain's small constants (biases, readout vectors, layer scales) go
+// to LDS at the start, so that no layer waits on a global load of them: each
+// thread loads its share into registers before the chain's row loads issue,
+// and writes it to LDS after they have (the first publish's barriers make
+// it visible).  Loads issued together overlap; a load and its LDS write in
+// sequence would cost one round trip each.
+struct ChainConsts {
+    float b0, b1, c1, r2, c2;
+    int sc;
+};
+template <int F>
+__device__ inline ChainConsts load_consts(const ChainArgs &a) {
+    ChainConsts c = {0.f, 0.f, 0.f, 0.f, 0.f, 0};
+    const int f = threadIdx.x;   // F <= 128: threads 0..F-1 take a feature each
     if (f < F) {
-        if (a.bo1) sm.bias[0][f] = a.bo1[f];
-        if (a.bo2) sm.bias[1][f] = a.bo2[f];
+        if (a.bo1) c.b0 = a.bo1[f];
+        if (a.bo2) c.b1 = a.bo2[f];
         if (a.c1 && f < F / 2) {
-            sm.rc1[f] = a.c1[f];
-            sm.rr2[f] = a.R2[f];
+            c.c1 = a.c1[f];
+            c.r2 = a.R2[f];
         }
-        if (a.c2 && f == 0) sm.rc2 = a.c2[0];
     }
-    // one scale per wavefront (the loads of different wavefronts overlap)
-#pragma unroll
-    for (int k = 0; k < 6; ++k)
-        if (threadIdx.x == 64 * k && a.w[k].sc) sm.sc[k] = a.w[k].sc[0];
+    if (a.c2 && f == 255) c.c2 = a.c2[0];
+    const int k = f - 256;      // threads 256..261: the six layer scales
+    if (k >= 0 && k < 6) {
+        const int *p = k == 0 ? a.w[0].sc : k == 1 ? a.w[1].sc : k == 2 ? a.w[2].sc
+                     : k == 3 ? a.w[3].sc : k == 4 ? a.w[4].sc : a.w[5].sc;
+        if (p) c.sc = *p;
+    }
+    return c;
+}
+template <int F, int NA>
+__device__ inline void store_consts(ChainSmem<F, NA> &sm, const ChainArgs &a, const ChainConsts &c) {
+    const int f = threadIdx.x;
+    if (f < F) {
+        sm.bias[0][f] = c.b0;
+        sm.bias[1][f] = c.b1;
+        if (f < F / 2) {
+            sm.rc1[f] = c.c1;
+            sm.rr2[f] = c.r2;
+        }
+    }
+    if (f == 255) sm.rc2 = c.c2;
+    if (f >= 256 && f < 262) sm.sc[f - 256] = c.sc;
 }
 
 template <int F, int PROG, int NA>
@@ -389,7 +414,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
     b.nt = min(NA, (a.N + 15) / 16 - b.tile0);
     b.N = a.N;
     Accs<M, NA> acc;
-    stage_consts<F, NA>(a, sm);
+    const ChainConsts cst = load_consts<F>(a);
 
     if (PROG == P_EMBED_X) {
         AFrag<M, T, NA> A0;
@@ -412,6 +437,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
             }
         }
         store_vals<F, M, NA>(a.h, b, h);
+        store_consts<F, NA>(sm, a, cst);
         publish<F, M, NA>(sm, 0, b, h);
         layer_mma<F, M, T, NA>(sm, 0, b, A0, acc);
         Vals<M, NA> x;
@@ -428,6 +454,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
         Vals<M, NA> v, hin;   // every row load is issued up front
         load_vals<F, M, NA>(a.in, b, v);
         load_vals<F, M, NA>(a.h_in, b, hin);
+        store_consts<F, NA>(sm, a, cst);
         publish<F, M, NA>(sm, 0, b, v);
         layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
         load_a<M, T, NA>(a.w[1], b, A);
@@ -479,6 +506,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
         Vals<M, NA> v, o, hin;   // every row load is issued up front
         load_vals<F, M, NA>(a.in, b, v);
         load_vals<F, M, NA>(a.h_in, b, hin);
+        store_consts<F, NA>(sm, a, cst);
         publish<F, M, NA>(sm, 0, b, v);
         layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
         load_a<M, T, NA>(a.w[1], b, A);
@@ -576,6 +604,7 @@ __global__ __launch_bounds__(kMlpThreads) void chain_kernel(ChainArgs a) {
     load_vals<F, M, NA>(a.in, b, v);
     load_vals<F, M, NA>(a.gh, b, gh);
     load_vals<F, M, NA>(a.o_prev, b, op);
+    store_consts<F, NA>(sm, a, cst);
     publish<F, M, NA>(sm, 0, b, v);
     layer_mma<F, M, T, NA>(sm, 0, b, A, acc);
     load_a<M, T, NA>(a.w[1], b, A);
