@@ -1,7 +1,8 @@
 """Benchmark of the SchNet CFConv energy/force MD step on one MI355X.
 
 A step is one velocity-Verlet step of all replicas: half kick + drift,
-neighbour-list rebuild (cell list, exact fp32 predicate), one energy+force
+neighbour-list rebuild (cell list, or all-pairs bit-mask tiles for replicas
+of at most 512 atoms; exact fp32 predicate), one energy+force
 evaluation (radial basis, filter network, CFConv, readout, analytic
 backward, forces) and the second half kick.  Inputs are seeded synthetic CG
 chains resident in HBM before timing starts.
@@ -544,7 +545,7 @@ def mode_drift(sn, torch, mode: str, steps=100):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batched_replicas", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--filter-format", type=int, default=0, choices=[0, 1])
