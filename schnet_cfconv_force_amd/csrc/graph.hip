@@ -152,8 +152,12 @@ __global__ __launch_bounds__(256) void pair_refresh_kernel(RefreshArgs a) {
 constexpr int kCfFPL = 8;
 constexpr int kCfWaves = 4;
 constexpr int kCfChunk = 16;
+// Systems of fewer rows than this are latency-bound: their CFConv issues
+// every round of a chunk's loads at once, and their force assembly gives a
+// wavefront to each row.
+constexpr int kSmallRows = 4096;
 
-template <int F, int FPL>
+template <int F, int FPL, int UNROLL>
 __global__ __launch_bounds__(64 * kCfWaves) void cfconv_kernel(int N, const int32_t *row_ptr, const int32_t *col,
                                                                const int32_t *edge_pair, const uint32_t *phi24,
                                                                const float *in, float *out, const int *guard) {
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(64 * kCfWaves) void cfconv_kernel(int N, const int3
         }
         const int n = min(kCfChunk, e1 - eb);
         const int rounds = (n + G - 1) / G;     // uniform over the wavefront
-#pragma unroll 2
+#pragma unroll UNROLL
         for (int r = 0; r < rounds; ++r) {
             const int t = r * G + grp;
             const int src = t < n ? t : n - 1;  // shuffle sources are always live lanes
@@ -227,7 +231,11 @@ __global__ __launch_bounds__(64 * kCfWaves) void cfconv_kernel(int N, const int3
         }
 }
 
-constexpr int kFrLanes = 16;   // lanes per row of the force assembly (32 was faster for forces alone, slower with the MD kicks)
+// lanes per row of the force assembly: 16 (32 was faster for forces alone,
+// slower with the MD kicks); 64 for systems of fewer than kSmallRows rows,
+// whose rows are then summed in one round of loads instead of four
+constexpr int kFrLanes = 16;
+constexpr int kFrLanesSmall = 64;
 
 struct ForcesArgs {
     int N, row_blocks;
@@ -251,9 +259,10 @@ __device__ inline int load_status(const int *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Blocks [0, row_blocks): F_i = sum_{e in row i} S[p(e)] u_e, kFrLanes lanes
+// Blocks [0, row_blocks): F_i = sum_{e in row i} S[p(e)] u_e, LANES lanes
 // per row, then the Verlet part for atom i.  Blocks past them: the energy of one
 // replica each (fixed-order tree, deterministic).
+template <int LANES>
 __global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
     __shared__ double red[256];
     __shared__ int s_go, s_open;
@@ -280,12 +289,12 @@ __global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
             s_open = a.vf.open && (a.vf.n_total < 0 || step + 1 < a.vf.n_total);
         }
         __syncthreads();
-        const int sub = threadIdx.x % kFrLanes;
-        const int i = (blockIdx.x * 256 + threadIdx.x) / kFrLanes;
+        const int sub = threadIdx.x % LANES;
+        const int i = (blockIdx.x * 256 + threadIdx.x) / LANES;
         if (i < a.N && !(a.guard && *a.guard)) {
             const int e0 = a.row_ptr[i], e1 = a.row_ptr[i + 1];
             float fx = 0.f, fy = 0.f, fz = 0.f;
-            for (int e = e0 + sub; e < e1; e += kFrLanes) {
+            for (int e = e0 + sub; e < e1; e += LANES) {
                 const int p = a.edge_pair[e];
                 const float4 g = a.pgeo[p];
                 float sv = a.S[(a.s_parts - 1) * a.s_stride + p];
@@ -295,10 +304,10 @@ __global__ __launch_bounds__(256) void forces_kernel(ForcesArgs a) {
                 fy += s * g.y;
                 fz += s * g.z;
             }
-            for (int o = kFrLanes / 2; o > 0; o >>= 1) {
-                fx += __shfl_xor(fx, o, kFrLanes);
-                fy += __shfl_xor(fy, o, kFrLanes);
-                fz += __shfl_xor(fz, o, kFrLanes);
+            for (int o = LANES / 2; o > 0; o >>= 1) {
+                fx += __shfl_xor(fx, o, LANES);
+                fy += __shfl_xor(fy, o, LANES);
+                fz += __shfl_xor(fz, o, LANES);
             }
             if (sub == 0) {
                 a.forces[3 * i] = fx;
@@ -409,12 +418,17 @@ sn_status cfconv(int F, int N, const int32_t *row_ptr, const int32_t *col, const
     ProfScope ps(K_CFCONV, s);
     const int grid = xcd_grid(N);        // one block per row
     constexpr int T = 64 * kCfWaves;
+    const bool small = N < kSmallRows;
+#define SN_CF(FF)                                                                                          \
+    (small ? cfconv_kernel<FF, kCfFPL, 4><<<grid, T, 0, s>>>(N, row_ptr, col, edge_pair, phi24, in, out, guard) \
+           : cfconv_kernel<FF, kCfFPL, 2><<<grid, T, 0, s>>>(N, row_ptr, col, edge_pair, phi24, in, out, guard))
     switch (F) {
-        case 32: cfconv_kernel<32, kCfFPL><<<grid, T, 0, s>>>(N, row_ptr, col, edge_pair, phi24, in, out, guard); break;
-        case 64: cfconv_kernel<64, kCfFPL><<<grid, T, 0, s>>>(N, row_ptr, col, edge_pair, phi24, in, out, guard); break;
-        case 128: cfconv_kernel<128, kCfFPL><<<grid, T, 0, s>>>(N, row_ptr, col, edge_pair, phi24, in, out, guard); break;
+        case 32: SN_CF(32); break;
+        case 64: SN_CF(64); break;
+        case 128: SN_CF(128); break;
         default: return SN_ERR_INVALID;
     }
+#undef SN_CF
     return launch_status();
 }
 
@@ -425,7 +439,8 @@ sn_status forces_rows(int N, int B, const int32_t *replica_ptr, const float *eps
     ProfScope ps(K_FORCES, s);
     ForcesArgs a;
     a.N = N;
-    a.row_blocks = (N + 256 / kFrLanes - 1) / (256 / kFrLanes);
+    const int lanes = N < kSmallRows ? kFrLanesSmall : kFrLanes;
+    a.row_blocks = (N + 256 / lanes - 1) / (256 / lanes);
     a.row_ptr = row_ptr; a.col = col; a.edge_pair = edge_pair; a.pgeo = pgeo; a.S = S; a.forces = forces;
     a.s_parts = s_parts;
     a.s_stride = s_stride;
@@ -436,7 +451,10 @@ sn_status forces_rows(int N, int B, const int32_t *replica_ptr, const float *eps
     if (!vf) a.vf.n_total = -1;
     a.status = status;
     a.guard = guard;
-    forces_kernel<<<a.row_blocks + B, 256, 0, s>>>(a);
+    if (lanes == kFrLanesSmall)
+        forces_kernel<kFrLanesSmall><<<a.row_blocks + B, 256, 0, s>>>(a);
+    else
+        forces_kernel<kFrLanes><<<a.row_blocks + B, 256, 0, s>>>(a);
     return launch_status();
 }
 
