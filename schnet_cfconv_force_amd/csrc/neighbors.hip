@@ -504,8 +504,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t *in, i
 //   fill   offsets of the earlier blocks (from rep), row_ptr, col, rev and
 //          optionally the pair arrays (one pair per upper edge, numbered
 //          replica by replica and row by row, as the pair setup numbers them)
-// Each fill block reads the masks of its whole replica.  The predicate is
-// the cell-list path's, so both give the same CSR.
+// Each fill block reads the masks of its whole replica.  A system of one
+// replica of at most kTileOneMax atoms takes one launch instead (every block
+// evaluates all of the replica's masks itself).  The predicate is the
+// cell-list path's, so all of them give the same CSR.
 
 constexpr int kTileThreads = kScanThreads;   // the block size block_exclusive assumes
 constexpr int kTileWaves = kTileThreads / kWave;
@@ -590,19 +592,114 @@ __global__ __launch_bounds__(kTileThreads) void tile_count_kernel(TileArgs a) {
     }
 }
 
+// LDS of a fill block: the replica's row masks and positions, and per row
+// the prefix counts of its words, its edge offset, its first upper edge and
+// its pair offset.
+struct TileSmem {
+    uint64_t sm[kRepMaxAtoms][kTileWords];
+    int wpre[kRepMaxAtoms][kTileWords];          // set bits of the row's earlier words
+    int rptr[kRepMaxAtoms + 1], upf[kRepMaxAtoms], upp[kRepMaxAtoms];
+    float sp[3 * kRepMaxAtoms];
+    int sw[kTileWaves];
+};
+
+// Row offsets of the replica (masks in LDS): thread q takes row q.  Returns
+// the replica's edge and upper-edge totals and, with LONGEST, its longest
+// row; the row offsets, first upper edges and pair offsets go to LDS.  Holds
+// barriers.
+struct RowTotals {
+    int edges, upper, longest;
+};
+template <bool LONGEST>
+__device__ inline RowTotals tile_row_offsets(TileSmem &t, int n) {
+    const int W = (n + kWave - 1) / kWave;
+    const int q = threadIdx.x;
+    int cnt = 0, upf = 0;
+    if (q < n) {
+        for (int w = 0; w < W; ++w) {
+            t.wpre[q][w] = cnt;
+            cnt += __popcll(t.sm[q][w]);
+        }
+        upf = t.wpre[q][q / kWave] + __popcll(t.sm[q][q / kWave] & below_mask(q % kWave));
+        t.upf[q] = upf;
+    }
+    RowTotals r;
+    const int pre = block_exclusive(cnt, t.sw, &r.edges);
+    const int pup = block_exclusive(cnt - upf, t.sw, &r.upper);
+    r.longest = LONGEST ? block_max(cnt, t.sw) : 0;
+    if (q < n) {
+        t.rptr[q] = pre;
+        t.upp[q] = pup;
+    }
+    if (q == 0) t.rptr[n] = r.edges;
+    return r;
+}
+
+// The totals of the build into the status words (block 0) and the error
+// flags; returns whether the build failed (capacity or row length).
+__device__ inline bool tile_publish_totals(const TileArgs &a, int64_t total, int max_row) {
+    const bool fail = max_row > SN_MAX_ROW || total > a.capacity || total > INT32_MAX;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.status[kEdgeTotal] = (int)min(total, (int64_t)INT32_MAX);
+        a.status[kMaxRow] = max_row;
+        if (a.flag && fail) flag_status(a.status, max_row > SN_MAX_ROW ? SN_ERR_ROW : SN_ERR_CAPACITY);
+        if (a.pr.edge_pair) a.status[kPairTotal] = fail ? 0 : (int)(total / 2);
+    }
+    return fail;
+}
+
+// Rows [q0, q1) of replica b (first atom s, n atoms; masks, positions and row
+// offsets in LDS; `before` edges in earlier replicas): columns, reverse
+// edges and, when asked for, the pair arrays.  One wavefront per row.
+__device__ inline void tile_fill_rows(const TileArgs &a, const TileSmem &t, int s, int n, int q0, int q1,
+                                      int64_t before) {
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int W = (n + kWave - 1) / kWave;
+    const int64_t pbase = before / 2;           // pairs of the earlier replicas
+    for (int r = q0 + wv; r < q1; r += kTileWaves) {
+        const int i = s + r;
+        const int64_t rbase = before + t.rptr[r];
+#pragma unroll
+        for (int w = 0; w < kTileWords; ++w) {
+            if (w >= W) break;
+            const uint64_t m = t.sm[r][w];
+            if (!((m >> lane) & 1ull)) continue;
+            const int c = kWave * w + lane;       // column, local index
+            const int k = t.wpre[r][w] + __popcll(m & below_mask(lane));
+            const int64_t ed = rbase + k;
+            a.col[ed] = s + c;
+            // position of r in row c (present when the predicate is symmetric)
+            const uint64_t mc = t.sm[c][r / kWave];
+            const int kc = t.wpre[c][r / kWave] + __popcll(mc & below_mask(r % kWave));
+            const bool sym = (mc >> (r % kWave)) & 1ull;
+            if (!sym) flag_status(a.status, SN_ERR_INVALID);
+            a.rev[ed] = sym ? (int)(before + t.rptr[c] + kc) : -1;
+            if (!a.pr.edge_pair) continue;
+            if (c > r) {
+                const int64_t p = pbase + t.upp[r] + (k - t.upf[r]);
+                a.pr.edge_pair[ed] = (int)p;
+                a.pr.pair_ij[p] = make_int2(i, s + c);
+                float4 g;
+                float fc, lfc;
+                pair_geometry(t.sp + 3 * r, t.sp + 3 * c, a.pp.periodic, a.pp.L, a.pp.invL, a.pr.cutoff, g, fc, lfc);
+                a.pr.pgeo[p] = g;
+                a.pr.pfc[p] = fc;
+                a.pr.plfc[p] = lfc;
+            } else {
+                a.pr.edge_pair[ed] = sym ? (int)(pbase + t.upp[c] + (kc - t.upf[c])) : 0;
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(kTileThreads, 8) void tile_fill_kernel(TileArgs a) {
-    __shared__ uint64_t sm[kRepMaxAtoms][kTileWords];
-    __shared__ int wpre[kRepMaxAtoms][kTileWords];   // set bits of the row's earlier words
-    __shared__ int s_rptr[kRepMaxAtoms + 1], s_upf[kRepMaxAtoms], s_upp[kRepMaxAtoms];
-    __shared__ float sp[3 * kRepMaxAtoms];
-    __shared__ int s_sw[kTileWaves];
+    __shared__ TileSmem t;
     __shared__ unsigned long long s_before, s_total;
     __shared__ int s_max, s_st;
     if (skipped(a.run_flag)) return;
     const int b = blockIdx.x / a.R, part = blockIdx.x % a.R;
     const int s = a.rptr[b], e = a.rptr[b + 1], n = e - s;
-    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-    const int W = (n + kWave - 1) / kWave;
+    const int lane = threadIdx.x % kWave;
     if (threadIdx.x == 0) {
         s_before = 0;
         s_total = 0;
@@ -635,84 +732,73 @@ __global__ __launch_bounds__(kTileThreads, 8) void tile_fill_kernel(TileArgs a) 
     __syncthreads();
     if (s_st != 0) return;                        // uniform: nothing is written after an error
     const int64_t before = (int64_t)s_before, total = (int64_t)s_total;
-    const int max_row = s_max;
-    const bool fail = max_row > SN_MAX_ROW || total > a.capacity || total > INT32_MAX;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        a.status[kEdgeTotal] = (int)min(total, (int64_t)INT32_MAX);
-        a.status[kMaxRow] = max_row;
-        if (a.flag && fail) flag_status(a.status, max_row > SN_MAX_ROW ? SN_ERR_ROW : SN_ERR_CAPACITY);
-        if (a.pr.edge_pair) a.status[kPairTotal] = fail ? 0 : (int)(total / 2);
-    }
+    const bool fail = tile_publish_totals(a, total, s_max);
     for (int k = threadIdx.x; k < n * kTileWords; k += kTileThreads)
-        (&sm[0][0])[k] = a.mask[(int64_t)s * kTileWords + k];
-    for (int k = threadIdx.x; k < 3 * n; k += kTileThreads) sp[k] = a.pos[3 * (int64_t)s + k];
+        (&t.sm[0][0])[k] = a.mask[(int64_t)s * kTileWords + k];
+    for (int k = threadIdx.x; k < 3 * n; k += kTileThreads) t.sp[k] = a.pos[3 * (int64_t)s + k];
     __syncthreads();
-    // per row (one thread each): prefix counts of the words, length, first upper edge
-    const int q = threadIdx.x;
-    int cnt = 0, upf = 0;
-    if (q < n) {
-        for (int w = 0; w < W; ++w) {
-            wpre[q][w] = cnt;
-            cnt += __popcll(sm[q][w]);
-        }
-        upf = wpre[q][q / kWave] + __popcll(sm[q][q / kWave] & below_mask(q % kWave));
-        s_upf[q] = upf;
-    }
-    int tot_edges, tot_upper;
-    const int pre = block_exclusive(cnt, s_sw, &tot_edges);
-    const int pup = block_exclusive(cnt - upf, s_sw, &tot_upper);
+    const RowTotals rt = tile_row_offsets<false>(t, n);
     const int per = (n + a.R - 1) / a.R, q0 = part * per, q1 = min(n, q0 + per);
-    if (q < n) {
-        s_rptr[q] = pre;
-        s_upp[q] = pup;
-        if (q >= q0 && q < q1) a.row_ptr[s + q] = (int)(before + pre);
-    }
-    if (q == 0) s_rptr[n] = tot_edges;
+    const int q = threadIdx.x;
+    if (q >= q0 && q < q1) a.row_ptr[s + q] = (int)(before + t.rptr[q]);
     if (blockIdx.x == gridDim.x - 1 && q == 0) a.row_ptr[a.N] = (int)min(total, (int64_t)INT32_MAX);
     if (fail) return;                             // uniform
-    if (2 * tot_upper != tot_edges) {             // not symmetric: the pair numbering would not fit
+    if (2 * rt.upper != rt.edges) {               // not symmetric: the pair numbering would not fit
         if (q == 0) flag_status(a.status, SN_ERR_INVALID);
         return;                                   // uniform
     }
     __syncthreads();
+    tile_fill_rows(a, t, s, n, q0, q1, before);
+}
 
-    const int64_t pbase = before / 2;           // pairs of the earlier replicas
-    for (int r = q0 + wv; r < q1; r += kTileWaves) {
-        const int i = s + r;
-        const int64_t rbase = before + s_rptr[r];
+// A system of one small replica (n <= kTileOneMax): count and fill in one
+// launch.  Each block evaluates every row mask of the replica itself (n^2
+// predicate tests, a few per thread at this size) into LDS, so no masks or
+// counts go through global memory, then writes its share of the rows as the
+// fill pass does.
+__global__ __launch_bounds__(kTileThreads, 8) void tile_one_kernel(TileArgs a) {
+    __shared__ TileSmem t;
+    __shared__ int s_st;
+    if (skipped(a.run_flag)) return;
+    const int s = a.rptr[0], n = a.rptr[1] - s;
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    if (threadIdx.x == 0) {
+        s_st = *a.status;                         // read before this kernel flags anything
+        if (blockIdx.x == 0 && a.step_mark >= 0 && s_st == 0) a.status[kStepsDone] = a.step_mark;
+    }
+    if (tile_positions(a.pos, s, n, t.sp)) {      // (holds a barrier, so s_st is visible below)
+        if (blockIdx.x == 0 && threadIdx.x == 0) flag_status(a.status, SN_ERR_NONFINITE);
+        return;                                   // uniform
+    }
+    if (s_st != 0) return;                        // uniform: nothing is written after an error
+    const int W = (n + kWave - 1) / kWave;
+    for (int q = wv; q < n; q += kTileWaves) {
+        const float xi = t.sp[3 * q], yi = t.sp[3 * q + 1], zi = t.sp[3 * q + 2];
 #pragma unroll
         for (int w = 0; w < kTileWords; ++w) {
             if (w >= W) break;
-            const uint64_t m = sm[r][w];
-            if (!((m >> lane) & 1ull)) continue;
-            const int c = kWave * w + lane;       // column, local index
-            const int k = wpre[r][w] + __popcll(m & below_mask(lane));
-            const int64_t ed = rbase + k;
-            a.col[ed] = s + c;
-            // position of r in row c (present when the predicate is symmetric)
-            const uint64_t mc = sm[c][r / kWave];
-            const int kc = wpre[c][r / kWave] + __popcll(mc & below_mask(r % kWave));
-            const bool sym = (mc >> (r % kWave)) & 1ull;
-            if (!sym) flag_status(a.status, SN_ERR_INVALID);
-            a.rev[ed] = sym ? (int)(before + s_rptr[c] + kc) : -1;
-            if (!a.pr.edge_pair) continue;
-            if (c > r) {
-                const int64_t p = pbase + s_upp[r] + (k - s_upf[r]);
-                a.pr.edge_pair[ed] = (int)p;
-                a.pr.pair_ij[p] = make_int2(i, s + c);
-                float4 g;
-                float fc, lfc;
-                pair_geometry(sp + 3 * r, sp + 3 * c, a.pp.periodic, a.pp.L, a.pp.invL, a.pr.cutoff, g, fc, lfc);
-                a.pr.pgeo[p] = g;
-                a.pr.pfc[p] = fc;
-                a.pr.plfc[p] = lfc;
-            } else {
-                a.pr.edge_pair[ed] = sym ? (int)(pbase + s_upp[c] + (kc - s_upf[c])) : 0;
-            }
+            const int j = kWave * w + lane, jj = j < n ? j : 0;
+            const float4 pj = make_float4(t.sp[3 * jj], t.sp[3 * jj + 1], t.sp[3 * jj + 2], 0.0f);
+            const bool pass = j < n && j != q && within(xi, yi, zi, pj, a.pp);
+            const uint64_t m = __ballot(pass);
+            if (lane == 0) t.sm[q][w] = m;
         }
     }
+    __syncthreads();
+    const RowTotals rt = tile_row_offsets<true>(t, n);
+    const bool fail = tile_publish_totals(a, rt.edges, rt.longest);
+    const int per = (n + gridDim.x - 1) / gridDim.x, q0 = blockIdx.x * per, q1 = min(n, q0 + per);
+    const int q = threadIdx.x;
+    if (q >= q0 && q < q1) a.row_ptr[s + q] = t.rptr[q];
+    if (blockIdx.x == gridDim.x - 1 && q == 0) a.row_ptr[a.N] = rt.edges;
+    if (fail) return;                             // uniform
+    if (2 * rt.upper != rt.edges) {               // not symmetric: the pair numbering would not fit
+        if (q == 0) flag_status(a.status, SN_ERR_INVALID);
+        return;                                   // uniform
+    }
+    __syncthreads();
+    tile_fill_rows(a, t, s, n, q0, q1, 0);
 }
-
 }  // namespace
 
 sn_status scan_exclusive(const int32_t *in, int32_t *out, int n, int32_t *total_slot, int32_t *max_slot,
@@ -838,15 +924,23 @@ sn_status nb_build(const sn_system &sys, const float *pos, float r_list, int32_t
         a.step_mark = step_mark;
         a.status = status;
         a.run_flag = run_flag;
-        {
-            ProfScope ps(K_NB_COUNT, s);
-            tile_count_kernel<<<B * a.Rc, kTileThreads, 0, s>>>(a);
-            SN_TRY(launch_status());
-        }
-        {
+        if (B == 1 && max_rep <= kTileOneMax) {
+            // one small replica: a block per 16 rows (one per wavefront)
             ProfScope ps(K_NB_FILL, s);
-            tile_fill_kernel<<<B * a.R, kTileThreads, 0, s>>>(a);
+            const int R = std::max(1, (max_rep + kTileWaves - 1) / kTileWaves);
+            tile_one_kernel<<<R, kTileThreads, 0, s>>>(a);
             SN_TRY(launch_status());
+        } else {
+            {
+                ProfScope ps(K_NB_COUNT, s);
+                tile_count_kernel<<<B * a.Rc, kTileThreads, 0, s>>>(a);
+                SN_TRY(launch_status());
+            }
+            {
+                ProfScope ps(K_NB_FILL, s);
+                tile_fill_kernel<<<B * a.R, kTileThreads, 0, s>>>(a);
+                SN_TRY(launch_status());
+            }
         }
         if (pairs_done) *pairs_done = pairs != nullptr;
         if (sync) {

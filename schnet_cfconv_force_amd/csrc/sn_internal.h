@@ -274,10 +274,12 @@ struct NbPairOut {
 // Largest replica (atoms), read from the device (synchronises `s`); -1 on error.
 int max_replica_atoms(const sn_system &sys, hipStream_t s);
 // Replicas of at most this many atoms are built by one block each from
-// all-pairs bit masks in LDS (two launches for the whole build).
+// all-pairs bit masks in LDS (two launches for the whole build; one for a
+// system of a single replica of at most kTileOneMax atoms).
 constexpr int kRepMaxAtoms = 512;
 constexpr int kRepMaxReplicas = 4096;   // each block of that build reads every replica's count
 constexpr int kTileMaxSplit = 16;       // blocks per replica in that build
+constexpr int kTileOneMax = 128;        // one replica of at most this many atoms: one launch
 // sync: read the edge count back (into *n_edges) and check it on the host
 // before the rows are filled.  Otherwise nothing is read back: the fill
 // checks the capacity and row lengths on the device and flags errors; every

@@ -1,11 +1,12 @@
 """GPU: both neighbour-build paths against the oracle.
 
 Replicas of at most 512 atoms are built from all-pairs row bit masks (one
-block per replica slice, two launches, pair arrays included on the MD path);
-larger ones by the cell list.  The library picks the path from the largest
-replica, so systems just below and just above that size run each path on
-the same kind of input: the CSR must be bit-identical to the oracle's either
-way, and a few Verlet steps must follow the oracle's trajectory.
+block per replica slice, two launches, pair arrays included on the MD path;
+a system of one replica of at most 128 atoms in one launch); larger ones by
+the cell list.  The library picks the path from the largest replica, so
+systems just below and just above each size run both paths on the same kind
+of input: the CSR must be bit-identical to the oracle's either way, and a few
+Verlet steps must follow the oracle's trajectory.
 """
 import sys
 
@@ -19,6 +20,7 @@ from helpers import E_TOL, F_TOL, md_evaluation_errors
 pytestmark = pytest.mark.gpu
 
 TILE_MAX = 512   # the largest replica the mask path builds
+TILE_ONE_MAX = 128   # the largest single replica the mask path builds in one launch
 
 
 def say(*a):
@@ -81,6 +83,11 @@ def test_cell_list_rows_longer_and_shorter_than_the_kept_length(sn):
     ([300, 0, 1, 2, 211], False),          # empty and tiny replicas on the mask path
     ([400], True),                         # periodic, mask path
     ([TILE_MAX + 88], True),               # periodic, cell list
+    ([64], False),                         # one replica, one launch: one mask word per row
+    ([65], False),                         # ... two words
+    ([TILE_ONE_MAX], False),               # ... at its largest
+    ([TILE_ONE_MAX + 1], False),           # one atom more: two launches
+    ([100], True),                         # periodic, one launch
 ])
 def test_csr_bit_exact_on_both_paths(sn, sizes, periodic):
     say(f"[build paths] sizes={sizes} periodic={periodic}")
@@ -102,8 +109,36 @@ def test_csr_bit_exact_on_both_paths(sn, sizes, periodic):
         assert np.array_equal(rev.cpu().numpy()[:E], ref[2])
 
 
-def test_capacity_error_on_the_mask_path(sn):
-    pos, rp = _system([200, 200], 20.0, 3)
+def test_one_launch_build_edge_cases(sn):
+    """One-replica systems on the one-launch mask build: a lone atom (no edges), pairs at the
+    strict fp32 cutoff (just below, at and just above r_list), and a periodic wrap."""
+    rc = np.float32(10.0)
+    below = np.nextafter(rc, np.float32(0))
+    above = np.nextafter(rc, np.float32(20))
+    cases = [
+        (np.array([[1.0, 2.0, 3.0]], np.float32), None, 10.0),
+        (np.array([[0, 0, 0], [below, 0, 0], [0, rc, 0], [0, 0, above]], np.float32), None, 10.0),
+        (np.array([[0.5, 10, 10], [19.5, 10, 10], [10, 10, 10]], np.float32), np.array([20.0] * 3, np.float32),
+         6.0),
+    ]
+    params, hyper = _model(rc=6.0)
+    for pos, box, r_list in cases:
+        say(f"[build paths] one launch, {len(pos)} atoms, periodic={box is not None}")
+        rp = np.array([0, len(pos)], np.int32)
+        model = sn.Model(params, hyper)
+        system = sn.System(rp, np.zeros(len(pos), np.int32), box)
+        ws = sn.workspace(model, system, 64)
+        row_ptr, col, rev, E = sn.build_csr_neighbors(system, dev(pos), r_list, 64, ws)
+        ref = O.neighbors_bruteforce(pos, rp, r_list, box)
+        assert E == len(ref[1])
+        assert np.array_equal(row_ptr.cpu().numpy(), ref[0])
+        assert np.array_equal(col.cpu().numpy()[:E], ref[1])
+        assert np.array_equal(rev.cpu().numpy()[:E], ref[2])
+
+
+@pytest.mark.parametrize("sizes", [[200, 200], [120]])
+def test_capacity_error_on_the_mask_path(sn, sizes):
+    pos, rp = _system(sizes, 20.0, 3)
     params, hyper = _model()
     model = sn.Model(params, hyper)
     system = sn.System(rp, np.zeros(len(pos), np.int32))
@@ -115,9 +150,10 @@ def test_capacity_error_on_the_mask_path(sn):
     assert st == sn.SN_OK and ne == len(ref[1])
 
 
-@pytest.mark.parametrize("sizes", [[250, 250], [TILE_MAX + 100]])
+@pytest.mark.parametrize("sizes", [[250, 250], [TILE_MAX + 100], [120]])
 def test_verlet_on_both_paths_matches_oracle(sn, sizes):
-    """Three steps: the mask path also writes the pair arrays; the cell path runs the pair setup."""
+    """Three steps: the mask path (two launches, or one for a single small replica) also writes the
+    pair arrays; the cell path runs the pair setup."""
     import torch
     say(f"[build paths] verlet sizes={sizes}")
     pos, rp = _system(sizes, 24.0 if len(sizes) > 1 else 28.0, 21)
