@@ -705,13 +705,24 @@ sn_status launch_bwd(const FilterArgs &a, hipStream_t s) {
     return launch_status();
 }
 
-// All interactions at once (systems with few pair tiles): at most num_cus
-// blocks in all, so that one pass over the GPU covers every interaction.
+// All interactions at once (systems with few pair tiles): one pass over the
+// compute units, each interaction taking a multiple of the XCD count of
+// blocks (one block per CU: the staged weights take most of the LDS).  When
+// the tiles outnumber one wavefront per SIMD of those blocks, the blocks get
+// two wavefronts per SIMD, so that no wavefront runs two tiles in sequence.
+inline int fused_blocks_per_interaction(int I) { return std::max(kXcds, num_cus() / I / kXcds * kXcds); }
+
 template <int F, int ONE>
 sn_status launch_fwd_all(const FilterArgsSet &set, int I, int64_t P, hipStream_t s) {
     const int64_t tiles = (P + 15) / 16;
+    const int per = fused_blocks_per_interaction(I);
+    if (tiles > (int64_t)per * (kSmallThreads / 64)) {
+        constexpr int T = 2 * kSmallThreads;
+        const int gx = xcd_grid((int)std::min<int64_t>(per, (tiles + T / 64 - 1) / (T / 64)));
+        filter_fwd_all_kernel<F, T, ONE><<<dim3(gx, I), T, 0, s>>>(set);
+        return launch_status();
+    }
     const int waves = kSmallThreads / 64;
-    const int per = std::max(1, num_cus() / I);
     const int gx = xcd_grid((int)std::min<int64_t>(per, (tiles + waves - 1) / waves));
     filter_fwd_all_kernel<F, kSmallThreads, ONE><<<dim3(gx, I), kSmallThreads, 0, s>>>(set);
     return launch_status();
@@ -720,8 +731,14 @@ sn_status launch_fwd_all(const FilterArgsSet &set, int I, int64_t P, hipStream_t
 template <int F, int ONE>
 sn_status launch_bwd_all(const FilterArgsSet &set, int I, int64_t P, hipStream_t s) {
     const int64_t tiles = (P + 15) / 16;
+    const int per = fused_blocks_per_interaction(I);
+    if (tiles > (int64_t)per * (kSmallThreads / 64)) {
+        constexpr int T = 2 * kSmallThreads;
+        const int gx = xcd_grid((int)std::min<int64_t>(per, (tiles + T / 64 - 1) / (T / 64)));
+        filter_bwd_all_kernel<F, T, ONE><<<dim3(gx, I), T, 0, s>>>(set);
+        return launch_status();
+    }
     const int waves = kSmallThreads / 64;
-    const int per = std::max(1, num_cus() / I);
     const int gx = xcd_grid((int)std::min<int64_t>(per, (tiles + waves - 1) / waves));
     filter_bwd_all_kernel<F, kSmallThreads, ONE><<<dim3(gx, I), kSmallThreads, 0, s>>>(set);
     return launch_status();
