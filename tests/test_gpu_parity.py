@@ -274,6 +274,27 @@ def test_energy_forces_other_model_shapes(sn, F, K, I, T):
     _compare(E, Fo, E_ref, F_ref, eps_abs, rp, f"F={F} K={K}")
 
 
+@pytest.mark.parametrize("I", [8, 9, 16])
+def test_energy_forces_interaction_counts(sn, I):
+    """Small systems run every interaction's filter in one launch up to 8 interactions (each
+    writing its own slice of the per-pair force scalar, summed by the force assembly) and one
+    launch per interaction beyond; 16 is the largest count the library takes.  Against the
+    oracle either way."""
+    say(f"[interaction counts] I={I}")
+    pos, rp = _random_system(3, 90, 18.0, 3000 + I)
+    rc, F, K, T = 7.0, 32, 8, 3
+    cfg = {"pos": pos, "replica_ptr": rp, "box": None,
+           "types": np.random.default_rng(I).integers(0, T, len(pos)).astype(np.int32),
+           "params": synth.init_params(T, I, F, K, [F, K, I, 7]),
+           "hyper": {"n_types": T, "n_interactions": I, "n_features": F, "n_rbf": K, "cutoff": rc,
+                     **synth.rbf_hyper(K, 0.0, rc)}}
+    L = Loaded(sn, cfg)
+    E, Fo = L.eval(sn)
+    E_ref, F_ref, eps_abs, csr = oracle_full(cfg)
+    assert len(csr[1]) > 100
+    _compare(E, Fo, E_ref, F_ref, eps_abs, rp, f"I={I}")
+
+
 @pytest.mark.parametrize("F,K,I,T,n_rep", [(32, 16, 2, 4, 56), (64, 33, 2, 4, 100), (64, 16, 1, 3, 60),
                                            (128, 50, 2, 5, 150), (32, 16, 2, 4, 190)])
 def test_energy_forces_atomwise_block_sizes(sn, F, K, I, T, n_rep):
