@@ -648,9 +648,34 @@ __device__ inline bool tile_publish_totals(const TileArgs &a, int64_t total, int
     return fail;
 }
 
+// Position of the j-th set bit (from 0) of m, which has more than j set bits.
+__device__ inline int select_bit(uint64_t m, int j) {
+    int pos = 0;
+    int c = __popc((uint32_t)m);
+    uint32_t x = (uint32_t)m;
+    if (j >= c) {
+        j -= c;
+        x = (uint32_t)(m >> 32);
+        pos = 32;
+    }
+#pragma unroll
+    for (int sh = 16; sh >= 2; sh >>= 1) {
+        c = __popc(x & ((1u << sh) - 1u));
+        if (j >= c) {
+            j -= c;
+            x >>= sh;
+            pos += sh;
+        }
+    }
+    return pos + (j >= (int)(x & 1u) ? 1 : 0);
+}
+
 // Rows [q0, q1) of replica b (first atom s, n atoms; masks, positions and row
 // offsets in LDS; `before` edges in earlier replicas): columns, reverse
-// edges and, when asked for, the pair arrays.  One wavefront per row.
+// edges and, when asked for, the pair arrays.  One wavefront per row, one
+// lane per edge: lane k finds the row's k-th set bit (the mask word from the
+// word prefix counts, the bit by halving popcounts), so every lane has work
+// instead of the few whose column bit is set in each word.
 __device__ inline void tile_fill_rows(const TileArgs &a, const TileSmem &t, int s, int n, int q0, int q1,
                                       int64_t before) {
     const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
@@ -658,14 +683,13 @@ __device__ inline void tile_fill_rows(const TileArgs &a, const TileSmem &t, int 
     const int64_t pbase = before / 2;           // pairs of the earlier replicas
     for (int r = q0 + wv; r < q1; r += kTileWaves) {
         const int i = s + r;
+        const int len = t.rptr[r + 1] - t.rptr[r];
         const int64_t rbase = before + t.rptr[r];
-#pragma unroll
-        for (int w = 0; w < kTileWords; ++w) {
-            if (w >= W) break;
-            const uint64_t m = t.sm[r][w];
-            if (!((m >> lane) & 1ull)) continue;
-            const int c = kWave * w + lane;       // column, local index
-            const int k = t.wpre[r][w] + __popcll(m & below_mask(lane));
+        for (int k = lane; k < len; k += kWave) {
+            int w = 0;                            // the word of the k-th set bit
+            for (int u = 1; u < W; ++u)
+                if (t.wpre[r][u] <= k) w = u;
+            const int c = kWave * w + select_bit(t.sm[r][w], k - t.wpre[r][w]);   // column, local index
             const int64_t ed = rbase + k;
             a.col[ed] = s + c;
             // position of r in row c (present when the predicate is symmetric)
