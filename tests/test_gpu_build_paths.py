@@ -136,7 +136,7 @@ def test_one_launch_build_edge_cases(sn):
         assert np.array_equal(rev.cpu().numpy()[:E], ref[2])
 
 
-@pytest.mark.parametrize("sizes", [[200, 200], [120]])
+@pytest.mark.parametrize("sizes", [[200, 200], [120], [60]])
 def test_capacity_error_on_the_mask_path(sn, sizes):
     pos, rp = _system(sizes, 20.0, 3)
     params, hyper = _model()
@@ -150,10 +150,10 @@ def test_capacity_error_on_the_mask_path(sn, sizes):
     assert st == sn.SN_OK and ne == len(ref[1])
 
 
-@pytest.mark.parametrize("sizes", [[250, 250], [TILE_MAX + 100], [120]])
+@pytest.mark.parametrize("sizes", [[250, 250], [TILE_MAX + 100], [120], [60]])
 def test_verlet_on_both_paths_matches_oracle(sn, sizes):
-    """Three steps: the mask path (two launches, or one for a single small replica) also writes the
-    pair arrays; the cell path runs the pair setup."""
+    """Three steps: the mask path (two launches, or one for a single replica of at most 128 atoms)
+    also writes the pair arrays; the cell path runs the pair setup."""
     import torch
     say(f"[build paths] verlet sizes={sizes}")
     pos, rp = _system(sizes, 24.0 if len(sizes) > 1 else 28.0, 21)
