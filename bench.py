@@ -531,6 +531,13 @@ def mode_drift(sn, torch, mode: str, steps=100):
     e1, f1, t1, _ = runs[1]
     W1 = work[1]
     prof = W1.profile(lambda: W1.md(1), 10)
+
+    def slope_per_ns(tot):
+        # least-squares slope of each replica's total energy over time (2 fs steps)
+        t_ns = np.arange(tot.shape[0]) * 2.0e-6
+        tc = t_ns - t_ns.mean()
+        return (tc[:, None] * (tot - tot.mean(axis=0))).sum(axis=0) / max((tc ** 2).sum(), 1e-30)
+    s0, s1 = slope_per_ns(t0), slope_per_ns(t1)
     return {"kernels": {k: v for k, v in kernels_table(prof, 10).items() if k.startswith("filter")},
             "rel_dE_max": float(np.abs(e1 - e0).max() / np.abs(e0).max()),
             "rms_dF_over_rms_F": float(np.sqrt(((f1 - f0) ** 2).mean() / (f0 ** 2).mean())),
@@ -538,6 +545,8 @@ def mode_drift(sn, torch, mode: str, steps=100):
             "etot_trace_diff_over_mean_ekin": float(np.abs(t1 - t0).max() / k0.mean()),
             "etot_drift_fp32_kcal_mol": float(np.abs(t0 - t0[0]).max()),
             f"etot_drift_{mode}_kcal_mol": float(np.abs(t1 - t1[0]).max()),
+            "etot_slope_fp32_kcal_mol_per_ns": {"mean": float(s0.mean()), "max_abs": float(np.abs(s0).max())},
+            f"etot_slope_{mode}_kcal_mol_per_ns": {"mean": float(s1.mean()), "max_abs": float(np.abs(s1).max())},
             "md_steps": steps,
             "md_steps_per_s_fp32": round(1.0 / sec[0], 2), f"md_steps_per_s_{mode}": round(1.0 / sec[1], 2)}
 
@@ -553,6 +562,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="only the headline workload")
+    ap.add_argument("--drift-steps", type=int, default=0,
+                    help="only the long-run drift of the int16 weights and of the fp16-product filter against "
+                         "the default on the 64 x 269 workload, over this many MD steps; one JSON line")
     ap.add_argument("--no-measure-peaks", dest="measure_peaks", action="store_false",
                     help="skip the device-copy and fp16-GEMM rate measurements (fractions of measured rates)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -584,6 +596,15 @@ def main():
         print(md)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.drift_steps > 0 and args.gpus == 1 and world == 1:
+        import torch
+        import schnet_cfconv_force_amd as sn
+        out = {"drift_steps": args.drift_steps, "workload": WORKLOAD_TEXT["batched_replicas"]}
+        for mode in ("int16", "fp16_math"):
+            print(f"[bench] {args.drift_steps}-step drift, {mode}", file=sys.stderr, flush=True)
+            out[mode] = mode_drift(sn, torch, mode, steps=args.drift_steps)
+        print(json.dumps(out))
+        return
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not part of "
               f"this build", file=sys.stderr)
