@@ -186,6 +186,47 @@ def test_verlet_on_both_paths_matches_oracle(sn, sizes):
     assert e_err.max() <= E_TOL and f_err.max() <= F_TOL
 
 
+@pytest.mark.parametrize("n", [400, TILE_MAX + 88])
+def test_periodic_verlet_on_both_paths_matches_oracle(sn, n):
+    """Three steps in a periodic box on the mask path (400 particles) and the cell list (600), with
+    the particles shifted so that nearly all of them lie outside [0, L): the library never wraps
+    positions, the predicate takes the minimum image and the cell binning wraps.  Against the
+    oracle's trajectory, and the final state at the contract tolerances."""
+    import torch
+    say(f"[build paths] periodic verlet n={n}")
+    side = 26.0
+    pos, rp = _system([n], side, 31 + n)
+    pos = (pos + np.array([-0.3, 0.2, 25.9], np.float32)).astype(np.float32)   # mostly outside the box
+    box = np.array([side] * 3, np.float32)
+    params, hyper = _model(F=32, K=8, I=2, rc=7.0)
+    types = np.random.default_rng(n).integers(0, 3, len(pos)).astype(np.int32)
+    inv_mass = np.full(len(pos), 1.0 / 110.0, np.float32)
+    vel = synth.maxwell_boltzmann(len(pos), rp, 110.0, 300.0, 13).astype(np.float32)
+    model = sn.Model(params, hyper)
+    system = sn.System(rp, types, box)
+    cap = 200 * len(pos)
+    ws = sn.workspace(model, system, cap)
+    p, v, im = dev(pos), dev(vel), dev(inv_mass)
+    row_ptr, col, rev, E = sn.build_csr_neighbors(system, p, 7.0, cap, ws)
+    _, forces = sn.energy_forces(model, system, p, row_ptr, col, rev, E, ws)
+    steps = 3
+    epot = torch.zeros((steps, 1), dtype=torch.float64, device="cuda")
+    sn.verlet_step(model, system, p, v, forces, im, 2.0, synth.FORCE_TO_ACCEL, steps, 7.0, cap, ws, epot)
+    torch.cuda.synchronize()
+    r_ref, v_ref, f_ref, ep_ref, _ = O.verlet(params, hyper, types, pos, vel, inv_mass, rp, 2.0,
+                                              synth.FORCE_TO_ACCEL, steps, 7.0, box)
+    dr = np.abs(p.cpu().numpy() - r_ref).max()
+    dv = np.abs(v.cpu().numpy() - v_ref).max() / np.abs(v_ref).max()
+    outside = int(((r_ref < 0) | (r_ref >= side)).any(axis=1).sum())
+    say(f"   {outside} particles outside [0, L); max |dr| {dr:.2e} A, max rel dv {dv:.2e}")
+    assert outside > 0
+    assert dr < 5e-5 and dv < 5e-5
+    e_err, f_err = md_evaluation_errors(params, hyper, types, rp, box, p.cpu().numpy(), forces.cpu().numpy(),
+                                        epot.cpu().numpy()[-1])
+    say(f"   final state: energy err {e_err.max():.2e}, force err {f_err.max():.2e}")
+    assert e_err.max() <= E_TOL and f_err.max() <= F_TOL
+
+
 @pytest.mark.parametrize("F,I,log_ekin", [(32, 1, False), (64, 1, True), (64, 2, False), (128, 2, True)])
 def test_verlet_model_shapes_match_oracle(sn, F, I, log_ekin):
     """MD on the tile path for other feature widths and interaction counts: with one interaction
