@@ -197,15 +197,21 @@ def test_graph_replay_is_bit_identical(sn, path, log_ekin):
 
 # ------------------------------------------------------------------ neighbour skin
 
-@pytest.mark.parametrize("path", ["mask", "cell"])
+@pytest.mark.parametrize("path", ["mask", "cell", "periodic"])
 @pytest.mark.parametrize("rebuild_every", [0, 4])
 def test_skin_matches_the_oracle(sn, path, rebuild_every):
     """A list built at cutoff + 1 A and kept across steps (rebuilt every 4 steps, or only on
     displacement): states meet the contract at their positions and the trajectory matches both the
     oracle's (rebuilt every step at the cutoff) and the per-step rebuild's; with the graph the same
-    bits again."""
+    bits again.  "periodic": the cell-list system in a periodic 30 A box (the kept pairs' geometry
+    is refreshed with the minimum image)."""
     say(f"[md skin] {path} path, rebuild_every={rebuild_every}")
-    cfg = _batched(4) if path == "mask" else _cell_path_cfg()
+    if path == "mask":
+        cfg = _batched(4)
+    else:
+        cfg = _cell_path_cfg()
+        if path == "periodic":
+            cfg["box"] = np.array([30.0, 30.0, 30.0], np.float32)
     rc = cfg["hyper"]["cutoff"]
     md = MD(sn, cfg)
     every = md.run(10, log_ekin=False)
