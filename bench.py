@@ -207,6 +207,52 @@ def summarize_util(csv_path: str, workload: str, command: str, n_simd: int = 102
     ])
 
 
+CACHE_COUNTERS = ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_DRAM_sum", "TCP_TOTAL_CACHE_ACCESSES_sum",
+                  "TCP_TCC_READ_REQ_sum", "TCP_TCC_READ_REQ_LATENCY_sum")
+
+
+def summarize_cache(csv_path: str, workload: str, command: str) -> str:
+    """Markdown summary of one rocprofv3 --pmc pass over CACHE_COUNTERS, per kernel (mean per
+    dispatch): L2 hit rate, L2 read requests to DRAM, vector L1 accesses, L1-to-L2 read requests and
+    their mean latency."""
+    import collections
+    import csv
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        vals[_short_kernel(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    rows = []
+    for k in ("filter_bwd_kernel", "filter_fwd_kernel", "cfconv_kernel", "chain_kernel", "tile_count_kernel",
+              "tile_fill_kernel", "forces_kernel"):
+        if k not in vals:
+            continue
+        m = {c: sum(v) / len(v) for c, v in vals[k].items()}
+        hit, miss = m.get("TCC_HIT_sum", 0.0), m.get("TCC_MISS_sum", 0.0)
+        req = m.get("TCP_TCC_READ_REQ_sum", 0.0)
+        lat = m.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0) / req if req > 0 else 0.0
+        rows.append(f"| {k} | {100.0 * hit / max(hit + miss, 1.0):.1f} % | {hit + miss:.3g} | "
+                    f"{m.get('TCC_EA0_RDREQ_DRAM_sum', 0.0):.3g} | {m.get('TCP_TOTAL_CACHE_ACCESSES_sum', 0.0):.3g} | "
+                    f"{req:.3g} | {lat:.0f} |")
+    return "\n".join([
+        f"# L1 and L2 counters per launch, {workload}",
+        "",
+        "One `rocprofv3 --pmc` pass (mean per dispatch).  L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS);",
+        "DRAM read requests = TCC_EA0_RDREQ_DRAM (L2 misses sent to memory); L1 accesses =",
+        "TCP_TOTAL_CACHE_ACCESSES; L1-to-L2 reads = TCP_TCC_READ_REQ and their mean latency in cycles =",
+        "TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ.",
+        "",
+        "Command (repository root):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| kernel | L2 hit rate | L2 requests | DRAM read requests | L1 accesses | L1-to-L2 reads | mean L1-to-L2 read latency (cycles) |",
+        "|---|---|---|---|---|---|---|",
+        *rows,
+        "",
+    ])
+
+
 def summarize_stats(csv_path: str, workload: str, command: str) -> str:
     """Markdown summary of a rocprofv3 --kernel-trace --stats run (its kernel_stats.csv), one row per
     kernel: calls, average / min / max duration in microseconds and share of GPU time."""
@@ -574,12 +620,20 @@ def main():
     ap.add_argument("--pmc-command", default="", help="command line recorded in the traffic summary")
     ap.add_argument("--summarize-util", metavar="CSV",
                     help="write the MFMA/VALU/LDS counter summary of one rocprofv3 --pmc run to profiles/ and exit")
+    ap.add_argument("--summarize-cache", metavar="CSV",
+                    help="write the L1/L2 counter summary of one rocprofv3 --pmc run to profiles/ and exit")
     ap.add_argument("--summarize-stats", metavar="CSV",
                     help="write the summary of a rocprofv3 --kernel-trace --stats run to profiles/ and exit")
     args = ap.parse_args()
     if args.summarize_stats:
         md = summarize_stats(args.summarize_stats, args.workload, args.pmc_command)
         with open(os.path.join(ROOT, "profiles", f"kernel_stats_{args.workload}.md"), "w") as f:
+            f.write(md)
+        print(md)
+        return
+    if args.summarize_cache:
+        md = summarize_cache(args.summarize_cache, args.workload, args.pmc_command)
+        with open(os.path.join(ROOT, "profiles", f"cache_{args.workload}.md"), "w") as f:
             f.write(md)
         print(md)
         return
